@@ -1,0 +1,202 @@
+"""ctypes binding of the CPU oracle (qerl_oracle.cpp).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, the smoke check and the benchmark's CPU-baseline leg. The product
+library never imports this package, and this package never imports the product library.
+
+Arrays are numpy: bf16 tensors are uint16 bit patterns, NVFP4 codes and E4M3 scales are uint8.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qerl_oracle.cpp")
+_LIB = os.path.join(_HERE, "liboracle.so")
+CXXFLAGS = ["-std=c++17", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+
+
+def build(force: bool = False) -> str:
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["g++", *CXXFLAGS, _SRC, "-o", tmp])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P, i64, i32, dbl, f32, u16 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double,
+                                      ctypes.c_float, ctypes.c_uint16)
+        sig = {
+            "orc_bf16_value": ([u16], dbl),
+            "orc_bf16_round": ([dbl], u16),
+            "orc_bf16_round_array": ([P, i64, P], None),
+            "orc_e2m1_value": ([i32], dbl),
+            "orc_e4m3_value": ([i32], dbl),
+            "orc_e4m3_encode": ([dbl], i32),
+            "orc_nvfp4_code": ([u16, dbl], i32),
+            "orc_nvfp4_bytes": ([i64, i64], i64),
+            "orc_nvfp4_quantize": ([P, i64, i64, i64, i32, P, P, P, P], None),
+            "orc_nvfp4_dequantize": ([P, P, f32, i64, i64, P, P], None),
+            "orc_aqn_sigma": ([i32, dbl, dbl], dbl),
+            "orc_aqn_rmsnorm": ([P, i64, i64, i64, P, P, i64, f32, f32, P, P], None),
+            "orc_lora_linear": ([P, i64, i64, i64, P, P, f32, i64, P, P, i32, dbl, P], None),
+            "orc_dense_linear": ([P, i64, i64, P, i64, P], None),
+            "orc_group_advantage": ([P, i32, i32, dbl, P], None),
+            "orc_silu_mul": ([P, P, i64, P], None),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# ---- formats -----------------------------------------------------------------------------------------------------
+def bf16_value(b: int) -> float:
+    return lib().orc_bf16_value(int(b))
+
+
+def bf16_round(v: float) -> int:
+    return int(lib().orc_bf16_round(float(v)))
+
+
+def bf16_round_array(v: np.ndarray) -> np.ndarray:
+    """fp64 values -> bf16 bit patterns, one RNE rounding each."""
+    a = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(a.shape, dtype=np.uint16)
+    lib().orc_bf16_round_array(_p(a), a.size, _p(out))
+    return out
+
+
+def e2m1_value(code: int) -> float:
+    return lib().orc_e2m1_value(int(code))
+
+
+def e4m3_value(byte: int) -> float:
+    return lib().orc_e4m3_value(int(byte))
+
+
+def e4m3_encode(v: float) -> int:
+    return int(lib().orc_e4m3_encode(float(v)))
+
+
+def nvfp4_code(w_bf16: int, S: float) -> int:
+    return int(lib().orc_nvfp4_code(int(w_bf16), float(S)))
+
+
+def nvfp4_bytes(n: int, k: int) -> int:
+    return int(lib().orc_nvfp4_bytes(n, k))
+
+
+# ---- quantizer ---------------------------------------------------------------------------------------------------
+def nvfp4_quantize(w: np.ndarray, scale_mode: int = 0, s_b: np.ndarray | None = None, s_g: float | None = None):
+    """W bf16 [n, k] -> (codes u8 [n, k/2], s_b u8 [n, k/16], s_g float, flags int); canonical layout."""
+    w = _c(w, np.uint16)
+    n, k = w.shape
+    assert k % 16 == 0
+    codes = np.zeros((n, k // 2), dtype=np.uint8)
+    sb = np.zeros((n, k // 16), dtype=np.uint8) if s_b is None else _c(s_b, np.uint8).copy()
+    sg = np.array([0.0 if s_g is None else s_g], dtype=np.float32)
+    flags = np.zeros(1, dtype=np.int32)
+    lib().orc_nvfp4_quantize(_p(w), n, k, k, int(scale_mode), _p(codes), _p(sb), _p(sg), _p(flags))
+    return codes, sb, float(sg[0]), int(flags[0])
+
+
+def nvfp4_dequantize(codes: np.ndarray, s_b: np.ndarray, s_g: float):
+    """-> (exact fp64 [n, k], RNE f32 [n, k])."""
+    codes = _c(codes, np.uint8)
+    s_b = _c(s_b, np.uint8)
+    n, k2 = codes.shape
+    k = 2 * k2
+    we = np.empty((n, k), dtype=np.float64)
+    wf = np.empty((n, k), dtype=np.float32)
+    lib().orc_nvfp4_dequantize(_p(codes), _p(s_b), float(s_g), n, k, _p(we), _p(wf))
+    return we, wf
+
+
+# ---- AQN ---------------------------------------------------------------------------------------------------------
+def aqn_sigma(stage: int, start: float = 1e-2, end: float = 5e-4) -> float:
+    return float(lib().orc_aqn_sigma(int(stage), float(start), float(end)))
+
+
+def aqn_rmsnorm(x: np.ndarray, gamma: np.ndarray, noise: np.ndarray | None, sigma: float, eps: float = 1e-6,
+                noise_per_row: bool = False):
+    """x bf16 [m, d] -> (h exact fp64 [m, d], h bf16 [m, d])."""
+    x = _c(x, np.uint16)
+    m, d = x.shape
+    gamma = _c(gamma, np.uint16)
+    nz = None if noise is None else _c(noise, np.float32)
+    noise_ld = d if noise_per_row else 0
+    he = np.empty((m, d), dtype=np.float64)
+    hb = np.empty((m, d), dtype=np.uint16)
+    lib().orc_aqn_rmsnorm(_p(x), m, d, d, _p(gamma), _p(nz), noise_ld, float(sigma), float(eps), _p(he), _p(hb))
+    return he, hb
+
+
+# ---- linear ------------------------------------------------------------------------------------------------------
+def lora_linear(h: np.ndarray, codes: np.ndarray, s_b: np.ndarray, s_g: float, A: np.ndarray | None,
+                B: np.ndarray | None, lam: float) -> np.ndarray:
+    """h bf16 [m, k]; NVFP4 W [n, k] canonical; A bf16 [r, k]; B bf16 [n, r] -> y fp64 [m, n]."""
+    h = _c(h, np.uint16)
+    m, k = h.shape
+    codes = _c(codes, np.uint8)
+    s_b = _c(s_b, np.uint8)
+    n = codes.shape[0]
+    assert codes.shape[1] * 2 == k
+    r = 0
+    if A is not None:
+        A = _c(A, np.uint16)
+        B = _c(B, np.uint16)
+        r = A.shape[0]
+        assert A.shape == (r, k) and B.shape == (n, r)
+    y = np.empty((m, n), dtype=np.float64)
+    lib().orc_lora_linear(_p(h), m, k, k, _p(codes), _p(s_b), float(s_g), n, _p(A), _p(B), r, float(lam), _p(y))
+    return y
+
+
+def dense_linear(h: np.ndarray, w: np.ndarray) -> np.ndarray:
+    h = _c(h, np.uint16)
+    w = _c(w, np.uint16)
+    m, k = h.shape
+    n = w.shape[0]
+    y = np.empty((m, n), dtype=np.float64)
+    lib().orc_dense_linear(_p(h), m, k, _p(w), n, _p(y))
+    return y
+
+
+def group_advantage(rewards: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    """rewards f32 [groups, g] -> advantages fp64 [groups, g]."""
+    R = _c(rewards, np.float32)
+    groups, g = R.shape
+    adv = np.empty((groups, g), dtype=np.float64)
+    lib().orc_group_advantage(_p(R), groups, g, float(eps), _p(adv))
+    return adv
+
+
+def silu_mul(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
+    g = _c(gate, np.float64)
+    u = _c(up, np.float64)
+    out = np.empty_like(g)
+    lib().orc_silu_mul(_p(g), _p(u), g.size, _p(out))
+    return out

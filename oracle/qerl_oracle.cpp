@@ -1,0 +1,312 @@
+// Reference oracle for the QeRL rollout-decode linear layer: NVFP4 weights, bf16 LoRA, AQN-RMSNorm.
+//
+// TEST INFRASTRUCTURE ONLY. This file is a plain, slow, single-threaded CPU model of what the HIP library
+// computes. Only the test suite, the smoke check and the benchmark's CPU-baseline leg may load it; the product
+// path never calls it and shares no code, header, table or constant with it.
+//
+// Sources (cited by page title and section; the pages are web text about the QeRL paper, arXiv 2510.11696):
+//   [review]  "QeRL: When Quantized Weights Help Reinforcement Learning, and Where the Evidence Stops"
+//             (Zhongzhu Zhou, English technical review, zhongzhuzhou.org)
+//   [notes]   "QeRL 阅读笔记" (the same author's Chinese reading notes; near-parallel text)
+//
+// Arithmetic is fp64 unless a step decides an integer (an E4M3 scale code), where the pages fix no precision
+// and the step is defined in IEEE f32 so that the GPU library can take the same decision in the same precision.
+// Build: g++ -std=c++17 -O2 -ffp-contract=off (no fast-math), so every f32/f64 operation is a single IEEE op.
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <limits>
+
+namespace {
+
+// ---------------------------------------------------------------------------------------------------------------
+// Number formats.
+
+// bf16: the upper 16 bits of an IEEE binary32.
+double bf16_value(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+// Round a finite double to a binary format with `p` significand bits and minimum normal exponent `emin`
+// (values below 2^emin are rounded on the subnormal grid 2^(emin-p+1)). Round-to-nearest, ties-to-even.
+// No upper exponent bound is applied here; callers handle overflow. This is the textbook definition:
+// scale by the quantum, round to an integer with rint (current mode = nearest-even), scale back.
+double round_to_format(double v, int p, int emin) {
+  if (v == 0.0 || !std::isfinite(v)) return v;
+  int e;
+  std::frexp(std::fabs(v), &e);  // |v| = f * 2^e, f in [0.5, 1)  =>  floor(log2|v|) = e - 1
+  int ex = e - 1;
+  if (ex < emin) ex = emin;
+  double quantum = std::ldexp(1.0, ex - (p - 1));
+  double n = std::rint(v / quantum);  // v / quantum is exact (power-of-two scaling, no underflow here)
+  return n * quantum;
+}
+
+// Double -> bf16 bits, RNE, overflow to infinity, NaN kept.
+uint16_t bf16_from_double(double v) {
+  float f;
+  if (std::isnan(v)) {
+    f = std::numeric_limits<float>::quiet_NaN();
+  } else {
+    double r = round_to_format(v, 8, -126);
+    // largest finite bf16 is (2 - 2^-7) * 2^127; rounding beyond it means overflow
+    if (std::fabs(r) > 3.3895313892515355e38) r = std::copysign(INFINITY, v);
+    f = (float)r;  // exact: r is a bf16 value (or infinity)
+  }
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  return (uint16_t)(u >> 16);
+}
+
+// E2M1 (FP4): 1 sign, 2 exponent, 1 mantissa bit, exponent bias 1, no infinities or NaN.
+// Exponent field 0 is subnormal (0 or 0.5); otherwise (1 + m/2) * 2^(e-1).
+// Non-negative values {0, 0.5, 1, 1.5, 2, 3, 4, 6} [review §3.1].
+double e2m1_value(unsigned code) {
+  unsigned e = (code >> 1) & 3u, m = code & 1u;
+  double mag = (e == 0) ? 0.5 * m : std::ldexp(1.0 + 0.5 * m, (int)e - 1);
+  return (code & 8u) ? -mag : mag;
+}
+
+// E4M3 (FP8, the OCP "FN" variant): 1 sign, 4 exponent, 3 mantissa bits, bias 7, no infinities,
+// S.1111.111 is NaN, max finite 448, min subnormal 2^-9. The pages name only "FP8 E4M3" [review §3.1].
+double e4m3_value(unsigned byte) {
+  unsigned s = (byte >> 7) & 1u, e = (byte >> 3) & 15u, m = byte & 7u;
+  if (e == 15u && m == 7u) return std::numeric_limits<double>::quiet_NaN();
+  double mag = (e == 0) ? std::ldexp((double)m, -9) : std::ldexp(8.0 + m, (int)e - 10);
+  return s ? -mag : mag;
+}
+
+// Non-negative finite value -> E4M3 code, round-to-nearest-even on the E4M3 grid, saturating at 448.
+unsigned e4m3_encode_satfinite(double v) {
+  double r = round_to_format(v, 4, -6);
+  if (r > 448.0) r = 448.0;
+  if (r == 0.0) return 0u;
+  if (r < std::ldexp(1.0, -6)) return (unsigned)(r / std::ldexp(1.0, -9));  // subnormal: m * 2^-9
+  int e;
+  std::frexp(r, &e);
+  int ex = e - 1;                                              // r = (8 + m) * 2^(ex - 3)
+  unsigned m = (unsigned)(r / std::ldexp(1.0, ex - 3)) - 8u;
+  return ((unsigned)(ex + 7) << 3) | m;
+}
+
+bool bf16_is_finite(uint16_t b) { return ((b >> 7) & 0xffu) != 0xffu; }
+
+// ---------------------------------------------------------------------------------------------------------------
+// NVFP4 scales. The pages leave the choice of s_g and s_b to calibration [review §3.1]; the reading used here is
+// the amax rule: the tensor scale maps the tensor's largest magnitude onto (E2M1 max 6) x (E4M3 max 448), and each
+// 16-weight block's E4M3 scale maps that block's largest magnitude onto 6. Both divisions are IEEE f32.
+void nvfp4_scales(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, float* s_g_out, uint8_t* s_b, int* flags) {
+  float amax = 0.0f;
+  for (int64_t i = 0; i < n; ++i)
+    for (int64_t j = 0; j < k; ++j) {
+      uint16_t b = w[i * ldw + j];
+      if (!bf16_is_finite(b)) { if (flags) *flags |= 1; continue; }
+      float a = (float)std::fabs(bf16_value(b));
+      if (a > amax) amax = a;
+    }
+  float s_g = (amax > 0.0f) ? amax / 2688.0f : 1.0f;  // 2688 = 6 * 448
+  float denom = 6.0f * s_g;
+  *s_g_out = s_g;
+  for (int64_t i = 0; i < n; ++i)
+    for (int64_t b = 0; b < k / 16; ++b) {
+      float amax_b = 0.0f;
+      for (int64_t j = 0; j < 16; ++j) {
+        uint16_t v = w[i * ldw + b * 16 + j];
+        if (!bf16_is_finite(v)) continue;
+        float a = (float)std::fabs(bf16_value(v));
+        if (a > amax_b) amax_b = a;
+      }
+      float t = amax_b / denom;
+      s_b[i * (k / 16) + b] = (uint8_t)e4m3_encode_satfinite((double)t);
+    }
+}
+
+// Exact three-way comparison of the distances |a - x| and |a - y| (a, x, y >= 0 exact doubles, x and y candidate
+// grid values S*g). Subtracting in floating point is not exact when a is many binades above S (both distances then
+// round to the same value), so the comparison is made by position: two candidates on the same side of a are ordered by
+// value; for candidates on both sides, |a - lo| < |hi - a| iff 2a < lo + hi, and lo + hi = S*(g_lo + g_hi) is exact.
+// Returns -1 if x is nearer, 0 on a tie, +1 if y is nearer.
+int compare_distance(double a, double x, double y) {
+  if (x == y) return 0;
+  if (x <= a && y <= a) return x > y ? -1 : 1;
+  if (x >= a && y >= a) return x < y ? -1 : 1;
+  double lo = x < y ? x : y, hi = x < y ? y : x;
+  double two_a = 2.0 * a, sum = lo + hi;
+  if (two_a == sum) return 0;
+  bool lo_nearer = two_a < sum;
+  return (lo_nearer == (x == lo)) ? -1 : 1;
+}
+
+// Nearest grid point under fixed scales [review §3.1, argmin equation]: q = argmin over E2M1 of |w - s_g s_b q|.
+// S = s_g*s_b is exact in fp64 (24 + 4 significant bits) and so is every candidate S*g. Ties (exact midpoints) go to
+// the even code (mantissa bit 0), the usual round-half-to-even convention; the pages fix no tie rule. The sign is
+// copied from w, so a negative weight that rounds to zero keeps code 8 (-0).
+unsigned nvfp4_code(uint16_t wb, double S) {
+  if (!bf16_is_finite(wb)) return 0u;
+  double w = bf16_value(wb);
+  unsigned sign = std::signbit(w) ? 8u : 0u;
+  if (S == 0.0) return sign;
+  double a = std::fabs(w);
+  unsigned best = 0;
+  for (unsigned c = 1; c < 8; ++c) {
+    int cmp = compare_distance(a, S * e2m1_value(c), S * e2m1_value(best));
+    if (cmp < 0 || (cmp == 0 && (c & 1u) == 0u)) best = c;
+  }
+  return sign | best;
+}
+
+}  // namespace
+
+// =================================================================================================================
+extern "C" {
+
+double orc_bf16_value(uint16_t b) { return bf16_value(b); }
+uint16_t orc_bf16_round(double v) { return bf16_from_double(v); }
+void orc_bf16_round_array(const double* v, int64_t count, uint16_t* out) {
+  for (int64_t i = 0; i < count; ++i) out[i] = bf16_from_double(v[i]);
+}
+double orc_e2m1_value(int code) { return e2m1_value((unsigned)code & 15u); }
+double orc_e4m3_value(int byte) { return e4m3_value((unsigned)byte & 255u); }
+int orc_e4m3_encode(double v) { return (int)e4m3_encode_satfinite(v); }
+int orc_nvfp4_code(uint16_t w, double S) { return (int)nvfp4_code(w, S); }
+
+// Bytes of one NVFP4 tensor in the canonical layout: P/2 code bytes + P/16 scale bytes + one f32 tensor scale
+// [review §3.1, M_NVFP4 equation: 9P/16 ignoring the tensor-global scale].
+int64_t orc_nvfp4_bytes(int64_t n, int64_t k) { return n * k / 2 + n * k / 16; }
+
+// Quantize W [n x k] (bf16, row stride ldw) to NVFP4 in the canonical layout:
+//   codes [n][k/2]: byte j holds element 2j in bits 3:0 and element 2j+1 in bits 7:4;
+//   s_b   [n][k/16]: E4M3 block scale of 16 consecutive elements along k;
+//   s_g   one f32 tensor scale.
+// scale_mode 0 computes the scales by the amax rule; scale_mode 1 reads caller-fixed s_b and s_g.
+// flags bit 0 is set when a non-finite weight is seen (it is excluded from the amax and encoded as code 0).
+void orc_nvfp4_quantize(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, int scale_mode, uint8_t* codes,
+                        uint8_t* s_b, float* s_g, int* flags) {
+  if (scale_mode == 0) nvfp4_scales(w, n, k, ldw, s_g, s_b, flags);
+  for (int64_t i = 0; i < n; ++i)
+    for (int64_t j = 0; j < k; ++j) {
+      uint16_t b = w[i * ldw + j];
+      if (!bf16_is_finite(b) && flags) *flags |= 1;
+      double S = (double)(*s_g) * e4m3_value(s_b[i * (k / 16) + j / 16]);  // exact product
+      unsigned c = nvfp4_code(b, S);
+      uint8_t& byte = codes[i * (k / 2) + j / 2];
+      if ((j & 1) == 0) byte = (uint8_t)c; else byte = (uint8_t)(byte | (c << 4));
+    }
+}
+
+// Reconstruction w_hat = s_g * s_b * q [review §3.1, reconstruction equation], exact in fp64 (at most 30
+// significant bits), and its single RNE rounding to f32.
+void orc_nvfp4_dequantize(const uint8_t* codes, const uint8_t* s_b, float s_g, int64_t n, int64_t k,
+                          double* w_exact, float* w_f32) {
+  for (int64_t i = 0; i < n; ++i)
+    for (int64_t j = 0; j < k; ++j) {
+      uint8_t byte = codes[i * (k / 2) + j / 2];
+      unsigned c = (j & 1) ? (byte >> 4) : (byte & 15u);
+      double v = (double)s_g * (e4m3_value(s_b[i * (k / 16) + j / 16]) * e2m1_value(c));
+      if (w_exact) w_exact[i * k + j] = v;
+      if (w_f32) w_f32[i * k + j] = (float)v;
+    }
+}
+
+// Exponential AQN schedule with a zero warm-up stage [review §5.2, schedule equation]:
+// sigma_0 = 0, sigma_k = start * (end/start)^((k-1)/8) for k = 1..9.
+double orc_aqn_sigma(int stage, double start, double end) {
+  if (stage <= 0) return 0.0;
+  return start * std::pow(end / start, (double)(stage - 1) / 8.0);
+}
+
+// AQN-RMSNorm [review §5.1, RMSNorm identity]: u = x / sqrt(mean_j x_j^2 + eps), h_z = u (.) (w + z), with the
+// additive noise z = sigma * eps_noise on the clean scale w (replacement semantics, §9.1: w is never written).
+// noise_ld == 0 shares one noise vector [d] across all rows; otherwise row i uses noise[i * noise_ld ...].
+// h_exact gets the fp64 value; h_bf16 (if non-null) its RNE bf16 rounding, the activation the linear consumes.
+void orc_aqn_rmsnorm(const uint16_t* x, int64_t m, int64_t d, int64_t ldx, const uint16_t* gamma,
+                     const float* noise, int64_t noise_ld, float sigma, float eps, double* h_exact,
+                     uint16_t* h_bf16) {
+  for (int64_t i = 0; i < m; ++i) {
+    double ss = 0.0;
+    for (int64_t j = 0; j < d; ++j) { double v = bf16_value(x[i * ldx + j]); ss += v * v; }
+    double rstd = 1.0 / std::sqrt(ss / (double)d + (double)eps);
+    const float* z = noise ? noise + i * noise_ld : nullptr;
+    for (int64_t j = 0; j < d; ++j) {
+      double g = bf16_value(gamma[j]) + (z ? (double)sigma * (double)z[j] : 0.0);
+      double h = bf16_value(x[i * ldx + j]) * rstd * g;
+      if (h_exact) h_exact[i * d + j] = h;
+      if (h_bf16) h_bf16[i * d + j] = bf16_from_double(h);
+    }
+  }
+}
+
+// LoRA-adapted linear with an NVFP4 base [review §2.1, forward map y = W_hat x + lambda B (A x)], row-batched:
+//   y[i][o] = sum_c W_hat[o][c] h[i][c] + lambda * sum_j B[o][j] * t[i][j],   t[i][j] = sum_c A[j][c] h[i][c]
+// h [m x k] bf16 (row stride ldh), W_hat from the canonical NVFP4 layout [n x k], A [r x k] bf16, B [n x r] bf16.
+// Everything in fp64 from the exact input values; t is not rounded. A or B may be null (no LoRA branch).
+void orc_lora_linear(const uint16_t* h, int64_t m, int64_t k, int64_t ldh, const uint8_t* codes,
+                     const uint8_t* s_b, float s_g, int64_t n, const uint16_t* A, const uint16_t* B, int r,
+                     double lambda, double* y) {
+  double* t = new double[(size_t)(m * (r > 0 ? r : 1))];
+  bool lora = A && B && r > 0;
+  if (lora)
+    for (int64_t i = 0; i < m; ++i)
+      for (int j = 0; j < r; ++j) {
+        double acc = 0.0;
+        for (int64_t c = 0; c < k; ++c) acc += bf16_value(A[j * k + c]) * bf16_value(h[i * ldh + c]);
+        t[i * r + j] = acc;
+      }
+  double* wrow = new double[(size_t)k];
+  for (int64_t o = 0; o < n; ++o) {
+    for (int64_t c = 0; c < k; ++c) {
+      uint8_t byte = codes[o * (k / 2) + c / 2];
+      unsigned q = (c & 1) ? (byte >> 4) : (byte & 15u);
+      wrow[c] = (double)s_g * (e4m3_value(s_b[o * (k / 16) + c / 16]) * e2m1_value(q));
+    }
+    for (int64_t i = 0; i < m; ++i) {
+      double acc = 0.0;
+      for (int64_t c = 0; c < k; ++c) acc += wrow[c] * bf16_value(h[i * ldh + c]);
+      if (lora) {
+        double lr = 0.0;
+        for (int j = 0; j < r; ++j) lr += bf16_value(B[o * r + j]) * t[i * r + j];
+        acc += lambda * lr;
+      }
+      y[i * n + o] = acc;
+    }
+  }
+  delete[] wrow;
+  delete[] t;
+}
+
+// Dense bf16 linear y = x W^T (no quantization), used by the tests as the "BF16 LoRA" comparison baseline.
+void orc_dense_linear(const uint16_t* h, int64_t m, int64_t k, const uint16_t* w, int64_t n, double* y) {
+  for (int64_t o = 0; o < n; ++o)
+    for (int64_t i = 0; i < m; ++i) {
+      double acc = 0.0;
+      for (int64_t c = 0; c < k; ++c) acc += bf16_value(w[o * k + c]) * bf16_value(h[i * k + c]);
+      y[i * n + o] = acc;
+    }
+}
+
+// Group-relative advantage with the population standard deviation [review §2.2]:
+//   A_i = (R_i - mean) / (s_R + eps),  s_R = sqrt(mean (R_i - mean)^2), per group of g consecutive rewards.
+void orc_group_advantage(const float* rewards, int groups, int g, double eps, double* adv) {
+  for (int q = 0; q < groups; ++q) {
+    const float* R = rewards + (int64_t)q * g;
+    double mean = 0.0;
+    for (int i = 0; i < g; ++i) mean += (double)R[i];
+    mean /= (double)g;
+    double var = 0.0;
+    for (int i = 0; i < g; ++i) { double d = (double)R[i] - mean; var += d * d; }
+    double s = std::sqrt(var / (double)g);
+    for (int i = 0; i < g; ++i) adv[(int64_t)q * g + i] = ((double)R[i] - mean) / (s + eps);
+  }
+}
+
+// SwiGLU gating of the feed-forward block (the "gating multiplication and nonlinearity" before Down,
+// [review §5.1]): a = SiLU(g) * u with SiLU(v) = v / (1 + exp(-v)). fp64, element-wise.
+void orc_silu_mul(const double* gate, const double* up, int64_t count, double* out) {
+  for (int64_t i = 0; i < count; ++i) out[i] = gate[i] / (1.0 + std::exp(-gate[i])) * up[i];
+}
+
+}  // extern "C"
