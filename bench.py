@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Decode benchmark: one Qwen2.5-7B-shaped decoder layer on NVFP4 weights with rank-32 bf16 LoRA on every
+projection and two AQN-RMSNorms (hidden 3584; q/o 3584x3584; k/v 512x3584; gate/up 18944x3584; down 3584x18944).
+
+A step is one decode pass of the whole layer over a batch of M tokens: AQN-RMSNorm -> q|k|v (v broadcast to its
+query heads; attention scores excluded) -> o + residual -> AQN-RMSNorm -> gate|up + SiLU*up -> down + residual.
+Steps rotate over several copies of the layer's weights so the working set is well beyond the 256 MB Infinity Cache
+(cold HBM). All inputs are seeded synthetic tensors (synth/), W ~ N(0, 0.02) quantized on the GPU, x ~ N(0, 1),
+sigma = 1e-2.
+
+Prints one JSON line. `value` is 28-layer-equivalent decode tokens/s: M / (28 * layer step time), i.e. the rate of
+a 28-layer linear stack of this layer with attention scores excluded.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def algorithmic_bytes(shape, m):
+    """NVFP4 9NK/16 + 4, LoRA 2r(N+K), activations in/out 2M(N+K) per projection; gamma + noise 6d per norm."""
+    total = 0
+    for n, k in shape.projections().values():
+        total += 9 * n * k // 16 + 4 + 2 * shape.rank * (n + k) + 2 * m * (n + k)
+    return total + 2 * 6 * shape.hidden
+
+
+def gateup_main_bytes(shape, m):
+    """Algorithmic bytes of the gate|up main kernel: both NVFP4 weights, both LoRA-B, the activation in, a out."""
+    n, k = shape.inter, shape.hidden
+    return 2 * (9 * n * k // 16 + 4) + 2 * 2 * shape.rank * n + 2 * m * k + 2 * m * n
+
+
+def flops(shape, m):
+    return sum(2 * m * n * k + 2 * m * shape.rank * (n + k) for n, k in shape.projections().values())
+
+
+def build_layers(shape, m, copies, sigma, dev):
+    import numpy as np
+    import torch
+
+    import synth
+    from nvfp4_weight_only_amd.layer import DecoderLayer
+
+    def bf16_dev(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    s = lambda t: synth.seed_for(2, 0, t)
+    w = {nm: bf16_dev(synth.normal_bf16(s("w_" + nm), nk, std=0.02)) for nm, nk in shape.projections().items()}
+    lora = {nm: (bf16_dev(synth.normal_bf16(s("a_" + nm), (shape.rank, nk[1]), std=0.02)),
+                 bf16_dev(synth.normal_bf16(s("b_" + nm), (nk[0], shape.rank), std=0.02)))
+            for nm, nk in shape.projections().items()}
+    g1 = bf16_dev(synth.bf16_const(1.0, (shape.hidden,)))
+    g2 = bf16_dev(synth.bf16_const(1.0, (shape.hidden,)))
+    e1 = torch.from_numpy(synth.normal_f32(s("eps_norm1"), (shape.hidden,))).to(dev)
+    e2 = torch.from_numpy(synth.normal_f32(s("eps_norm2"), (shape.hidden,))).to(dev)
+    x = bf16_dev(synth.normal_bf16(s("x"), (m, shape.hidden)))
+    base = DecoderLayer.from_bf16(shape, w, lora, g1, g2, e1, e2, sigma, 2.0)
+    del w
+    layers = [base]
+    for _ in range(copies - 1):  # distinct copies of the packed weights and adapters (same values, new addresses)
+        wq = {nm: type(q)(q.codes.clone(), q.scales.clone(), q.tensor_scale.clone(), q.n, q.k, q.layout)
+              for nm, q in base.w.items()}
+        lo = {nm: (a.clone(), b.clone()) for nm, (a, b) in lora.items()}
+        layers.append(DecoderLayer(shape, wq, lo, g1, g2, e1, e2, sigma, 2.0))
+    torch.cuda.synchronize()
+    return layers, x
+
+
+def cpu_baseline(shape, m, sigma, row_stride=4, repeats=2):
+    """The oracle (single-threaded fp64 C++) timed on a row-sampled layer step: both norms in full, every
+    `row_stride`-th output row of each of the seven projections; time scaled by row_stride to the full layer."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    s = lambda t: synth.seed_for(2, 0, t)
+    x = synth.normal_bf16(s("x"), (m, shape.hidden))
+    g = synth.bf16_const(1.0, (shape.hidden,))
+    e1 = synth.normal_f32(s("eps_norm1"), (shape.hidden,))
+    e2 = synth.normal_f32(s("eps_norm2"), (shape.hidden,))
+    proj = {}
+    for nm, (n, k) in shape.projections().items():
+        w = synth.normal_bf16(s("w_" + nm), (n, k), std=0.02)[::row_stride]
+        c, sb, sg, _ = oracle.nvfp4_quantize(w)
+        A = synth.normal_bf16(s("a_" + nm), (shape.rank, k), std=0.02)
+        B = synth.normal_bf16(s("b_" + nm), (n, shape.rank), std=0.02)[::row_stride]
+        proj[nm] = (c, sb, sg, A, np.ascontiguousarray(B))
+    act = {k: synth.normal_bf16(99, (m, k)) for k in {shape.hidden, shape.q_dim, shape.inter}}
+    best = float("inf")
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        _, h1 = oracle.aqn_rmsnorm(x, g, e1, sigma)
+        for nm in ("q", "k", "v"):
+            oracle.lora_linear(h1, *proj[nm][:3], proj[nm][3], proj[nm][4], 2.0)
+        oracle.lora_linear(act[shape.q_dim], *proj["o"][:3], proj["o"][3], proj["o"][4], 2.0)
+        _, h2 = oracle.aqn_rmsnorm(x, g, e2, sigma)
+        yg = oracle.lora_linear(h2, *proj["gate"][:3], proj["gate"][3], proj["gate"][4], 2.0)
+        yu = oracle.lora_linear(h2, *proj["up"][:3], proj["up"][3], proj["up"][4], 2.0)
+        oracle.silu_mul(yg, yu)
+        oracle.lora_linear(act[shape.inter], *proj["down"][:3], proj["down"][3], proj["down"][4], 2.0)
+        best = min(best, time.perf_counter() - t0)
+    t_layer = best * row_stride
+    return {"value": m / (28 * t_layer), "unit": "tokens/s (28-layer equivalent)", "cores": 1, "kind": "oracle",
+            "sample": f"one layer step at M={m}: both norms in full, every {row_stride}th output row of all seven "
+                      f"projections (fp64, single thread), best of {repeats}; time x{row_stride} to the full layer",
+            "layer_step_s": t_layer}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--batch", type=int, default=16, help="decode tokens per step (M)")
+    ap.add_argument("--copies", type=int, default=5, help="layer weight copies rotated for cold-HBM timing")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one plain 256 MiB device copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import nvfp4_weight_only_amd as qn
+    from nvfp4_weight_only_amd.layer import QWEN25_7B
+
+    shape = QWEN25_7B
+    m = args.batch
+    sigma = float(qn.aqn_sigma(1))
+    dev = torch.device("cuda:0")
+    print(f"[bench] building {args.copies} layer copies, M={m}", file=sys.stderr, flush=True)
+    layers, x = build_layers(shape, m, args.copies, sigma, dev)
+    ws = qn.Workspace(dev)
+    bound = [L.bind(x, ws) for L in layers]
+    stream = torch.cuda.current_stream()
+
+    # the gate|up call of every step is split into its prologue and main kernel with events around the main kernel
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+
+    def step(i, timed):
+        b = bound[i % len(bound)]
+        c = b.calls
+        c[0]()
+        c[1]()
+        c[2](phases=qn.RUN_PROLOGUE_ONLY)
+        if timed:
+            ev[i][0].record(stream)
+        c[2](phases=qn.RUN_MAIN_ONLY)
+        if timed:
+            ev[i][1].record(stream)
+        c[3]()
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    print(f"[bench] timed {args.steps} steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
+
+    if args.calib_copy:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    ms_step = elapsed * 1e3 / args.steps
+    main_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / args.steps
+    step_bytes = algorithmic_bytes(shape, m)
+    gu_bytes = gateup_main_bytes(shape, m)
+    achieved = gu_bytes / (main_ms * 1e-3) / 1e9
+    result = {
+        "metric": "decode tokens/s & achieved HBM GB/s (% of peak), Qwen2.5-7B-shaped NVFP4+LoRA",
+        "value": m / (28 * ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 weights x bf16 activations (f16 MFMA operands), f32 accumulate",
+        "data": "synthetic (seeded SplitMix64/Box-Muller; W ~ N(0,0.02) quantized on device, x ~ N(0,1))",
+        "config": {"workload": "Qwen2.5-7B-shaped decoder layer at decode, NVFP4 + rank-32 bf16 LoRA on every "
+                               "projection, two AQN-RMSNorms (sigma 1e-2), attention scores excluded",
+                   "global_batch": m, "hidden": shape.hidden, "intermediate": shape.inter, "lora_rank": shape.rank,
+                   "layer_copies_rotated": args.copies, "tokens_per_s_basis": "M / (28 x layer step time)"},
+        "layer_step_us": ms_step * 1e3,
+        "step_algorithmic_bytes": step_bytes,
+        "step_achieved_GBps": step_bytes / (ms_step * 1e-3) / 1e9,
+        "step_frac_of_hbm_peak": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "step_tflops": flops(shape, m) / (ms_step * 1e-3) / 1e12,
+        "roofline": {"kernel": "k_linear gate|up (SiLU epilogue)", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "launch_us": main_ms * 1e3, "bytes_per_launch": gu_bytes},
+    }
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(shape, m, sigma)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

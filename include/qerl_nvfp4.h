@@ -1,0 +1,173 @@
+/* qerl_nvfp4.h — C ABI of the MI355X (gfx950) NVFP4 + LoRA + AQN-RMSNorm rollout-decode library.
+ *
+ * The operations follow the QeRL papers' decode linear layer as described in
+ *   "QeRL: When Quantized Weights Help Reinforcement Learning, and Where the Evidence Stops" (technical review,
+ *   zhongzhuzhou.org; cited below as [review §n]) and its Chinese counterpart "QeRL 阅读笔记".
+ *
+ * Conventions for every entry point:
+ *   - Buffer pointers are DEVICE pointers (hipMalloc / torch CUDA tensors) unless a comment says "host".
+ *     bf16 tensors are passed as uint16_t bit patterns, E2M1 codes and E4M3 scales as uint8_t.
+ *   - The caller owns every buffer. The library allocates no device memory; scratch space comes from `workspace`.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Calls only enqueue work on it and
+ *     return; results are ready when the stream reaches that point.
+ *   - Errors: arguments are validated on the host before anything is launched; a failed validation returns a
+ *     status other than QN_OK and enqueues nothing. QN_ERR_HIP reports a failed launch. Nothing is printed and
+ *     nothing aborts. Conditions seen on the device are reported through an optional device flag word.
+ *   - Thread safety: calls on different streams may run concurrently; the library keeps no mutable global state.
+ *   - Empty inputs (m == 0 or n == 0) are valid and enqueue nothing.
+ */
+#ifndef QERL_NVFP4_H
+#define QERL_NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QN_OK = 0,
+  QN_ERR_NULL = 1,        /* a required pointer is NULL */
+  QN_ERR_SHAPE = 2,       /* negative size, k % 16 != 0, leading dimension too small, mismatched projections */
+  QN_ERR_ALIGN = 3,       /* a pointer is not aligned as documented */
+  QN_ERR_VALUE = 4,       /* a scalar is out of range (negative or non-finite sigma/eps/lambda, bad enum) */
+  QN_ERR_WORKSPACE = 5,   /* workspace is NULL or smaller than nvfp4_lora_linear_workspace() */
+  QN_ERR_UNSUPPORTED = 6, /* a valid request this build does not implement (e.g. LoRA rank > 64, > 4 projections) */
+  QN_ERR_HIP = 7          /* a HIP launch failed */
+} qn_status;
+
+/* Layouts of a packed NVFP4 weight W [n x k] (row n = output channel, k = input channel).
+ *
+ * QN_LAYOUT_ROWMAJOR (the canonical layout; what the pages call packing into "the layout the kernel needs" is the
+ * tiled one below, this one is for exchange and checking):
+ *   codes  [n][k/2] bytes: byte j of row n holds element 2j in bits 3:0 and element 2j+1 in bits 7:4;
+ *   scales [n][k/16] bytes: E4M3 block scale of elements 16b .. 16b+15 of row n (blocks run along k) [review §3.1].
+ *   Total n*k/2 + n*k/16 = 9P/16 bytes [review §3.1, M_NVFP4 equation], plus the f32 tensor scale.
+ *
+ * QN_LAYOUT_TILED (what nvfp4_lora_linear reads): rows are padded to np = ceil(n/16)*16 and k to
+ * kp = ceil(k/128)*128 with zero codes and zero scales. For row group g = n/16 and k-tile t = k/128:
+ *   codes  tile (g, t) is 1024 bytes at ((g * kp/128 + t) * 1024); its 16-byte lane chunk L (L = 0..63) holds four
+ *          little-endian dwords, dword s (s = 0..3) = the 8 codes of row 16g + L%16, elements
+ *          128t + 32s + 8(L/16) .. +7, nibble order as in the row-major layout;
+ *   scales tile (g, t) is 128 bytes at ((g * kp/128 + t) * 128): byte [r][h][s] (r = 0..15, h = 0..1, s = 0..3) is the
+ *          scale of row 16g + r, elements 128t + 32s + 16h .. +15.
+ *   Sizes: nvfp4_tiled_codes_bytes(n, k) and nvfp4_tiled_scales_bytes(n, k). Codes must be 16-byte aligned,
+ *   scales 4-byte aligned. The permutation is chosen so that one 16-byte load per lane feeds four 16x16x32 MFMA
+ *   A-fragments and every wave-wide load is one contiguous 1 KiB.
+ */
+typedef enum { QN_LAYOUT_ROWMAJOR = 0, QN_LAYOUT_TILED = 1 } qn_layout;
+
+/* Output element type of a projection. */
+typedef enum { QN_BF16 = 0, QN_F32 = 1 } qn_dtype;
+
+/* Epilogues of nvfp4_lora_linear. */
+typedef enum {
+  QN_EPI_NONE = 0,
+  /* SwiGLU gating before Down [review §5.1]: requires nproj == 2 with equal n; writes silu(y_0) * y_1 into projs[0].y
+   * (projs[1].y is ignored and may be NULL). silu(v) = v / (1 + exp(-v)). */
+  QN_EPI_SILU_MUL = 1
+} qn_epilogue;
+
+/* Phase flags, OR-ed into the `epilogue` argument of nvfp4_lora_linear. A call runs a prologue (the norm/convert and
+ * the LoRA-down kernels, which fill the workspace) and then the main kernel (the weight stream and its epilogue).
+ * A caller may split one call into two to place events or other work between the phases: first PROLOGUE_ONLY, then
+ * MAIN_ONLY with the same arguments and workspace (the workspace must not be touched in between). */
+#define QN_RUN_PROLOGUE_ONLY 0x100
+#define QN_RUN_MAIN_ONLY 0x200
+
+/* AQN-RMSNorm parameters [review §5.1 and §5.2]: h = u * (gamma + sigma * noise), u = x / sqrt(mean(x^2) + eps).
+ * The clean scale gamma is only read, never written, so every call draws afresh around it (noise replacement,
+ * [review §9.1]). */
+typedef struct {
+  const uint16_t* gamma; /* [d] bf16 norm scale (device) */
+  const float* noise;    /* NULL (no noise) or standard-normal noise: [d] shared by all rows if noise_ld == 0, else
+                            row i uses noise + i * noise_ld (device, f32) */
+  int64_t noise_ld;
+  float sigma;           /* noise standard deviation for this stage, >= 0 (see aqn_sigma); 0 gives plain RMSNorm */
+  float eps;             /* >= 0, added to the mean square */
+} qn_aqn;
+
+/* One projection consuming the shared activation: y = s_g * W_hat(codes, scales) x + lambda * B (A x)
+ * [review §2.1, forward map], with optional residual and output broadcast. */
+typedef struct {
+  const uint8_t* codes;        /* QN_LAYOUT_TILED codes of W [n x k] (16-byte aligned) */
+  const uint8_t* block_scales; /* QN_LAYOUT_TILED E4M3 block scales (4-byte aligned) */
+  const float* tensor_scale;   /* one f32 s_g (device) */
+  int64_t n;                   /* output channels */
+  const uint16_t* lora_a;      /* [r][k] bf16 row-major, or NULL for no LoRA branch */
+  const uint16_t* lora_b;      /* [n][r] bf16 row-major, or NULL for no LoRA branch */
+  int32_t r;                   /* LoRA rank, 0..64 (0 = no branch) */
+  float lambda;                /* adapter multiplier, applied as is (not divided by r) */
+  void* y;                     /* output [m][ldy] of type y_dtype */
+  int32_t y_dtype;             /* qn_dtype */
+  int64_t ldy;                 /* output row stride in elements */
+  const uint16_t* residual;    /* NULL or bf16 [m][ld_res] added to y before rounding; may alias y */
+  int64_t ld_res;
+  /* Output broadcast (grouped-query attention with the score computation excluded: each key/value head's vector is
+   * copied to the `y_repeat` query heads of its group). 0 or 1 = off. When on, output element j of row i goes to
+   * y[i*ldy + ((j / head_dim) * y_repeat + g) * head_dim + j % head_dim] for g = 0..y_repeat-1. */
+  int32_t y_repeat;
+  int32_t head_dim;
+} qn_proj;
+
+/* ---------------------------------------------------------------------------------------------------------------- */
+
+/* Quantize a bf16 weight to NVFP4 [review §3.1: reconstruction w = s_g * s_b * q, q = argmin over the E2M1 grid of
+ * |w - s_g s_b q| for fixed scales].
+ *   w [n][ldw] bf16 (device), k % 16 == 0, ldw >= k.
+ *   scale_mode 0: compute the scales by the amax rule (s_g = amax(|W|) / (6 * 448) in f32, or 1 if W == 0;
+ *                 s_b = E4M3 round-to-nearest-even, saturating, of f32(amax_b / f32(6 * s_g))) and write them;
+ *   scale_mode 1: read caller-fixed scales from block_scales (same layout as the output codes) and *tensor_scale;
+ *                 they must be finite and non-negative.
+ *   Codes: nearest E2M1 value under the fixed scales; exact midpoints go to the even code (mantissa bit 0); the sign
+ *   is copied from w (a negative weight that rounds to zero gets code 8). Non-finite weights are left out of the
+ *   amax, get code 0 and set bit 0 of *d_flags (if d_flags != NULL; the caller zeroes it beforehand).
+ *   layout: qn_layout of codes and block_scales (the tiled layout also writes its zero padding).
+ *   Launches four small kernels on `stream`; tensor_scale is used as scratch until the last one. */
+qn_status nvfp4_quantize(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, int32_t scale_mode, int32_t layout,
+                         uint8_t* codes, uint8_t* block_scales, float* tensor_scale, int32_t* d_flags, void* stream);
+
+/* Bytes of the tiled codes / scales of an [n x k] weight (host, pure). */
+size_t nvfp4_tiled_codes_bytes(int64_t n, int64_t k);
+size_t nvfp4_tiled_scales_bytes(int64_t n, int64_t k);
+
+/* Reconstruct W_hat = s_g * s_b * q [review §3.1] into f32 w_out [n][ldo]: the exact product rounded once to f32
+ * (s_b * q is exact in f32). codes/block_scales in `layout`. */
+qn_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* block_scales, const float* tensor_scale, int64_t n,
+                           int64_t k, int32_t layout, float* w_out, int64_t ldo, void* stream);
+
+/* AQN-RMSNorm [review §5.1]: h = bf16(x * rstd * (gamma + sigma * noise)), rstd = 1 / sqrt(sum_j x_j^2 / d + eps),
+ * per row, f32 arithmetic, round-to-nearest-even to bf16.  x [m][ldx] bf16, h [m][ldh] bf16 (device). */
+qn_status aqn_rmsnorm(const uint16_t* x, int64_t m, int64_t d, int64_t ldx, const qn_aqn* aqn, uint16_t* h,
+                      int64_t ldh, void* stream);
+
+/* Workspace bytes nvfp4_lora_linear needs for these arguments (host, pure). */
+size_t nvfp4_lora_linear_workspace(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj);
+
+/* The rollout-decode linear layer [review §2.1 forward map, §3.2, §5.1]:
+ *   h = aqn ? AQN-RMSNorm(x) rounded to bf16 : x
+ *   y_p = s_g,p * W_hat_p h + lambda_p * B_p (A_p h) (+ residual_p), for p = 0 .. nproj-1, then the epilogue.
+ * One norm feeds all projections of the call (Q/K/V share the attention norm, Gate/Up the feed-forward norm,
+ * [review §5.1]). x [m][ldx] bf16 with ldx >= k; k % 16 == 0; 1 <= nproj <= 4; all projections share k.
+ * Activations enter the contraction as f16 after an exact per-token power-of-two rescale (see the library notes);
+ * accumulation is f32. `projs` and `aqn` are host pointers to structs holding device pointers. */
+qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const qn_aqn* aqn,
+                            const qn_proj* projs, int32_t nproj, int32_t epilogue, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Exponential AQN noise schedule [review §5.2]: sigma_0 = 0, sigma_k = start * (end/start)^((k-1)/8), k = 1..9
+ * (stages beyond 9 continue the same geometric decay). Host, pure, fp64. */
+double aqn_sigma(int32_t stage, double sigma_start, double sigma_end);
+
+/* Group-relative advantages [review §2.2]: A_i = (R_i - mean) / (pop_std + eps) over each group of g consecutive
+ * rewards. rewards, adv: [groups][g] f32 (device); fp64 arithmetic on the device, rounded to f32. */
+qn_status grpo_group_advantage(const float* rewards, int32_t groups, int32_t g, float eps, float* adv, void* stream);
+
+/* Static description of a status code (host). */
+const char* qn_status_string(qn_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QERL_NVFP4_H */

@@ -1,0 +1,258 @@
+"""Python binding of libqerl_nvfp4.so (include/qerl_nvfp4.h): argument marshalling only.
+
+Every computation runs in the HIP library. PyTorch provides device memory and the current stream. Importing this
+package without the built library raises, and calls never fall back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqerl_nvfp4.so")
+
+QN_OK, QN_ERR_NULL, QN_ERR_SHAPE, QN_ERR_ALIGN, QN_ERR_VALUE, QN_ERR_WORKSPACE, QN_ERR_UNSUPPORTED, QN_ERR_HIP = range(8)
+LAYOUT_ROWMAJOR, LAYOUT_TILED = 0, 1
+BF16, F32 = 0, 1
+EPI_NONE, EPI_SILU_MUL = 0, 1
+RUN_PROLOGUE_ONLY, RUN_MAIN_ONLY = 0x100, 0x200
+
+EXPORTS = ["nvfp4_quantize", "nvfp4_tiled_codes_bytes", "nvfp4_tiled_scales_bytes", "nvfp4_dequantize", "aqn_rmsnorm",
+           "nvfp4_lora_linear_workspace", "nvfp4_lora_linear", "aqn_sigma", "grpo_group_advantage",
+           "qn_status_string"]
+
+
+class QnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_string(status)})")
+
+
+class QnAqn(ctypes.Structure):
+    _fields_ = [("gamma", ctypes.c_void_p), ("noise", ctypes.c_void_p), ("noise_ld", ctypes.c_int64),
+                ("sigma", ctypes.c_float), ("eps", ctypes.c_float)]
+
+
+class QnProj(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("block_scales", ctypes.c_void_p), ("tensor_scale", ctypes.c_void_p),
+                ("n", ctypes.c_int64), ("lora_a", ctypes.c_void_p), ("lora_b", ctypes.c_void_p), ("r", ctypes.c_int32),
+                ("lambda_", ctypes.c_float), ("y", ctypes.c_void_p), ("y_dtype", ctypes.c_int32),
+                ("ldy", ctypes.c_int64), ("residual", ctypes.c_void_p), ("ld_res", ctypes.c_int64),
+                ("y_repeat", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() (hipcc for gfx950) first")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i64, i32, f32, f64, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_double,
+                                 ctypes.c_size_t)
+    sig = {
+        "nvfp4_quantize": ([P, i64, i64, i64, i32, i32, P, P, P, P, P], i32),
+        "nvfp4_tiled_codes_bytes": ([i64, i64], sz),
+        "nvfp4_tiled_scales_bytes": ([i64, i64], sz),
+        "nvfp4_dequantize": ([P, P, P, i64, i64, i32, P, i64, P], i32),
+        "aqn_rmsnorm": ([P, i64, i64, i64, ctypes.POINTER(QnAqn), P, i64, P], i32),
+        "nvfp4_lora_linear_workspace": ([i64, i64, ctypes.POINTER(QnProj), i32], sz),
+        "nvfp4_lora_linear": ([P, i64, i64, i64, ctypes.POINTER(QnAqn), ctypes.POINTER(QnProj), i32, i32, P, sz, P],
+                              i32),
+        "aqn_sigma": ([i32, f64, f64], f64),
+        "grpo_group_advantage": ([P, i32, i32, f32, P, P], i32),
+        "qn_status_string": ([i32], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    return L
+
+
+lib = _load()
+
+
+def status_string(s: int) -> str:
+    return lib.qn_status_string(int(s)).decode()
+
+
+def _check(status: int, where: str):
+    if status != QN_OK:
+        raise QnError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+# ---- NVFP4 weights ------------------------------------------------------------------------------------------------
+@dataclass
+class NVFP4Weight:
+    """A packed NVFP4 weight [n x k]: codes + E4M3 block scales (in `layout`) + one f32 tensor scale (device)."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    tensor_scale: torch.Tensor
+    n: int
+    k: int
+    layout: int
+
+    def nbytes(self) -> int:
+        return self.codes.numel() + self.scales.numel() + 4
+
+
+def tiled_bytes(n: int, k: int):
+    return int(lib.nvfp4_tiled_codes_bytes(n, k)), int(lib.nvfp4_tiled_scales_bytes(n, k))
+
+
+def alloc_weight(n: int, k: int, layout: int = LAYOUT_TILED, device="cuda") -> NVFP4Weight:
+    if layout == LAYOUT_TILED:
+        cb, sb = tiled_bytes(n, k)
+    else:
+        cb, sb = n * k // 2, n * k // 16
+    return NVFP4Weight(torch.zeros(max(cb, 16), dtype=torch.uint8, device=device),
+                       torch.zeros(max(sb, 4), dtype=torch.uint8, device=device),
+                       torch.zeros(1, dtype=torch.float32, device=device), n, k, layout)
+
+
+def quantize(w: torch.Tensor, layout: int = LAYOUT_TILED, scale_mode: int = 0, out: Optional[NVFP4Weight] = None,
+             flags: Optional[torch.Tensor] = None, stream=None) -> NVFP4Weight:
+    """bf16 W [n, k] (device) -> NVFP4Weight. scale_mode 1 reads the scales already in `out`."""
+    assert w.dtype == torch.bfloat16 and w.dim() == 2
+    n, k = w.shape
+    if out is None:
+        out = alloc_weight(n, k, layout, w.device)
+    _check(lib.nvfp4_quantize(_ptr(w), n, k, w.stride(0), scale_mode, out.layout, _ptr(out.codes), _ptr(out.scales),
+                              _ptr(out.tensor_scale), _ptr(flags), _stream(stream)), "nvfp4_quantize")
+    return out
+
+
+def dequantize(wq: NVFP4Weight, stream=None) -> torch.Tensor:
+    out = torch.empty(wq.n, wq.k, dtype=torch.float32, device=wq.codes.device)
+    _check(lib.nvfp4_dequantize(_ptr(wq.codes), _ptr(wq.scales), _ptr(wq.tensor_scale), wq.n, wq.k, wq.layout,
+                                _ptr(out), wq.k, _stream(stream)), "nvfp4_dequantize")
+    return out
+
+
+# ---- AQN ----------------------------------------------------------------------------------------------------------
+def aqn_sigma(stage: int, start: float = 1e-2, end: float = 5e-4) -> float:
+    return float(lib.aqn_sigma(stage, start, end))
+
+
+class AqnParams:
+    """AQN-RMSNorm parameters: keeps the device tensors alive for as long as the C struct that points at them."""
+
+    def __init__(self, gamma: torch.Tensor, noise: Optional[torch.Tensor], sigma: float, eps: float = 1e-6,
+                 noise_per_row: bool = False):
+        self.gamma, self.noise = gamma, noise
+        self.c = QnAqn()
+        self.c.gamma = gamma.data_ptr()
+        self.c.noise = None if noise is None else noise.data_ptr()
+        self.c.noise_ld = noise.shape[-1] if (noise is not None and noise_per_row) else 0
+        self.c.sigma = sigma
+        self.c.eps = eps
+
+
+def make_aqn(gamma: torch.Tensor, noise: Optional[torch.Tensor], sigma: float, eps: float = 1e-6,
+             noise_per_row: bool = False) -> AqnParams:
+    return AqnParams(gamma, noise, sigma, eps, noise_per_row)
+
+
+def aqn_rmsnorm(x: torch.Tensor, gamma: torch.Tensor, noise: Optional[torch.Tensor], sigma: float, eps: float = 1e-6,
+                noise_per_row: bool = False, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    m, d = x.shape
+    h = out if out is not None else torch.empty(m, d, dtype=torch.bfloat16, device=x.device)
+    a = make_aqn(gamma, noise, sigma, eps, noise_per_row)
+    _check(lib.aqn_rmsnorm(_ptr(x), m, d, x.stride(0), ctypes.byref(a.c), _ptr(h), h.stride(0), _stream(stream)),
+           "aqn_rmsnorm")
+    return h
+
+
+# ---- linear -------------------------------------------------------------------------------------------------------
+@dataclass
+class Projection:
+    weight: NVFP4Weight
+    y: Optional[torch.Tensor]
+    lora_a: Optional[torch.Tensor] = None
+    lora_b: Optional[torch.Tensor] = None
+    lam: float = 1.0
+    residual: Optional[torch.Tensor] = None
+    y_repeat: int = 0
+    head_dim: int = 0
+
+    def to_c(self) -> QnProj:
+        p = QnProj()
+        w = self.weight
+        p.codes, p.block_scales, p.tensor_scale = w.codes.data_ptr(), w.scales.data_ptr(), w.tensor_scale.data_ptr()
+        p.n = w.n
+        if self.lora_a is not None:
+            p.lora_a, p.lora_b, p.r = self.lora_a.data_ptr(), self.lora_b.data_ptr(), self.lora_a.shape[0]
+        p.lambda_ = self.lam
+        if self.y is not None:
+            p.y = self.y.data_ptr()
+            p.y_dtype = F32 if self.y.dtype == torch.float32 else BF16
+            p.ldy = self.y.stride(0)
+        if self.residual is not None:
+            p.residual, p.ld_res = self.residual.data_ptr(), self.residual.stride(0)
+        p.y_repeat, p.head_dim = self.y_repeat, self.head_dim
+        return p
+
+
+class Workspace:
+    """Grow-only device workspace for nvfp4_lora_linear (allocated by torch, outside the timed calls)."""
+
+    def __init__(self, device="cuda"):
+        self.device = device
+        self.buf = torch.empty(0, dtype=torch.uint8, device=device)
+
+    def get(self, nbytes: int) -> torch.Tensor:
+        if self.buf.numel() < nbytes:
+            self.buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+def linear_workspace_bytes(m: int, k: int, projs: Sequence[Projection]) -> int:
+    arr = (QnProj * len(projs))(*[p.to_c() for p in projs])
+    return int(lib.nvfp4_lora_linear_workspace(m, k, arr, len(projs)))
+
+
+class LinearCall:
+    """A prepared nvfp4_lora_linear call: the C structs are built once, so repeated launches only cross ctypes."""
+
+    def __init__(self, x: torch.Tensor, projs: Sequence[Projection], aqn: Optional[AqnParams] = None,
+                 epilogue: int = EPI_NONE, workspace: Optional[Workspace] = None):
+        self.x = x
+        self.m, self.k = x.shape
+        self.projs = list(projs)
+        self.arr = (QnProj * len(projs))(*[p.to_c() for p in projs])
+        self.aqn = aqn
+        self.epilogue = epilogue
+        need = int(lib.nvfp4_lora_linear_workspace(self.m, self.k, self.arr, len(projs)))
+        self.ws = (workspace or Workspace(x.device)).get(need)
+        self.ws_bytes = self.ws.numel()
+
+    def __call__(self, stream=None, phases: int = 0):
+        _check(lib.nvfp4_lora_linear(_ptr(self.x), self.m, self.k, self.x.stride(0),
+                                     ctypes.byref(self.aqn.c) if self.aqn is not None else None, self.arr,
+                                     len(self.projs), self.epilogue | phases, _ptr(self.ws), self.ws_bytes,
+                                     _stream(stream)),
+               "nvfp4_lora_linear")
+
+
+def lora_linear(x: torch.Tensor, projs: Sequence[Projection], aqn: Optional[AqnParams] = None, epilogue: int = EPI_NONE,
+                workspace: Optional[Workspace] = None, stream=None):
+    LinearCall(x, projs, aqn, epilogue, workspace)(stream)
+
+
+def group_advantage(rewards: torch.Tensor, eps: float = 1e-6, stream=None) -> torch.Tensor:
+    groups, g = rewards.shape
+    adv = torch.empty_like(rewards)
+    _check(lib.grpo_group_advantage(_ptr(rewards), groups, g, eps, _ptr(adv), _stream(stream)),
+           "grpo_group_advantage")
+    return adv

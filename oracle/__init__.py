@@ -200,3 +200,35 @@ def silu_mul(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
     out = np.empty_like(g)
     lib().orc_silu_mul(_p(g), _p(u), g.size, _p(out))
     return out
+
+
+# ---- decoder layer at decode (composition of the functions above) -------------------------------------------------
+def gqa_broadcast(v: np.ndarray, group: int, head_dim: int) -> np.ndarray:
+    """Each key/value head's vector repeated for the `group` query heads that share it (attention over a single key
+    position: the output of every query head in the group is that head's value)."""
+    m, kv = v.shape
+    heads = kv // head_dim
+    return np.repeat(v.reshape(m, heads, 1, head_dim), group, axis=2).reshape(m, kv * group)
+
+
+def decoder_layer(x, q, lora, gamma1, gamma2, noise1, noise2, sigma, lam, group, head_dim, eps=1e-6):
+    """Oracle of one decode layer. q[name] = (codes, s_b, s_g) canonical NVFP4; lora[name] = (A, B) bf16 or None.
+    bf16 rounding happens where the device stores bf16 tensors: the norm outputs, q/k/v, x2, SiLU(g)*u, out.
+    Returns a dict of the bf16 tensors (uint16 bit patterns)."""
+    def lin(h, name):
+        c, s, g = q[name]
+        A, B = lora.get(name, (None, None))
+        return lora_linear(h, c, s, g, A, B, lam)
+
+    _, h1 = aqn_rmsnorm(x, gamma1, noise1, sigma, eps)
+    qo = bf16_round_array(lin(h1, "q"))
+    ko = bf16_round_array(lin(h1, "k"))
+    vo = bf16_round_array(lin(h1, "v"))
+    attn = gqa_broadcast(vo, group, head_dim)
+    xf = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    x2 = bf16_round_array(lin(attn, "o") + xf)
+    _, h2 = aqn_rmsnorm(x2, gamma2, noise2, sigma, eps)
+    a = bf16_round_array(silu_mul(lin(h2, "gate"), lin(h2, "up")))
+    x2f = (x2.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    out = bf16_round_array(lin(a, "down") + x2f)
+    return {"q": qo, "k": ko, "attn": attn, "x2": x2, "a": a, "out": out}

@@ -1,0 +1,109 @@
+"""The C-ABI library loads, exports every entry point the header declares, and validates arguments on the host
+(these calls return before anything touches a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "qerl_nvfp4.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def qn():
+    import nvfp4_weight_only_amd as qn
+    return qn
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for f in ("nvfp4_quantize", "nvfp4_lora_linear", "aqn_rmsnorm"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(qn):
+    lib = ctypes.CDLL(qn.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert sorted(qn.EXPORTS) == declared_functions()
+
+
+def test_validation_errors(qn):
+    L = qn.lib
+    P = ctypes.c_void_p
+    fake = P(256)  # never dereferenced: validation fails first
+    # quantize: k % 16 != 0, negative n, bad enum, NULL, misaligned codes
+    assert L.nvfp4_quantize(fake, 16, 24, 24, 0, 1, fake, fake, fake, None, None) == qn.QN_ERR_SHAPE
+    assert L.nvfp4_quantize(fake, -1, 32, 32, 0, 1, fake, fake, fake, None, None) == qn.QN_ERR_SHAPE
+    assert L.nvfp4_quantize(fake, 16, 32, 32, 2, 1, fake, fake, fake, None, None) == qn.QN_ERR_VALUE
+    assert L.nvfp4_quantize(fake, 16, 32, 32, 0, 7, fake, fake, fake, None, None) == qn.QN_ERR_VALUE
+    assert L.nvfp4_quantize(None, 16, 32, 32, 0, 1, fake, fake, fake, None, None) == qn.QN_ERR_NULL
+    assert L.nvfp4_quantize(fake, 16, 32, 16, 0, 1, fake, fake, fake, None, None) == qn.QN_ERR_SHAPE
+    assert L.nvfp4_quantize(fake, 16, 32, 32, 0, 1, P(258), fake, fake, None, None) == qn.QN_ERR_ALIGN
+    assert L.nvfp4_quantize(fake, 0, 32, 32, 0, 1, None, None, None, None, None) == qn.QN_OK  # empty
+    # dequantize
+    assert L.nvfp4_dequantize(fake, fake, fake, 16, 20, 1, fake, 20, None) == qn.QN_ERR_SHAPE
+    assert L.nvfp4_dequantize(fake, fake, None, 16, 32, 1, fake, 32, None) == qn.QN_ERR_NULL
+    # norm: negative sigma, NaN eps, NULL aqn
+    a = qn.QnAqn(gamma=256, noise=None, noise_ld=0, sigma=-1.0, eps=1e-6)
+    assert L.aqn_rmsnorm(fake, 2, 32, 32, ctypes.byref(a), fake, 32, None) == qn.QN_ERR_VALUE
+    a.sigma, a.eps = 0.01, float("nan")
+    assert L.aqn_rmsnorm(fake, 2, 32, 32, ctypes.byref(a), fake, 32, None) == qn.QN_ERR_VALUE
+    assert L.aqn_rmsnorm(fake, 2, 32, 32, None, fake, 32, None) == qn.QN_ERR_NULL
+    # linear
+    p = qn.QnProj(codes=256, block_scales=256, tensor_scale=256, n=64, lora_a=256, lora_b=256, r=32, lambda_=2.0,
+                  y=256, y_dtype=0, ldy=64)
+    arr = (qn.QnProj * 1)(p)
+    need = L.nvfp4_lora_linear_workspace(4, 128, arr, 1)
+    assert need > 0
+    ok_args = lambda **kw: dict(dict(x=fake, m=4, k=128, ldx=128, aqn=None, projs=arr, nproj=1, epi=0, ws=P(1 << 20),
+                                     wsb=need, stream=None), **kw)
+
+    def call(**kw):
+        a_ = ok_args(**kw)
+        return L.nvfp4_lora_linear(a_["x"], a_["m"], a_["k"], a_["ldx"], a_["aqn"], a_["projs"], a_["nproj"],
+                                   a_["epi"], a_["ws"], a_["wsb"], a_["stream"])
+
+    assert call(k=120) == qn.QN_ERR_SHAPE
+    assert call(ldx=64) == qn.QN_ERR_SHAPE
+    assert call(nproj=0) == qn.QN_ERR_SHAPE
+    assert call(nproj=5) == qn.QN_ERR_UNSUPPORTED
+    assert call(epi=3) == qn.QN_ERR_VALUE
+    assert call(epi=1) == qn.QN_ERR_SHAPE  # SiLU epilogue needs two projections
+    assert call(wsb=need - 1) == qn.QN_ERR_WORKSPACE
+    assert call(ws=None) == qn.QN_ERR_WORKSPACE
+    assert call(x=None) == qn.QN_ERR_NULL
+    assert call(m=0) == qn.QN_OK  # empty batch: nothing to do
+    p.r = 65
+    arr[0] = p
+    assert call() == qn.QN_ERR_UNSUPPORTED
+    p.r = 32
+    p.codes = 264  # not 16-byte aligned
+    arr[0] = p
+    assert call() == qn.QN_ERR_ALIGN
+    p.codes = 256
+    p.lambda_ = float("inf")
+    arr[0] = p
+    assert call() == qn.QN_ERR_VALUE
+    # advantage
+    assert L.grpo_group_advantage(fake, 8, 8, -1.0, fake, None) == qn.QN_ERR_VALUE
+    assert L.grpo_group_advantage(None, 8, 8, 1e-6, fake, None) == qn.QN_ERR_NULL
+
+
+def test_host_helpers(qn):
+    assert qn.aqn_sigma(0) == 0.0 and qn.aqn_sigma(1) == 0.01
+    assert abs(qn.aqn_sigma(9) - 5e-4) < 1e-18
+    cb, sb = qn.tiled_bytes(4096, 4096)
+    assert cb == 4096 * 4096 // 2 and sb == 4096 * 4096 // 16  # no padding when n % 16 == 0 and k % 128 == 0
+    cb, sb = qn.tiled_bytes(17, 144)
+    assert cb == 2 * 2 * 1024 and sb == 2 * 2 * 128
+    for s in range(8):
+        assert qn.status_string(s)

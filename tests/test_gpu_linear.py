@@ -1,0 +1,258 @@
+"""GPU parity of AQN-RMSNorm, the NVFP4 + LoRA linear and the decode layer against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import DEV, LINEAR_TOL, bf16_bits_to_f64, dev_bf16, dev_f32, host_bf16, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def qn():
+    import nvfp4_weight_only_amd as qn
+    return qn
+
+
+class Case:
+    """Seeded inputs of one projection group: x [m, k]; weights [n_p, k]; LoRA; norm parameters."""
+
+    def __init__(self, m, ns, k, r=32, seed=0, aqn=True, sigma=1e-2, wdist="normal", lam=2.0):
+        self.m, self.ns, self.k, self.r, self.lam = m, ns, k, r, lam
+        s = lambda t, p=0: synth.seed_for(100 + seed, p, t)
+        self.x = synth.normal_bf16(s("x"), (m, k))
+        self.w, self.A, self.B = [], [], []
+        for p, n in enumerate(ns):
+            if wdist == "normal":
+                self.w.append(synth.normal_bf16(s("w_q", p), (n, k), std=0.02))
+            else:
+                self.w.append(synth.student_t4_bf16(s("w_q", p), (n, k), 0.02, 16, s("block_exp", p), -14))
+            self.A.append(synth.normal_bf16(s("a_q", p), (r, k), std=0.02) if r else None)
+            self.B.append(synth.normal_bf16(s("b_q", p), (n, r), std=0.02) if r else None)
+        self.aqn = aqn
+        self.gamma = synth.normal_bf16(s("gamma"), (k,), std=1.0) if aqn else None
+        self.noise = synth.normal_f32(s("eps_norm1"), (k,)) if aqn else None
+        self.sigma = float(np.float32(sigma))
+
+    def oracle_h(self):
+        if not self.aqn:
+            return self.x
+        return oracle.aqn_rmsnorm(self.x, self.gamma, self.noise, self.sigma, 1e-6)[1]
+
+    def oracle_y(self, p, rows=None):
+        c, sb, sg, _ = oracle.nvfp4_quantize(self.w[p])
+        B = self.B[p]
+        if rows is not None:
+            c, sb = c[rows], sb[rows]
+            B = None if B is None else B[rows]
+        return oracle.lora_linear(self.oracle_h(), c, sb, sg, self.A[p], B, self.lam)
+
+    def gpu(self, qn, y_dtype=torch.float32, epilogue=0, residual=None):
+        self.wq = [qn.quantize(dev_bf16(w), qn.LAYOUT_TILED) for w in self.w]
+        ys, projs = [], []
+        for p, n in enumerate(self.ns):
+            y = torch.full((self.m, n), float("nan"), dtype=y_dtype, device=DEV)
+            ys.append(y)
+            A = dev_bf16(self.A[p]) if self.r else None
+            B = dev_bf16(self.B[p]) if self.r else None
+            projs.append(qn.Projection(self.wq[p], y, A, B, self.lam, residual=residual))
+        aqn = qn.make_aqn(dev_bf16(self.gamma), dev_f32(self.noise), self.sigma, 1e-6) if self.aqn else None
+        self.xd = dev_bf16(self.x)
+        qn.lora_linear(self.xd, projs, aqn, epilogue)
+        torch.cuda.synchronize()
+        return ys
+
+
+@pytest.mark.parametrize("m", [1, 2, 5, 16, 17, 40, 64, 65, 128, 130])
+def test_linear_batch_sizes(qn, m):
+    c = Case(m, [200], 1024, seed=m)
+    y = c.gpu(qn)[0].cpu().numpy()
+    assert rel_err(y, c.oracle_y(0)) <= LINEAR_TOL
+
+
+@pytest.mark.parametrize("n,k", [(16, 128), (40, 272), (1000, 144), (33, 3584), (512, 1040)])
+def test_linear_ragged_shapes(qn, n, k):
+    for m in (1, 16):
+        c = Case(m, [n], k, seed=n + k)
+        y = c.gpu(qn)[0].cpu().numpy()
+        assert rel_err(y, c.oracle_y(0)) <= LINEAR_TOL, (m, n, k)
+
+
+def test_linear_three_projections_share_norm(qn):
+    """q | k | v in one call, one AQN-RMSNorm feeding all three."""
+    c = Case(8, [256, 64, 64], 512, seed=3)
+    ys = c.gpu(qn)
+    for p in range(3):
+        assert rel_err(ys[p].cpu().numpy(), c.oracle_y(p)) <= LINEAR_TOL, p
+
+
+@pytest.mark.parametrize("r", [0, 4, 8, 12, 32, 64])
+def test_linear_lora_ranks(qn, r):
+    c = Case(4, [128], 256, r=r, seed=r)
+    y = c.gpu(qn)[0].cpu().numpy()
+    assert rel_err(y, c.oracle_y(0)) <= LINEAR_TOL
+
+
+def test_linear_no_norm_heavy_tail(qn):
+    c = Case(16, [256], 5120, aqn=False, wdist="student", seed=9)
+    y = c.gpu(qn)[0].cpu().numpy()
+    assert rel_err(y, c.oracle_y(0)) <= LINEAR_TOL
+
+
+def test_linear_lambda_zero_is_base(qn):
+    c = Case(3, [64], 256, lam=0.0, seed=4)
+    y = c.gpu(qn)[0].cpu().numpy()
+    h = c.oracle_h()
+    cc, sb, sg, _ = oracle.nvfp4_quantize(c.w[0])
+    assert rel_err(y, oracle.lora_linear(h, cc, sb, sg, None, None, 0.0)) <= LINEAR_TOL
+
+
+def test_linear_silu_mul_epilogue(qn):
+    c = Case(16, [384, 384], 512, seed=5)
+    ys = c.gpu(qn, epilogue=qn.EPI_SILU_MUL)
+    ref = oracle.silu_mul(c.oracle_y(0), c.oracle_y(1))
+    assert rel_err(ys[0].cpu().numpy(), ref) <= LINEAR_TOL
+
+
+def test_linear_residual(qn):
+    m, n, k = 8, 256, 256
+    res = synth.normal_bf16(55, (m, n))
+    c = Case(m, [n], k, seed=6)
+    y = c.gpu(qn, residual=dev_bf16(res))[0].cpu().numpy()
+    assert rel_err(y, c.oracle_y(0) + bf16_bits_to_f64(res)) <= LINEAR_TOL
+
+
+def test_linear_bf16_output_is_rounded_f32(qn):
+    """The bf16 output is the RNE rounding of the same kernel's f32 result (the kernel is deterministic)."""
+    c = Case(16, [256], 1024, seed=7)
+    y32 = c.gpu(qn, torch.float32)[0]
+    y16 = c.gpu(qn, torch.bfloat16)[0]
+    assert torch.equal(y16, y32.to(torch.bfloat16))
+
+
+def test_linear_gqa_broadcast(qn):
+    m, kv, hd, group, k = 4, 256, 128, 3, 384
+    c = Case(m, [kv], k, seed=8)
+    wq = qn.quantize(dev_bf16(c.w[0]), qn.LAYOUT_TILED)
+    y = torch.full((m, kv * group), float("nan"), dtype=torch.float32, device=DEV)
+    aqn = qn.make_aqn(dev_bf16(c.gamma), dev_f32(c.noise), c.sigma, 1e-6)
+    qn.lora_linear(dev_bf16(c.x), [qn.Projection(wq, y, dev_bf16(c.A[0]), dev_bf16(c.B[0]), c.lam, y_repeat=group,
+                                                 head_dim=hd)], aqn)
+    ref = oracle.gqa_broadcast(c.oracle_y(0), group, hd)
+    assert rel_err(y.cpu().numpy(), ref) <= LINEAR_TOL
+
+
+def test_linear_per_row_noise(qn):
+    m, n, k = 5, 128, 256
+    c = Case(m, [n], k, seed=10)
+    noise = synth.normal_f32(77, (m, k))
+    wq = qn.quantize(dev_bf16(c.w[0]), qn.LAYOUT_TILED)
+    y = torch.empty(m, n, dtype=torch.float32, device=DEV)
+    aqn = qn.make_aqn(dev_bf16(c.gamma), dev_f32(noise), c.sigma, 1e-6, noise_per_row=True)
+    qn.lora_linear(dev_bf16(c.x), [qn.Projection(wq, y, dev_bf16(c.A[0]), dev_bf16(c.B[0]), c.lam)], aqn)
+    _, h = oracle.aqn_rmsnorm(c.x, c.gamma, noise, c.sigma, 1e-6, noise_per_row=True)
+    cc, sb, sg, _ = oracle.nvfp4_quantize(c.w[0])
+    assert rel_err(y.cpu().numpy(), oracle.lora_linear(h, cc, sb, sg, c.A[0], c.B[0], c.lam)) <= LINEAR_TOL
+
+
+def test_linear_deterministic(qn):
+    c = Case(16, [512], 2048, seed=11)
+    a = c.gpu(qn)[0].clone()
+    b = c.gpu(qn)[0]
+    assert torch.equal(a, b)
+
+
+def test_aqn_rmsnorm_parity(qn):
+    m, d = 16, 3584
+    x = synth.normal_bf16(61, (m, d))
+    gamma = synth.normal_bf16(62, (d,), std=1.0)
+    noise = synth.normal_f32(63, (d,))
+    sigma = float(np.float32(oracle.aqn_sigma(3)))
+    h = host_bf16(qn.aqn_rmsnorm(dev_bf16(x), dev_bf16(gamma), dev_f32(noise), sigma, 1e-6))
+    he, hb = oracle.aqn_rmsnorm(x, gamma, noise, sigma, 1e-6)
+    hv = bf16_bits_to_f64(h)
+    # f32 arithmetic then one bf16 rounding: within one bf16 ulp (2^-7 relative) of the exact value, and equal to
+    # the oracle's rounding except where the exact value sits within f32 error of a rounding boundary
+    assert np.all(np.abs(hv - he) <= 2.0 ** -7 * np.abs(he) + 1e-30)
+    assert np.mean(h == hb) > 0.999
+    # sigma = 0 is plain RMSNorm
+    h0 = host_bf16(qn.aqn_rmsnorm(dev_bf16(x), dev_bf16(gamma), None, 0.0, 1e-6))
+    he0, _ = oracle.aqn_rmsnorm(x, gamma, None, 0.0, 1e-6)
+    assert np.all(np.abs(bf16_bits_to_f64(h0) - he0) <= 2.0 ** -7 * np.abs(he0) + 1e-30)
+
+
+def test_empty_batch(qn):
+    c = Case(1, [64], 128, seed=12)
+    wq = qn.quantize(dev_bf16(c.w[0]), qn.LAYOUT_TILED)
+    y = torch.empty(0, 64, dtype=torch.float32, device=DEV)
+    x = torch.empty(0, 128, dtype=torch.bfloat16, device=DEV)
+    qn.lora_linear(x, [qn.Projection(wq, y)])
+    torch.cuda.synchronize()
+
+
+# ---- full-size shapes, sampled outputs ------------------------------------------------------------------------------
+def sampled_rows(n, count=96, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, count)]))
+    return rows
+
+
+@pytest.mark.parametrize("m,n,k,aqn", [
+    (1, 4096, 4096, True),       # single 4096 x 4096 projection, one token
+    (16, 18944, 3584, True),     # 7B gate shape at decode batch 16
+    (8, 3584, 18944, False),     # 7B down shape
+    (32, 5120, 5120, True),      # 32B q/o shape at batch 32
+    (128, 1024, 5120, True),     # 32B k/v shape at batch 128
+])
+def test_linear_full_size_sampled(qn, m, n, k, aqn):
+    c = Case(m, [n], k, seed=n % 97, aqn=aqn)
+    y = c.gpu(qn)[0].cpu().numpy()
+    rows = sampled_rows(n)
+    ref = c.oracle_y(0, rows)
+    assert rel_err(y[:, rows], ref) <= LINEAR_TOL
+
+
+# ---- decoder layer ---------------------------------------------------------------------------------------------------
+def make_layer_inputs(shape, m, seed, sigma):
+    s = lambda t: synth.seed_for(2, seed, t)
+    w = {nm: synth.normal_bf16(s("w_" + nm), nk, std=0.02) for nm, nk in shape.projections().items()}
+    lora = {nm: (synth.normal_bf16(s("a_" + nm), (shape.rank, nk[1]), std=0.02),
+                 synth.normal_bf16(s("b_" + nm), (nk[0], shape.rank), std=0.02)) for nm, nk in shape.projections().items()}
+    x = synth.normal_bf16(s("x"), (m, shape.hidden))
+    g1 = synth.bf16_const(1.0, (shape.hidden,))
+    g2 = synth.bf16_const(1.0, (shape.hidden,))
+    e1 = synth.normal_f32(s("eps_norm1"), (shape.hidden,))
+    e2 = synth.normal_f32(s("eps_norm2"), (shape.hidden,))
+    return w, lora, x, g1, g2, e1, e2, float(np.float32(sigma))
+
+
+def bf16_chain_ok(got, ref):
+    """A bf16 result of a chain with bf16 storage between ops: within two bf16 ulps (a rounding decision may flip
+    at each of the two last storage points) plus the linear bar, and tight (within the linear bar) almost
+    everywhere."""
+    g = bf16_bits_to_f64(got)
+    r = bf16_bits_to_f64(ref)
+    scale = np.abs(r).max()
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(r), 1e-30))) - 7)
+    err = np.abs(g - r)
+    return bool(np.all(err <= 2 * ulp + LINEAR_TOL * scale)) and float(np.mean(err <= LINEAR_TOL * scale)) > 0.99
+
+
+@pytest.mark.parametrize("m", [1, 8, 16])
+def test_decoder_layer_small(qn, m):
+    from nvfp4_weight_only_amd.layer import DecoderLayer, LayerShape
+    shape = LayerShape(hidden=512, q_dim=512, kv_dim=128, inter=1024, head_dim=128, rank=32)
+    w, lora, x, g1, g2, e1, e2, sigma = make_layer_inputs(shape, m, 1, 1e-2)
+    layer = DecoderLayer.from_bf16(shape, {k: dev_bf16(v) for k, v in w.items()},
+                                   {k: (dev_bf16(a), dev_bf16(b)) for k, (a, b) in lora.items()},
+                                   dev_bf16(g1), dev_bf16(g2), dev_f32(e1), dev_f32(e2), sigma, 2.0)
+    bound = layer.bind(dev_bf16(x))
+    bound()
+    torch.cuda.synchronize()
+    qref = {k: oracle.nvfp4_quantize(v)[:3] for k, v in w.items()}
+    ref = oracle.decoder_layer(x, qref, lora, g1, g2, e1, e2, sigma, 2.0, shape.group, shape.head_dim)
+    for name in ("q", "k", "attn", "x2", "a", "out"):
+        got = host_bf16(getattr(bound, name))
+        assert bf16_chain_ok(got, ref[name]), name
