@@ -10,16 +10,19 @@
 //                      h = x), written row-major for the LoRA branch, plus the MFMA B-fragments of h as f16 scaled by a
 //                      per-token power of two 2^p (exact: bf16 has 8 significant bits, f16 11, and the scale keeps the
 //                      token's largest magnitude in [2^14, 2^15), so every element above 2^-32 of it converts exactly).
-//   P2 k_lora_down     t = A h with bf16 16x16x32 MFMAs (8 waves split k), written as the B-operand fragments of the
-//                      LoRA-up MFMA: t = t_hi + t_lo, both bf16 (t - t_hi is exact in f32; 16 significant bits kept).
+//   P2 k_lora_down     t = A h with bf16 16x16x32 MFMAs over at most 8 k-chunks per projection and token tile; each
+//                      chunk's partial sums are stored in the layout of the LoRA-up MFMA's B-fragments.
 //   L  k_linear        streams the tiled NVFP4 weight once: per lane one 16-byte load of codes (32 weights) and one
 //                      dword of block scales per 128-wide k-tile; FP4 -> f16 with the hardware converter (scale 2^8),
 //                      times the E4M3 scale reinterpreted as f16 (byte << 7 is the E4M3 value * 2^-8, exact for
 //                      normals and subnormals) gives s_b * q exactly in f16; f16 16x16x32 MFMAs accumulate in f32.
-//                      Waves split k; partials meet in LDS. The LoRA term B (t_hi + t_lo) is two bf16 MFMAs per row
-//                      group. The epilogue applies s_g, the per-token 2^-p, lambda, residual, SiLU(gate) * up,
+//                      Waves split k; partials meet in LDS. The LoRA term: the chunk partials of t are summed in a fixed
+//                      order (so results do not depend on scheduling) and split t = t_hi + t_lo, both bf16 (t - t_hi is
+//                      exact in f32, 16 significant bits kept); B t is then two bf16 MFMAs per row group. The epilogue applies s_g, the per-token 2^-p, lambda, residual, SiLU(gate) * up,
 //                      broadcast and rounding. Everything the epilogue reads is fetched before the weight stream.
 #include <cmath>
+#include <cstdio>
+#include <cstdlib>
 
 #include "qn_device.hpp"
 #include "qn_norm.hpp"
@@ -55,15 +58,20 @@ struct LinearArgs {
   int64_t tok0;            // first token of this launch
   const u32x4* xs;         // activation fragments, [tile][kp/128][4][64] x 16 bytes
   const float* xunscale;   // [m] 2^-p per token
-  const u32x4* t_frag;     // LoRA-up B-fragments, [nproj][tile][kRankChunks][hi, lo][64] x 16 bytes
+  const u32x4* t_part;     // LoRA-down partials, [nproj][tile][kRankChunks][ks][64 lanes][8 f32]
+  int32_t ks;              // LoRA-down k-chunks
 };
 
 // Workspace carve-up (256-byte aligned regions).
 struct Workspace {
-  size_t xs, xunscale, h, t_frag, t_part, cnt, total;
+  size_t xs, xunscale, h, t_part, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// LoRA-down k-chunks: as few as possible, each a multiple of 32 and at most 4096 wide (one pass of the 16 waves)
+inline int64_t lora_chunks(int64_t k) { return ceil_div(k, 4096); }
+inline int64_t lora_chunk_width(int64_t k) { return ceil_div(ceil_div(k, lora_chunks(k)), 32) * 32; }
 
 Workspace workspace_layout(int64_t m, int64_t k, int32_t nproj) {
   const int64_t kp = ceil_div(k, kKTile) * kKTile;
@@ -73,9 +81,7 @@ Workspace workspace_layout(int64_t m, int64_t k, int32_t nproj) {
   w.xs = off;       off = align256(off + (size_t)mp * kp * 2);
   w.xunscale = off; off = align256(off + (size_t)mp * 4);
   w.h = off;        off = align256(off + (size_t)mp * kp * 2);
-  w.t_frag = off;   off = align256(off + (size_t)nproj * (mp / 16) * kRankChunks * 2 * kWave * 16);
-  w.t_part = off;   off = align256(off + (size_t)nproj * (mp / 16) * (kMaxRank / 16) * ceil_div(k, 1024) * 256 * 4);
-  w.cnt = off;      off = align256(off + (size_t)nproj * (mp / 16) * (kMaxRank / 16) * 4);
+  w.t_part = off;   off = align256(off + (size_t)nproj * (mp / 16) * kRankChunks * lora_chunks(k) * kWave * 32);
   w.total = off;
   return w;
 }
@@ -91,13 +97,9 @@ __global__ void __launch_bounds__(NT) k_norm_convert(const uint16_t* __restrict_
                                                      int64_t kp, int has_aqn, const uint16_t* gamma, const float* noise,
                                                      int64_t noise_ld, float sigma, float eps, int vec_in, int vec_g,
                                                      int vec_z, uint16_t* __restrict__ h_out, u32x4* __restrict__ xs,
-                                                     float* __restrict__ xunscale, uint32_t* __restrict__ lora_cnt,
-                                                     int n_cnt) {
+                                                     float* __restrict__ xunscale) {
   __shared__ float red[NT / kWave];
   const int64_t row = blockIdx.x;
-  // the LoRA-down completion counters of this call start at zero (the next kernel on the stream counts them up)
-  if (row == 0)
-    for (int i = threadIdx.x; i < n_cnt; i += NT) lora_cnt[i] = 0u;
   RowRegs<CPT> r;
   load_row<NT, CPT>(x + row * ldx, k, vec_in != 0, r);
   if (has_aqn) {
@@ -157,29 +159,27 @@ __global__ void __launch_bounds__(NT) k_norm_convert(const uint16_t* __restrict_
 }
 
 // ------------------------------------------------------------------------------------------------------------------
-// P2: t[p][tok][j] = sum_k A_p[j][k] * h[tok][k]. Workgroup (token tile, projection p, rank group jg of 16, k chunk
-// kc of 1024): 4 waves take the chunk's 32-wide slices (8 each, in two batches of 4 in flight) with bf16 16x16x32
-// MFMAs and meet in LDS; the 16x16 partial goes to t_part. The last workgroup of a (p, tile, jg) to finish (counted
-// with a device-scope atomic after a release fence) sums the partials in chunk order, so the result does not depend
-// on scheduling, and writes its rank rows of the LoRA-up B-fragments (hi and lo bf16 parts; ranks past r are 0).
-constexpr int kLoraChunk = 1024;
+// P2: partial t over one k-chunk, t_c[p][tok][j] = sum over k in chunk c of A_p[j][k] * h[tok][k].
+// Workgroup (token tile, projection p, rank group jg of 16, chunk c): 16 waves take the chunk's 32-wide slices, issue
+// all their loads (at most 8 slices each), run bf16 16x16x32 MFMAs and meet in LDS. The 16 x 16 partial is stored
+// where the LoRA-up B-fragment wants it: element (rank j, token tok) of chunk c at
+// [p][tile][j / 32][c][lane = ((j % 32) / 8) * 16 + tok][j % 8]. Ranks past r come out 0 (their A rows read as 0).
+constexpr int kLoraWaves = 16;
+constexpr int kLoraSlicesPerWave = 8;
 
 struct LoraDownArgs {
   const uint16_t* A[kMaxProj];
   int32_t r[kMaxProj];
   int32_t nproj, jgmax, ks;
-  int64_t m, k, kp, ntiles;
+  int64_t m, k, kp, kc_width;
   const uint16_t* h;  // [mp][kp]
-  float* t_part;      // [nproj][ntiles][jgmax][ks][16 ranks][16 tokens]
-  uint32_t* cnt;      // [nproj][ntiles][jgmax]
-  u32x4* t_frag;
+  float* t_part;
 };
 
-__global__ void __launch_bounds__(256) k_lora_down(LoraDownArgs a) {
-  __shared__ f32x4 red[4][kWave];
-  __shared__ uint32_t last;
+__global__ void __launch_bounds__(kLoraWaves * kWave) k_lora_down(LoraDownArgs a) {
+  __shared__ f32x4 red[kLoraWaves][kWave];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
-  const int64_t tile = blockIdx.x;
+  const int64_t tile = blockIdx.x, ntiles = gridDim.x;
   int job = blockIdx.y;
   const int kc = job % a.ks;
   job /= a.ks;
@@ -188,49 +188,33 @@ __global__ void __launch_bounds__(256) k_lora_down(LoraDownArgs a) {
   const int r = a.r[p];
   const int j = jg * 16 + lane % 16;
   const int64_t tok = tile * 16 + lane % 16;
+  const int64_t k0 = kc * a.kc_width, k1 = k0 + a.kc_width < a.k ? k0 + a.kc_width : a.k;
+  u32x4 av[kLoraSlicesPerWave], bv[kLoraSlicesPerWave];
+#pragma unroll
+  for (int i = 0; i < kLoraSlicesPerWave; ++i) {
+    const int64_t kk = k0 + (int64_t)(i * kLoraWaves + wave) * 32 + (lane / 16) * 8;
+    const bool in = kk < k1;
+    av[i] = *((in && j < r) ? reinterpret_cast<const u32x4*>(a.A[p] + (int64_t)j * a.k + kk) : kZero16);
+    bv[i] = *((in && tok < a.m) ? reinterpret_cast<const u32x4*>(a.h + tok * a.kp + kk) : kZero16);
+  }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    u32x4 av[4], bv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t kk = (int64_t)kc * kLoraChunk + ((b * 4 + i) * 4 + wave) * 32 + (lane / 16) * 8;
-      const bool in = kk < a.k;
-      av[i] = *((in && j < r) ? reinterpret_cast<const u32x4*>(a.A[p] + (int64_t)j * a.k + kk) : kZero16);
-      bv[i] = *((in && tok < a.m) ? reinterpret_cast<const u32x4*>(a.h + tok * a.kp + kk) : kZero16);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[i]), __builtin_bit_cast(bf16x8, bv[i]),
-                                                    acc, 0, 0, 0);
-  }
+  for (int i = 0; i < kLoraSlicesPerWave; ++i)
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[i]), __builtin_bit_cast(bf16x8, bv[i]),
+                                                  acc, 0, 0, 0);
   red[wave][lane] = acc;
   __syncthreads();
-  // thread t holds partial element (rank row jr = t / 16, token column tc = t % 16); D lane = (jr/4)*16 + tc, q = jr%4
-  const int jr = threadIdx.x / 16, tc = threadIdx.x % 16;
-  const int src = (jr / 4) * 16 + tc, q = jr % 4;
-  float v = red[0][src][q];
+  if (threadIdx.x < 256) {
+    // thread (rank row jr, token column tc); D lane (jr/4)*16 + tc, element jr%4
+    const int jr = threadIdx.x / 16, tc = threadIdx.x % 16;
+    const int src = (jr / 4) * 16 + tc, q = jr % 4;
+    float v = 0.f;
 #pragma unroll
-  for (int w = 1; w < 4; ++w) v += red[w][src][q];
-  const int64_t grp = ((int64_t)p * a.ntiles + tile) * a.jgmax + jg;
-  a.t_part[(grp * a.ks + kc) * 256 + threadIdx.x] = v;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) last = atomicAdd(&a.cnt[grp], 1u) == (uint32_t)(a.ks - 1);
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  float t = 0.f;
-  for (int c = 0; c < a.ks; ++c) t += __builtin_nontemporal_load(&a.t_part[(grp * a.ks + c) * 256 + threadIdx.x]);
-  // B-fragment element of (rank jj = jg*16 + jr, token tc): chunk jc = jj/32, lane (jj%32/8)*16 + tc, element jj%8
-  const int jj = jg * 16 + jr;
-  const int jc = jj / 32, L = ((jj % 32) / 8) * 16 + tc, e = jj % 8;
-  const uint16_t th = f32_to_bf16(t);
-  const uint16_t tl = f32_to_bf16(t - bf16_to_f32(th));  // t - th is exact in f32
-  uint16_t* dst = reinterpret_cast<uint16_t*>(a.t_frag + ((((int64_t)p * a.ntiles + tile) * kRankChunks + jc) * 2) *
-                                                             kWave + L);
-  dst[e] = th;
-  dst[kWave * 8 + e] = tl;
+    for (int w = 0; w < kLoraWaves; ++w) v += red[w][src][q];
+    const int jj = jg * 16 + jr;
+    const int L = ((jj % 32) / 8) * 16 + tc;
+    a.t_part[((((int64_t)p * ntiles + tile) * kRankChunks + jj / 32) * a.ks + kc) * kWave * 8 + L * 8 + jj % 8] = v;
+  }
 }
 
 // ------------------------------------------------------------------------------------------------------------------
@@ -319,9 +303,16 @@ struct LoraOps {
   u32x4 thi[kRankChunks][TMT], tlo[kRankChunks][TMT];
 };
 
+// LoRA-up operands in two steps: issue (rows of B and the raw k-chunk partials of t, before the weight stream) and
+// finish (after it: partials summed in chunk order, split into bf16 hi and lo parts).
 template <int TMT>
-__device__ __forceinline__ void load_lora(LoraOps<TMT>& o, const ProjArgs& P, int p, int64_t rg, int lane,
-                                          const LinearArgs& a, int64_t tile0, int64_t ntiles) {
+struct LoraRaw {
+  u32x4 part[kRankChunks][TMT][2];  // the first k-chunk's partial (the whole t when k <= 4096)
+};
+
+template <int TMT>
+__device__ __forceinline__ void issue_lora(LoraOps<TMT>& o, LoraRaw<TMT>& raw, const ProjArgs& P, int p, int64_t rg,
+                                           int lane, const LinearArgs& a, int64_t tile0, int64_t ntiles) {
   const int64_t n = rg * 16 + lane % 16;
 #pragma unroll
   for (int jc = 0; jc < kRankChunks; ++jc) {
@@ -341,11 +332,47 @@ __device__ __forceinline__ void load_lora(LoraOps<TMT>& o, const ProjArgs& P, in
 #pragma unroll
     for (int tt = 0; tt < TMT; ++tt) {
       const bool ok = jc * 32 < P.r && tile0 + tt < ntiles;
-      const u32x4* base = a.t_frag + (((int64_t)p * ntiles + tile0 + tt) * kRankChunks + jc) * 2 * kWave + lane;
-      o.thi[jc][tt] = *(ok ? base : kZero16);
-      o.tlo[jc][tt] = *(ok ? base + kWave : kZero16);
+      const u32x4* base = a.t_part + ((((int64_t)p * ntiles + tile0 + tt) * kRankChunks + jc) * a.ks) * kWave * 2 +
+                          lane * 2;
+      raw.part[jc][tt][0] = *(ok ? base : kZero16);
+      raw.part[jc][tt][1] = *(ok ? base + 1 : kZero16);
     }
   }
+}
+
+template <int TMT>
+__device__ __forceinline__ void finish_lora(LoraOps<TMT>& o, const LoraRaw<TMT>& raw, const ProjArgs& P, int p,
+                                            int lane, const LinearArgs& a, int64_t tile0, int64_t ntiles) {
+#pragma unroll
+  for (int jc = 0; jc < kRankChunks; ++jc)
+#pragma unroll
+    for (int tt = 0; tt < TMT; ++tt) {
+      f32x4 s0 = __builtin_bit_cast(f32x4, raw.part[jc][tt][0]);
+      f32x4 s1 = __builtin_bit_cast(f32x4, raw.part[jc][tt][1]);
+      const bool ok = jc * 32 < P.r && tile0 + tt < ntiles;
+      const u32x4* base = a.t_part + ((((int64_t)p * ntiles + tile0 + tt) * kRankChunks + jc) * a.ks) * kWave * 2 +
+                          lane * 2;
+      for (int c = 1; c < a.ks; ++c) {  // k > 4096: the remaining chunks, in chunk order
+        s0 += __builtin_bit_cast(f32x4, *(ok ? base + (int64_t)c * kWave * 2 : kZero16));
+        s1 += __builtin_bit_cast(f32x4, *(ok ? base + (int64_t)c * kWave * 2 + 1 : kZero16));
+      }
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float t = e < 4 ? s0[e] : s1[e - 4];
+        const uint32_t th = f32_to_bf16(t);
+        const uint32_t tl = f32_to_bf16(t - bf16_to_f32((uint16_t)th));  // t - th is exact in f32
+        if (e % 2 == 0) {
+          hi[e / 2] = th;
+          lo[e / 2] = tl;
+        } else {
+          hi[e / 2] |= th << 16;
+          lo[e / 2] |= tl << 16;
+        }
+      }
+      o.thi[jc][tt] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+      o.tlo[jc][tt] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    }
 }
 
 template <int TMT>
@@ -413,11 +440,13 @@ __global__ void __launch_bounds__(W * kWave) k_linear(LinearArgs a) {
   // LoRA-up: wave w owns the slots rr with rr % W == w
   constexpr int kLoraSlots = (R + W - 1) / W;
   LoraOps<TMT> lops[kLoraSlots];
+  LoraRaw<TMT> lraw[kLoraSlots];
   if (kEarlyLora) {
 #pragma unroll
     for (int q = 0; q < kLoraSlots; ++q) {
       const int rr = wave + q * W;
-      if (rr < R && a.p[pj[rr]].r > 0) load_lora<TMT>(lops[q], a.p[pj[rr]], pj[rr], rg[rr], lane, a, tile0, ntiles);
+      if (rr < R && a.p[pj[rr]].r > 0)
+        issue_lora<TMT>(lops[q], lraw[q], a.p[pj[rr]], pj[rr], rg[rr], lane, a, tile0, ntiles);
     }
   }
 
@@ -472,7 +501,8 @@ __global__ void __launch_bounds__(W * kWave) k_linear(LinearArgs a) {
 #pragma unroll
     for (int tt = 0; tt < TMT; ++tt) la[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (a.p[pj[rr]].r > 0) {
-      if (!kEarlyLora) load_lora<TMT>(lops[q], a.p[pj[rr]], pj[rr], rg[rr], lane, a, tile0, ntiles);
+      if (!kEarlyLora) issue_lora<TMT>(lops[q], lraw[q], a.p[pj[rr]], pj[rr], rg[rr], lane, a, tile0, ntiles);
+      finish_lora<TMT>(lops[q], lraw[q], a.p[pj[rr]], pj[rr], lane, a, tile0, ntiles);
       lora_mfma<TMT>(lops[q], la);
     }
 #pragma unroll
@@ -642,14 +672,11 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
   u32x4* xs = reinterpret_cast<u32x4*>(ws + wl.xs);
   float* xunscale = reinterpret_cast<float*>(ws + wl.xunscale);
   uint16_t* h = reinterpret_cast<uint16_t*>(ws + wl.h);
-  u32x4* t_frag = reinterpret_cast<u32x4*>(ws + wl.t_frag);
   float* t_part = reinterpret_cast<float*>(ws + wl.t_part);
-  uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + wl.cnt);
   int max_r = 0;
   for (int p = 0; p < nproj; ++p) max_r = projs[p].r > max_r ? projs[p].r : max_r;
   const int jgmax = 2 * (int)ceil_div(max_r, 32);  // whole 32-rank chunks, so every fragment element gets written
-  const int ks = (int)ceil_div(k, kLoraChunk);
-  const int n_cnt = nproj * (int)(mp / 16) * jgmax;
+  const int ks = (int)lora_chunks(k);
 
   // P1
   const int vec_in = ((uintptr_t)x % 16 == 0) && (ldx % 8 == 0);
@@ -665,7 +692,7 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
     const int vec_z = nz && (uintptr_t)nz % 16 == 0 && nld % 4 == 0;
 #define QN_P1(NT_, CPT_)                                                                                          \
   hipLaunchKernelGGL((k_norm_convert<NT_, CPT_>), dim3((unsigned)m), dim3(NT_), 0, s, x, ldx, k, kp, has_aqn, g, nz, \
-                     nld, sg, ep, vec_in, vec_g, vec_z, h, xs, xunscale, cnt, n_cnt)
+                     nld, sg, ep, vec_in, vec_g, vec_z, h, xs, xunscale)
     if (nt == 256) {
       if (cpt <= 1) QN_P1(256, 1);
       else if (cpt <= 2) QN_P1(256, 2);
@@ -691,12 +718,11 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
     la.m = m;
     la.k = k;
     la.kp = kp;
-    la.ntiles = mp / 16;
+    la.kc_width = lora_chunk_width(k);
     la.h = h;
     la.t_part = t_part;
-    la.cnt = cnt;
-    la.t_frag = t_frag;
-    hipLaunchKernelGGL(k_lora_down, dim3((unsigned)(mp / 16), (unsigned)(nproj * jgmax * ks)), dim3(256), 0, s, la);
+    hipLaunchKernelGGL(k_lora_down, dim3((unsigned)(mp / 16), (unsigned)(nproj * jgmax * ks)),
+                       dim3(kLoraWaves * kWave), 0, s, la);
   }
 
   // L
@@ -730,7 +756,8 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
   la.kp = kp;
   la.xs = xs;
   la.xunscale = xunscale;
-  la.t_frag = t_frag;
+  la.t_part = reinterpret_cast<const u32x4*>(t_part);
+  la.ks = ks;
   const bool silu = epilogue == QN_EPI_SILU_MUL;
   const int64_t nrg = silu ? 2 * ceil_div(projs[0].n, 16) : rg_total;
   if (nrg == 0 || !run_main) return hipGetLastError() == hipSuccess ? QN_OK : QN_ERR_HIP;
@@ -742,6 +769,14 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
     tmt = tmt <= 2 ? tmt : (tmt <= 4 ? 4 : 8);
     int R, W;
     pick_shape(tmt, mt, silu, nrg, KT, &R, &W);
+    // tuning override "R,W" (row groups and waves per workgroup); ignored unless that kernel variant is built
+    if (const char* ov = std::getenv("QN_LINEAR_SHAPE")) {
+      int r2 = 0, w2 = 0;
+      if (std::sscanf(ov, "%d,%d", &r2, &w2) == 2 && r2 > 0 && w2 > 0 && (!silu || r2 % 2 == 0)) {
+        R = r2;
+        W = w2;
+      }
+    }
     const int64_t nwg = ceil_div(nrg, R);
     if (!dispatch_linear(tmt, R, W, silu, la, nwg, s)) return QN_ERR_UNSUPPORTED;
   }
