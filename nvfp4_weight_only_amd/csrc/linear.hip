@@ -59,6 +59,7 @@ struct LinearArgs {
   const u32x4* xs;         // activation fragments, [tile][kp/128][4][64] x 16 bytes
   const float* xunscale;   // [m] 2^-p per token
   const u32x4* t_part;     // LoRA-down partials, [nproj][tile][kRankChunks][ks][64 lanes][8 f32]
+  int64_t t_bytes;
   int32_t ks;              // LoRA-down k-chunks
 };
 
@@ -86,8 +87,37 @@ Workspace workspace_layout(int64_t m, int64_t k, int32_t nproj) {
   return w;
 }
 
-// Zero vector read by lanes whose operand is absent: a branch-free stand-in for a masked load. Read-only.
-__device__ const u32x4 kZero16[1] = {{0u, 0u, 0u, 0u}};
+// Loads. Every load issued ahead of the weight stream is a buffer load or a global-segment load, never a flat one:
+// a pending flat load may be an LDS access, which forces the compiler to drain all loads at every later wait and
+// so would serialize the double-buffered stream.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit data format (gfx9 family)
+constexpr int kNonTemporal = 2;                 // streamed once: do not keep in cache
+constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset past every num_records: the load returns 0
+
+// Wave-uniform copies (readfirstlane) of values the compiler cannot prove uniform on its own, so that buffer
+// descriptors built from them stay in SGPRs.
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Raw buffer descriptor over [base, base + bytes); bytes < 2^31 (checked on the host).
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)uniform64((uint64_t)base), (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane((uint32_t)bytes), kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// Load through a pointer known to address global memory.
+template <class T>
+__device__ __forceinline__ T gload(const T* p) {
+  return *reinterpret_cast<const __attribute__((address_space(1))) T*>(reinterpret_cast<uintptr_t>(p));
+}
 
 // ------------------------------------------------------------------------------------------------------------------
 // P1: one workgroup per token row. The row stays in registers between passes: sum of squares -> AQN -> token amax ->
@@ -173,6 +203,7 @@ struct LoraDownArgs {
   int32_t nproj, jgmax, ks;
   int64_t m, k, kp, kc_width;
   const uint16_t* h;  // [mp][kp]
+  int64_t h_bytes;
   float* t_part;
 };
 
@@ -189,13 +220,14 @@ __global__ void __launch_bounds__(kLoraWaves * kWave) k_lora_down(LoraDownArgs a
   const int j = jg * 16 + lane % 16;
   const int64_t tok = tile * 16 + lane % 16;
   const int64_t k0 = kc * a.kc_width, k1 = k0 + a.kc_width < a.k ? k0 + a.kc_width : a.k;
+  const rsrc_t asrc = make_rsrc(a.A[p], (int64_t)r * a.k * 2), hsrc = make_rsrc(a.h, a.h_bytes);
   u32x4 av[kLoraSlicesPerWave], bv[kLoraSlicesPerWave];
 #pragma unroll
   for (int i = 0; i < kLoraSlicesPerWave; ++i) {
     const int64_t kk = k0 + (int64_t)(i * kLoraWaves + wave) * 32 + (lane / 16) * 8;
     const bool in = kk < k1;
-    av[i] = *((in && j < r) ? reinterpret_cast<const u32x4*>(a.A[p] + (int64_t)j * a.k + kk) : kZero16);
-    bv[i] = *((in && tok < a.m) ? reinterpret_cast<const u32x4*>(a.h + tok * a.kp + kk) : kZero16);
+    av[i] = bload16(asrc, (in && j < r) ? (uint32_t)(((int64_t)j * a.k + kk) * 2) : kOutOfRange);
+    bv[i] = bload16(hsrc, (in && tok < a.m) ? (uint32_t)((tok * a.kp + kk) * 2) : kOutOfRange);
   }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -230,24 +262,6 @@ struct TileBuf {
   uint32_t sc[R];
   u32x4 b[TMT][4];
 };
-
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit data format (gfx9 family)
-constexpr int kNonTemporal = 2;                 // streamed once: do not keep in cache
-constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset past every num_records: the load returns 0
-
-// Wave-uniform copies (readfirstlane) of values the compiler cannot prove uniform on its own, so that buffer
-// descriptors built from them stay in SGPRs.
-__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return ((uint64_t)hi << 32) | lo;
-}
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc((void*)uniform64((uint64_t)base), (short)0,
-                                           (int)__builtin_amdgcn_readfirstlane((uint32_t)bytes), kRsrcWord3);
-}
 
 // Operand streams of one workgroup. Buffer descriptors are wave-uniform (SGPRs); each lane adds one 32-bit offset.
 // Dead row-group slots have num_records = 0 and absent tokens an out-of-range offset, so their loads return zeros.
@@ -314,17 +328,21 @@ template <int TMT>
 __device__ __forceinline__ void issue_lora(LoraOps<TMT>& o, LoraRaw<TMT>& raw, const ProjArgs& P, int p, int64_t rg,
                                            int lane, const LinearArgs& a, int64_t tile0, int64_t ntiles) {
   const int64_t n = rg * 16 + lane % 16;
+  const rsrc_t bsrc = make_rsrc(P.B, P.n * P.r * 2), tsrc = make_rsrc(a.t_part, a.t_bytes);
 #pragma unroll
   for (int jc = 0; jc < kRankChunks; ++jc) {
     const int j0 = jc * 32 + (lane / 16) * 8;
     if (P.r % 8 == 0) {
-      o.bfrag[jc] = *((n < P.n && j0 < P.r) ? reinterpret_cast<const u32x4*>(P.B + n * P.r + j0) : kZero16);
+      o.bfrag[jc] = bload16(bsrc, (n < P.n && j0 < P.r) ? (uint32_t)((n * P.r + j0) * 2) : kOutOfRange);
     } else {
       uint32_t w[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = (n < P.n && j0 + 2 * e < P.r) ? P.B[n * P.r + j0 + 2 * e] : 0u;
-        const uint32_t hi = (n < P.n && j0 + 2 * e + 1 < P.r) ? P.B[n * P.r + j0 + 2 * e + 1] : 0u;
+        const int64_t off = (n * P.r + j0 + 2 * e) * 2;
+        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(
+            bsrc, (n < P.n && j0 + 2 * e < P.r) ? (uint32_t)off : kOutOfRange, 0, 0);
+        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(
+            bsrc, (n < P.n && j0 + 2 * e + 1 < P.r) ? (uint32_t)(off + 2) : kOutOfRange, 0, 0);
         w[e] = lo | (hi << 16);
       }
       o.bfrag[jc] = u32x4{w[0], w[1], w[2], w[3]};
@@ -332,10 +350,10 @@ __device__ __forceinline__ void issue_lora(LoraOps<TMT>& o, LoraRaw<TMT>& raw, c
 #pragma unroll
     for (int tt = 0; tt < TMT; ++tt) {
       const bool ok = jc * 32 < P.r && tile0 + tt < ntiles;
-      const u32x4* base = a.t_part + ((((int64_t)p * ntiles + tile0 + tt) * kRankChunks + jc) * a.ks) * kWave * 2 +
-                          lane * 2;
-      raw.part[jc][tt][0] = *(ok ? base : kZero16);
-      raw.part[jc][tt][1] = *(ok ? base + 1 : kZero16);
+      const uint32_t off =
+          (uint32_t)((((((int64_t)p * ntiles + tile0 + tt) * kRankChunks + jc) * a.ks) * kWave + lane) * 32);
+      raw.part[jc][tt][0] = bload16(tsrc, ok ? off : kOutOfRange);
+      raw.part[jc][tt][1] = bload16(tsrc, ok ? off + 16 : kOutOfRange);
     }
   }
 }
@@ -350,11 +368,13 @@ __device__ __forceinline__ void finish_lora(LoraOps<TMT>& o, const LoraRaw<TMT>&
       f32x4 s0 = __builtin_bit_cast(f32x4, raw.part[jc][tt][0]);
       f32x4 s1 = __builtin_bit_cast(f32x4, raw.part[jc][tt][1]);
       const bool ok = jc * 32 < P.r && tile0 + tt < ntiles;
-      const u32x4* base = a.t_part + ((((int64_t)p * ntiles + tile0 + tt) * kRankChunks + jc) * a.ks) * kWave * 2 +
-                          lane * 2;
+      const rsrc_t tsrc = make_rsrc(a.t_part, a.t_bytes);
+      const uint32_t off =
+          (uint32_t)((((((int64_t)p * ntiles + tile0 + tt) * kRankChunks + jc) * a.ks) * kWave + lane) * 32);
       for (int c = 1; c < a.ks; ++c) {  // k > 4096: the remaining chunks, in chunk order
-        s0 += __builtin_bit_cast(f32x4, *(ok ? base + (int64_t)c * kWave * 2 : kZero16));
-        s1 += __builtin_bit_cast(f32x4, *(ok ? base + (int64_t)c * kWave * 2 + 1 : kZero16));
+        const uint32_t oc = off + (uint32_t)c * kWave * 32;
+        s0 += __builtin_bit_cast(f32x4, bload16(tsrc, ok ? oc : kOutOfRange));
+        s1 += __builtin_bit_cast(f32x4, bload16(tsrc, ok ? oc + 16 : kOutOfRange));
       }
       uint32_t hi[4], lo[4];
 #pragma unroll
@@ -388,6 +408,14 @@ __device__ __forceinline__ void lora_mfma(const LoraOps<TMT>& o, f32x4 (&acc)[TM
     }
 }
 
+// What the epilogue needs of the projection an output slot belongs to (n = 0 for a slot past the last row group).
+struct SlotOut {
+  void* y;
+  const uint16_t* res;
+  int64_t n, ldy, ld_res, n0;  // n0: first output row of the slot
+  int32_t y_dtype, y_repeat, head_dim;
+};
+
 template <int TMT, int R, int W, bool SILU>
 __global__ void __launch_bounds__(W * kWave) k_linear(LinearArgs a) {
   constexpr int kSlots = SILU ? R / 2 : R;                  // output row groups per workgroup
@@ -420,34 +448,49 @@ __global__ void __launch_bounds__(W * kWave) k_linear(LinearArgs a) {
   const int mt = (int)(mrem < TMT * 16 ? mrem : TMT * 16);  // tokens in this launch
   const int64_t tile0 = a.tok0 / 16, ntiles = ceil_div(a.m, 16);
 
+  // Per-slot epilogue constants, read once (wave-uniform) and selected per output from registers: indexing the
+  // argument block with a per-lane slot would turn each read into a dependent vector load.
+  constexpr int kPer = SILU ? 2 : 1;
+  SlotOut so[kSlots];
+#pragma unroll
+  for (int sl = 0; sl < kSlots; ++sl) {
+    const ProjArgs& P = a.p[pj[sl * kPer]];
+    so[sl] = SlotOut{P.y, P.res, live[sl * kPer] ? P.n : 0, P.ldy, P.ld_res, rg[sl * kPer] * 16, P.y_dtype,
+                     P.y_repeat, P.head_dim};
+  }
+  float sgv[R], lam[R];
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    sgv[rr] = gload(a.p[pj[rr]].s_g);
+    lam[rr] = a.p[pj[rr]].lambda;
+  }
+
   // epilogue operands fetched now, consumed after the weight stream: per output the token's 2^-p and the residual
+  // (unconditional loads: outputs the epilogue skips read a valid stand-in address instead)
   float xu[kOut];
   uint16_t res[kOut];
 #pragma unroll
   for (int i = 0; i < kOut; ++i) {
     const int o = threadIdx.x + i * W * kWave;
     const int row = o % 16, tok = (o / 16) % mt, slot = o / (16 * mt);
-    xu[i] = 0.f;
-    res[i] = 0;
-    if (slot < kSlots) {
-      const int r0 = slot * (SILU ? 2 : 1);
-      const ProjArgs& P = a.p[pj[r0]];
-      const int64_t n = rg[r0] * 16 + row;
-      xu[i] = a.xunscale[a.tok0 + tok];
-      if (P.res && live[r0] && n < P.n) res[i] = P.res[(a.tok0 + tok) * P.ld_res + n];
+    xu[i] = gload(a.xunscale + a.tok0 + tok);
+    const uint16_t* rp = reinterpret_cast<const uint16_t*>(a.xunscale);
+#pragma unroll
+    for (int sl = 0; sl < kSlots; ++sl) {
+      const int64_t n = so[sl].n0 + row;
+      if (slot == sl && so[sl].res && n < so[sl].n) rp = so[sl].res + (a.tok0 + tok) * so[sl].ld_res + n;
     }
+    res[i] = gload(rp);
   }
-  // LoRA-up: wave w owns the slots rr with rr % W == w
+  // LoRA-up: wave w owns the slots rr with rr % W == w (lops / lraw index rr / W)
   constexpr int kLoraSlots = (R + W - 1) / W;
   LoraOps<TMT> lops[kLoraSlots];
   LoraRaw<TMT> lraw[kLoraSlots];
   if (kEarlyLora) {
 #pragma unroll
-    for (int q = 0; q < kLoraSlots; ++q) {
-      const int rr = wave + q * W;
-      if (rr < R && a.p[pj[rr]].r > 0)
-        issue_lora<TMT>(lops[q], lraw[q], a.p[pj[rr]], pj[rr], rg[rr], lane, a, tile0, ntiles);
-    }
+    for (int rr = 0; rr < R; ++rr)
+      if (rr % W == wave && a.p[pj[rr]].r > 0)
+        issue_lora<TMT>(lops[rr / W], lraw[rr / W], a.p[pj[rr]], pj[rr], rg[rr], lane, a, tile0, ntiles);
   }
 
   Streams<TMT, R> st;
@@ -494,9 +537,9 @@ __global__ void __launch_bounds__(W * kWave) k_linear(LinearArgs a) {
 #pragma unroll
     for (int tt = 0; tt < TMT; ++tt) red[wave][rr][tt][lane] = acc[rr][tt];
 #pragma unroll
-  for (int q = 0; q < kLoraSlots; ++q) {
-    const int rr = wave + q * W;
-    if (rr >= R) continue;
+  for (int rr = 0; rr < R; ++rr) {
+    if (rr % W != wave) continue;
+    const int q = rr / W;
     f32x4 la[TMT];
 #pragma unroll
     for (int tt = 0; tt < TMT; ++tt) la[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -522,33 +565,40 @@ __global__ void __launch_bounds__(W * kWave) k_linear(LinearArgs a) {
     const int tt = tok / 16, col = tok % 16;
     const int ln = (row / 4) * 16 + col, ii = row % 4;
     const int64_t gtok = a.tok0 + tok;
-    constexpr int kPer = SILU ? 2 : 1;
     float val[kPer];
-    const int r0 = slot * kPer;
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
-      const int rr = r0 + q;
-      const ProjArgs& P = a.p[pj[rr]];
+      const int rr = slot * kPer + q;
+      float sg = sgv[q], lm = lam[q];
+#pragma unroll
+      for (int r2 = kPer + q; r2 < R; r2 += kPer)
+        if (rr == r2) {
+          sg = sgv[r2];
+          lm = lam[r2];
+        }
       float s = 0.f;
 #pragma unroll
       for (int w = 0; w < W; ++w) s += red[w][rr][tt][ln][ii];
-      val[q] = (*P.s_g) * (s * xu[i]) + P.lambda * red[W][rr][tt][ln][ii];
+      val[q] = sg * (s * xu[i]) + lm * red[W][rr][tt][ln][ii];
     }
-    const ProjArgs& P0 = a.p[pj[r0]];
-    const int64_t n = rg[r0] * 16 + row;
-    if (!live[r0] || n >= P0.n) continue;
+    SlotOut O = so[0];
+#pragma unroll
+    for (int sl = 1; sl < kSlots; ++sl)
+      if (slot == sl) O = so[sl];
+    const int64_t n = O.n0 + row;
+    if (n >= O.n) continue;
     float out = val[0];
     if (SILU) {
       const float g = val[0];
       out = g / (1.0f + __expf(-g)) * val[kPer - 1];
     }
-    if (P0.res) out += bf16_to_f32(res[i]);
-    const int rep = P0.y_repeat > 1 ? P0.y_repeat : 1;
+    if (O.res) out += bf16_to_f32(res[i]);
+    const int rep = O.y_repeat > 1 ? O.y_repeat : 1;
     for (int g = 0; g < rep; ++g) {
-      const int64_t col_out = rep > 1 ? ((n / P0.head_dim) * rep + g) * P0.head_dim + n % P0.head_dim : n;
-      const int64_t off = gtok * P0.ldy + col_out;
-      if (P0.y_dtype == QN_F32) reinterpret_cast<float*>(P0.y)[off] = out;
-      else reinterpret_cast<uint16_t*>(P0.y)[off] = f32_to_bf16(out);
+      const int64_t col_out = rep > 1 ? ((n / O.head_dim) * rep + g) * O.head_dim + n % O.head_dim : n;
+      const int64_t off = gtok * O.ldy + col_out;
+      if (O.y_dtype == QN_F32) reinterpret_cast<float*>(O.y)[off] = out;
+      else reinterpret_cast<uint16_t*>(O.y)[off] = f32_to_bf16(out);
     }
   }
 }
@@ -664,6 +714,10 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
   if (!workspace || workspace_bytes < wl.total) return QN_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return QN_ERR_ALIGN;
   if (k > 131072) return QN_ERR_UNSUPPORTED;
+  // 32-bit buffer offsets: the row-major copy of h and every LoRA-B matrix stay below 2 GiB
+  if (ceil_div(m, 16) * 16 * ceil_div(k, kKTile) * kKTile * 2 >= ((int64_t)1 << 31)) return QN_ERR_UNSUPPORTED;
+  for (int p = 0; p < nproj; ++p)
+    if ((int64_t)projs[p].n * projs[p].r * 2 >= ((int64_t)1 << 31)) return QN_ERR_UNSUPPORTED;
 
   hipStream_t s = (hipStream_t)stream;
   char* ws = static_cast<char*>(workspace);
@@ -720,6 +774,7 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
     la.kp = kp;
     la.kc_width = lora_chunk_width(k);
     la.h = h;
+    la.h_bytes = mp * kp * 2;
     la.t_part = t_part;
     hipLaunchKernelGGL(k_lora_down, dim3((unsigned)(mp / 16), (unsigned)(nproj * jgmax * ks)),
                        dim3(kLoraWaves * kWave), 0, s, la);
@@ -757,6 +812,7 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
   la.xs = xs;
   la.xunscale = xunscale;
   la.t_part = reinterpret_cast<const u32x4*>(t_part);
+  la.t_bytes = (int64_t)(wl.total - wl.t_part);
   la.ks = ks;
   const bool silu = epilogue == QN_EPI_SILU_MUL;
   const int64_t nrg = silu ? 2 * ceil_div(projs[0].n, 16) : rg_total;
