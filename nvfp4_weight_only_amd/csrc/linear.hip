@@ -5,21 +5,25 @@
 //   §3.1 W_hat = s_g * s_b * q (NVFP4); §3.2 decode reads large packed weights for few tokens, so unpack, scale
 //   and conversion must keep up with the byte stream; §5.1 AQN-RMSNorm feeds the projections that share its input.
 //
-// Three kernels per call, all on the caller's stream:
-//   P1 k_norm_convert  one workgroup per token: RMSNorm statistics, h = bf16(x * rstd * (gamma + sigma * noise)) (or
-//                      h = x), written row-major for the LoRA branch, plus the MFMA B-fragments of h as f16 scaled by a
-//                      per-token power of two 2^p (exact: bf16 has 8 significant bits, f16 11, and the scale keeps the
-//                      token's largest magnitude in [2^14, 2^15), so every element above 2^-32 of it converts exactly).
-//   P2 k_lora_down     t = A h with bf16 16x16x32 MFMAs over at most 8 k-chunks per projection and token tile; each
-//                      chunk's partial sums are stored in the layout of the LoRA-up MFMA's B-fragments.
-//   L  k_linear        streams the tiled NVFP4 weight once: per lane one 16-byte load of codes (32 weights) and one
-//                      dword of block scales per 128-wide k-tile; FP4 -> f16 with the hardware converter (scale 2^8),
-//                      times the E4M3 scale reinterpreted as f16 (byte << 7 is the E4M3 value * 2^-8, exact for
-//                      normals and subnormals) gives s_b * q exactly in f16; f16 16x16x32 MFMAs accumulate in f32.
-//                      Waves split k; partials meet in LDS. The LoRA term: the chunk partials of t are summed in a fixed
-//                      order (so results do not depend on scheduling) and split t = t_hi + t_lo, both bf16 (t - t_hi is
-//                      exact in f32, 16 significant bits kept); B t is then two bf16 MFMAs per row group. The epilogue applies s_g, the per-token 2^-p, lambda, residual, SiLU(gate) * up,
-//                      broadcast and rounding. Everything the epilogue reads is fetched before the weight stream.
+// Two kernels per call (three when many tokens share a norm), all on the caller's stream:
+//   P  k_prologue  workgroup (token tile of 16, k-chunk, 32-rank LoRA chunk): RMSNorm statistics of its 16 tokens
+//                  (one wave per token, in the summation order of the standalone norm, so h is bit-identical to it),
+//                  h = bf16(x * rstd * (gamma + sigma * noise)) (or h = x) over its k-chunk, the MFMA B-fragments of h
+//                  as f16 scaled by 2^p per (token, 128-wide k-tile) (exact: bf16 has 8 significant bits, f16 11, and
+//                  the scale puts the tile's largest magnitude in [2^14, 2^15), so every element above 2^-32 of it
+//                  converts exactly), and the chunk's LoRA-down partial t_c = A[:, chunk] h[chunk] with bf16
+//                  16x16x32 MFMAs, stored where the LoRA-up MFMA's B-fragments want it.
+//   (k_rstd)       with 256 or more tokens the statistics are computed once per token by a kernel of their own and
+//                  read by the prologue workgroups instead of recomputed by each.
+//   L  k_linear    streams the tiled NVFP4 weight once: per lane one 16-byte load of codes (32 weights) and one dword
+//                  of block scales per 128-wide k-tile; FP4 -> f16 with the hardware converter (scale 2^8), times the
+//                  E4M3 scale reinterpreted as f16 (byte << 7 is the E4M3 value * 2^-8, exact for normals and
+//                  subnormals) gives s_b * q exactly in f16; f16 16x16x32 MFMAs over the tile, whose f32 result is
+//                  scaled by the tile's 2^-p (exact) and added to the f32 accumulator. Waves split k; partials meet in
+//                  LDS. The LoRA term: the chunk partials of t are summed in chunk order (results do not depend on
+//                  scheduling) and split t = t_hi + t_lo, both bf16 (t - t_hi is exact in f32, 16 significant bits
+//                  kept); B t is then two bf16 MFMAs per row group. The epilogue applies s_g, lambda, residual,
+//                  SiLU(gate) * up, broadcast and rounding. Everything it reads is fetched before the weight stream.
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -33,7 +37,10 @@ namespace {
 constexpr int kMaxProj = 4;
 constexpr int kMaxRank = 64;
 constexpr int kRankChunks = kMaxRank / 32;  // 32-wide rank chunks of the LoRA-up MFMA
+constexpr int kMaxPg = kMaxProj * kRankChunks;
 constexpr int kMaxTokensPerLaunch = 128;
+constexpr int kMaxChunkTiles = 8;           // k-tiles per prologue chunk (h of the chunk is staged in LDS)
+constexpr int kRstdKernelTiles = 16;        // token tiles from which the statistics get a kernel of their own
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -57,7 +64,7 @@ struct LinearArgs {
   int64_t m, k, kp;
   int64_t tok0;            // first token of this launch
   const u32x4* xs;         // activation fragments, [tile][kp/128][4][64] x 16 bytes
-  const float* xunscale;   // [m] 2^-p per token
+  const float* xsc;        // [tile][kp/128][16] 2^-p per (token, k-tile)
   const u32x4* t_part;     // LoRA-down partials, [nproj][tile][kRankChunks][ks][64 lanes][8 f32]
   int64_t t_bytes;
   int32_t ks;              // LoRA-down k-chunks
@@ -65,24 +72,32 @@ struct LinearArgs {
 
 // Workspace carve-up (256-byte aligned regions).
 struct Workspace {
-  size_t xs, xunscale, h, t_part, total;
+  size_t xs, xsc, rstd, t_part, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// LoRA-down k-chunks: as few as possible, each a multiple of 32 and at most 4096 wide (one pass of the 16 waves)
-inline int64_t lora_chunks(int64_t k) { return ceil_div(k, 4096); }
-inline int64_t lora_chunk_width(int64_t k) { return ceil_div(ceil_div(k, lora_chunks(k)), 32) * 32; }
+// Prologue k-chunks: at most 8 where possible, each a whole number of k-tiles, at most kMaxChunkTiles of them. The
+// chunking depends on k alone, so a call with the norm and one fed the standalone norm's output sum the LoRA-down
+// partials in the same order.
+inline int64_t chunk_tiles(int64_t KT) {
+  const int64_t ct = ceil_div(KT, 8);
+  return ct < kMaxChunkTiles ? ct : kMaxChunkTiles;
+}
+inline int64_t lora_chunks(int64_t k) {
+  const int64_t KT = ceil_div(k, kKTile);
+  return ceil_div(KT, chunk_tiles(KT));
+}
 
 Workspace workspace_layout(int64_t m, int64_t k, int32_t nproj) {
-  const int64_t kp = ceil_div(k, kKTile) * kKTile;
+  const int64_t KT = ceil_div(k, kKTile), kp = KT * kKTile;
   const int64_t mp = ceil_div(m, 16) * 16;
   Workspace w;
   size_t off = 0;
-  w.xs = off;       off = align256(off + (size_t)mp * kp * 2);
-  w.xunscale = off; off = align256(off + (size_t)mp * 4);
-  w.h = off;        off = align256(off + (size_t)mp * kp * 2);
-  w.t_part = off;   off = align256(off + (size_t)nproj * (mp / 16) * kRankChunks * lora_chunks(k) * kWave * 32);
+  w.xs = off;     off = align256(off + (size_t)mp * kp * 2);
+  w.xsc = off;    off = align256(off + (size_t)mp * KT * 4);
+  w.rstd = off;   off = align256(off + (size_t)mp * 4);
+  w.t_part = off; off = align256(off + (size_t)nproj * (mp / 16) * kRankChunks * lora_chunks(k) * kWave * 32);
   w.total = off;
   return w;
 }
@@ -120,132 +135,212 @@ __device__ __forceinline__ T gload(const T* p) {
 }
 
 // ------------------------------------------------------------------------------------------------------------------
-// P1: one workgroup per token row. The row stays in registers between passes: sum of squares -> AQN -> token amax ->
-// stores of h (row-major bf16, for the LoRA branch) and of the f16 MFMA B-fragments scaled by 2^p.
-template <int NT, int CPT>
-__global__ void __launch_bounds__(NT) k_norm_convert(const uint16_t* __restrict__ x, int64_t ldx, int64_t k,
-                                                     int64_t kp, int has_aqn, const uint16_t* gamma, const float* noise,
-                                                     int64_t noise_ld, float sigma, float eps, int vec_in, int vec_g,
-                                                     int vec_z, uint16_t* __restrict__ h_out, u32x4* __restrict__ xs,
-                                                     float* __restrict__ xunscale) {
-  __shared__ float red[NT / kWave];
-  const int64_t row = blockIdx.x;
-  RowRegs<CPT> r;
-  load_row<NT, CPT>(x + row * ldx, k, vec_in != 0, r);
-  if (has_aqn) {
-    ScaleRegs<CPT> sr;
-    load_scales<NT, CPT>(gamma, noise ? noise + row * noise_ld : nullptr, k, vec_g != 0, vec_z != 0, sr);
-    const float rstd = rms_rstd(row_sumsq<NT, CPT>(r, red), k, eps);
-    apply_aqn<NT, CPT>(r, sr, k, rstd, sigma);
-  }
-  // token amax and the row-major copy of h (zero padding up to kp)
-  float amax = 0.0f;
-  uint16_t* hr = h_out + row * kp;
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int64_t j0 = ((int64_t)threadIdx.x + (int64_t)i * NT) * 8;
-    if (j0 >= kp) continue;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fmaxf(fabsf(lo_bf16(r.v[i][e])), fabsf(hi_bf16(r.v[i][e]))));
-    *reinterpret_cast<u32x4*>(hr + j0) = u32x4{r.v[i][0], r.v[i][1], r.v[i][2], r.v[i][3]};
-  }
-  amax = wave_max(amax);
-  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = amax;
-  __syncthreads();
-  amax = 0.0f;
-#pragma unroll
-  for (int w = 0; w < NT / kWave; ++w) amax = fmaxf(amax, red[w]);
-  // 2^p with amax * 2^p in [2^14, 2^15): p = 14 - floor(log2 amax), read off the exponent field; kept within the
-  // normal exponent range so 2^p and 2^-p are plain f32 powers of two
-  int p = 0;
-  if (amax > 0.0f) {
-    const int e = (int)((__float_as_uint(amax) >> 23) & 0xffu) - 127;  // floor(log2 amax) for normal amax
-    p = 14 - (e < -126 ? -126 : e);
-    p = p > 126 ? 126 : p;
-  }
-  const float up = __uint_as_float((uint32_t)(p + 127) << 23);
-  if (threadIdx.x == 0) xunscale[row] = __uint_as_float((uint32_t)(127 - p) << 23);
-  // MFMA B-fragments: chunk of 8 consecutive k of this token sits in token tile row/16 at ((kt*4 + s)*64 + lane),
-  // lane = 16 * ((k % 32) / 8) + row % 16
-  const int64_t tile = row / 16;
-  const int col = (int)(row % 16);
-  const int64_t KT = kp / kKTile;
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int64_t j0 = ((int64_t)threadIdx.x + (int64_t)i * NT) * 8;
-    if (j0 >= kp) continue;
-    uint32_t packed[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      f16x2 v;
-      v[0] = (_Float16)__fmul_rn(lo_bf16(r.v[i][e]), up);
-      v[1] = (_Float16)__fmul_rn(hi_bf16(r.v[i][e]), up);
-      packed[e] = __builtin_bit_cast(uint32_t, v);
-    }
-    const int64_t kt = j0 / kKTile;
-    const int s = (int)((j0 % kKTile) / 32), lhi = (int)((j0 % 32) / 8);
-    xs[((tile * KT + kt) * 4 + s) * kWave + lhi * 16 + col] = u32x4{packed[0], packed[1], packed[2], packed[3]};
-  }
+// Statistics kernel (many tokens): one wave per token, rstd[tok] = 1 / sqrt(mean x^2 + eps).
+template <int NT>
+__global__ void __launch_bounds__(16 * kWave) k_rstd(const uint16_t* __restrict__ x, int64_t ldx, int64_t m,
+                                                     int64_t k, int vec_x, float eps, float* __restrict__ rstd) {
+  const int64_t tok = (int64_t)blockIdx.x * 16 + threadIdx.x / kWave;
+  if (tok >= m) return;
+  const float r = rms_rstd(row_sumsq_one_wave<NT>(x + tok * ldx, k, vec_x != 0), k, eps);
+  if (threadIdx.x % kWave == 0) rstd[tok] = r;
 }
 
 // ------------------------------------------------------------------------------------------------------------------
-// P2: partial t over one k-chunk, t_c[p][tok][j] = sum over k in chunk c of A_p[j][k] * h[tok][k].
-// Workgroup (token tile, projection p, rank group jg of 16, chunk c): 16 waves take the chunk's 32-wide slices, issue
-// all their loads (at most 8 slices each), run bf16 16x16x32 MFMAs and meet in LDS. The 16 x 16 partial is stored
-// where the LoRA-up B-fragment wants it: element (rank j, token tok) of chunk c at
-// [p][tile][j / 32][c][lane = ((j % 32) / 8) * 16 + tok][j % 8]. Ranks past r come out 0 (their A rows read as 0).
-constexpr int kLoraWaves = 16;
-constexpr int kLoraSlicesPerWave = 8;
+// P: prologue. Workgroup (token tile, k-chunk c of CT k-tiles, pair group pg = one 32-rank chunk jc of projection p);
+// 16 waves. Every pair group of a chunk computes the same h; pair group 0 stores the MFMA fragments and tile scales.
+constexpr int kProWaves = 16;
 
-struct LoraDownArgs {
+struct PrologueArgs {
+  const uint16_t* x;
+  int64_t ldx, m, k, KT;
+  int32_t CT, ks, npg, has_aqn;
+  int32_t vec_x, vec_g, vec_z;
+  const uint16_t* gamma;
+  const float* noise;
+  int64_t noise_ld;
+  float sigma, eps;
+  const float* rstd_in;  // statistics from k_rstd, or null: computed here
   const uint16_t* A[kMaxProj];
   int32_t r[kMaxProj];
-  int32_t nproj, jgmax, ks;
-  int64_t m, k, kp, kc_width;
-  const uint16_t* h;  // [mp][kp]
-  int64_t h_bytes;
+  int8_t pg_p[kMaxPg], pg_jc[kMaxPg];
+  u32x4* xs;
+  float* xsc;
   float* t_part;
 };
 
-__global__ void __launch_bounds__(kLoraWaves * kWave) k_lora_down(LoraDownArgs a) {
-  __shared__ f32x4 red[kLoraWaves][kWave];
+template <int NT, bool AQN>
+__global__ void __launch_bounds__(kProWaves * kWave) k_prologue(PrologueArgs a) {
+  constexpr int kCT = kMaxChunkTiles;                              // k-tiles per chunk (at most)
+  constexpr int kProSlices = kCT * 4 / kProWaves;                // 32-wide k-slices per wave (at most)
+  constexpr int kPasses = kCT * 256 / (kProWaves * kWave);        // 8-element groups per thread (at most)
+  constexpr int kHRow = kMaxChunkTiles * kKTile + 8;  // LDS row of h (bf16), padded against bank conflicts
+  __shared__ float s_rstd[16];
+  __shared__ __attribute__((aligned(16))) uint16_t s_h[16][kHRow];
+  __shared__ f32x4 s_red[kProWaves][2][kWave];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
   const int64_t tile = blockIdx.x, ntiles = gridDim.x;
-  int job = blockIdx.y;
-  const int kc = job % a.ks;
-  job /= a.ks;
-  const int jg = job % a.jgmax;
-  const int p = job / a.jgmax;
-  const int r = a.r[p];
-  const int j = jg * 16 + lane % 16;
-  const int64_t tok = tile * 16 + lane % 16;
-  const int64_t k0 = kc * a.kc_width, k1 = k0 + a.kc_width < a.k ? k0 + a.kc_width : a.k;
-  const rsrc_t asrc = make_rsrc(a.A[p], (int64_t)r * a.k * 2), hsrc = make_rsrc(a.h, a.h_bytes);
-  u32x4 av[kLoraSlicesPerWave], bv[kLoraSlicesPerWave];
+  const int c = blockIdx.y, pg = blockIdx.z;
+  const int64_t kt0 = (int64_t)c * a.CT;
+  const int ctn = (int)(a.KT - kt0 < a.CT ? a.KT - kt0 : a.CT);  // k-tiles in this chunk
+  const int64_t kc0 = kt0 * kKTile;
+  const bool lora = pg < a.npg;
+  const int p = lora ? a.pg_p[pg] : 0, jc = lora ? a.pg_jc[pg] : 0;
+
+  // LoRA-down A fragments of this wave's slices, issued first (they do not depend on x). Fragment (g, slice s): ranks
+  // jc*32 + g*16 + lane%16, k = kc0 + 32 s + 8 (lane/16) .. + 8; ranks past r and k past the row read as 0.
+  const int nsl = ctn * 4;
+  u32x4 af[2][kProSlices];
+  if (lora) {
+    const int r = a.r[p];
+    const rsrc_t asrc = make_rsrc(a.A[p], (int64_t)r * a.k * 2);
 #pragma unroll
-  for (int i = 0; i < kLoraSlicesPerWave; ++i) {
-    const int64_t kk = k0 + (int64_t)(i * kLoraWaves + wave) * 32 + (lane / 16) * 8;
-    const bool in = kk < k1;
-    av[i] = bload16(asrc, (in && j < r) ? (uint32_t)(((int64_t)j * a.k + kk) * 2) : kOutOfRange);
-    bv[i] = bload16(hsrc, (in && tok < a.m) ? (uint32_t)((tok * a.kp + kk) * 2) : kOutOfRange);
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int i = 0; i < kProSlices; ++i) {
+        const int s = wave + i * kProWaves;
+        const int j = jc * 32 + g * 16 + lane % 16;
+        const int64_t kk = kc0 + (int64_t)s * 32 + (lane / 16) * 8;
+        const bool ok = s < nsl && j < r && kk < a.k;
+        af[g][i] = bload16(asrc, ok ? (uint32_t)(((int64_t)j * a.k + kk) * 2) : kOutOfRange);
+      }
   }
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+
+  // inputs of h for this thread's 8-element groups (x, and gamma and noise with the norm), fetched before the
+  // statistics so that every load of the prologue is in flight at once. Group g: token g / (ctn*16), k-tile
+  // (g % (ctn*16)) / 16 of the chunk; the 16 groups of one (token, k-tile) are 16 consecutive lanes.
+  const int ngroups = 16 * ctn * 16;  // a multiple of 256: a wave is either wholly in range or wholly out
+  uint32_t hx[kPasses][4], hg[kPasses][4];
+  float hz[kPasses][8];
 #pragma unroll
-  for (int i = 0; i < kLoraSlicesPerWave; ++i)
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[i]), __builtin_bit_cast(bf16x8, bv[i]),
-                                                  acc, 0, 0, 0);
-  red[wave][lane] = acc;
+  for (int ps = 0; ps < kPasses; ++ps) {
+    const int g = threadIdx.x + ps * kProWaves * kWave;
+    const int t = g / (ctn * 16), kg = g % (ctn * 16);
+    const int64_t tok = tile * 16 + t, kk = kc0 + (int64_t)kg * 8;
+    const bool ok = g < ngroups && tok < a.m && kk < a.k;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) hx[ps][e] = hg[ps][e] = 0u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) hz[ps][e] = 0.f;
+    if (!ok) continue;
+    const uint16_t* xr = a.x + tok * a.ldx + kk;
+    if (a.vec_x) {
+      const u32x4 q = *reinterpret_cast<const u32x4*>(xr);
+      hx[ps][0] = q[0]; hx[ps][1] = q[1]; hx[ps][2] = q[2]; hx[ps][3] = q[3];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hx[ps][e] = (uint32_t)xr[2 * e] | ((uint32_t)xr[2 * e + 1] << 16);
+    }
+    if (AQN) {
+      if (a.vec_g) {
+        const u32x4 q = *reinterpret_cast<const u32x4*>(a.gamma + kk);
+        hg[ps][0] = q[0]; hg[ps][1] = q[1]; hg[ps][2] = q[2]; hg[ps][3] = q[3];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          hg[ps][e] = (uint32_t)a.gamma[kk + 2 * e] | ((uint32_t)a.gamma[kk + 2 * e + 1] << 16);
+      }
+      const float* nz = a.noise ? a.noise + tok * a.noise_ld + kk : nullptr;
+      if (nz && a.vec_z) {
+        const f32x4 z0 = *reinterpret_cast<const f32x4*>(nz), z1 = *reinterpret_cast<const f32x4*>(nz + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { hz[ps][e] = z0[e]; hz[ps][4 + e] = z1[e]; }
+      } else if (nz) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hz[ps][e] = nz[e];
+      }
+    }
+  }
+
+  // statistics: wave w <-> token w of the tile
+  if (AQN) {
+    const int64_t tok = tile * 16 + wave;
+    float rstd = 0.f;
+    if (tok < a.m)
+      rstd = a.rstd_in ? gload(a.rstd_in + tok)
+                       : rms_rstd(row_sumsq_one_wave<NT>(a.x + tok * a.ldx, a.k, a.vec_x != 0), a.k, a.eps);
+    if (lane == 0) s_rstd[wave] = rstd;
+  }
   __syncthreads();
-  if (threadIdx.x < 256) {
-    // thread (rank row jr, token column tc); D lane (jr/4)*16 + tc, element jr%4
-    const int jr = threadIdx.x / 16, tc = threadIdx.x % 16;
+
+  // h, its LDS copy for the LoRA-down, and (pair group 0) the f16 fragments and tile scales
+#pragma unroll
+  for (int ps = 0; ps < kPasses; ++ps) {
+    const int g = threadIdx.x + ps * kProWaves * kWave;
+    if (g >= ngroups) break;
+    const int t = g / (ctn * 16), kg = g % (ctn * 16), ktl = kg / 16, jj = kg % 16;
+    uint32_t hv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) hv[e] = hx[ps][e];
+    if (AQN) {
+      const float rstd = s_rstd[t];
+      const int64_t tok = tile * 16 + t, kk = kc0 + (int64_t)kg * 8;
+      if (tok < a.m && kk < a.k) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t lo = aqn_value(lo_bf16(hv[e]), rstd, (uint16_t)hg[ps][e], hz[ps][2 * e], a.sigma);
+          const uint32_t hi = aqn_value(hi_bf16(hv[e]), rstd, (uint16_t)(hg[ps][e] >> 16), hz[ps][2 * e + 1], a.sigma);
+          hv[e] = lo | (hi << 16);
+        }
+      }
+    }
+    *reinterpret_cast<u32x4*>(&s_h[t][kg * 8]) = u32x4{hv[0], hv[1], hv[2], hv[3]};
+    if (pg == 0) {
+      // tile amax over the 16 lanes of this (token, k-tile), then 2^p with amax * 2^p in [2^14, 2^15), read off the
+      // exponent field and kept within the normal range so 2^p and 2^-p are plain f32 powers of two
+      float amax = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fmaxf(fabsf(lo_bf16(hv[e])), fabsf(hi_bf16(hv[e]))));
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+      int pw = 0;
+      if (amax > 0.0f) {
+        const int e = (int)((__float_as_uint(amax) >> 23) & 0xffu) - 127;
+        pw = 14 - (e < -126 ? -126 : e);
+        pw = pw > 126 ? 126 : pw;
+      }
+      const float up = __uint_as_float((uint32_t)(pw + 127) << 23);
+      uint32_t packed[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f16x2 v;
+        v[0] = (_Float16)__fmul_rn(lo_bf16(hv[e]), up);
+        v[1] = (_Float16)__fmul_rn(hi_bf16(hv[e]), up);
+        packed[e] = __builtin_bit_cast(uint32_t, v);
+      }
+      const int64_t kt = kt0 + ktl;
+      const int s = jj / 4, lhi = jj % 4;
+      a.xs[((tile * a.KT + kt) * 4 + s) * kWave + lhi * 16 + t] = u32x4{packed[0], packed[1], packed[2], packed[3]};
+      if (jj == 0) a.xsc[(tile * a.KT + kt) * 16 + t] = __uint_as_float((uint32_t)(127 - pw) << 23);
+    }
+  }
+  __syncthreads();
+  if (!lora) return;
+
+  // LoRA-down over the chunk: B-fragment (token lane%16, k = 32 s + 8 (lane/16) .. + 8) from LDS
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int i = 0; i < kProSlices; ++i) {
+    const int s = wave + i * kProWaves;
+    if (s >= nsl) break;
+    const u32x4 b = *reinterpret_cast<const u32x4*>(&s_h[lane % 16][s * 32 + (lane / 16) * 8]);
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+      acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[g][i]),
+                                                       __builtin_bit_cast(bf16x8, b), acc[g], 0, 0, 0);
+  }
+  s_red[wave][0][lane] = acc[0];
+  s_red[wave][1][lane] = acc[1];
+  __syncthreads();
+  if (threadIdx.x < 512) {
+    // thread (rank group g, rank row jr, token column tc); D lane (jr/4)*16 + tc, element jr%4; waves in order
+    const int g = threadIdx.x / 256, jr = (threadIdx.x % 256) / 16, tc = threadIdx.x % 16;
     const int src = (jr / 4) * 16 + tc, q = jr % 4;
     float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < kLoraWaves; ++w) v += red[w][src][q];
-    const int jj = jg * 16 + jr;
-    const int L = ((jj % 32) / 8) * 16 + tc;
-    a.t_part[((((int64_t)p * ntiles + tile) * kRankChunks + jj / 32) * a.ks + kc) * kWave * 8 + L * 8 + jj % 8] = v;
+    for (int w = 0; w < kProWaves; ++w) v += s_red[w][g][src][q];
+    const int jl = g * 16 + jr;  // rank within the 32-rank chunk
+    const int L = (jl / 8) * 16 + tc;
+    a.t_part[((((int64_t)p * ntiles + tile) * kRankChunks + jc) * a.ks + c) * kWave * 8 + L * 8 + jl % 8] = v;
   }
 }
 
@@ -255,20 +350,22 @@ __global__ void __launch_bounds__(kLoraWaves * kWave) k_lora_down(LoraDownArgs a
 //   R    row groups (16 rows each) per workgroup; with SILU they are (gate, up) pairs: slot 2i = gate, 2i+1 = up
 //   W    waves; wave w takes the contiguous k-tile range [w*KT/W, (w+1)*KT/W) for all R row groups
 // Per k-tile and row group a lane loads one 16-byte code chunk and one dword of scales; per token tile and slice one
-// 16-byte B-fragment. Loads of tile i+1 are issued before tile i is computed.
+// 16-byte B-fragment, plus one dword: the 2^-p of the lane's token for this k-tile. Loads of tile i+1 are issued
+// before tile i is computed.
 template <int TMT, int R>
 struct TileBuf {
   u32x4 c[R];
   uint32_t sc[R];
   u32x4 b[TMT][4];
+  uint32_t xu[TMT];
 };
 
 // Operand streams of one workgroup. Buffer descriptors are wave-uniform (SGPRs); each lane adds one 32-bit offset.
 // Dead row-group slots have num_records = 0 and absent tokens an out-of-range offset, so their loads return zeros.
 template <int TMT, int R>
 struct Streams {
-  rsrc_t c[R], s[R], b;
-  uint32_t c_off, s_off, b_off[TMT];
+  rsrc_t c[R], s[R], b, x;
+  uint32_t c_off, s_off, b_off[TMT], x_off[TMT];
 };
 
 template <int TMT, int R>
@@ -276,6 +373,7 @@ __device__ __forceinline__ void load_tile(TileBuf<TMT, R>& t, const Streams<TMT,
   const int kc = __builtin_amdgcn_readfirstlane((int)(kt * kTileCodeBytes));
   const int ks = __builtin_amdgcn_readfirstlane((int)(kt * kTileScaleBytes));
   const int kb = __builtin_amdgcn_readfirstlane((int)(kt * 4 * kWave * 16));
+  const int kx = __builtin_amdgcn_readfirstlane((int)(kt * 16 * 4));
 #pragma unroll
   for (int rr = 0; rr < R; ++rr) {
     t.c[rr] = __builtin_amdgcn_raw_buffer_load_b128(st.c[rr], st.c_off, kc, kNonTemporal);
@@ -286,10 +384,17 @@ __device__ __forceinline__ void load_tile(TileBuf<TMT, R>& t, const Streams<TMT,
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       t.b[tt][q] = __builtin_amdgcn_raw_buffer_load_b128(st.b, st.b_off[tt] + q * kWave * 16, kb, 0);
+#pragma unroll
+  for (int tt = 0; tt < TMT; ++tt) t.xu[tt] = __builtin_amdgcn_raw_buffer_load_b32(st.x, st.x_off[tt], kx, 0);
 }
 
 template <int TMT, int R>
 __device__ __forceinline__ void compute_tile(const TileBuf<TMT, R>& t, f32x4 (&acc)[R][TMT]) {
+  f32x4 part[R][TMT];
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+    for (int tt = 0; tt < TMT; ++tt) part[rr][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
 #pragma unroll
@@ -304,10 +409,19 @@ __device__ __forceinline__ void compute_tile(const TileBuf<TMT, R>& t, f32x4 (&a
       const f16x8 av = {q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
 #pragma unroll
       for (int tt = 0; tt < TMT; ++tt)
-        acc[rr][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(f16x8, t.b[tt][s]), acc[rr][tt],
-                                                              0, 0, 0);
+        part[rr][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(f16x8, t.b[tt][s]),
+                                                               part[rr][tt], 0, 0, 0);
     }
   }
+  // the tile's sums times the token's 2^-p (exact) into the accumulator; D column = token = lane % 16
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+    for (int tt = 0; tt < TMT; ++tt) {
+      const float u = __uint_as_float(t.xu[tt]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[rr][tt][e] = __builtin_fmaf(part[rr][tt][e], u, acc[rr][tt][e]);
+    }
 }
 
 // LoRA-up operands of one row-group slot: rows of B (bf16, ranks past r read as 0) and the t fragments.
@@ -371,10 +485,22 @@ __device__ __forceinline__ void finish_lora(LoraOps<TMT>& o, const LoraRaw<TMT>&
       const rsrc_t tsrc = make_rsrc(a.t_part, a.t_bytes);
       const uint32_t off =
           (uint32_t)((((((int64_t)p * ntiles + tile0 + tt) * kRankChunks + jc) * a.ks) * kWave + lane) * 32);
-      for (int c = 1; c < a.ks; ++c) {  // k > 4096: the remaining chunks, in chunk order
-        const uint32_t oc = off + (uint32_t)c * kWave * 32;
-        s0 += __builtin_bit_cast(f32x4, bload16(tsrc, ok ? oc : kOutOfRange));
-        s1 += __builtin_bit_cast(f32x4, bload16(tsrc, ok ? oc + 16 : kOutOfRange));
+      // the remaining chunks, in chunk order; loads issued eight chunks at a time
+      for (int c0 = 1; c0 < a.ks; c0 += 8) {
+        u32x4 q[8][2];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const uint32_t oc = off + (uint32_t)(c0 + u) * kWave * 32;
+          const bool in = ok && c0 + u < a.ks;
+          q[u][0] = bload16(tsrc, in ? oc : kOutOfRange);
+          q[u][1] = bload16(tsrc, in ? oc + 16 : kOutOfRange);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (c0 + u >= a.ks) break;
+          s0 += __builtin_bit_cast(f32x4, q[u][0]);
+          s1 += __builtin_bit_cast(f32x4, q[u][1]);
+        }
       }
       uint32_t hi[4], lo[4];
 #pragma unroll
@@ -465,16 +591,14 @@ __global__ void __launch_bounds__(W * kWave) k_linear(LinearArgs a) {
     lam[rr] = a.p[pj[rr]].lambda;
   }
 
-  // epilogue operands fetched now, consumed after the weight stream: per output the token's 2^-p and the residual
-  // (unconditional loads: outputs the epilogue skips read a valid stand-in address instead)
-  float xu[kOut];
+  // epilogue operand fetched now, consumed after the weight stream: per output the residual (an unconditional load:
+  // outputs the epilogue skips read a valid stand-in address instead)
   uint16_t res[kOut];
 #pragma unroll
   for (int i = 0; i < kOut; ++i) {
     const int o = threadIdx.x + i * W * kWave;
     const int row = o % 16, tok = (o / 16) % mt, slot = o / (16 * mt);
-    xu[i] = gload(a.xunscale + a.tok0 + tok);
-    const uint16_t* rp = reinterpret_cast<const uint16_t*>(a.xunscale);
+    const uint16_t* rp = reinterpret_cast<const uint16_t*>(a.xsc);
 #pragma unroll
     for (int sl = 0; sl < kSlots; ++sl) {
       const int64_t n = so[sl].n0 + row;
@@ -503,9 +627,13 @@ __global__ void __launch_bounds__(W * kWave) k_linear(LinearArgs a) {
   st.c_off = lane * 16;
   st.s_off = ((lane % 16) * 2 + (lane / 16) / 2) * 4;
   st.b = make_rsrc(a.xs + tile0 * KT * 4 * kWave, TMT * KT * 4 * kWave * 16);
+  st.x = make_rsrc(a.xsc + tile0 * KT * 16, TMT * KT * 16 * 4);
 #pragma unroll
-  for (int tt = 0; tt < TMT; ++tt)
-    st.b_off[tt] = (tt * 16 + lane % 16 < mt) ? (uint32_t)((tt * KT * 4 * kWave + lane) * 16) : kOutOfRange;
+  for (int tt = 0; tt < TMT; ++tt) {
+    const bool in = tt * 16 + lane % 16 < mt;
+    st.b_off[tt] = in ? (uint32_t)((tt * KT * 4 * kWave + lane) * 16) : kOutOfRange;
+    st.x_off[tt] = in ? (uint32_t)((tt * KT * 16 + lane % 16) * 4) : kOutOfRange;
+  }
 
   f32x4 acc[R][TMT];
 #pragma unroll
@@ -579,7 +707,7 @@ __global__ void __launch_bounds__(W * kWave) k_linear(LinearArgs a) {
       float s = 0.f;
 #pragma unroll
       for (int w = 0; w < W; ++w) s += red[w][rr][tt][ln][ii];
-      val[q] = sg * (s * xu[i]) + lm * red[W][rr][tt][ln][ii];
+      val[q] = sg * s + lm * red[W][rr][tt][ln][ii];
     }
     SlotOut O = so[0];
 #pragma unroll
@@ -714,70 +842,70 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
   if (!workspace || workspace_bytes < wl.total) return QN_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return QN_ERR_ALIGN;
   if (k > 131072) return QN_ERR_UNSUPPORTED;
-  // 32-bit buffer offsets: the row-major copy of h and every LoRA-B matrix stay below 2 GiB
-  if (ceil_div(m, 16) * 16 * ceil_div(k, kKTile) * kKTile * 2 >= ((int64_t)1 << 31)) return QN_ERR_UNSUPPORTED;
+  // 32-bit buffer offsets: the LoRA-down partials and every LoRA-B matrix stay below 2 GiB
+  if (wl.total - wl.t_part >= ((size_t)1 << 31)) return QN_ERR_UNSUPPORTED;
   for (int p = 0; p < nproj; ++p)
     if ((int64_t)projs[p].n * projs[p].r * 2 >= ((int64_t)1 << 31)) return QN_ERR_UNSUPPORTED;
 
   hipStream_t s = (hipStream_t)stream;
   char* ws = static_cast<char*>(workspace);
-  const int64_t kp = ceil_div(k, kKTile) * kKTile;
-  const int64_t mp = ceil_div(m, 16) * 16;
+  const int64_t KT = ceil_div(k, kKTile), kp = KT * kKTile;
+  const int64_t ntiles = ceil_div(m, 16);
   u32x4* xs = reinterpret_cast<u32x4*>(ws + wl.xs);
-  float* xunscale = reinterpret_cast<float*>(ws + wl.xunscale);
-  uint16_t* h = reinterpret_cast<uint16_t*>(ws + wl.h);
+  float* xsc = reinterpret_cast<float*>(ws + wl.xsc);
+  float* rstd = reinterpret_cast<float*>(ws + wl.rstd);
   float* t_part = reinterpret_cast<float*>(ws + wl.t_part);
-  int max_r = 0;
-  for (int p = 0; p < nproj; ++p) max_r = projs[p].r > max_r ? projs[p].r : max_r;
-  const int jgmax = 2 * (int)ceil_div(max_r, 32);  // whole 32-rank chunks, so every fragment element gets written
+  const int CT = (int)chunk_tiles(KT);
   const int ks = (int)lora_chunks(k);
 
-  // P1
-  const int vec_in = ((uintptr_t)x % 16 == 0) && (ldx % 8 == 0);
+  // P (and the statistics kernel for many tokens)
   if (run_prologue) {
-    const int nt = norm_threads(kp);
-    const int64_t cpt = ceil_div(ceil_div(kp, 8), nt);
-    const int has_aqn = aqn ? 1 : 0;
-    const uint16_t* g = aqn ? aqn->gamma : nullptr;
-    const float* nz = aqn ? aqn->noise : nullptr;
-    const int64_t nld = aqn ? aqn->noise_ld : 0;
-    const float sg = aqn ? aqn->sigma : 0.f, ep = aqn ? aqn->eps : 0.f;
-    const int vec_g = g && (uintptr_t)g % 16 == 0;
-    const int vec_z = nz && (uintptr_t)nz % 16 == 0 && nld % 4 == 0;
-#define QN_P1(NT_, CPT_)                                                                                          \
-  hipLaunchKernelGGL((k_norm_convert<NT_, CPT_>), dim3((unsigned)m), dim3(NT_), 0, s, x, ldx, k, kp, has_aqn, g, nz, \
-                     nld, sg, ep, vec_in, vec_g, vec_z, h, xs, xunscale)
-    if (nt == 256) {
-      if (cpt <= 1) QN_P1(256, 1);
-      else if (cpt <= 2) QN_P1(256, 2);
-      else if (cpt <= 4) QN_P1(256, 4);
-      else if (cpt <= 8) QN_P1(256, 8);
-      else QN_P1(256, 16);
-    } else {
-      QN_P1(1024, 16);
+    PrologueArgs pa{};
+    pa.x = x;
+    pa.ldx = ldx;
+    pa.m = m;
+    pa.k = k;
+    pa.KT = KT;
+    pa.CT = CT;
+    pa.ks = ks;
+    pa.has_aqn = aqn ? 1 : 0;
+    pa.vec_x = ((uintptr_t)x % 16 == 0) && (ldx % 8 == 0);
+    if (aqn) {
+      pa.gamma = aqn->gamma;
+      pa.noise = aqn->noise;
+      pa.noise_ld = aqn->noise ? aqn->noise_ld : 0;
+      pa.sigma = aqn->sigma;
+      pa.eps = aqn->eps;
+      pa.vec_g = (uintptr_t)aqn->gamma % 16 == 0;
+      pa.vec_z = aqn->noise && (uintptr_t)aqn->noise % 16 == 0 && pa.noise_ld % 4 == 0;
     }
-#undef QN_P1
-  }
-
-  // P2
-  if (run_prologue && max_r > 0) {
-    LoraDownArgs la{};
+    int npg = 0;
     for (int p = 0; p < nproj; ++p) {
-      la.A[p] = projs[p].lora_a;
-      la.r[p] = projs[p].r;
+      pa.A[p] = projs[p].r > 0 ? projs[p].lora_a : nullptr;
+      pa.r[p] = projs[p].r;
+      for (int jc = 0; jc * 32 < projs[p].r; ++jc) {
+        pa.pg_p[npg] = (int8_t)p;
+        pa.pg_jc[npg] = (int8_t)jc;
+        ++npg;
+      }
     }
-    la.nproj = nproj;
-    la.jgmax = jgmax;
-    la.ks = ks;
-    la.m = m;
-    la.k = k;
-    la.kp = kp;
-    la.kc_width = lora_chunk_width(k);
-    la.h = h;
-    la.h_bytes = mp * kp * 2;
-    la.t_part = t_part;
-    hipLaunchKernelGGL(k_lora_down, dim3((unsigned)(mp / 16), (unsigned)(nproj * jgmax * ks)),
-                       dim3(kLoraWaves * kWave), 0, s, la);
+    pa.npg = npg;
+    pa.xs = xs;
+    pa.xsc = xsc;
+    pa.t_part = t_part;
+    const bool big = aqn && ntiles >= kRstdKernelTiles;
+    pa.rstd_in = big ? rstd : nullptr;
+    const dim3 grid((unsigned)ntiles, (unsigned)ks, (unsigned)(npg > 0 ? npg : 1));
+    const dim3 block(kProWaves * kWave);
+    if (!aqn) {
+      hipLaunchKernelGGL((k_prologue<256, false>), grid, block, 0, s, pa);
+    } else if (norm_threads(k) == 256) {
+      if (big) hipLaunchKernelGGL(k_rstd<256>, dim3((unsigned)ntiles), block, 0, s, x, ldx, m, k, pa.vec_x, pa.eps, rstd);
+      hipLaunchKernelGGL((k_prologue<256, true>), grid, block, 0, s, pa);
+    } else {
+      if (big) hipLaunchKernelGGL(k_rstd<1024>, dim3((unsigned)ntiles), block, 0, s, x, ldx, m, k, pa.vec_x, pa.eps, rstd);
+      hipLaunchKernelGGL((k_prologue<1024, true>), grid, block, 0, s, pa);
+    }
   }
 
   // L
@@ -810,14 +938,13 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
   la.k = k;
   la.kp = kp;
   la.xs = xs;
-  la.xunscale = xunscale;
+  la.xsc = xsc;
   la.t_part = reinterpret_cast<const u32x4*>(t_part);
   la.t_bytes = (int64_t)(wl.total - wl.t_part);
   la.ks = ks;
   const bool silu = epilogue == QN_EPI_SILU_MUL;
   const int64_t nrg = silu ? 2 * ceil_div(projs[0].n, 16) : rg_total;
   if (nrg == 0 || !run_main) return hipGetLastError() == hipSuccess ? QN_OK : QN_ERR_HIP;
-  const int64_t KT = kp / kKTile;
   for (int64_t t0 = 0; t0 < m; t0 += kMaxTokensPerLaunch) {
     la.tok0 = t0;
     const int64_t mt = (m - t0) < kMaxTokensPerLaunch ? (m - t0) : kMaxTokensPerLaunch;

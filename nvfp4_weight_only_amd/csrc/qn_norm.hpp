@@ -66,6 +66,59 @@ __device__ inline float row_sumsq(const RowRegs<CPT>& r, float* red) {
   return tot;
 }
 
+// The same sum of squares computed by one wave alone, in exactly the order row_sumsq<NT, CPT> takes with NT threads:
+// lane l stands in for threads l, l + 64, ..., each summing its own chunks (c = t, t + NT, ...); the wave totals of
+// those stand-ins are then added in order. The row is read in whole 8-element chunks (d % 8 == 0, 16-byte aligned
+// chunks when vec_ok, else element loads). Every lane returns the total.
+template <int NT>
+__device__ inline float row_sumsq_one_wave(const uint16_t* __restrict__ xr, int64_t d, bool vec_ok) {
+  constexpr int V = NT / kWave;           // stand-in threads per lane
+  constexpr int VB = V < 8 ? V : 8;       // stand-ins whose chunks are loaded together
+  constexpr int IB = 8 / VB;              // chunk rounds loaded together
+  const int lane = threadIdx.x % kWave;
+  const int64_t nch = d / 8;
+  float ss[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) ss[v] = 0.0f;
+  for (int64_t i0 = 0; i0 * NT < nch; i0 += IB) {
+#pragma unroll
+    for (int v0 = 0; v0 < V; v0 += VB) {
+      uint32_t q[IB][VB][4];
+#pragma unroll
+      for (int ib = 0; ib < IB; ++ib)
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb) {
+          const int64_t c = (i0 + ib) * NT + (v0 + vb) * kWave + lane;
+          if (c < nch && vec_ok) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(xr + c * 8);
+            q[ib][vb][0] = w[0]; q[ib][vb][1] = w[1]; q[ib][vb][2] = w[2]; q[ib][vb][3] = w[3];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              q[ib][vb][e] = c < nch ? (uint32_t)xr[c * 8 + 2 * e] | ((uint32_t)xr[c * 8 + 2 * e + 1] << 16) : 0u;
+          }
+        }
+      // each stand-in adds its chunks in chunk order (ib ascending), elements in order
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+        for (int ib = 0; ib < IB; ++ib) {
+          if ((i0 + ib) * NT + (v0 + vb) * kWave + lane >= nch) continue;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float a = lo_bf16(q[ib][vb][e]), b = hi_bf16(q[ib][vb][e]);
+            ss[v0 + vb] = __fadd_rn(ss[v0 + vb], __fmul_rn(a, a));
+            ss[v0 + vb] = __fadd_rn(ss[v0 + vb], __fmul_rn(b, b));
+          }
+        }
+    }
+  }
+  float tot = 0.0f;
+#pragma unroll
+  for (int v = 0; v < V; ++v) tot = __fadd_rn(tot, wave_sum(ss[v]));
+  return tot;
+}
+
 // rstd = 1 / sqrt(ss / d + eps), each operation correctly rounded.
 __device__ inline float rms_rstd(float ss, int64_t d, float eps) {
   return __fdiv_rn(1.0f, __fsqrt_rn(__fadd_rn(__fdiv_rn(ss, (float)d), eps)));

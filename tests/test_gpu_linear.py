@@ -157,6 +157,26 @@ def test_linear_per_row_noise(qn):
     assert rel_err(y.cpu().numpy(), oracle.lora_linear(h, cc, sb, sg, c.A[0], c.B[0], c.lam)) <= LINEAR_TOL
 
 
+@pytest.mark.parametrize("m,k,per_row", [(16, 3584, False), (5, 272, True), (300, 1024, False), (17, 40960, True)])
+def test_fused_norm_matches_standalone_norm(qn, m, k, per_row):
+    """The norm inside the linear call gives the bits of the standalone norm: y(fused) == y(norm, then plain linear).
+
+    Covers the one-wave statistics in both thread counts (k > 32768 uses 1024), per-row noise, a ragged k and the
+    separate statistics kernel taken from 256 tokens on."""
+    c = Case(m, [96], k, seed=m + k)
+    noise = synth.normal_f32(78, (m, k) if per_row else (k,))
+    wq = qn.quantize(dev_bf16(c.w[0]), qn.LAYOUT_TILED)
+    A, B = dev_bf16(c.A[0]), dev_bf16(c.B[0])
+    g, z, x = dev_bf16(c.gamma), dev_f32(noise), dev_bf16(c.x)
+    y1 = torch.empty(m, 96, dtype=torch.float32, device=DEV)
+    qn.lora_linear(x, [qn.Projection(wq, y1, A, B, c.lam)], qn.make_aqn(g, z, c.sigma, 1e-6, noise_per_row=per_row))
+    h = qn.aqn_rmsnorm(x, g, z, c.sigma, 1e-6, noise_per_row=per_row)
+    y2 = torch.empty(m, 96, dtype=torch.float32, device=DEV)
+    qn.lora_linear(h, [qn.Projection(wq, y2, A, B, c.lam)])
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
 def test_linear_deterministic(qn):
     c = Case(16, [512], 2048, seed=11)
     a = c.gpu(qn)[0].clone()
