@@ -72,7 +72,7 @@ struct LinearArgs {
 
 // Workspace carve-up (256-byte aligned regions).
 struct Workspace {
-  size_t xs, xsc, rstd, t_part, total;
+  size_t xs, xsc, rstd, t_part, pbuf, cnt, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -89,7 +89,9 @@ inline int64_t lora_chunks(int64_t k) {
   return ceil_div(KT, chunk_tiles(KT));
 }
 
-Workspace workspace_layout(int64_t m, int64_t k, int32_t nproj) {
+size_t gemv_pbuf_bytes(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj);
+
+Workspace workspace_layout(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj) {
   const int64_t KT = ceil_div(k, kKTile), kp = KT * kKTile;
   const int64_t mp = ceil_div(m, 16) * 16;
   Workspace w;
@@ -98,6 +100,8 @@ Workspace workspace_layout(int64_t m, int64_t k, int32_t nproj) {
   w.xsc = off;    off = align256(off + (size_t)mp * KT * 4);
   w.rstd = off;   off = align256(off + (size_t)mp * 4);
   w.t_part = off; off = align256(off + (size_t)nproj * (mp / 16) * kRankChunks * lora_chunks(k) * kWave * 32);
+  w.pbuf = off;   off = align256(off + gemv_pbuf_bytes(m, k, projs, nproj));
+  w.cnt = off;    off = align256(off + 256 * 4);
   w.total = off;
   return w;
 }
@@ -166,6 +170,8 @@ struct PrologueArgs {
   u32x4* xs;
   float* xsc;
   float* t_part;
+  uint32_t* cnt;  // arrival counters of the linear kernel, zeroed here
+  int32_t ncnt;
 };
 
 template <int NT, bool AQN>
@@ -185,6 +191,7 @@ __global__ void __launch_bounds__(kProWaves * kWave) k_prologue(PrologueArgs a) 
   const int64_t kc0 = kt0 * kKTile;
   const bool lora = pg < a.npg;
   const int p = lora ? a.pg_p[pg] : 0, jc = lora ? a.pg_jc[pg] : 0;
+  if (tile == 0 && c == 0 && pg == 0 && (int)threadIdx.x < a.ncnt) a.cnt[threadIdx.x] = 0u;
 
   // LoRA-down A fragments of this wave's slices, issued first (they do not depend on x). Fragment (g, slice s): ranks
   // jc*32 + g*16 + lane%16, k = kc0 + 32 s + 8 (lane/16) .. + 8; ranks past r and k past the row read as 0.
@@ -496,8 +503,7 @@ __device__ __forceinline__ void finish_lora(LoraOps<TMT>& o, const LoraRaw<TMT>&
           q[u][1] = bload16(tsrc, in ? oc + 16 : kOutOfRange);
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          if (c0 + u >= a.ks) break;
+        for (int u = 0; u < 8; ++u) {  // loads past the last chunk read 0 and add nothing
           s0 += __builtin_bit_cast(f32x4, q[u][0]);
           s1 += __builtin_bit_cast(f32x4, q[u][1]);
         }
@@ -731,6 +737,536 @@ __global__ void __launch_bounds__(W * kWave) k_linear(LinearArgs a) {
   }
 }
 
+// ------------------------------------------------------------------------------------------------------------------
+// G: decode streaming kernel for up to 32 tokens per launch (TMT = 1 or 2 token tiles of 16).
+//   Work is row units (a row group of 16 rows; with SILU a (gate, up) pair of row groups) x k-tiles, cut into
+//   nbr row blocks x nk k-chunks, one workgroup each; the host sizes the cut so the grid is about one workgroup per CU
+//   with equal shares. The workgroup copies the activation fragments and tile scales of its k-chunk into LDS once;
+//   waves 0..14 split the block's units (and, with fewer units than waves, the chunk's k-tiles between them) and load
+//   only weights from memory, three tiles in flight each; wave 15 computes the LoRA-up term B t of the block's rows
+//   meanwhile (in the chunk-0 workgroup). With nk > 1 every workgroup stores its part sums, and the last of a block's
+//   workgroups to arrive (an atomic counter) adds the nk parts in chunk order and runs the epilogue, so results do not
+//   depend on scheduling.
+constexpr int kGWaves = 16;
+constexpr int kGStream = kGWaves - 1;
+constexpr int kGMaxUnits = 8;
+constexpr int kGLds = 144 * 1024;                   // LDS bytes per workgroup (besides the residual tile)
+constexpr int kGTileAct = 4 * kWave * 16 + 16 * 4;  // LDS bytes per (k-tile, token tile): 4 fragments + 16 scales
+constexpr int kGFragLoads = 10;                     // 16-byte activation loads per thread (at most)
+__host__ __device__ constexpr int gemv_lred_bytes(int nr, int tmt) { return kGMaxUnits * nr * tmt * kWave * 16; }
+__host__ __device__ constexpr int64_t gemv_block_floats(int nr, int tmt) { return (int64_t)kGMaxUnits * nr * tmt * 256; }
+
+struct GemvArgs {
+  LinearArgs L;
+  int32_t nu, nbr, nk;
+  int32_t KT, ntiles, mt;  // k-tiles, token tiles, tokens (32-bit copies: the kernel's preamble avoids 64-bit division)
+  float* pbuf;    // [nbr][nk + 1][gemv_block_floats] part sums; slot nk holds the LoRA term
+  uint32_t* cnt;  // [nbr] arrival counters, zero between calls
+};
+
+// Per-projection epilogue data, staged in LDS so that each output reads its projection's entry by index.
+struct ProjEpi {
+  void* y;
+  const uint16_t* res;
+  int64_t n, ldy, ld_res;
+  float sg, lambda;
+  int32_t y_dtype, y_repeat, head_dim, rg_begin, r;
+};
+
+template <int NR>
+struct GTile {
+  u32x4 c[NR];
+  uint32_t sc[NR];
+};
+
+// Projection and row group of row unit g (flattened over the projections; with SILU both projections' group g).
+__device__ __forceinline__ int unit_proj(const ProjEpi* pe, int nproj, int64_t g) {
+  int p = 0;
+  for (int q = 1; q < nproj; ++q)
+    if (g >= pe[q].rg_begin) p = q;
+  return p;
+}
+
+template <int TMT, bool SILU>
+__global__ void __launch_bounds__(kGWaves * kWave) k_gemv(GemvArgs g) {
+  constexpr int NR = SILU ? 2 : 1;
+  constexpr int kOut = (kGMaxUnits * 16 * TMT * 16 + kGWaves * kWave - 1) / (kGWaves * kWave);
+  constexpr int kTB = 4 / TMT;  // LoRA-down chunk partials loaded together
+  __shared__ __attribute__((aligned(16))) uint8_t s_lds[kGLds];
+  __shared__ uint16_t s_res[kGMaxUnits * 16 * TMT * 16];  // residual of each output (epilogue order)
+  __shared__ ProjEpi s_pe[kMaxProj];
+  __shared__ int s_last;
+  const LinearArgs& a = g.L;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+  const unsigned bid = blockIdx.x, nbr = (unsigned)g.nbr, nk = (unsigned)g.nk;
+  const int b = (int)(bid % nbr), c = (int)(bid / nbr);
+  const int KT = g.KT, mt = g.mt, ntiles = g.ntiles;
+  const int u0 = (int)((unsigned)b * (unsigned)g.nu / nbr);
+  const int U = (int)((unsigned)(b + 1) * (unsigned)g.nu / nbr) - u0;
+  const int t0 = (int)((unsigned)c * (unsigned)KT / nk), T = (int)((unsigned)(c + 1) * (unsigned)KT / nk) - t0;
+  constexpr int64_t tile0 = 0;  // one launch covers every token (at most 32)
+  const int ntl = ntiles < TMT ? ntiles : TMT;  // token tiles present
+  uint8_t* const lred = s_lds + kGLds - gemv_lred_bytes(NR, TMT);
+  const int fr_bytes = TMT * T * 4 * kWave * 16;
+
+  // 1. stream waves: unit u, k-part j of h. Their first two weight tiles are requested before anything else (they
+  //    come from HBM); the preamble is kept short because every instruction of it is fetched cold at each launch.
+  constexpr unsigned char kParts[kGMaxUnits + 1] = {1, 15, 7, 5, 3, 3, 2, 2, 1};  // kGStream / U
+  static_assert(kGStream == 15 && kGMaxUnits == 8, "parts table");
+  const int h = kParts[U];
+  const bool streams = wave < U * h;
+  const int su = streams ? (int)((unsigned)wave / (unsigned)h) : 0, sj = streams ? wave - su * h : 0;
+  // wave-uniform tile range (readfirstlane: keeps the loop counter scalar and the loop's wait counts exact)
+  const int ta = __builtin_amdgcn_readfirstlane(t0 + (int)((unsigned)(sj * T) / (unsigned)h));
+  const int tb = __builtin_amdgcn_readfirstlane(streams ? t0 + (int)((unsigned)((sj + 1) * T) / (unsigned)h) : ta);
+  rsrc_t cd[NR], sd[NR];
+#pragma unroll
+  for (int nr = 0; nr < NR; ++nr) {
+    const int64_t gu = u0 + su;
+    int p = nr;
+    if (!SILU) {
+      p = 0;
+      for (int q = 1; q < a.nproj; ++q)
+        if (gu >= a.p[q].rg_begin) p = q;
+      p = __builtin_amdgcn_readfirstlane(p);
+    }
+    const ProjArgs& P = a.p[p];
+    const int64_t rg = SILU ? gu : gu - P.rg_begin;
+    const bool live = streams && rg * 16 < P.n;
+    cd[nr] = make_rsrc(P.codes + rg * KT * kTileCodeBytes, live ? KT * kTileCodeBytes : 0);
+    sd[nr] = make_rsrc(P.scales + rg * KT * kTileScaleBytes, live ? KT * kTileScaleBytes : 0);
+  }
+  const uint32_t c_off = lane * 16, s_off = ((lane % 16) * 2 + (lane / 16) / 2) * 4;
+  auto load = [&](GTile<NR>& t, int kt) {
+    const bool in = kt < tb;
+    const int kc = __builtin_amdgcn_readfirstlane(in ? kt * kTileCodeBytes : 0);
+    const int ks = __builtin_amdgcn_readfirstlane(in ? kt * kTileScaleBytes : 0);
+#pragma unroll
+    for (int nr = 0; nr < NR; ++nr) {
+      t.c[nr] = __builtin_amdgcn_raw_buffer_load_b128(cd[nr], in ? c_off : kOutOfRange, kc, kNonTemporal);
+      t.sc[nr] = __builtin_amdgcn_raw_buffer_load_b32(sd[nr], in ? s_off : kOutOfRange, ks, kNonTemporal);
+    }
+  };
+  GTile<NR> B0, B1, B2;
+  load(B0, ta);
+  __builtin_amdgcn_sched_barrier(0);  // issue order B0, B1: the loop's wait counts rely on it
+  load(B1, ta + 1);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. the chunk's activation fragments ([tt][lt][s][lane], 16 bytes) and tile scales ([tt][lt][16] f32), loaded
+  //    straight into LDS (1 KB per wave and step; a chunk never straddles token tiles: T * 256 is a multiple of 64)
+  const int nfc = TMT * T * 4 * kWave, nsc = TMT * T * 4;  // 16-byte pieces of fragments, of scales
+  {
+    const rsrc_t xsrc = make_rsrc(a.xs + tile0 * KT * 4 * kWave, (int64_t)ntl * KT * 4 * kWave * 16);
+    for (int ch = wave; ch * kWave < nfc; ch += kGWaves) {
+      const int q0 = ch * kWave, tt = q0 >= T * 4 * kWave ? 1 : 0, rem = q0 - tt * T * 4 * kWave;  // TMT <= 2
+      const int so = __builtin_amdgcn_readfirstlane((int)((((int64_t)tt * KT + t0) * 4 * kWave + rem) * 16));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xsrc, (__attribute__((address_space(3))) void*)(s_lds + q0 * 16), 16,
+                                               lane * 16, so, 0, 0);
+    }
+    const rsrc_t ssrc = make_rsrc(a.xsc + tile0 * KT * 16, (int64_t)ntl * KT * 16 * 4);
+    for (int ch = wave; ch * kWave < nsc; ch += kGWaves) {
+      // scale piece q: token tile q / (T*4), then 16 bytes of the [lt][16] block; lanes past nsc load nothing
+      const int q = ch * kWave + lane, tt = q >= T * 4 ? 1 : 0, rem = q - tt * T * 4;  // TMT <= 2
+      if (q < nsc)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ssrc, (__attribute__((address_space(3))) void*)(s_lds + fr_bytes + ch * kWave * 16), 16,
+            (uint32_t)((((int64_t)tt * KT + t0) * 16) * 4 + rem * 16), 0, 0, 0);
+    }
+  }
+  if (threadIdx.x < kMaxProj) {
+#pragma unroll
+    for (int q = 0; q < kMaxProj; ++q)
+      if (threadIdx.x == q && q < a.nproj) {
+        const ProjArgs& P = a.p[q];
+        s_pe[q] = ProjEpi{P.y, P.res, P.n, P.ldy, P.ld_res, gload(P.s_g), P.lambda, P.y_dtype, P.y_repeat,
+                          P.head_dim, P.rg_begin, P.r};
+      }
+  }
+  // residual of this thread's outputs (output e = (unit, token, row) = ((u * TMT*16 + tok) * 16 + row)); outputs
+  // without one read a valid stand-in address. Issued here, the barrier's wait covers them at no extra cost.
+  uint16_t res[kOut];
+#pragma unroll
+  for (int i = 0; i < kOut; ++i) {
+    const int e = threadIdx.x + i * kGWaves * kWave;
+    const int u = e >> (TMT == 1 ? 8 : 9), tok = (e >> 4) & (TMT * 16 - 1), row = e & 15;
+    const int64_t gu = u0 + u;
+    const uint16_t* rb = a.p[0].res;
+    int64_t rbeg = 0, nl = a.p[0].n, ld = a.p[0].ld_res;
+    if (!SILU) {
+#pragma unroll
+      for (int q = 1; q < kMaxProj; ++q)
+        if (q < a.nproj && gu >= a.p[q].rg_begin) {
+          rb = a.p[q].res;
+          rbeg = a.p[q].rg_begin;
+          nl = a.p[q].n;
+          ld = a.p[q].ld_res;
+        }
+    }
+    const int64_t n = (gu - rbeg) * 16 + row;
+    const bool ok = rb && u < U && tok < mt && n < nl;
+    res[i] = gload(ok ? rb + tok * ld + n : reinterpret_cast<const uint16_t*>(a.xsc));
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's loads have landed (loads to LDS are counted by vmcnt)
+#pragma unroll
+  for (int i = 0; i < kOut; ++i) s_res[threadIdx.x + i * kGWaves * kWave] = res[i];
+  __syncthreads();
+
+  f32x4 acc[NR][TMT];
+#pragma unroll
+  for (int nr = 0; nr < NR; ++nr)
+#pragma unroll
+    for (int tt = 0; tt < TMT; ++tt) acc[nr][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // (a tile past the wave's range has zero weights; its activations are read at the last tile of the range, which
+  // are finite, so it adds exactly zero)
+  auto compute = [&](const GTile<NR>& t, int kt) {
+    const int lt = (kt < tb ? kt : tb - 1) - t0;
+    f32x4 part[NR][TMT];
+#pragma unroll
+    for (int nr = 0; nr < NR; ++nr)
+#pragma unroll
+      for (int tt = 0; tt < TMT; ++tt) part[nr][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 bf[TMT];
+#pragma unroll
+      for (int tt = 0; tt < TMT; ++tt)
+        bf[tt] = *reinterpret_cast<const u32x4*>(s_lds + (((tt * T + lt) * 4 + s) * kWave + lane) * 16);
+#pragma unroll
+      for (int nr = 0; nr < NR; ++nr) {
+        const uint32_t scv = ((t.sc[nr] >> (8 * s)) & 0xFFu) * 0x00800080u;  // E4M3 byte << 7 = E4M3 * 2^-8 in f16
+        const f16x2 sh = __builtin_bit_cast(f16x2, scv);
+        const uint32_t cw = t.c[nr][s];
+        const f16x2 q0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 256.0f, 0) * sh;
+        const f16x2 q1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 256.0f, 1) * sh;
+        const f16x2 q2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 256.0f, 2) * sh;
+        const f16x2 q3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 256.0f, 3) * sh;
+        const f16x8 wv = {q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
+#pragma unroll
+        for (int tt = 0; tt < TMT; ++tt)
+          part[nr][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, __builtin_bit_cast(f16x8, bf[tt]), part[nr][tt],
+                                                                0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < TMT; ++tt) {
+      const float u = *reinterpret_cast<const float*>(s_lds + fr_bytes + ((tt * T + lt) * 16 + lane % 16) * 4);
+#pragma unroll
+      for (int nr = 0; nr < NR; ++nr)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[nr][tt][e] = __builtin_fmaf(part[nr][tt][e], u, acc[nr][tt][e]);
+    }
+  };
+
+  if (streams) {
+    // three tiles in flight: the load two tiles ahead is issued before the current tile is computed. The body has no
+    // early exit (a loop with several exits gets flow edges that make the compiler's wait counts conservative); tiles
+    // past the range are loaded out of range (no memory traffic) and add zero.
+    for (int kt = ta; kt < tb; kt += 3) {
+      load(B2, kt + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(B0, kt);
+      __builtin_amdgcn_sched_barrier(0);
+      load(B0, kt + 3);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(B1, kt + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      load(B1, kt + 4);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(B2, kt + 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // (a separate block after the loop, so that the loop's entry state holds the stream's loads only)
+  if (wave == kGWaves - 1 && c == 0) {
+    // 3. LoRA-up of the block's rows: per projection and 32-rank chunk, t (the LoRA-down chunk partials summed in
+    //    chunk order, split into bf16 hi and lo parts), then two bf16 MFMAs per unit, accumulated over rank chunks
+    //    in LDS. Lane layouts: B rows (lane%16 = row, ranks 8 (lane/16) ..) and t (lane%16 = token, same ranks).
+    const rsrc_t tsrc = make_rsrc(a.t_part, a.t_bytes);
+#pragma unroll
+    for (int nr = 0; nr < NR; ++nr) {
+      int pfirst = SILU ? nr : unit_proj(s_pe, a.nproj, u0), plast = SILU ? nr : unit_proj(s_pe, a.nproj, u0 + U - 1);
+      pfirst = __builtin_amdgcn_readfirstlane(pfirst);
+      plast = __builtin_amdgcn_readfirstlane(plast);
+      for (int p = pfirst; p <= plast; ++p) {
+        const ProjEpi& E = s_pe[p];
+        const uint16_t* Bm = nullptr;
+#pragma unroll
+        for (int q = 0; q < kMaxProj; ++q)
+          if (q == p) Bm = a.p[q].B;
+        const int r = E.r;
+        for (int jc = 0; jc * 32 < r; ++jc) {
+          // t of each token tile: chunk partials in chunk order
+          const rsrc_t bsrc = make_rsrc(Bm, E.n * r * 2);
+          u32x4 thi[TMT], tlo[TMT];
+#pragma unroll
+          for (int tt = 0; tt < TMT; ++tt) {
+            const bool ok = tt < ntl;
+            const uint32_t off =
+                (uint32_t)((((((int64_t)p * ntiles + tile0 + tt) * kRankChunks + jc) * a.ks) * kWave + lane) * 32);
+            // chunks in order, kTB loads at a time; loads past the last chunk read 0 and add nothing
+            f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+            for (int c0 = 0; c0 < a.ks; c0 += kTB) {
+              u32x4 q[kTB][2];
+#pragma unroll
+              for (int v = 0; v < kTB; ++v) {
+                const bool in = ok && c0 + v < a.ks;
+                const uint32_t oc = off + (uint32_t)(c0 + v) * kWave * 32;
+                q[v][0] = bload16(tsrc, in ? oc : kOutOfRange);
+                q[v][1] = bload16(tsrc, in ? oc + 16 : kOutOfRange);
+              }
+#pragma unroll
+              for (int v = 0; v < kTB; ++v) {
+                s0 += __builtin_bit_cast(f32x4, q[v][0]);
+                s1 += __builtin_bit_cast(f32x4, q[v][1]);
+              }
+            }
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float t = e < 4 ? s0[e] : s1[e - 4];
+              const uint32_t th = f32_to_bf16(t);
+              const uint32_t tl = f32_to_bf16(t - bf16_to_f32((uint16_t)th));  // t - th is exact in f32
+              if (e % 2 == 0) {
+                hi[e / 2] = th;
+                lo[e / 2] = tl;
+              } else {
+                hi[e / 2] |= th << 16;
+                lo[e / 2] |= tl << 16;
+              }
+            }
+            thi[tt] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+            tlo[tt] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+          }
+          // B t for the units of this projection, four at a time, added into the LDS slot (unit, nr, tt)
+          for (int ug = 0; ug < U; ug += 4) {
+            u32x4 bfr[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int u = ug + v;
+              const int64_t gu = u0 + u;
+              const bool mine = u < U && (SILU || unit_proj(s_pe, a.nproj, gu) == p);
+              const int64_t n = (SILU ? gu : gu - E.rg_begin) * 16 + lane % 16;
+              const int j0 = jc * 32 + (lane / 16) * 8;
+              if (r % 8 == 0) {
+                bfr[v] = bload16(bsrc, (mine && n < E.n && j0 < r) ? (uint32_t)((n * r + j0) * 2) : kOutOfRange);
+              } else {
+                uint32_t w[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const int64_t off = (n * r + j0 + 2 * e) * 2;
+                  const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(
+                      bsrc, (mine && n < E.n && j0 + 2 * e < r) ? (uint32_t)off : kOutOfRange, 0, 0);
+                  const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(
+                      bsrc, (mine && n < E.n && j0 + 2 * e + 1 < r) ? (uint32_t)(off + 2) : kOutOfRange, 0, 0);
+                  w[e] = lo | (hi << 16);
+                }
+                bfr[v] = u32x4{w[0], w[1], w[2], w[3]};
+              }
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int u = ug + v;
+              if (u >= U) break;
+              if (!SILU && unit_proj(s_pe, a.nproj, u0 + u) != p) continue;
+#pragma unroll
+              for (int tt = 0; tt < TMT; ++tt) {
+                f32x4 la = {0.f, 0.f, 0.f, 0.f};
+                la = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bfr[v]),
+                                                             __builtin_bit_cast(bf16x8, thi[tt]), la, 0, 0, 0);
+                la = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bfr[v]),
+                                                             __builtin_bit_cast(bf16x8, tlo[tt]), la, 0, 0, 0);
+                f32x4* slot = reinterpret_cast<f32x4*>(lred + ((((u * NR + nr) * TMT + tt) * kWave) + lane) * 16);
+                *slot = jc == 0 ? la : *slot + la;
+              }
+            }
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();  // every wave is done with the activations in LDS
+
+  // 4. part sums of the stream waves into LDS (over the activation area), then the per-output sums
+  if (streams) {
+#pragma unroll
+    for (int nr = 0; nr < NR; ++nr)
+#pragma unroll
+      for (int tt = 0; tt < TMT; ++tt)
+        *reinterpret_cast<f32x4*>(s_lds + (((((su * h + sj) * NR + nr) * TMT + tt) * kWave) + lane) * 16) =
+            acc[nr][tt];
+  }
+  __syncthreads();
+
+  const bool has_lora = c == 0;  // LoRA slots were written in chunk 0 (zero where the projection has no adapter)
+  const int nout = U * TMT * 256;  // outputs (unit, token, row); tokens past mt are skipped
+  float vsum[kOut][NR], vlo[kOut][NR];
+#pragma unroll
+  for (int i = 0; i < kOut; ++i) {
+    const int e = threadIdx.x + i * kGWaves * kWave;
+    const int u = e >> (TMT == 1 ? 8 : 9), tok = (e >> 4) & (TMT * 16 - 1), row = e & 15;
+    const int tt = tok / 16, col = tok % 16;
+    const int ln = (row / 4) * 16 + col, ii = row % 4;
+#pragma unroll
+    for (int nr = 0; nr < NR; ++nr) {
+      float s = 0.f, lo = 0.f;
+      if (e < nout) {
+        for (int j = 0; j < h; ++j)
+          s += reinterpret_cast<const float*>(s_lds + (((((u * h + j) * NR + nr) * TMT + tt) * kWave) + ln) * 16)[ii];
+        if (has_lora && s_pe[SILU ? nr : unit_proj(s_pe, a.nproj, u0 + u)].r > 0)
+          lo = reinterpret_cast<const float*>(lred + ((((u * NR + nr) * TMT + tt) * kWave) + ln) * 16)[ii];
+      }
+      vsum[i][nr] = s;
+      vlo[i][nr] = lo;
+    }
+  }
+
+  // 5. split k: store this chunk's sums (and, in chunk 0, the LoRA terms); the last workgroup of the block to arrive
+  //    adds the chunks in order. The sums are written and read with device-scope relaxed atomic accesses, which go
+  //    to memory past the per-XCD L2 caches; the stores have completed (s_waitcnt) before the workgroup's barrier and
+  //    its arrival. No cache-wide fence is needed, so no L2 writeback or invalidation.
+  if (g.nk > 1) {
+    const int64_t PB = gemv_block_floats(NR, TMT);
+    float* pb = g.pbuf + (int64_t)b * (g.nk + 1) * PB;
+#pragma unroll
+    for (int i = 0; i < kOut; ++i) {
+      const int e = threadIdx.x + i * kGWaves * kWave;
+      if (e >= nout) break;
+#pragma unroll
+      for (int nr = 0; nr < NR; ++nr) {
+        __hip_atomic_store(pb + (int64_t)c * PB + (int64_t)e * NR + nr, vsum[i][nr], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        if (c == 0)
+          __hip_atomic_store(pb + (int64_t)g.nk * PB + (int64_t)e * NR + nr, vlo[i][nr], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // every store of this thread has completed
+    __syncthreads();
+    if (threadIdx.x == 0)
+      s_last = __hip_atomic_fetch_add(g.cnt + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               (uint32_t)(g.nk - 1);
+    __syncthreads();
+    if (!s_last) return;
+#pragma unroll
+    for (int i = 0; i < kOut; ++i) {
+      const int e = threadIdx.x + i * kGWaves * kWave;
+      if (e >= nout) break;
+#pragma unroll
+      for (int nr = 0; nr < NR; ++nr) {
+        float s = __hip_atomic_load(pb + (int64_t)e * NR + nr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int cc = 1; cc < g.nk; ++cc)
+          s += __hip_atomic_load(pb + (int64_t)cc * PB + (int64_t)e * NR + nr, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+        vsum[i][nr] = s;
+        vlo[i][nr] = __hip_atomic_load(pb + (int64_t)g.nk * PB + (int64_t)e * NR + nr, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(g.cnt + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // 6. epilogue: y = s_g * sum + lambda * lora (SILU: SiLU(gate) * up), + residual, broadcast, rounding
+#pragma unroll
+  for (int i = 0; i < kOut; ++i) {
+    const int e = threadIdx.x + i * kGWaves * kWave;
+    if (e >= nout) break;
+    const int u = e >> (TMT == 1 ? 8 : 9), tok = (e >> 4) & (TMT * 16 - 1), row = e & 15;
+    if (tok >= mt) continue;
+    const int64_t gu = u0 + u;
+    const int p0 = SILU ? 0 : unit_proj(s_pe, a.nproj, gu);
+    const ProjEpi& E = s_pe[p0];
+    const int64_t n = (SILU ? gu : gu - E.rg_begin) * 16 + row;
+    if (n >= E.n) continue;
+    float val[NR];
+#pragma unroll
+    for (int nr = 0; nr < NR; ++nr) {
+      const ProjEpi& F = s_pe[SILU ? nr : p0];
+      val[nr] = F.sg * vsum[i][nr] + F.lambda * vlo[i][nr];
+    }
+    float out = val[0];
+    if (SILU) out = val[0] / (1.0f + __expf(-val[0])) * val[NR - 1];
+    if (E.res) out += bf16_to_f32(s_res[e]);
+    const int64_t gtok = a.tok0 + tok;
+    const int rep = E.y_repeat > 1 ? E.y_repeat : 1;
+    for (int gi = 0; gi < rep; ++gi) {
+      const int64_t col_out = rep > 1 ? ((n / E.head_dim) * rep + gi) * E.head_dim + n % E.head_dim : n;
+      const int64_t off = gtok * E.ldy + col_out;
+      if (E.y_dtype == QN_F32) reinterpret_cast<float*>(E.y)[off] = out;
+      else reinterpret_cast<uint16_t*>(E.y)[off] = f32_to_bf16(out);
+    }
+  }
+}
+
+// Row blocks x k-chunks of the decode kernel: about one workgroup per CU, at most kGMaxUnits units per block, the
+// chunk's activations within LDS; among those, the cut with the least estimated time (largest share streamed at
+// ~25 GB/s per CU, the activation copy at ~80 GB/s, ~1.5 us more for a split k).
+struct GemvCut {
+  int nbr, nk;
+};
+inline GemvCut gemv_cut(int64_t nu, int64_t KT, int tmt, int nr) {
+  const int64_t act_cap = (kGLds - gemv_lred_bytes(nr, tmt)) / ((int64_t)tmt * kGTileAct);
+  GemvCut best{0, 0};
+  double best_t = 1e30;
+  int nk_only = 0;  // tuning override: QN_GEMV_NK=<k-chunks>
+  if (const char* ov = std::getenv("QN_GEMV_NK")) nk_only = std::atoi(ov);
+  for (int64_t nk = 1; nk <= KT && nk <= 64; ++nk) {
+    if (nk_only > 0 && nk != nk_only) continue;
+    const int64_t tmax = ceil_div(KT, nk);
+    if (tmax > act_cap) continue;
+    if (tmax * tmt * 4 * kWave > kGFragLoads * kGWaves * kWave || tmax * tmt * 4 > kGWaves * kWave) continue;
+    int64_t nbr = 256 / nk;
+    if (nbr > nu) nbr = nu;
+    if (nbr < 1) break;
+    const int64_t umax = ceil_div(nu, nbr);
+    if (umax > kGMaxUnits) continue;
+    const double stream = (double)umax * tmax * nr * 1152.0 / 25e3;  // us
+    const double act = (double)tmax * tmt * kGTileAct / 80e3;
+    const double t = (stream + act) + (nk > 1 ? 1.5 : 0.0);
+    if (t < best_t) {
+      best_t = t;
+      best = GemvCut{(int)nbr, (int)nk};
+    }
+  }
+  return best;
+}
+
+// Decode kernel use: up to 32 tokens and a cut that fits. By default it is taken where it measured faster than the
+// general kernel: no split k and at least four row units per workgroup (the wide feed-forward projections); split
+// k pays for its partial sums with memory round trips that cost more than the better balance gains. Tuning
+// overrides (read at each call): QN_GEMV_OFF=1 always takes the general kernel, QN_GEMV_NK=<k-chunks> takes the
+// decode kernel with that cut whenever it fits.
+inline bool gemv_on(int64_t m) {
+  if (m < 1 || m > 32) return false;
+  const char* off = std::getenv("QN_GEMV_OFF");
+  return !(off && off[0] == '1');
+}
+inline bool gemv_pick(const GemvCut& cut, int64_t nu) {
+  if (cut.nbr <= 0) return false;
+  if (std::getenv("QN_GEMV_NK")) return true;
+  return cut.nk == 1 && ceil_div(nu, cut.nbr) >= 4;
+}
+
+size_t gemv_pbuf_bytes(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj) {
+  if (!gemv_on(m) || !projs || nproj < 1) return 0;
+  const int tmt = (int)ceil_div(m, 16);
+  const int64_t KT = ceil_div(k, kKTile);
+  int64_t nu_flat = 0;
+  for (int p = 0; p < nproj; ++p) nu_flat += ceil_div(projs[p].n, 16);
+  size_t bytes = 0;
+  const GemvCut cf = gemv_cut(nu_flat, KT, tmt, 1);
+  if (cf.nk > 1) bytes = (size_t)cf.nbr * (cf.nk + 1) * gemv_block_floats(1, tmt) * 4;
+  if (nproj == 2) {
+    const GemvCut cp = gemv_cut(ceil_div(projs[0].n, 16), KT, tmt, 2);
+    if (cp.nk > 1) {
+      const size_t bp = (size_t)cp.nbr * (cp.nk + 1) * gemv_block_floats(2, tmt) * 4;
+      bytes = bp > bytes ? bp : bytes;
+    }
+  }
+  return bytes;
+}
+
 template <int TMT, int R, int W, bool SILU>
 void launch_linear(const LinearArgs& a, int64_t nwg, hipStream_t s) {
   hipLaunchKernelGGL((k_linear<TMT, R, W, SILU>), dim3((unsigned)nwg), dim3(W * kWave), 0, s, a);
@@ -786,9 +1322,8 @@ inline bool aligned(const void* p, size_t al) { return ((uintptr_t)p % al) == 0;
 using namespace qn;
 
 extern "C" size_t nvfp4_lora_linear_workspace(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj) {
-  (void)projs;
   if (m <= 0 || k <= 0 || nproj <= 0) return 0;
-  return workspace_layout(m, k, nproj).total;
+  return workspace_layout(m, k, projs, nproj).total;
 }
 
 extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const qn_aqn* aqn,
@@ -838,7 +1373,7 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
     if (aqn->noise && aqn->noise_ld < 0) return QN_ERR_SHAPE;
     if (aqn->noise && aqn->noise_ld > 0 && aqn->noise_ld < k) return QN_ERR_SHAPE;
   }
-  const Workspace wl = workspace_layout(m, k, nproj);
+  const Workspace wl = workspace_layout(m, k, projs, nproj);
   if (!workspace || workspace_bytes < wl.total) return QN_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return QN_ERR_ALIGN;
   if (k > 131072) return QN_ERR_UNSUPPORTED;
@@ -893,6 +1428,8 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
     pa.xs = xs;
     pa.xsc = xsc;
     pa.t_part = t_part;
+    pa.cnt = reinterpret_cast<uint32_t*>(ws + wl.cnt);
+    pa.ncnt = 256;
     const bool big = aqn && ntiles >= kRstdKernelTiles;
     pa.rstd_in = big ? rstd : nullptr;
     const dim3 grid((unsigned)ntiles, (unsigned)ks, (unsigned)(npg > 0 ? npg : 1));
@@ -940,11 +1477,35 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
   la.xs = xs;
   la.xsc = xsc;
   la.t_part = reinterpret_cast<const u32x4*>(t_part);
-  la.t_bytes = (int64_t)(wl.total - wl.t_part);
+  la.t_bytes = (int64_t)(wl.pbuf - wl.t_part);
   la.ks = ks;
   const bool silu = epilogue == QN_EPI_SILU_MUL;
   const int64_t nrg = silu ? 2 * ceil_div(projs[0].n, 16) : rg_total;
   if (nrg == 0 || !run_main) return hipGetLastError() == hipSuccess ? QN_OK : QN_ERR_HIP;
+  if (gemv_on(m)) {
+    const int tmt = (int)ceil_div(m, 16);
+    const int64_t nu = silu ? ceil_div(projs[0].n, 16) : rg_total;
+    const GemvCut cut = gemv_cut(nu, KT, tmt, silu ? 2 : 1);
+    if (gemv_pick(cut, nu)) {
+      GemvArgs ga{};
+      ga.L = la;
+      ga.L.tok0 = 0;
+      ga.KT = (int32_t)KT;
+      ga.ntiles = (int32_t)ceil_div(m, 16);
+      ga.mt = (int32_t)m;
+      ga.nu = (int32_t)nu;
+      ga.nbr = cut.nbr;
+      ga.nk = cut.nk;
+      ga.pbuf = reinterpret_cast<float*>(ws + wl.pbuf);
+      ga.cnt = reinterpret_cast<uint32_t*>(ws + wl.cnt);
+      const dim3 grid((unsigned)(cut.nbr * cut.nk)), block(kGWaves * kWave);
+      if (tmt == 1 && !silu) hipLaunchKernelGGL((k_gemv<1, false>), grid, block, 0, s, ga);
+      else if (tmt == 1) hipLaunchKernelGGL((k_gemv<1, true>), grid, block, 0, s, ga);
+      else if (!silu) hipLaunchKernelGGL((k_gemv<2, false>), grid, block, 0, s, ga);
+      else hipLaunchKernelGGL((k_gemv<2, true>), grid, block, 0, s, ga);
+      return hipGetLastError() == hipSuccess ? QN_OK : QN_ERR_HIP;
+    }
+  }
   for (int64_t t0 = 0; t0 < m; t0 += kMaxTokensPerLaunch) {
     la.tok0 = t0;
     const int64_t mt = (m - t0) < kMaxTokensPerLaunch ? (m - t0) : kMaxTokensPerLaunch;

@@ -177,6 +177,59 @@ def test_fused_norm_matches_standalone_norm(qn, m, k, per_row):
     assert torch.equal(y1, y2)
 
 
+# The two streaming kernels and the split-k form of the decode kernel, each forced through the library's tuning
+# overrides (read at every call), on the same cases: default choice, the general kernel, the decode kernel without
+# and with a split k.
+KERNEL_PATHS = {"default": {}, "general": {"QN_GEMV_OFF": "1"}, "decode": {"QN_GEMV_NK": "1"},
+                "decode-splitk": {"QN_GEMV_NK": "3"}}
+
+
+@pytest.mark.parametrize("path", list(KERNEL_PATHS))
+@pytest.mark.parametrize("m,ns,k,silu,residual,r,gqa", [
+    (1, [200], 1024, False, False, 32, 1),
+    (16, [520, 64, 64], 1040, False, False, 64, 1),
+    (17, [96], 3584, False, True, 12, 1),
+    (32, [256], 512, False, True, 32, 1),
+    (16, [384, 384], 512, True, False, 32, 1),
+    (5, [1040, 1040], 384, True, False, 8, 1),
+    (32, [128, 128], 1024, True, False, 0, 1),
+    (9, [512, 128, 128], 640, False, False, 32, 4),
+])
+def test_linear_kernel_paths(qn, monkeypatch, path, m, ns, k, silu, residual, r, gqa):
+    for key in ("QN_GEMV_OFF", "QN_GEMV_NK"):
+        monkeypatch.delenv(key, raising=False)
+    for key, val in KERNEL_PATHS[path].items():
+        monkeypatch.setenv(key, val)
+    c = Case(m, ns, k, r=r, seed=m * 7 + k)
+    wq = [qn.quantize(dev_bf16(w), qn.LAYOUT_TILED) for w in c.w]
+    res = synth.normal_bf16(56, (m, ns[0])) if residual else None
+    ys, projs = [], []
+    for p, n in enumerate(ns):
+        rep = gqa if p == len(ns) - 1 and gqa > 1 else 1
+        y = torch.full((m, n * rep), float("nan"), dtype=torch.float32, device=DEV)
+        ys.append(y)
+        A = dev_bf16(c.A[p]) if r else None
+        B = dev_bf16(c.B[p]) if r else None
+        projs.append(qn.Projection(wq[p], None if (silu and p == 1) else y, A, B, c.lam,
+                                   residual=dev_bf16(res) if (residual and p == 0) else None,
+                                   y_repeat=rep, head_dim=64))
+    aqn = qn.make_aqn(dev_bf16(c.gamma), dev_f32(c.noise), c.sigma, 1e-6)
+    qn.lora_linear(dev_bf16(c.x), projs, aqn, qn.EPI_SILU_MUL if silu else qn.EPI_NONE)
+    torch.cuda.synchronize()
+    if silu:
+        ref = oracle.silu_mul(c.oracle_y(0), c.oracle_y(1))
+        assert rel_err(ys[0].cpu().numpy(), ref) <= LINEAR_TOL
+        return
+    for p in range(len(ns)):
+        ref = c.oracle_y(p)
+        if residual and p == 0:
+            ref = ref + bf16_bits_to_f64(res)
+        rep = gqa if p == len(ns) - 1 and gqa > 1 else 1
+        if rep > 1:
+            ref = oracle.gqa_broadcast(ref, rep, 64)
+        assert rel_err(ys[p].cpu().numpy(), ref) <= LINEAR_TOL, (path, p)
+
+
 def test_linear_deterministic(qn):
     c = Case(16, [512], 2048, seed=11)
     a = c.gpu(qn)[0].clone()
