@@ -205,7 +205,7 @@ def main():
         "step_achieved_GBps": step_bytes / (ms_step * 1e-3) / 1e9,
         "step_frac_of_hbm_peak": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "step_tflops": flops(shape, m) / (ms_step * 1e-3) / 1e12,
-        "roofline": {"kernel": "k_linear gate|up (SiLU epilogue)", "bound": "hbm", "achieved": achieved,
+        "roofline": {"kernel": "k_gemv gate|up (SiLU epilogue)", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "launch_us": main_ms * 1e3, "bytes_per_launch": gu_bytes},
     }

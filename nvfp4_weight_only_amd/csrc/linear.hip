@@ -157,7 +157,7 @@ constexpr int kProWaves = 16;
 struct PrologueArgs {
   const uint16_t* x;
   int64_t ldx, m, k, KT;
-  int32_t CT, ks, npg, has_aqn;
+  int32_t CT, ks, npg, has_aqn, nproj;
   int32_t vec_x, vec_g, vec_z;
   const uint16_t* gamma;
   const float* noise;
@@ -174,7 +174,116 @@ struct PrologueArgs {
   int32_t ncnt;
 };
 
-template <int NT, bool AQN>
+// Sum of squares of one row by one wave, in the summation order of the standalone norm with NT threads (as
+// row_sumsq_one_wave), read through a buffer descriptor: row_off is the row's byte offset in it. VEC: 16-byte loads.
+// The first batch of loads (eight chunks per lane) is issued separately by row_sumsq_load, ahead of other loads, so
+// the sum waits for the row alone.
+template <int NT>
+struct RowSqPlan {
+  static constexpr int V = NT / kWave;  // stand-in threads per lane
+  static constexpr int VB = V < 8 ? V : 8;
+  static constexpr int IB = 8 / VB;
+};
+
+template <bool VEC>
+__device__ __forceinline__ void bload_chunk(rsrc_t src, uint32_t off, uint32_t (&w)[4]) {
+  if (VEC) {
+    const u32x4 q = bload16(src, off);
+    w[0] = q[0]; w[1] = q[1]; w[2] = q[2]; w[3] = q[3];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(src, off == kOutOfRange ? off : off + 4 * e, 0, 0);
+      const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(src, off == kOutOfRange ? off : off + 4 * e + 2, 0, 0);
+      w[e] = lo | (hi << 16);
+    }
+  }
+}
+
+template <int NT, bool VEC>
+__device__ __forceinline__ void row_sumsq_load(rsrc_t src, uint32_t row_off, int d, uint32_t (&q)[8][4]) {
+  using P = RowSqPlan<NT>;
+  const int lane = threadIdx.x % kWave, nch = d / 8;
+#pragma unroll
+  for (int ib = 0; ib < P::IB; ++ib)
+#pragma unroll
+    for (int vb = 0; vb < P::VB; ++vb) {
+      const int ch = ib * NT + vb * kWave + lane;
+      bload_chunk<VEC>(src, ch < nch ? row_off + (uint32_t)ch * 16 : kOutOfRange, q[ib * P::VB + vb]);
+    }
+}
+
+template <int NT, bool VEC>
+__device__ inline float row_sumsq_buf(rsrc_t src, uint32_t row_off, int d, const uint32_t (&pre)[8][4]) {
+  using P = RowSqPlan<NT>;
+  constexpr int V = P::V, VB = P::VB, IB = P::IB;
+  const int lane = threadIdx.x % kWave;
+  const int nch = d / 8;
+  float ss[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) ss[v] = 0.0f;
+  for (int i0 = 0; i0 * NT < nch; i0 += IB) {
+#pragma unroll
+    for (int v0 = 0; v0 < V; v0 += VB) {
+      uint32_t q[IB][VB][4];
+      if (i0 == 0 && v0 == 0) {
+#pragma unroll
+        for (int ib = 0; ib < IB; ++ib)
+#pragma unroll
+          for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) q[ib][vb][e] = pre[ib * VB + vb][e];
+      } else {
+#pragma unroll
+        for (int ib = 0; ib < IB; ++ib)
+#pragma unroll
+          for (int vb = 0; vb < VB; ++vb) {
+            const int ch = (i0 + ib) * NT + (v0 + vb) * kWave + lane;
+            bload_chunk<VEC>(src, ch < nch ? row_off + (uint32_t)ch * 16 : kOutOfRange, q[ib][vb]);
+          }
+      }
+      // each stand-in adds its chunks in chunk order, elements in order
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+        for (int ib = 0; ib < IB; ++ib) {
+          if ((i0 + ib) * NT + (v0 + vb) * kWave + lane >= nch) continue;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x0 = lo_bf16(q[ib][vb][e]), x1 = hi_bf16(q[ib][vb][e]);
+            ss[v0 + vb] = __fadd_rn(ss[v0 + vb], __fmul_rn(x0, x0));
+            ss[v0 + vb] = __fadd_rn(ss[v0 + vb], __fmul_rn(x1, x1));
+          }
+        }
+    }
+  }
+  float tot = 0.0f;
+#pragma unroll
+  for (int v = 0; v < V; ++v) tot = __fadd_rn(tot, wave_sum(ss[v]));
+  return tot;
+}
+
+// Eight consecutive bf16 (VEC: one 16-byte load) and eight f32 (two loads) through a buffer descriptor.
+template <bool VEC>
+__device__ __forceinline__ void bload_bf16x8(rsrc_t src, uint32_t off, uint32_t (&w)[4]) {
+  bload_chunk<VEC>(src, off, w);
+}
+template <bool VEC>
+__device__ __forceinline__ void bload_f32x8(rsrc_t src, uint32_t off, float (&z)[8]) {
+  if (VEC) {
+    const f32x4 z0 = __builtin_bit_cast(f32x4, bload16(src, off));
+    const f32x4 z1 = __builtin_bit_cast(f32x4, bload16(src, off == kOutOfRange ? off : off + 16));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { z[e] = z0[e]; z[4 + e] = z1[e]; }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      z[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(src, off == kOutOfRange ? off : off + 4 * e, 0, 0));
+  }
+}
+
+// VEC: x rows, gamma and the noise rows start 16-byte aligned at every 8-element group (all loads 16 bytes wide).
+template <int NT, bool AQN, bool VEC>
 __global__ void __launch_bounds__(kProWaves * kWave) k_prologue(PrologueArgs a) {
   constexpr int kCT = kMaxChunkTiles;                              // k-tiles per chunk (at most)
   constexpr int kProSlices = kCT * 4 / kProWaves;                // 32-wide k-slices per wave (at most)
@@ -184,37 +293,46 @@ __global__ void __launch_bounds__(kProWaves * kWave) k_prologue(PrologueArgs a) 
   __shared__ __attribute__((aligned(16))) uint16_t s_h[16][kHRow];
   __shared__ f32x4 s_red[kProWaves][2][kWave];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
-  const int64_t tile = blockIdx.x, ntiles = gridDim.x;
+  const int tile = blockIdx.x, ntiles = gridDim.x;
   const int c = blockIdx.y, pg = blockIdx.z;
-  const int64_t kt0 = (int64_t)c * a.CT;
-  const int ctn = (int)(a.KT - kt0 < a.CT ? a.KT - kt0 : a.CT);  // k-tiles in this chunk
-  const int64_t kc0 = kt0 * kKTile;
-  const bool lora = pg < a.npg;
-  const int p = lora ? a.pg_p[pg] : 0, jc = lora ? a.pg_jc[pg] : 0;
+  const int KT = (int)a.KT, k = (int)a.k, m = (int)a.m;
+  const int kt0 = c * a.CT;
+  const int ctn = KT - kt0 < a.CT ? KT - kt0 : a.CT;  // k-tiles in this chunk
+  const int kc0 = kt0 * kKTile;
+  const int rows = m - tile * 16 < 16 ? m - tile * 16 : 16;  // tokens of this tile
+  // pair group -> (projection p, 32-rank chunk jc), from the adapter ranks (constant-index argument reads)
+  int p = -1, jc = 0, base = 0;
+  const uint16_t* Ap = nullptr;
+  int r = 0;
+#pragma unroll
+  for (int q = 0; q < kMaxProj; ++q) {
+    const int nq = q < a.nproj ? (a.r[q] + 31) / 32 : 0;
+    if (p < 0 && pg < base + nq) {
+      p = q;
+      jc = pg - base;
+      Ap = a.A[q];
+      r = a.r[q];
+    }
+    base += nq;
+  }
+  const bool lora = p >= 0;
   if (tile == 0 && c == 0 && pg == 0 && (int)threadIdx.x < a.ncnt) a.cnt[threadIdx.x] = 0u;
 
-  // LoRA-down A fragments of this wave's slices, issued first (they do not depend on x). Fragment (g, slice s): ranks
-  // jc*32 + g*16 + lane%16, k = kc0 + 32 s + 8 (lane/16) .. + 8; ranks past r and k past the row read as 0.
-  const int nsl = ctn * 4;
-  u32x4 af[2][kProSlices];
-  if (lora) {
-    const int r = a.r[p];
-    const rsrc_t asrc = make_rsrc(a.A[p], (int64_t)r * a.k * 2);
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int i = 0; i < kProSlices; ++i) {
-        const int s = wave + i * kProWaves;
-        const int j = jc * 32 + g * 16 + lane % 16;
-        const int64_t kk = kc0 + (int64_t)s * 32 + (lane / 16) * 8;
-        const bool ok = s < nsl && j < r && kk < a.k;
-        af[g][i] = bload16(asrc, ok ? (uint32_t)(((int64_t)j * a.k + kk) * 2) : kOutOfRange);
-      }
-  }
+  // Loads, in the order they are needed (each wait then covers its own loads only): the first batch of the
+  // statistics row, the inputs of h, the LoRA-down A fragments.
+  const rsrc_t xsrc = make_rsrc(a.x + (int64_t)tile * 16 * a.ldx, ((int64_t)(rows - 1) * a.ldx + k) * 2);
+  const bool own_stats = AQN && !a.rstd_in && wave < rows;  // wave w <-> token w of the tile
+  const uint32_t stats_row = (uint32_t)((int64_t)wave * a.ldx * 2);
+  uint32_t sq[8][4];
+  if (AQN) row_sumsq_load<NT, VEC>(xsrc, own_stats ? stats_row : kOutOfRange, own_stats ? k : 0, sq);
 
-  // inputs of h for this thread's 8-element groups (x, and gamma and noise with the norm), fetched before the
-  // statistics so that every load of the prologue is in flight at once. Group g: token g / (ctn*16), k-tile
-  // (g % (ctn*16)) / 16 of the chunk; the 16 groups of one (token, k-tile) are 16 consecutive lanes.
+  // inputs of h for this thread's 8-element groups (x, and gamma and noise with the norm). Group g: token
+  // g / (ctn*16), k-tile (g % (ctn*16)) / 16 of the chunk; the 16 groups of one (token, k-tile) are 16 consecutive
+  // lanes.
+  const rsrc_t gsrc = make_rsrc(a.gamma, AQN ? (int64_t)k * 2 : 0);
+  const int64_t nld = a.noise_ld;
+  const rsrc_t zsrc = make_rsrc(a.noise ? a.noise + (int64_t)tile * 16 * nld : nullptr,
+                                (AQN && a.noise) ? ((int64_t)(rows - 1) * nld + k) * 4 : 0);
   const int ngroups = 16 * ctn * 16;  // a multiple of 256: a wave is either wholly in range or wholly out
   uint32_t hx[kPasses][4], hg[kPasses][4];
   float hz[kPasses][8];
@@ -222,49 +340,39 @@ __global__ void __launch_bounds__(kProWaves * kWave) k_prologue(PrologueArgs a) 
   for (int ps = 0; ps < kPasses; ++ps) {
     const int g = threadIdx.x + ps * kProWaves * kWave;
     const int t = g / (ctn * 16), kg = g % (ctn * 16);
-    const int64_t tok = tile * 16 + t, kk = kc0 + (int64_t)kg * 8;
-    const bool ok = g < ngroups && tok < a.m && kk < a.k;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) hx[ps][e] = hg[ps][e] = 0u;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) hz[ps][e] = 0.f;
-    if (!ok) continue;
-    const uint16_t* xr = a.x + tok * a.ldx + kk;
-    if (a.vec_x) {
-      const u32x4 q = *reinterpret_cast<const u32x4*>(xr);
-      hx[ps][0] = q[0]; hx[ps][1] = q[1]; hx[ps][2] = q[2]; hx[ps][3] = q[3];
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) hx[ps][e] = (uint32_t)xr[2 * e] | ((uint32_t)xr[2 * e + 1] << 16);
-    }
+    const int kk = kc0 + kg * 8;
+    const bool ok = g < ngroups && t < rows && kk < k;
+    bload_bf16x8<VEC>(xsrc, ok ? (uint32_t)(((int64_t)t * a.ldx + kk) * 2) : kOutOfRange, hx[ps]);
     if (AQN) {
-      if (a.vec_g) {
-        const u32x4 q = *reinterpret_cast<const u32x4*>(a.gamma + kk);
-        hg[ps][0] = q[0]; hg[ps][1] = q[1]; hg[ps][2] = q[2]; hg[ps][3] = q[3];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          hg[ps][e] = (uint32_t)a.gamma[kk + 2 * e] | ((uint32_t)a.gamma[kk + 2 * e + 1] << 16);
-      }
-      const float* nz = a.noise ? a.noise + tok * a.noise_ld + kk : nullptr;
-      if (nz && a.vec_z) {
-        const f32x4 z0 = *reinterpret_cast<const f32x4*>(nz), z1 = *reinterpret_cast<const f32x4*>(nz + 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { hz[ps][e] = z0[e]; hz[ps][4 + e] = z1[e]; }
-      } else if (nz) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) hz[ps][e] = nz[e];
-      }
+      bload_bf16x8<VEC>(gsrc, ok ? (uint32_t)kk * 2 : kOutOfRange, hg[ps]);
+      bload_f32x8<VEC>(zsrc, ok ? (uint32_t)((t * nld + kk) * 4) : kOutOfRange, hz[ps]);
     }
+  }
+
+  // LoRA-down A fragments of this wave's slices, issued last (needed last). Fragment (g, slice s): ranks
+  // jc*32 + g*16 + lane%16, k = kc0 + 32 s + 8 (lane/16) .. + 8; ranks past r and k past the row read as 0.
+  const int nsl = ctn * 4;
+  u32x4 af[2][kProSlices];
+  {
+    const rsrc_t asrc = make_rsrc(Ap, lora ? (int64_t)r * k * 2 : 0);
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int i = 0; i < kProSlices; ++i) {
+        const int s = wave + i * kProWaves;
+        const int j = jc * 32 + g * 16 + lane % 16;
+        const int kk = kc0 + s * 32 + (lane / 16) * 8;
+        const bool ok = s < nsl && j < r && kk < k;
+        af[g][i] = bload16(asrc, ok ? (uint32_t)(((int64_t)j * k + kk) * 2) : kOutOfRange);
+      }
   }
 
   // statistics: wave w <-> token w of the tile
   if (AQN) {
-    const int64_t tok = tile * 16 + wave;
     float rstd = 0.f;
-    if (tok < a.m)
-      rstd = a.rstd_in ? gload(a.rstd_in + tok)
-                       : rms_rstd(row_sumsq_one_wave<NT>(a.x + tok * a.ldx, a.k, a.vec_x != 0), a.k, a.eps);
+    if (wave < rows)
+      rstd = a.rstd_in ? gload(a.rstd_in + tile * 16 + wave)
+                       : rms_rstd(row_sumsq_buf<NT, VEC>(xsrc, stats_row, k, sq), k, a.eps);
     if (lane == 0) s_rstd[wave] = rstd;
   }
   __syncthreads();
@@ -1377,7 +1485,9 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
   if (!workspace || workspace_bytes < wl.total) return QN_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return QN_ERR_ALIGN;
   if (k > 131072) return QN_ERR_UNSUPPORTED;
-  // 32-bit buffer offsets: the LoRA-down partials and every LoRA-B matrix stay below 2 GiB
+  // 32-bit buffer offsets: 16 rows of x or of the noise, the LoRA-down partials and every LoRA-B matrix stay below 2 GiB
+  if (ldx >= ((int64_t)1 << 26)) return QN_ERR_UNSUPPORTED;
+  if (aqn && aqn->noise && aqn->noise_ld >= ((int64_t)1 << 25)) return QN_ERR_UNSUPPORTED;
   if (wl.total - wl.t_part >= ((size_t)1 << 31)) return QN_ERR_UNSUPPORTED;
   for (int p = 0; p < nproj; ++p)
     if ((int64_t)projs[p].n * projs[p].r * 2 >= ((int64_t)1 << 31)) return QN_ERR_UNSUPPORTED;
@@ -1425,6 +1535,7 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
       }
     }
     pa.npg = npg;
+    pa.nproj = nproj;
     pa.xs = xs;
     pa.xsc = xsc;
     pa.t_part = t_part;
@@ -1434,15 +1545,22 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
     pa.rstd_in = big ? rstd : nullptr;
     const dim3 grid((unsigned)ntiles, (unsigned)ks, (unsigned)(npg > 0 ? npg : 1));
     const dim3 block(kProWaves * kWave);
+    const bool vec = pa.vec_x && (!aqn || (pa.vec_g && (!aqn->noise || pa.vec_z)));
+#define QN_PRO(NT_, AQN_)                                                                  \
+  do {                                                                                     \
+    if (vec) hipLaunchKernelGGL((k_prologue<NT_, AQN_, true>), grid, block, 0, s, pa);  \
+    else hipLaunchKernelGGL((k_prologue<NT_, AQN_, false>), grid, block, 0, s, pa);     \
+  } while (0)
     if (!aqn) {
-      hipLaunchKernelGGL((k_prologue<256, false>), grid, block, 0, s, pa);
+      QN_PRO(256, false);
     } else if (norm_threads(k) == 256) {
       if (big) hipLaunchKernelGGL(k_rstd<256>, dim3((unsigned)ntiles), block, 0, s, x, ldx, m, k, pa.vec_x, pa.eps, rstd);
-      hipLaunchKernelGGL((k_prologue<256, true>), grid, block, 0, s, pa);
+      QN_PRO(256, true);
     } else {
       if (big) hipLaunchKernelGGL(k_rstd<1024>, dim3((unsigned)ntiles), block, 0, s, x, ldx, m, k, pa.vec_x, pa.eps, rstd);
-      hipLaunchKernelGGL((k_prologue<1024, true>), grid, block, 0, s, pa);
+      QN_PRO(1024, true);
     }
+#undef QN_PRO
   }
 
   // L
