@@ -23,6 +23,24 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+PROFILE = os.path.join(ROOT, "profiles", "decode_layer_7b_m16.md")
+KERNEL_SOURCE = os.path.join(ROOT, "nvfp4_weight_only_amd", "csrc", "linear.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the gate|up kernel from the committed rocprofv3 counter summary (FETCH_SIZE and
+    WRITE_SIZE, scaled by a plain copy's readings), or None when the kernel source has changed since it was taken."""
+    import hashlib
+    import re
+    try:
+        text = open(PROFILE).read()
+        sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    mt = re.search(r"traffic_bytes_per_launch\[k_gemv gate\|up\] = (\d+) \(linear\.hip sha256 ([0-9a-f]{64})\)", text)
+    if not mt or mt.group(2) != sha:
+        return None
+    return int(mt.group(1))
 
 
 def algorithmic_bytes(shape, m):
@@ -206,8 +224,8 @@ def main():
         "step_frac_of_hbm_peak": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "step_tflops": flops(shape, m) / (ms_step * 1e-3) / 1e12,
         "roofline": {"kernel": "k_gemv gate|up (SiLU epilogue)", "bound": "hbm", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "launch_us": main_ms * 1e3, "bytes_per_launch": gu_bytes},
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(), "launch_us": main_ms * 1e3, "bytes_per_launch": gu_bytes},
     }
     if not args.no_cpu:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
