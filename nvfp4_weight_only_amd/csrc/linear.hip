@@ -40,7 +40,6 @@ constexpr int kRankChunks = kMaxRank / 32;  // 32-wide rank chunks of the LoRA-u
 constexpr int kMaxPg = kMaxProj * kRankChunks;
 constexpr int kMaxTokensPerLaunch = 128;
 constexpr int kMaxChunkTiles = 8;           // k-tiles per prologue chunk (h of the chunk is staged in LDS)
-constexpr int kRstdKernelTiles = 16;        // token tiles from which the statistics get a kernel of their own
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -72,7 +71,7 @@ struct LinearArgs {
 
 // Workspace carve-up (256-byte aligned regions).
 struct Workspace {
-  size_t xs, xsc, rstd, t_part, pbuf, cnt, total;
+  size_t xs, xsc, rstd, tok_p, t_part, t_fin, pbuf, cnt, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -99,7 +98,9 @@ Workspace workspace_layout(int64_t m, int64_t k, const qn_proj* projs, int32_t n
   w.xs = off;     off = align256(off + (size_t)mp * kp * 2);
   w.xsc = off;    off = align256(off + (size_t)mp * KT * 4);
   w.rstd = off;   off = align256(off + (size_t)mp * 4);
+  w.tok_p = off;  off = align256(off + (size_t)mp * 4);
   w.t_part = off; off = align256(off + (size_t)nproj * (mp / 16) * kRankChunks * lora_chunks(k) * kWave * 32);
+  w.t_fin = off;  off = align256(off + (m > kMaxTokensPerLaunch ? (size_t)nproj * (mp / 16) * kRankChunks * 2 * kWave * 16 : 0));
   w.pbuf = off;   off = align256(off + gemv_pbuf_bytes(m, k, projs, nproj));
   w.cnt = off;    off = align256(off + 256 * 4);
   w.total = off;
@@ -138,16 +139,6 @@ __device__ __forceinline__ T gload(const T* p) {
   return *reinterpret_cast<const __attribute__((address_space(1))) T*>(reinterpret_cast<uintptr_t>(p));
 }
 
-// ------------------------------------------------------------------------------------------------------------------
-// Statistics kernel (many tokens): one wave per token, rstd[tok] = 1 / sqrt(mean x^2 + eps).
-template <int NT>
-__global__ void __launch_bounds__(16 * kWave) k_rstd(const uint16_t* __restrict__ x, int64_t ldx, int64_t m,
-                                                     int64_t k, int vec_x, float eps, float* __restrict__ rstd) {
-  const int64_t tok = (int64_t)blockIdx.x * 16 + threadIdx.x / kWave;
-  if (tok >= m) return;
-  const float r = rms_rstd(row_sumsq_one_wave<NT>(x + tok * ldx, k, vec_x != 0), k, eps);
-  if (threadIdx.x % kWave == 0) rstd[tok] = r;
-}
 
 // ------------------------------------------------------------------------------------------------------------------
 // P: prologue. Workgroup (token tile, k-chunk c of CT k-tiles, pair group pg = one 32-rank chunk jc of projection p);
@@ -163,7 +154,8 @@ struct PrologueArgs {
   const float* noise;
   int64_t noise_ld;
   float sigma, eps;
-  const float* rstd_in;  // statistics from k_rstd, or null: computed here
+  const float* rstd_in;   // statistics from k_rowstats, or null: computed here
+  const int32_t* tok_p;   // per-token exponents p from k_rowstats (2^p for every k-tile of the token), or null
   const uint16_t* A[kMaxProj];
   int32_t r[kMaxProj];
   int8_t pg_p[kMaxPg], pg_jc[kMaxPg];
@@ -279,6 +271,76 @@ __device__ __forceinline__ void bload_f32x8(rsrc_t src, uint32_t off, float (&z)
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       z[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(src, off == kOutOfRange ? off : off + 4 * e, 0, 0));
+  }
+}
+
+// Power-of-two scale exponent of a group of bf16 values with largest magnitude amax: amax * 2^p in [2^14, 2^15), read
+// off the exponent field and kept within the normal range so 2^p and 2^-p are plain f32 powers of two.
+__device__ __forceinline__ int act_exponent(float amax) {
+  int pw = 0;
+  if (amax > 0.0f) {
+    const int e = (int)((__float_as_uint(amax) >> 23) & 0xffu) - 127;
+    pw = 14 - (e < -126 ? -126 : e);
+    pw = pw > 126 ? 126 : pw;
+  }
+  return pw;
+}
+
+// Row statistics for many tokens: one wave per token. With the norm, rstd in the summation order of the standalone
+// norm; then the token's largest |h| over its whole row (h exactly as the prologue computes it), giving one exponent
+// p per token for all its k-tiles.
+template <int NT, bool AQN, bool VEC>
+__global__ void __launch_bounds__(16 * kWave) k_rowstats(PrologueArgs a, float* __restrict__ rstd_out,
+                                                         int32_t* __restrict__ p_out) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+  const int tile = blockIdx.x, k = (int)a.k, m = (int)a.m;
+  const int rows = m - tile * 16 < 16 ? m - tile * 16 : 16;
+  if (wave >= rows) return;
+  const rsrc_t xsrc = make_rsrc(a.x + (int64_t)tile * 16 * a.ldx, ((int64_t)(rows - 1) * a.ldx + k) * 2);
+  const rsrc_t gsrc = make_rsrc(a.gamma, AQN ? (int64_t)k * 2 : 0);
+  const int64_t nld = a.noise_ld;
+  const rsrc_t zsrc = make_rsrc(a.noise ? a.noise + (int64_t)tile * 16 * nld : nullptr,
+                                (AQN && a.noise) ? ((int64_t)(rows - 1) * nld + k) * 4 : 0);
+  const uint32_t row = (uint32_t)((int64_t)wave * a.ldx * 2);
+  float rstd = 0.f;
+  if (AQN) {
+    uint32_t sq[8][4];
+    row_sumsq_load<NT, VEC>(xsrc, row, k, sq);
+    rstd = rms_rstd(row_sumsq_buf<NT, VEC>(xsrc, row, k, sq), k, a.eps);
+  }
+  float amax = 0.f;
+  const int nch = k / 8;
+  for (int c0 = 0; c0 < nch; c0 += 4 * kWave) {
+    uint32_t hx[4][4], hg[4][4];
+    float hz[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + u * kWave + lane;
+      bload_bf16x8<VEC>(xsrc, c < nch ? row + (uint32_t)c * 16 : kOutOfRange, hx[u]);
+      if (AQN) {
+        bload_bf16x8<VEC>(gsrc, c < nch ? (uint32_t)c * 16 : kOutOfRange, hg[u]);
+        bload_f32x8<VEC>(zsrc, c < nch ? (uint32_t)((wave * nld + c * 8) * 4) : kOutOfRange, hz[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (c0 + u * kWave + lane >= nch) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t lo = hx[u][e] & 0xffffu, hi = hx[u][e] >> 16;
+        if (AQN) {
+          lo = aqn_value(lo_bf16(hx[u][e]), rstd, (uint16_t)hg[u][e], hz[u][2 * e], a.sigma);
+          hi = aqn_value(hi_bf16(hx[u][e]), rstd, (uint16_t)(hg[u][e] >> 16), hz[u][2 * e + 1], a.sigma);
+        }
+        amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(lo << 16)), fabsf(__uint_as_float(hi << 16))));
+      }
+    }
+  }
+  amax = wave_max(amax);
+  if (lane == 0) {
+    const int64_t tok = (int64_t)tile * 16 + wave;
+    if (AQN) rstd_out[tok] = rstd;
+    p_out[tok] = act_exponent(amax);
   }
 }
 
@@ -402,16 +464,16 @@ __global__ void __launch_bounds__(kProWaves * kWave) k_prologue(PrologueArgs a) 
     if (pg == 0) {
       // tile amax over the 16 lanes of this (token, k-tile), then 2^p with amax * 2^p in [2^14, 2^15), read off the
       // exponent field and kept within the normal range so 2^p and 2^-p are plain f32 powers of two
-      float amax = 0.0f;
+      int pw;
+      if (a.tok_p) {
+        pw = t < rows ? gload(a.tok_p + tile * 16 + t) : 0;  // one exponent per token (many-token path)
+      } else {
+        float amax = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fmaxf(fabsf(lo_bf16(hv[e])), fabsf(hi_bf16(hv[e]))));
+        for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fmaxf(fabsf(lo_bf16(hv[e])), fabsf(hi_bf16(hv[e]))));
 #pragma unroll
-      for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
-      int pw = 0;
-      if (amax > 0.0f) {
-        const int e = (int)((__float_as_uint(amax) >> 23) & 0xffu) - 127;
-        pw = 14 - (e < -126 ? -126 : e);
-        pw = pw > 126 ? 126 : pw;
+        for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+        pw = act_exponent(amax);
       }
       const float up = __uint_as_float((uint32_t)(pw + 127) << 23);
       uint32_t packed[4];
@@ -1375,6 +1437,327 @@ size_t gemv_pbuf_bytes(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj
   return bytes;
 }
 
+// ------------------------------------------------------------------------------------------------------------------
+// T: LoRA-down sums for the many-token kernel: t of (projection, token tile, 32-rank chunk) = its k-chunk partials
+// added in chunk order, split into bf16 hi and lo B-fragments, [p][tile][jc][hi, lo][lane] x 16 bytes. One wave each.
+struct TsumArgs {
+  const u32x4* t_part;
+  u32x4* t_fin;
+  int32_t ks, ntiles;
+  int32_t r[kMaxProj];
+};
+
+__global__ void __launch_bounds__(kWave) k_lora_tsum(TsumArgs a) {
+  const int tile = blockIdx.x, p = blockIdx.y, jc = blockIdx.z, lane = threadIdx.x;
+  int r = 0;
+#pragma unroll
+  for (int q = 0; q < kMaxProj; ++q)
+    if (q == p) r = a.r[q];
+  if (jc * 32 >= r) return;
+  const u32x4* src = a.t_part + (((int64_t)(p * a.ntiles + tile) * kRankChunks + jc) * a.ks) * kWave * 2 + lane * 2;
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < a.ks; c0 += 4) {
+    u32x4 q[4][2];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int c = c0 + v < a.ks ? c0 + v : a.ks - 1;
+      q[v][0] = gload(src + (int64_t)c * kWave * 2);
+      q[v][1] = gload(src + (int64_t)c * kWave * 2 + 1);
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      if (c0 + v < a.ks) {
+        s0 += __builtin_bit_cast(f32x4, q[v][0]);
+        s1 += __builtin_bit_cast(f32x4, q[v][1]);
+      }
+  }
+  uint32_t hi[4], lo[4];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float t = e < 4 ? s0[e] : s1[e - 4];
+    const uint32_t th = f32_to_bf16(t);
+    const uint32_t tl = f32_to_bf16(t - bf16_to_f32((uint16_t)th));  // t - th is exact in f32
+    if (e % 2 == 0) {
+      hi[e / 2] = th;
+      lo[e / 2] = tl;
+    } else {
+      hi[e / 2] |= th << 16;
+      lo[e / 2] |= tl << 16;
+    }
+  }
+  u32x4* dst = a.t_fin + (((int64_t)(p * a.ntiles + tile) * kRankChunks + jc) * 2) * kWave + lane;
+  dst[0] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+  dst[kWave] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+}
+
+// ------------------------------------------------------------------------------------------------------------------
+// M: MFMA kernel for many tokens (prefill / log-prob forward, M > 128). Workgroup tile: 128 tokens (8 token tiles) x
+// 16 row groups (256 rows; with SILU 8 (gate, up) pairs); 8 waves = 2 token halves x 4 row quarters, each wave 64
+// tokens x 4 row groups. Per k-tile the workgroup's activation fragments (32 KB) are loaded straight into LDS, three
+// k-tiles in flight (one LDS array per stage); each wave loads its four row groups' codes and scales into registers,
+// also three k-tiles ahead, converts each weight fragment once per slice and runs 4 MFMAs on it. The activations of
+// this path carry one power of two per token (the same in every k-tile), so the MFMAs accumulate the whole row and
+// the token's 2^-p is applied once, in the epilogue.
+constexpr int kMWaves = 8;
+constexpr int kMTT = 8;                              // token tiles per workgroup
+constexpr int kMRG = 16;                             // row groups per workgroup
+constexpr int kMAct = kMTT * 4 * kWave * 16;         // activation fragments per stage (32 KB)
+// loads per k-tile and wave: 4 fragment pieces into LDS, 4 x (codes + scales) into registers
+constexpr int kMActLoads = 4, kMWLoads = 8;
+
+struct GemmArgs {
+  LinearArgs L;
+  const u32x4* t_fin;  // LoRA t fragments from k_lora_tsum
+  int32_t KT, ntiles, nrg;  // k-tiles; token tiles; row groups (flattened; with SILU: pairs x 2)
+};
+
+template <int NR>
+struct MW {
+  u32x4 c[4];
+  uint32_t sc[4];
+};
+
+__host__ __device__ constexpr int vmcnt_imm(int n) {  // s_waitcnt immediate: vmcnt = n, expcnt and lgkmcnt not waited
+  return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+}
+
+template <bool SILU>
+__global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_st0[kMAct];
+  __shared__ __attribute__((aligned(16))) uint8_t s_st1[kMAct];
+  __shared__ __attribute__((aligned(16))) uint8_t s_st2[kMAct];
+  __shared__ ProjEpi s_pe[kMaxProj];
+  const LinearArgs& a = g.L;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+  const int rb = blockIdx.x, tb = blockIdx.y;
+  const int KT = g.KT;
+  const int tile0 = tb * kMTT;
+  const int ntl = g.ntiles - tile0 < kMTT ? g.ntiles - tile0 : kMTT;
+  const int th = wave >> 2, rq = wave & 3;  // token half (tiles 4 th ..), row quarter (slots 4 rq ..)
+
+  // the wave's four row-group slots: SILU slot s = (pair rb*8 + s/2, projection s%2); else flattened group rb*16 + s
+  rsrc_t cd[4], sd[4];
+  int pj[4];
+  int64_t rgl[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int slot = rq * 4 + jj;
+    int p;
+    int64_t rl;
+    bool live;
+    if (SILU) {
+      p = slot & 1;
+      rl = (int64_t)rb * (kMRG / 2) + slot / 2;
+      live = rl * 16 < a.p[0].n;
+    } else {
+      const int64_t gf = (int64_t)rb * kMRG + slot;
+      p = 0;
+      for (int q = 1; q < a.nproj; ++q)
+        if (gf >= a.p[q].rg_begin) p = q;
+      p = __builtin_amdgcn_readfirstlane(p);
+      rl = gf - a.p[p].rg_begin;
+      live = gf < g.nrg && rl * 16 < a.p[p].n;
+    }
+    pj[jj] = p;
+    rgl[jj] = rl;
+    const ProjArgs& P = a.p[p];
+    cd[jj] = make_rsrc(P.codes + rl * KT * kTileCodeBytes, live ? (int64_t)KT * kTileCodeBytes : 0);
+    sd[jj] = make_rsrc(P.scales + rl * KT * kTileScaleBytes, live ? (int64_t)KT * kTileScaleBytes : 0);
+  }
+  const uint32_t c_off = lane * 16, s_off = ((lane % 16) * 2 + (lane / 16) / 2) * 4;
+  const rsrc_t xsrc = make_rsrc(a.xs + (int64_t)tile0 * KT * 4 * kWave, (int64_t)ntl * KT * 4 * kWave * 16);
+
+  // loads of k-tile kt (past KT: out of range, no memory traffic, same instruction count)
+  auto act_load = [&](uint8_t* st, int kt) {
+    const bool in = kt < KT;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q0 = i * kMWaves * kWave + wave * kWave;  // first 16-byte piece of this wave
+      const int tt = q0 >> 8, rem = q0 & 255;
+      const int so = __builtin_amdgcn_readfirstlane(in ? ((tt * KT + kt) * 4 * kWave + rem) * 16 : 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xsrc, (__attribute__((address_space(3))) void*)(st + q0 * 16), 16,
+                                               (in && tt < ntl) ? lane * 16 : kOutOfRange, so, 0, 0);
+    }
+  };
+  auto w_load = [&](MW<1>& w, int kt) {
+    const bool in = kt < KT;
+    const int kc = __builtin_amdgcn_readfirstlane(in ? kt * kTileCodeBytes : 0);
+    const int ks = __builtin_amdgcn_readfirstlane(in ? kt * kTileScaleBytes : 0);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      w.c[jj] = __builtin_amdgcn_raw_buffer_load_b128(cd[jj], in ? c_off : kOutOfRange, kc, kNonTemporal);
+      w.sc[jj] = __builtin_amdgcn_raw_buffer_load_b32(sd[jj], in ? s_off : kOutOfRange, ks, kNonTemporal);
+    }
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[jj][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const uint8_t* st, const MW<1>& w) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        bf[i] = *reinterpret_cast<const u32x4*>(st + ((((th * 4 + i) * 4 + s) * kWave) + lane) * 16);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const uint32_t scv = ((w.sc[jj] >> (8 * s)) & 0xFFu) * 0x00800080u;  // E4M3 byte << 7 = E4M3 * 2^-8 in f16
+        const f16x2 sh = __builtin_bit_cast(f16x2, scv);
+        const uint32_t cw = w.c[jj][s];
+        const f16x2 q0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 256.0f, 0) * sh;
+        const f16x2 q1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 256.0f, 1) * sh;
+        const f16x2 q2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 256.0f, 2) * sh;
+        const f16x2 q3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 256.0f, 3) * sh;
+        const f16x8 wv = {q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[jj][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, __builtin_bit_cast(f16x8, bf[i]), acc[jj][i], 0, 0, 0);
+      }
+    }
+  };
+
+  // pipeline: loads of k-tile kt + 2 are issued once every wave is done with stage (kt + 2) % 3, i.e. after the
+  // barrier of iteration kt; before that barrier each wave waits until its own activation loads of kt have landed
+  // (everything issued after them may stay in flight: its weights of kt and both groups of kt + 1)
+  MW<1> W0, W1, W2;
+  act_load(s_st0, 0);
+  w_load(W0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  act_load(s_st1, 1);
+  w_load(W1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  constexpr int kWaitAct = vmcnt_imm(kMWLoads + kMActLoads + kMWLoads);
+  // the wave's own activation loads of the stage about to be read have landed, then every wave is here. A plain
+  // s_barrier (a compiler barrier for memory, no fence): a workgroup fence would also wait for the next stage's
+  // loads into LDS, which are meant to stay in flight.
+  auto stage_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(kWaitAct);
+    asm volatile("s_barrier" ::: "memory");
+  };
+  for (int kt = 0; kt < KT; kt += 3) {
+    stage_barrier();
+    act_load(s_st2, kt + 2);
+    w_load(W2, kt + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s_st0, W0);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_barrier();
+    act_load(s_st0, kt + 3);
+    w_load(W0, kt + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s_st1, W1);  // (a k-tile past KT has zero weights and zero activations: adds exactly zero)
+    __builtin_amdgcn_sched_barrier(0);
+    stage_barrier();
+    act_load(s_st1, kt + 4);
+    w_load(W1, kt + 4);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s_st2, W2);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+
+  if (threadIdx.x < kMaxProj) {
+#pragma unroll
+    for (int q = 0; q < kMaxProj; ++q)
+      if (threadIdx.x == q && q < a.nproj) {
+        const ProjArgs& P = a.p[q];
+        s_pe[q] = ProjEpi{P.y, P.res, P.n, P.ldy, P.ld_res, gload(P.s_g), P.lambda, P.y_dtype, P.y_repeat,
+                          P.head_dim, P.rg_begin, P.r};
+      }
+  }
+  __syncthreads();
+
+  // LoRA-up for the wave's 4 x 4 output tiles: rows of B (bf16) against the t fragments, two MFMAs per rank chunk
+  f32x4 la[4][4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) la[jj][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int jc = 0; jc < kRankChunks; ++jc) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const ProjEpi& E = s_pe[pj[jj]];
+      const int r = E.r;
+      if (jc * 32 >= r) continue;
+      const uint16_t* Bm = nullptr;
+#pragma unroll
+      for (int q = 0; q < kMaxProj; ++q)
+        if (q == pj[jj]) Bm = a.p[q].B;
+      const rsrc_t bsrc = make_rsrc(Bm, E.n * r * 2);
+      const int64_t n = rgl[jj] * 16 + lane % 16;
+      const int j0 = jc * 32 + (lane / 16) * 8;
+      u32x4 bfr;
+      if (r % 8 == 0) {
+        bfr = bload16(bsrc, (n < E.n && j0 < r) ? (uint32_t)((n * r + j0) * 2) : kOutOfRange);
+      } else {
+        uint32_t wv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t off = (n * r + j0 + 2 * e) * 2;
+          const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(
+              bsrc, (n < E.n && j0 + 2 * e < r) ? (uint32_t)off : kOutOfRange, 0, 0);
+          const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(
+              bsrc, (n < E.n && j0 + 2 * e + 1 < r) ? (uint32_t)(off + 2) : kOutOfRange, 0, 0);
+          wv[e] = lo | (hi << 16);
+        }
+        bfr = u32x4{wv[0], wv[1], wv[2], wv[3]};
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tile = tile0 + th * 4 + i;
+        if (tile >= g.ntiles) break;
+        const u32x4* tf = g.t_fin + (((int64_t)(pj[jj] * g.ntiles + tile) * kRankChunks + jc) * 2) * kWave + lane;
+        const u32x4 thi = gload(tf), tlo = gload(tf + kWave);
+        la[jj][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bfr),
+                                                            __builtin_bit_cast(bf16x8, thi), la[jj][i], 0, 0, 0);
+        la[jj][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bfr),
+                                                            __builtin_bit_cast(bf16x8, tlo), la[jj][i], 0, 0, 0);
+      }
+    }
+  }
+
+  // epilogue: D lane l holds rows 4 (l/16) .. + 3 of the slot for token l % 16 of the tile; the token's 2^-p (exact)
+  float tsc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tile = tile0 + th * 4 + i;
+    tsc[i] = tile < g.ntiles ? gload(a.xsc + (int64_t)tile * KT * 16 + lane % 16) : 0.f;
+  }
+#pragma unroll
+  for (int jj = 0; jj < 4; jj += SILU ? 2 : 1) {
+    const ProjEpi& E = s_pe[pj[jj]];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t tok = ((int64_t)tile0 + th * 4 + i) * 16 + lane % 16;
+      if (tok >= a.m) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t n = rgl[jj] * 16 + (lane / 16) * 4 + e;
+        if (n >= E.n) continue;
+        float out = E.sg * (acc[jj][i][e] * tsc[i]) + E.lambda * la[jj][i][e];
+        if (SILU) {
+          const ProjEpi& F = s_pe[pj[jj + 1]];
+          const float up = F.sg * (acc[jj + 1][i][e] * tsc[i]) + F.lambda * la[jj + 1][i][e];
+          out = out / (1.0f + __expf(-out)) * up;
+        }
+        if (E.res) out += bf16_to_f32(E.res[tok * E.ld_res + n]);
+        const int rep = E.y_repeat > 1 ? E.y_repeat : 1;
+        for (int gi = 0; gi < rep; ++gi) {
+          const int64_t col_out = rep > 1 ? ((n / E.head_dim) * rep + gi) * E.head_dim + n % E.head_dim : n;
+          const int64_t off = tok * E.ldy + col_out;
+          if (E.y_dtype == QN_F32) reinterpret_cast<float*>(E.y)[off] = out;
+          else reinterpret_cast<uint16_t*>(E.y)[off] = f32_to_bf16(out);
+        }
+      }
+    }
+  }
+}
+
 template <int TMT, int R, int W, bool SILU>
 void launch_linear(const LinearArgs& a, int64_t nwg, hipStream_t s) {
   hipLaunchKernelGGL((k_linear<TMT, R, W, SILU>), dim3((unsigned)nwg), dim3(W * kWave), 0, s, a);
@@ -1499,6 +1882,10 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
   u32x4* xs = reinterpret_cast<u32x4*>(ws + wl.xs);
   float* xsc = reinterpret_cast<float*>(ws + wl.xsc);
   float* rstd = reinterpret_cast<float*>(ws + wl.rstd);
+  int32_t* tok_p = reinterpret_cast<int32_t*>(ws + wl.tok_p);
+  // many tokens go to the MFMA kernel (QN_GEMM_OFF=1 takes the general kernel, for comparisons)
+  const char* gemm_off = std::getenv("QN_GEMM_OFF");
+  const bool gemm_path = m > kMaxTokensPerLaunch && !(gemm_off && gemm_off[0] == '1');
   float* t_part = reinterpret_cast<float*>(ws + wl.t_part);
   const int CT = (int)chunk_tiles(KT);
   const int ks = (int)lora_chunks(k);
@@ -1541,8 +1928,10 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
     pa.t_part = t_part;
     pa.cnt = reinterpret_cast<uint32_t*>(ws + wl.cnt);
     pa.ncnt = 256;
-    const bool big = aqn && ntiles >= kRstdKernelTiles;
-    pa.rstd_in = big ? rstd : nullptr;
+    // many tokens: row statistics in a kernel of their own (rstd with the norm, and one exponent per token)
+    const bool big = m > kMaxTokensPerLaunch;
+    pa.rstd_in = big && aqn ? rstd : nullptr;
+    pa.tok_p = big && gemm_path ? tok_p : nullptr;
     const dim3 grid((unsigned)ntiles, (unsigned)ks, (unsigned)(npg > 0 ? npg : 1));
     const dim3 block(kProWaves * kWave);
     const bool vec = pa.vec_x && (!aqn || (pa.vec_g && (!aqn->noise || pa.vec_z)));
@@ -1551,15 +1940,24 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
     if (vec) hipLaunchKernelGGL((k_prologue<NT_, AQN_, true>), grid, block, 0, s, pa);  \
     else hipLaunchKernelGGL((k_prologue<NT_, AQN_, false>), grid, block, 0, s, pa);     \
   } while (0)
+#define QN_STATS(NT_, AQN_)                                                                                   \
+  do {                                                                                                        \
+    if (vec) hipLaunchKernelGGL((k_rowstats<NT_, AQN_, true>), dim3((unsigned)ntiles), dim3(16 * kWave), 0, s, pa, \
+                                rstd, tok_p);                                                                 \
+    else hipLaunchKernelGGL((k_rowstats<NT_, AQN_, false>), dim3((unsigned)ntiles), dim3(16 * kWave), 0, s, pa,  \
+                            rstd, tok_p);                                                                     \
+  } while (0)
     if (!aqn) {
+      if (big) QN_STATS(256, false);
       QN_PRO(256, false);
     } else if (norm_threads(k) == 256) {
-      if (big) hipLaunchKernelGGL(k_rstd<256>, dim3((unsigned)ntiles), block, 0, s, x, ldx, m, k, pa.vec_x, pa.eps, rstd);
+      if (big) QN_STATS(256, true);
       QN_PRO(256, true);
     } else {
-      if (big) hipLaunchKernelGGL(k_rstd<1024>, dim3((unsigned)ntiles), block, 0, s, x, ldx, m, k, pa.vec_x, pa.eps, rstd);
+      if (big) QN_STATS(1024, true);
       QN_PRO(1024, true);
     }
+#undef QN_STATS
 #undef QN_PRO
   }
 
@@ -1600,6 +1998,35 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
   const bool silu = epilogue == QN_EPI_SILU_MUL;
   const int64_t nrg = silu ? 2 * ceil_div(projs[0].n, 16) : rg_total;
   if (nrg == 0 || !run_main) return hipGetLastError() == hipSuccess ? QN_OK : QN_ERR_HIP;
+  // many tokens: LoRA t sums, then the MFMA kernel
+  if (gemm_path) {
+    const int64_t ntiles = ceil_div(m, 16);
+    u32x4* t_fin = reinterpret_cast<u32x4*>(ws + wl.t_fin);
+    int max_r = 0;
+    for (int p = 0; p < nproj; ++p) max_r = projs[p].r > max_r ? projs[p].r : max_r;
+    if (max_r > 0) {
+      TsumArgs ta{};
+      ta.t_part = reinterpret_cast<const u32x4*>(t_part);
+      ta.t_fin = t_fin;
+      ta.ks = ks;
+      ta.ntiles = (int32_t)ntiles;
+      for (int p = 0; p < nproj; ++p) ta.r[p] = projs[p].r;
+      hipLaunchKernelGGL(k_lora_tsum, dim3((unsigned)ntiles, (unsigned)nproj, (unsigned)kRankChunks), dim3(kWave), 0,
+                         s, ta);
+    }
+    GemmArgs ga{};
+    ga.L = la;
+    ga.L.tok0 = 0;
+    ga.t_fin = t_fin;
+    ga.KT = (int32_t)KT;
+    ga.ntiles = (int32_t)ntiles;
+    ga.nrg = (int32_t)nrg;
+    const int64_t nrb = silu ? ceil_div(ceil_div(projs[0].n, 16), kMRG / 2) : ceil_div(rg_total, kMRG);
+    const dim3 grid((unsigned)nrb, (unsigned)ceil_div(ntiles, kMTT)), block(kMWaves * kWave);
+    if (silu) hipLaunchKernelGGL((k_gemm<true>), grid, block, 0, s, ga);
+    else hipLaunchKernelGGL((k_gemm<false>), grid, block, 0, s, ga);
+    return hipGetLastError() == hipSuccess ? QN_OK : QN_ERR_HIP;
+  }
   if (gemv_on(m)) {
     const int tmt = (int)ceil_div(m, 16);
     const int64_t nu = silu ? ceil_div(projs[0].n, 16) : rg_total;

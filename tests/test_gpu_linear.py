@@ -230,6 +230,72 @@ def test_linear_kernel_paths(qn, monkeypatch, path, m, ns, k, silu, residual, r,
         assert rel_err(ys[p].cpu().numpy(), ref) <= LINEAR_TOL, (path, p)
 
 
+# Many tokens (more than 128): the MFMA kernel with one activation exponent per token, and the general kernel in
+# 128-token launches (its override), on shapes that leave ragged token blocks, ragged row blocks and mixed ranks.
+MANY_PATHS = {"mfma": {}, "general": {"QN_GEMM_OFF": "1"}}
+
+
+@pytest.mark.parametrize("path", list(MANY_PATHS))
+@pytest.mark.parametrize("m,ns,k,silu,residual,r,gqa,aqn", [
+    (129, [200], 1024, False, False, 32, 1, True),
+    (300, [384, 384], 512, True, False, 8, 1, True),
+    (257, [520, 64, 64], 1040, False, False, 64, 4, True),
+    (200, [96], 3584, False, True, 12, 1, False),
+    (513, [272, 272], 640, True, False, 0, 1, True),
+    (1000, [48], 256, False, False, 33, 1, True),
+])
+def test_linear_many_tokens(qn, monkeypatch, path, m, ns, k, silu, residual, r, gqa, aqn):
+    monkeypatch.delenv("QN_GEMM_OFF", raising=False)
+    for key, val in MANY_PATHS[path].items():
+        monkeypatch.setenv(key, val)
+    c = Case(m, ns, k, r=r, seed=m * 5 + k, aqn=aqn)
+    wq = [qn.quantize(dev_bf16(w), qn.LAYOUT_TILED) for w in c.w]
+    res = synth.normal_bf16(57, (m, ns[0])) if residual else None
+    ys, projs = [], []
+    for p, n in enumerate(ns):
+        rep = gqa if p == len(ns) - 1 and gqa > 1 else 1
+        y = torch.full((m, n * rep), float("nan"), dtype=torch.float32, device=DEV)
+        ys.append(y)
+        A = dev_bf16(c.A[p]) if r else None
+        B = dev_bf16(c.B[p]) if r else None
+        projs.append(qn.Projection(wq[p], None if (silu and p == 1) else y, A, B, c.lam,
+                                   residual=dev_bf16(res) if (residual and p == 0) else None,
+                                   y_repeat=rep, head_dim=16))
+    norm = qn.make_aqn(dev_bf16(c.gamma), dev_f32(c.noise), c.sigma, 1e-6) if aqn else None
+    qn.lora_linear(dev_bf16(c.x), projs, norm, qn.EPI_SILU_MUL if silu else qn.EPI_NONE)
+    torch.cuda.synchronize()
+    if silu:
+        ref = oracle.silu_mul(c.oracle_y(0), c.oracle_y(1))
+        assert rel_err(ys[0].cpu().numpy(), ref) <= LINEAR_TOL
+        return
+    for p in range(len(ns)):
+        ref = c.oracle_y(p)
+        if residual and p == 0:
+            ref = ref + bf16_bits_to_f64(res)
+        rep = gqa if p == len(ns) - 1 and gqa > 1 else 1
+        if rep > 1:
+            ref = oracle.gqa_broadcast(ref, rep, 16)
+        assert rel_err(ys[p].cpu().numpy(), ref) <= LINEAR_TOL, (path, p)
+
+
+def test_linear_many_tokens_row_scales(qn):
+    """One exponent per token: rows whose magnitudes differ by 2^40 across the batch, and a row of zeros, keep their
+    own relative accuracy (each token is checked against its own scale)."""
+    m, n, k = 200, 128, 512
+    c = Case(m, [n], k, r=16, seed=5, aqn=False)
+    scale = 2.0 ** np.linspace(-20, 20, m)
+    xs = (c.x.astype(np.uint32) << 16).view(np.float32).astype(np.float64) * scale[:, None]
+    xs[17] = 0.0
+    c.x = oracle.bf16_round_array(xs)  # power-of-two scaling of bf16 values: exact
+    y = c.gpu(qn)[0].cpu().numpy()
+    ref = c.oracle_y(0)
+    for t in range(m):
+        if t == 17:
+            assert np.all(y[t] == ref[t])
+            continue
+        assert np.abs(y[t] - ref[t]).max() <= LINEAR_TOL * np.abs(ref[t]).max(), t
+
+
 def test_linear_deterministic(qn):
     c = Case(16, [512], 2048, seed=11)
     a = c.gpu(qn)[0].clone()
@@ -285,6 +351,24 @@ def test_linear_full_size_sampled(qn, m, n, k, aqn):
     rows = sampled_rows(n)
     ref = c.oracle_y(0, rows)
     assert rel_err(y[:, rows], ref) <= LINEAR_TOL
+
+
+def test_prefill_gate_up_full_size_sampled(qn):
+    """7B gate/up at 8192 prefill tokens through the MFMA kernel with the SiLU product, rank-32 LoRA: sampled rows."""
+    m, n, k = 8192, 18944, 3584
+    c = Case(m, [n, n], k, seed=8192, r=32)
+    wq = [qn.quantize(dev_bf16(w), qn.LAYOUT_TILED) for w in c.w]
+    y = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=DEV)
+    projs = [qn.Projection(wq[0], y, dev_bf16(c.A[0]), dev_bf16(c.B[0]), c.lam),
+             qn.Projection(wq[1], None, dev_bf16(c.A[1]), dev_bf16(c.B[1]), c.lam)]
+    qn.lora_linear(dev_bf16(c.x), projs, qn.make_aqn(dev_bf16(c.gamma), dev_f32(c.noise), c.sigma, 1e-6),
+                   qn.EPI_SILU_MUL)
+    torch.cuda.synchronize()
+    rows = sampled_rows(n, 48)
+    got = bf16_bits_to_f64(host_bf16(y))[:, rows]
+    ref = oracle.silu_mul(c.oracle_y(0, rows), c.oracle_y(1, rows))
+    # bf16 output: one rounding (2^-8 relative) on top of the linear bar
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + LINEAR_TOL * np.abs(ref).max())
 
 
 # ---- decoder layer ---------------------------------------------------------------------------------------------------
