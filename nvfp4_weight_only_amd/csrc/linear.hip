@@ -1492,26 +1492,28 @@ __global__ void __launch_bounds__(kWave) k_lora_tsum(TsumArgs a) {
 
 // ------------------------------------------------------------------------------------------------------------------
 // M: MFMA kernel for many tokens (prefill / log-prob forward, M > 128). Workgroup tile: 128 tokens (8 token tiles) x
-// 16 row groups (256 rows; with SILU 8 (gate, up) pairs); 8 waves = 2 token halves x 4 row quarters, each wave 64
-// tokens x 4 row groups. Per k-tile the workgroup's activation fragments (32 KB) are loaded straight into LDS, three
-// k-tiles in flight (one LDS array per stage); each wave loads its four row groups' codes and scales into registers,
-// also three k-tiles ahead, converts each weight fragment once per slice and runs 4 MFMAs on it. The activations of
-// this path carry one power of two per token (the same in every k-tile), so the MFMAs accumulate the whole row and
-// the token's 2^-p is applied once, in the epilogue.
+// 32 row groups (512 rows; with SILU 16 (gate, up) pairs); 8 waves, wave w owning row-group slots 4w .. 4w + 3 for
+// all 128 tokens, so every weight fragment is loaded and converted once per workgroup. Per k-tile the activation
+// fragments of the 128 tokens (32 KB) are loaded straight into LDS, four stages (one LDS array each, loads three
+// k-tiles ahead), and read by every wave; each wave loads its own codes and scales into registers, one k-tile
+// ahead. The activations of this path carry one power of two per token (the same in every k-tile), so the MFMAs
+// accumulate the whole row and the token's 2^-p is applied once, in the epilogue. Workgroups are numbered so that
+// those running at the same time on one XCD (one L2) share a few row blocks and token blocks.
 constexpr int kMWaves = 8;
 constexpr int kMTT = 8;                              // token tiles per workgroup
-constexpr int kMRG = 16;                             // row groups per workgroup
+constexpr int kMRG = 32;                             // row groups per workgroup
+constexpr int kMTBGroup = 4;                         // token blocks per group of the workgroup order
 constexpr int kMAct = kMTT * 4 * kWave * 16;         // activation fragments per stage (32 KB)
 // loads per k-tile and wave: 4 fragment pieces into LDS, 4 x (codes + scales) into registers
 constexpr int kMActLoads = 4, kMWLoads = 8;
 
 struct GemmArgs {
   LinearArgs L;
-  const u32x4* t_fin;  // LoRA t fragments from k_lora_tsum
+  const u32x4* t_fin;       // LoRA t fragments from k_lora_tsum
   int32_t KT, ntiles, nrg;  // k-tiles; token tiles; row groups (flattened; with SILU: pairs x 2)
+  int32_t nrb, ntb;         // row blocks and token blocks of the grid
 };
 
-template <int NR>
 struct MW {
   u32x4 c[4];
   uint32_t sc[4];
@@ -1521,27 +1523,50 @@ __host__ __device__ constexpr int vmcnt_imm(int n) {  // s_waitcnt immediate: vm
   return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
 }
 
+// E2M1 codes (8 per dword) of one 32-wide slice times the E4M3 block scale, exactly, as the f16 A-fragment
+__device__ __forceinline__ f16x8 dequant_frag(uint32_t cw, uint32_t scale_byte) {
+  const f16x2 sh = __builtin_bit_cast(f16x2, scale_byte * 0x00800080u);  // E4M3 byte << 7 = E4M3 * 2^-8 in f16
+  const f16x2 q0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 256.0f, 0) * sh;
+  const f16x2 q1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 256.0f, 1) * sh;
+  const f16x2 q2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 256.0f, 2) * sh;
+  const f16x2 q3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 256.0f, 3) * sh;
+  return f16x8{q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
+}
+
 template <bool SILU>
 __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t s_st0[kMAct];
   __shared__ __attribute__((aligned(16))) uint8_t s_st1[kMAct];
   __shared__ __attribute__((aligned(16))) uint8_t s_st2[kMAct];
+  __shared__ __attribute__((aligned(16))) uint8_t s_st3[kMAct];
   __shared__ ProjEpi s_pe[kMaxProj];
   const LinearArgs& a = g.L;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
-  const int rb = blockIdx.x, tb = blockIdx.y;
   const int KT = g.KT;
+
+  // workgroup -> (row block, token block). Workgroup ids go round-robin over the 8 XCDs; each XCD's ids are given a
+  // contiguous range of tiles, walked kMTBGroup token blocks at a time, row blocks outer.
+  int rb, tb;
+  {
+    const int nrb = g.nrb, ntb = g.ntb, nwg = nrb * ntb;
+    const int id = blockIdx.x;
+    const int x = id % 8, q = nwg / 8, rem = nwg % 8;
+    const int gi = x * q + (x < rem ? x : rem) + id / 8;
+    const int grp = gi / (kMTBGroup * nrb), idx = gi % (kMTBGroup * nrb);
+    const int gsz = ntb - grp * kMTBGroup < kMTBGroup ? ntb - grp * kMTBGroup : kMTBGroup;
+    tb = grp * kMTBGroup + idx % gsz;
+    rb = idx / gsz;
+  }
   const int tile0 = tb * kMTT;
   const int ntl = g.ntiles - tile0 < kMTT ? g.ntiles - tile0 : kMTT;
-  const int th = wave >> 2, rq = wave & 3;  // token half (tiles 4 th ..), row quarter (slots 4 rq ..)
 
-  // the wave's four row-group slots: SILU slot s = (pair rb*8 + s/2, projection s%2); else flattened group rb*16 + s
+  // the wave's four row-group slots: SILU slot s = (pair rb*16 + s/2, projection s%2); else flattened group rb*32 + s
   rsrc_t cd[4], sd[4];
   int pj[4];
   int64_t rgl[4];
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
-    const int slot = rq * 4 + jj;
+    const int slot = wave * 4 + jj;
     int p;
     int64_t rl;
     bool live;
@@ -1579,84 +1604,72 @@ __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
                                                (in && tt < ntl) ? lane * 16 : kOutOfRange, so, 0, 0);
     }
   };
-  auto w_load = [&](MW<1>& w, int kt) {
+  auto w_load = [&](MW& w, int kt) {
     const bool in = kt < KT;
     const int kc = __builtin_amdgcn_readfirstlane(in ? kt * kTileCodeBytes : 0);
     const int ks = __builtin_amdgcn_readfirstlane(in ? kt * kTileScaleBytes : 0);
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      w.c[jj] = __builtin_amdgcn_raw_buffer_load_b128(cd[jj], in ? c_off : kOutOfRange, kc, kNonTemporal);
-      w.sc[jj] = __builtin_amdgcn_raw_buffer_load_b32(sd[jj], in ? s_off : kOutOfRange, ks, kNonTemporal);
+      w.c[jj] = __builtin_amdgcn_raw_buffer_load_b128(cd[jj], in ? c_off : kOutOfRange, kc, 0);
+      w.sc[jj] = __builtin_amdgcn_raw_buffer_load_b32(sd[jj], in ? s_off : kOutOfRange, ks, 0);
     }
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[4][kMTT];
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[jj][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < kMTT; ++i) acc[jj][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const uint8_t* st, const MW<1>& w) {
+  // one k-tile: per 32-wide slice, the wave's four weight fragments, then the 8 token tiles' activation fragments
+  // from LDS, 4 MFMAs each
+  auto compute = [&](const uint8_t* st, const MW& w) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      u32x4 bf[4];
+      f16x8 wv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        bf[i] = *reinterpret_cast<const u32x4*>(st + ((((th * 4 + i) * 4 + s) * kWave) + lane) * 16);
+      for (int jj = 0; jj < 4; ++jj) wv[jj] = dequant_frag(w.c[jj][s], (w.sc[jj] >> (8 * s)) & 0xFFu);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const uint32_t scv = ((w.sc[jj] >> (8 * s)) & 0xFFu) * 0x00800080u;  // E4M3 byte << 7 = E4M3 * 2^-8 in f16
-        const f16x2 sh = __builtin_bit_cast(f16x2, scv);
-        const uint32_t cw = w.c[jj][s];
-        const f16x2 q0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 256.0f, 0) * sh;
-        const f16x2 q1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 256.0f, 1) * sh;
-        const f16x2 q2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 256.0f, 2) * sh;
-        const f16x2 q3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 256.0f, 3) * sh;
-        const f16x8 wv = {q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
+      for (int i = 0; i < kMTT; ++i) {
+        const f16x8 bf = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(st + ((i * 4 + s) * kWave + lane) * 16));
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[jj][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, __builtin_bit_cast(f16x8, bf[i]), acc[jj][i], 0, 0, 0);
+        for (int jj = 0; jj < 4; ++jj)
+          acc[jj][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv[jj], bf, acc[jj][i], 0, 0, 0);
       }
     }
   };
 
-  // pipeline: loads of k-tile kt + 2 are issued once every wave is done with stage (kt + 2) % 3, i.e. after the
-  // barrier of iteration kt; before that barrier each wave waits until its own activation loads of kt have landed
-  // (everything issued after them may stay in flight: its weights of kt and both groups of kt + 1)
-  MW<1> W0, W1, W2;
+  // pipeline, step kt: wait for the wave's own activation loads of kt (what was issued after them may stay in
+  // flight), barrier (every wave is done with stage (kt + 3) % 4 = (kt - 1) % 4 and every wave's part of stage kt
+  // has landed), issue the weights of kt + 1 and the activations of kt + 3, compute kt. Activations: four LDS
+  // stages; weights: two register sets. Loads issued in the order act 0, act 1, W 0, act 2, then per step W, act:
+  // before step kt > 0 the loads after act kt are W kt-1, act kt+1, W kt, act kt+2; before step 0, act 1, W 0, act 2.
+  MW W0, W1;
   act_load(s_st0, 0);
-  w_load(W0, 0);
-  __builtin_amdgcn_sched_barrier(0);
   act_load(s_st1, 1);
-  w_load(W1, 1);
+  w_load(W0, 0);
+  act_load(s_st2, 2);
   __builtin_amdgcn_sched_barrier(0);
-  constexpr int kWaitAct = vmcnt_imm(kMWLoads + kMActLoads + kMWLoads);
-  // the wave's own activation loads of the stage about to be read have landed, then every wave is here. A plain
-  // s_barrier (a compiler barrier for memory, no fence): a workgroup fence would also wait for the next stage's
-  // loads into LDS, which are meant to stay in flight.
-  auto stage_barrier = [&]() {
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(kMActLoads + kMWLoads + kMActLoads));
+  asm volatile("s_barrier" ::: "memory");
+  constexpr int kWaitAct = vmcnt_imm(2 * (kMWLoads + kMActLoads));
+  // A plain s_barrier (a compiler barrier for memory, no fence): a workgroup fence would also wait for the next
+  // stages' loads into LDS, which are meant to stay in flight.
+  auto step = [&](const uint8_t* st_use, uint8_t* st_next, const MW& w_use, MW& w_next, int kt)
+                  __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(kWaitAct);
     asm volatile("s_barrier" ::: "memory");
+    w_load(w_next, kt + 1);
+    act_load(st_next, kt + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(st_use, w_use);  // (a k-tile past KT has zero weights and zero activations: adds exactly zero)
+    __builtin_amdgcn_sched_barrier(0);
   };
-  for (int kt = 0; kt < KT; kt += 3) {
-    stage_barrier();
-    act_load(s_st2, kt + 2);
-    w_load(W2, kt + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(s_st0, W0);
-    __builtin_amdgcn_sched_barrier(0);
-    stage_barrier();
-    act_load(s_st0, kt + 3);
-    w_load(W0, kt + 3);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(s_st1, W1);  // (a k-tile past KT has zero weights and zero activations: adds exactly zero)
-    __builtin_amdgcn_sched_barrier(0);
-    stage_barrier();
-    act_load(s_st1, kt + 4);
-    w_load(W1, kt + 4);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(s_st2, W2);
-    __builtin_amdgcn_sched_barrier(0);
+  for (int kt = 0; kt < KT; kt += 4) {
+    step(s_st0, s_st3, W0, W1, kt);
+    step(s_st1, s_st0, W1, W0, kt + 1);
+    step(s_st2, s_st1, W0, W1, kt + 2);
+    step(s_st3, s_st2, W1, W0, kt + 3);
   }
   __builtin_amdgcn_s_waitcnt(0);
 
@@ -1671,91 +1684,97 @@ __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
   }
   __syncthreads();
 
-  // LoRA-up for the wave's 4 x 4 output tiles: rows of B (bf16) against the t fragments, two MFMAs per rank chunk
-  f32x4 la[4][4];
+  // the token's 2^-p (exact), per token tile: D column = token = lane % 16
+  float tsc[kMTT];
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj)
+  for (int i = 0; i < kMTT; ++i)
+    tsc[i] = i < ntl ? gload(a.xsc + (int64_t)(tile0 + i) * KT * 16 + lane % 16) : 0.f;
+
+  // LoRA-up and epilogue, two slots at a time (with SILU the gate and up slots of one pair): rows of B (bf16)
+  // against the t fragments (hi and lo bf16 parts), then D lane l holds rows 4 (l/16) .. + 3 for token l % 16
+  auto epilogue_pair = [&](const int j0) __attribute__((always_inline)) {
+    f32x4 la[2][kMTT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) la[jj][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-  for (int jc = 0; jc < kRankChunks; ++jc) {
+      for (int i = 0; i < kMTT; ++i) la[u][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
+    for (int u = 0; u < 2; ++u) {
+      const int jj = j0 + u;
       const ProjEpi& E = s_pe[pj[jj]];
       const int r = E.r;
-      if (jc * 32 >= r) continue;
-      const uint16_t* Bm = nullptr;
 #pragma unroll
-      for (int q = 0; q < kMaxProj; ++q)
-        if (q == pj[jj]) Bm = a.p[q].B;
-      const rsrc_t bsrc = make_rsrc(Bm, E.n * r * 2);
-      const int64_t n = rgl[jj] * 16 + lane % 16;
-      const int j0 = jc * 32 + (lane / 16) * 8;
-      u32x4 bfr;
-      if (r % 8 == 0) {
-        bfr = bload16(bsrc, (n < E.n && j0 < r) ? (uint32_t)((n * r + j0) * 2) : kOutOfRange);
-      } else {
-        uint32_t wv[4];
+      for (int jc = 0; jc < kRankChunks; ++jc) {
+        if (jc * 32 >= r) continue;
+        const uint16_t* Bm = nullptr;
+#pragma unroll
+        for (int q = 0; q < kMaxProj; ++q)
+          if (q == pj[jj]) Bm = a.p[q].B;
+        const rsrc_t bsrc = make_rsrc(Bm, E.n * r * 2);
+        const int64_t n = rgl[jj] * 16 + lane % 16;
+        const int jr = jc * 32 + (lane / 16) * 8;
+        u32x4 bfr;
+        if (r % 8 == 0) {
+          bfr = bload16(bsrc, (n < E.n && jr < r) ? (uint32_t)((n * r + jr) * 2) : kOutOfRange);
+        } else {
+          uint32_t wv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int64_t off = (n * r + jr + 2 * e) * 2;
+            const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(
+                bsrc, (n < E.n && jr + 2 * e < r) ? (uint32_t)off : kOutOfRange, 0, 0);
+            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(
+                bsrc, (n < E.n && jr + 2 * e + 1 < r) ? (uint32_t)(off + 2) : kOutOfRange, 0, 0);
+            wv[e] = lo | (hi << 16);
+          }
+          bfr = u32x4{wv[0], wv[1], wv[2], wv[3]};
+        }
+        const rsrc_t tsrc = make_rsrc(g.t_fin + ((int64_t)(pj[jj] * g.ntiles + tile0) * kRankChunks) * 2 * kWave,
+                                      (int64_t)ntl * kRankChunks * 2 * kWave * 16);
+#pragma unroll
+        for (int i = 0; i < kMTT; ++i) {
+          const uint32_t o = (uint32_t)(((i * kRankChunks + jc) * 2 * kWave + lane) * 16);
+          const u32x4 thi = bload16(tsrc, i < ntl ? o : kOutOfRange);
+          const u32x4 tlo = bload16(tsrc, i < ntl ? o + kWave * 16 : kOutOfRange);
+          la[u][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bfr),
+                                                             __builtin_bit_cast(bf16x8, thi), la[u][i], 0, 0, 0);
+          la[u][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bfr),
+                                                             __builtin_bit_cast(bf16x8, tlo), la[u][i], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < (SILU ? 1 : 2); ++u) {
+      const int jj = j0 + u;
+      const ProjEpi& E = s_pe[pj[jj]];
+#pragma unroll
+      for (int i = 0; i < kMTT; ++i) {
+        const int64_t tok = ((int64_t)tile0 + i) * 16 + lane % 16;
+        if (tok >= a.m) continue;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int64_t off = (n * r + j0 + 2 * e) * 2;
-          const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(
-              bsrc, (n < E.n && j0 + 2 * e < r) ? (uint32_t)off : kOutOfRange, 0, 0);
-          const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(
-              bsrc, (n < E.n && j0 + 2 * e + 1 < r) ? (uint32_t)(off + 2) : kOutOfRange, 0, 0);
-          wv[e] = lo | (hi << 16);
-        }
-        bfr = u32x4{wv[0], wv[1], wv[2], wv[3]};
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tile = tile0 + th * 4 + i;
-        if (tile >= g.ntiles) break;
-        const u32x4* tf = g.t_fin + (((int64_t)(pj[jj] * g.ntiles + tile) * kRankChunks + jc) * 2) * kWave + lane;
-        const u32x4 thi = gload(tf), tlo = gload(tf + kWave);
-        la[jj][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bfr),
-                                                            __builtin_bit_cast(bf16x8, thi), la[jj][i], 0, 0, 0);
-        la[jj][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bfr),
-                                                            __builtin_bit_cast(bf16x8, tlo), la[jj][i], 0, 0, 0);
-      }
-    }
-  }
-
-  // epilogue: D lane l holds rows 4 (l/16) .. + 3 of the slot for token l % 16 of the tile; the token's 2^-p (exact)
-  float tsc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int tile = tile0 + th * 4 + i;
-    tsc[i] = tile < g.ntiles ? gload(a.xsc + (int64_t)tile * KT * 16 + lane % 16) : 0.f;
-  }
-#pragma unroll
-  for (int jj = 0; jj < 4; jj += SILU ? 2 : 1) {
-    const ProjEpi& E = s_pe[pj[jj]];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t tok = ((int64_t)tile0 + th * 4 + i) * 16 + lane % 16;
-      if (tok >= a.m) continue;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t n = rgl[jj] * 16 + (lane / 16) * 4 + e;
-        if (n >= E.n) continue;
-        float out = E.sg * (acc[jj][i][e] * tsc[i]) + E.lambda * la[jj][i][e];
-        if (SILU) {
-          const ProjEpi& F = s_pe[pj[jj + 1]];
-          const float up = F.sg * (acc[jj + 1][i][e] * tsc[i]) + F.lambda * la[jj + 1][i][e];
-          out = out / (1.0f + __expf(-out)) * up;
-        }
-        if (E.res) out += bf16_to_f32(E.res[tok * E.ld_res + n]);
-        const int rep = E.y_repeat > 1 ? E.y_repeat : 1;
-        for (int gi = 0; gi < rep; ++gi) {
-          const int64_t col_out = rep > 1 ? ((n / E.head_dim) * rep + gi) * E.head_dim + n % E.head_dim : n;
-          const int64_t off = tok * E.ldy + col_out;
-          if (E.y_dtype == QN_F32) reinterpret_cast<float*>(E.y)[off] = out;
-          else reinterpret_cast<uint16_t*>(E.y)[off] = f32_to_bf16(out);
+          const int64_t n = rgl[jj] * 16 + (lane / 16) * 4 + e;
+          if (n >= E.n) continue;
+          float out = E.sg * (acc[jj][i][e] * tsc[i]) + E.lambda * la[u][i][e];
+          if (SILU) {
+            const ProjEpi& F = s_pe[pj[jj + 1]];
+            const float up = F.sg * (acc[jj + 1][i][e] * tsc[i]) + F.lambda * la[1][i][e];
+            out = out / (1.0f + __expf(-out)) * up;
+          }
+          if (E.res) out += bf16_to_f32(E.res[tok * E.ld_res + n]);
+          const int rep = E.y_repeat > 1 ? E.y_repeat : 1;
+          for (int gi = 0; gi < rep; ++gi) {
+            const int64_t col_out = rep > 1 ? ((n / E.head_dim) * rep + gi) * E.head_dim + n % E.head_dim : n;
+            const int64_t off = tok * E.ldy + col_out;
+            if (E.y_dtype == QN_F32) reinterpret_cast<float*>(E.y)[off] = out;
+            else reinterpret_cast<uint16_t*>(E.y)[off] = f32_to_bf16(out);
+          }
         }
       }
     }
-  }
+  };
+  epilogue_pair(0);
+  epilogue_pair(2);
 }
 
 template <int TMT, int R, int W, bool SILU>
@@ -2021,8 +2040,10 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
     ga.KT = (int32_t)KT;
     ga.ntiles = (int32_t)ntiles;
     ga.nrg = (int32_t)nrg;
-    const int64_t nrb = silu ? ceil_div(ceil_div(projs[0].n, 16), kMRG / 2) : ceil_div(rg_total, kMRG);
-    const dim3 grid((unsigned)nrb, (unsigned)ceil_div(ntiles, kMTT)), block(kMWaves * kWave);
+    ga.nrb = (int32_t)(silu ? ceil_div(ceil_div(projs[0].n, 16), kMRG / 2) : ceil_div(rg_total, kMRG));
+    ga.ntb = (int32_t)ceil_div(ntiles, kMTT);
+    if ((int64_t)ga.nrb * ga.ntb >= ((int64_t)1 << 31)) return QN_ERR_UNSUPPORTED;
+    const dim3 grid((unsigned)(ga.nrb * ga.ntb)), block(kMWaves * kWave);
     if (silu) hipLaunchKernelGGL((k_gemm<true>), grid, block, 0, s, ga);
     else hipLaunchKernelGGL((k_gemm<false>), grid, block, 0, s, ga);
     return hipGetLastError() == hipSuccess ? QN_OK : QN_ERR_HIP;
