@@ -961,7 +961,7 @@ template <int TMT, bool SILU>
 __global__ void __launch_bounds__(kGWaves * kWave) k_gemv(GemvArgs g) {
   constexpr int NR = SILU ? 2 : 1;
   constexpr int kOut = (kGMaxUnits * 16 * TMT * 16 + kGWaves * kWave - 1) / (kGWaves * kWave);
-  constexpr int kTB = 4 / TMT;  // LoRA-down chunk partials loaded together
+  constexpr int kTBatch = 4 / TMT;  // LoRA-down chunk partials loaded together
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[kGLds];
   __shared__ uint16_t s_res[kGMaxUnits * 16 * TMT * 16];  // residual of each output (epilogue order)
   __shared__ ProjEpi s_pe[kMaxProj];
@@ -1153,6 +1153,8 @@ __global__ void __launch_bounds__(kGWaves * kWave) k_gemv(GemvArgs g) {
     // 3. LoRA-up of the block's rows: per projection and 32-rank chunk, t (the LoRA-down chunk partials summed in
     //    chunk order, split into bf16 hi and lo parts), then two bf16 MFMAs per unit, accumulated over rank chunks
     //    in LDS. Lane layouts: B rows (lane%16 = row, ranks 8 (lane/16) ..) and t (lane%16 = token, same ranks).
+    //    The rows of B of every unit are requested before the chunk partials of t, so a rank chunk costs as many
+    //    memory round trips as there are batches of partials, while the weights stream.
     const rsrc_t tsrc = make_rsrc(a.t_part, a.t_bytes);
 #pragma unroll
     for (int nr = 0; nr < NR; ++nr) {
@@ -1167,27 +1169,50 @@ __global__ void __launch_bounds__(kGWaves * kWave) k_gemv(GemvArgs g) {
           if (q == p) Bm = a.p[q].B;
         const int r = E.r;
         for (int jc = 0; jc * 32 < r; ++jc) {
-          // t of each token tile: chunk partials in chunk order
           const rsrc_t bsrc = make_rsrc(Bm, E.n * r * 2);
-          u32x4 thi[TMT], tlo[TMT];
+          // rows of B for every unit of the block that belongs to projection p (others read 0)
+          u32x4 bfr[kGMaxUnits];
+#pragma unroll
+          for (int u = 0; u < kGMaxUnits; ++u) {
+            const bool mine = u < U && (SILU || unit_proj(s_pe, a.nproj, u0 + u) == p);
+            const int64_t n = (SILU ? u0 + u : u0 + u - E.rg_begin) * 16 + lane % 16;
+            const int j0 = jc * 32 + (lane / 16) * 8;
+            if (r % 8 == 0) {
+              bfr[u] = bload16(bsrc, (mine && n < E.n && j0 < r) ? (uint32_t)((n * r + j0) * 2) : kOutOfRange);
+            } else {
+              uint32_t w[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int64_t off = (n * r + j0 + 2 * e) * 2;
+                const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(
+                    bsrc, (mine && n < E.n && j0 + 2 * e < r) ? (uint32_t)off : kOutOfRange, 0, 0);
+                const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(
+                    bsrc, (mine && n < E.n && j0 + 2 * e + 1 < r) ? (uint32_t)(off + 2) : kOutOfRange, 0, 0);
+                w[e] = lo | (hi << 16);
+              }
+              bfr[u] = u32x4{w[0], w[1], w[2], w[3]};
+            }
+          }
+          // per token tile: t (chunk partials in chunk order, kTBatch chunks per batch of loads; loads past the
+          // last chunk read 0 and add nothing), then B t for the units of this projection, added into the LDS slot
+          // (unit, nr, tt)
 #pragma unroll
           for (int tt = 0; tt < TMT; ++tt) {
             const bool ok = tt < ntl;
             const uint32_t off =
                 (uint32_t)((((((int64_t)p * ntiles + tile0 + tt) * kRankChunks + jc) * a.ks) * kWave + lane) * 32);
-            // chunks in order, kTB loads at a time; loads past the last chunk read 0 and add nothing
             f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-            for (int c0 = 0; c0 < a.ks; c0 += kTB) {
-              u32x4 q[kTB][2];
+            for (int c0 = 0; c0 < a.ks; c0 += kTBatch) {
+              u32x4 q[kTBatch][2];
 #pragma unroll
-              for (int v = 0; v < kTB; ++v) {
+              for (int v = 0; v < kTBatch; ++v) {
                 const bool in = ok && c0 + v < a.ks;
                 const uint32_t oc = off + (uint32_t)(c0 + v) * kWave * 32;
                 q[v][0] = bload16(tsrc, in ? oc : kOutOfRange);
                 q[v][1] = bload16(tsrc, in ? oc + 16 : kOutOfRange);
               }
 #pragma unroll
-              for (int v = 0; v < kTB; ++v) {
+              for (int v = 0; v < kTBatch; ++v) {
                 s0 += __builtin_bit_cast(f32x4, q[v][0]);
                 s1 += __builtin_bit_cast(f32x4, q[v][1]);
               }
@@ -1206,50 +1231,18 @@ __global__ void __launch_bounds__(kGWaves * kWave) k_gemv(GemvArgs g) {
                 lo[e / 2] |= tl << 16;
               }
             }
-            thi[tt] = u32x4{hi[0], hi[1], hi[2], hi[3]};
-            tlo[tt] = u32x4{lo[0], lo[1], lo[2], lo[3]};
-          }
-          // B t for the units of this projection, four at a time, added into the LDS slot (unit, nr, tt)
-          for (int ug = 0; ug < U; ug += 4) {
-            u32x4 bfr[4];
+            const u32x4 thi = u32x4{hi[0], hi[1], hi[2], hi[3]}, tlo = u32x4{lo[0], lo[1], lo[2], lo[3]};
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const int u = ug + v;
-              const int64_t gu = u0 + u;
-              const bool mine = u < U && (SILU || unit_proj(s_pe, a.nproj, gu) == p);
-              const int64_t n = (SILU ? gu : gu - E.rg_begin) * 16 + lane % 16;
-              const int j0 = jc * 32 + (lane / 16) * 8;
-              if (r % 8 == 0) {
-                bfr[v] = bload16(bsrc, (mine && n < E.n && j0 < r) ? (uint32_t)((n * r + j0) * 2) : kOutOfRange);
-              } else {
-                uint32_t w[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  const int64_t off = (n * r + j0 + 2 * e) * 2;
-                  const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(
-                      bsrc, (mine && n < E.n && j0 + 2 * e < r) ? (uint32_t)off : kOutOfRange, 0, 0);
-                  const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(
-                      bsrc, (mine && n < E.n && j0 + 2 * e + 1 < r) ? (uint32_t)(off + 2) : kOutOfRange, 0, 0);
-                  w[e] = lo | (hi << 16);
-                }
-                bfr[v] = u32x4{w[0], w[1], w[2], w[3]};
-              }
-            }
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const int u = ug + v;
+            for (int u = 0; u < kGMaxUnits; ++u) {
               if (u >= U) break;
               if (!SILU && unit_proj(s_pe, a.nproj, u0 + u) != p) continue;
-#pragma unroll
-              for (int tt = 0; tt < TMT; ++tt) {
-                f32x4 la = {0.f, 0.f, 0.f, 0.f};
-                la = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bfr[v]),
-                                                             __builtin_bit_cast(bf16x8, thi[tt]), la, 0, 0, 0);
-                la = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bfr[v]),
-                                                             __builtin_bit_cast(bf16x8, tlo[tt]), la, 0, 0, 0);
-                f32x4* slot = reinterpret_cast<f32x4*>(lred + ((((u * NR + nr) * TMT + tt) * kWave) + lane) * 16);
-                *slot = jc == 0 ? la : *slot + la;
-              }
+              f32x4 la = {0.f, 0.f, 0.f, 0.f};
+              la = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bfr[u]),
+                                                           __builtin_bit_cast(bf16x8, thi), la, 0, 0, 0);
+              la = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bfr[u]),
+                                                           __builtin_bit_cast(bf16x8, tlo), la, 0, 0, 0);
+              f32x4* slot = reinterpret_cast<f32x4*>(lred + ((((u * NR + nr) * TMT + tt) * kWave) + lane) * 16);
+              *slot = jc == 0 ? la : *slot + la;
             }
           }
         }
