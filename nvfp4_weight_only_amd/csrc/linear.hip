@@ -913,7 +913,7 @@ __global__ void __launch_bounds__(W * kWave) k_linear(LinearArgs a) {
 //   nbr row blocks x nk k-chunks, one workgroup each; the host sizes the cut so the grid is about one workgroup per CU
 //   with equal shares. The workgroup copies the activation fragments and tile scales of its k-chunk into LDS once;
 //   waves 0..14 split the block's units (and, with fewer units than waves, the chunk's k-tiles between them) and load
-//   only weights from memory, three tiles in flight each; wave 15 computes the LoRA-up term B t of the block's rows
+//   only weights from memory, D tiles in flight each; wave 15 computes the LoRA-up term B t of the block's rows
 //   meanwhile (in the chunk-0 workgroup). With nk > 1 every workgroup stores its part sums, and the last of a block's
 //   workgroups to arrive (an atomic counter) adds the nk parts in chunk order and runs the epilogue, so results do not
 //   depend on scheduling.
@@ -957,7 +957,7 @@ __device__ __forceinline__ int unit_proj(const ProjEpi* pe, int nproj, int64_t g
   return p;
 }
 
-template <int TMT, bool SILU>
+template <int TMT, bool SILU, int D>
 __global__ void __launch_bounds__(kGWaves * kWave) k_gemv(GemvArgs g) {
   constexpr int NR = SILU ? 2 : 1;
   constexpr int kOut = (kGMaxUnits * 16 * TMT * 16 + kGWaves * kWave - 1) / (kGWaves * kWave);
@@ -1017,11 +1017,12 @@ __global__ void __launch_bounds__(kGWaves * kWave) k_gemv(GemvArgs g) {
       t.sc[nr] = __builtin_amdgcn_raw_buffer_load_b32(sd[nr], in ? s_off : kOutOfRange, ks, kNonTemporal);
     }
   };
-  GTile<NR> B0, B1, B2;
-  load(B0, ta);
-  __builtin_amdgcn_sched_barrier(0);  // issue order B0, B1: the loop's wait counts rely on it
-  load(B1, ta + 1);
-  __builtin_amdgcn_sched_barrier(0);
+  GTile<NR> Bt[D];
+#pragma unroll
+  for (int j = 0; j < D - 1; ++j) {
+    load(Bt[j], ta + j);
+    __builtin_amdgcn_sched_barrier(0);  // issue order of the first tiles: the loop's wait counts rely on it
+  }
 
   // 2. the chunk's activation fragments ([tt][lt][s][lane], 16 bytes) and tile scales ([tt][lt][16] f32), loaded
   //    straight into LDS (1 KB per wave and step; a chunk never straddles token tiles: T * 256 is a multiple of 64)
@@ -1130,22 +1131,18 @@ __global__ void __launch_bounds__(kGWaves * kWave) k_gemv(GemvArgs g) {
   };
 
   if (streams) {
-    // three tiles in flight: the load two tiles ahead is issued before the current tile is computed. The body has no
-    // early exit (a loop with several exits gets flow edges that make the compiler's wait counts conservative); tiles
-    // past the range are loaded out of range (no memory traffic) and add zero.
-    for (int kt = ta; kt < tb; kt += 3) {
-      load(B2, kt + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(B0, kt);
-      __builtin_amdgcn_sched_barrier(0);
-      load(B0, kt + 3);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(B1, kt + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      load(B1, kt + 4);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(B2, kt + 2);
-      __builtin_amdgcn_sched_barrier(0);
+    // D tiles in flight: the load D - 1 tiles ahead is issued before the current tile is computed (D = 3 measured
+    // best; deeper prefetch was slower at the 7B shapes). The body has no early exit (a loop with several exits gets
+    // flow edges that make the compiler's wait counts conservative); tiles past the range are loaded out of range (no
+    // memory traffic) and add zero.
+    for (int kt = ta; kt < tb; kt += D) {
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        load(Bt[(j + D - 1) % D], kt + j + D - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(Bt[j], kt + j);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
   // (a separate block after the loop, so that the loop's entry state holds the stream's loads only)
@@ -1312,20 +1309,43 @@ __global__ void __launch_bounds__(kGWaves * kWave) k_gemv(GemvArgs g) {
                (uint32_t)(g.nk - 1);
     __syncthreads();
     if (!s_last) return;
+    // every output's chunk sums, kRedBatch chunks per batch of loads issued together (one memory round trip per
+    // batch, where one load after another would cost a round trip each), added in chunk order
+    constexpr int kRedBatch = 8;
 #pragma unroll
-    for (int i = 0; i < kOut; ++i) {
-      const int e = threadIdx.x + i * kGWaves * kWave;
-      if (e >= nout) break;
+    for (int i = 0; i < kOut; ++i)
 #pragma unroll
-      for (int nr = 0; nr < NR; ++nr) {
-        float s = __hip_atomic_load(pb + (int64_t)e * NR + nr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        for (int cc = 1; cc < g.nk; ++cc)
-          s += __hip_atomic_load(pb + (int64_t)cc * PB + (int64_t)e * NR + nr, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-        vsum[i][nr] = s;
-        vlo[i][nr] = __hip_atomic_load(pb + (int64_t)g.nk * PB + (int64_t)e * NR + nr, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
+      for (int nr = 0; nr < NR; ++nr) vsum[i][nr] = 0.f;
+    for (int c0 = 0; c0 < g.nk; c0 += kRedBatch) {
+      float q[kOut][NR][kRedBatch];
+#pragma unroll
+      for (int i = 0; i < kOut; ++i) {
+        const int e = threadIdx.x + i * kGWaves * kWave;
+#pragma unroll
+        for (int nr = 0; nr < NR; ++nr)
+#pragma unroll
+          for (int v = 0; v < kRedBatch; ++v)
+            q[i][nr][v] = (e < nout && c0 + v < g.nk)
+                              ? __hip_atomic_load(pb + (int64_t)(c0 + v) * PB + (int64_t)e * NR + nr, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT)
+                              : 0.f;
+        if (c0 == 0) {
+#pragma unroll
+          for (int nr = 0; nr < NR; ++nr)
+            vlo[i][nr] = e < nout ? __hip_atomic_load(pb + (int64_t)g.nk * PB + (int64_t)e * NR + nr,
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                  : 0.f;
+        }
       }
+#pragma unroll
+      for (int i = 0; i < kOut; ++i)
+#pragma unroll
+        for (int nr = 0; nr < NR; ++nr)
+#pragma unroll
+          for (int v = 0; v < kRedBatch; ++v) {
+            if (c0 + v >= g.nk) break;
+            vsum[i][nr] = (c0 + v == 0) ? q[i][nr][v] : vsum[i][nr] + q[i][nr][v];
+          }
     }
     if (threadIdx.x == 0) __hip_atomic_store(g.cnt + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -1368,8 +1388,11 @@ __global__ void __launch_bounds__(kGWaves * kWave) k_gemv(GemvArgs g) {
 struct GemvCut {
   int nbr, nk;
 };
+// k-tiles of activations a workgroup of the decode kernel can hold in LDS
+inline int64_t gemv_act_cap(int tmt, int nr) { return (kGLds - gemv_lred_bytes(nr, tmt)) / ((int64_t)tmt * kGTileAct); }
+
 inline GemvCut gemv_cut(int64_t nu, int64_t KT, int tmt, int nr) {
-  const int64_t act_cap = (kGLds - gemv_lred_bytes(nr, tmt)) / ((int64_t)tmt * kGTileAct);
+  const int64_t act_cap = gemv_act_cap(tmt, nr);
   GemvCut best{0, 0};
   double best_t = 1e30;
   int nk_only = 0;  // tuning override: QN_GEMV_NK=<k-chunks>
@@ -1396,19 +1419,22 @@ inline GemvCut gemv_cut(int64_t nu, int64_t KT, int tmt, int nr) {
 }
 
 // Decode kernel use: up to 32 tokens and a cut that fits. By default it is taken where it measured faster than the
-// general kernel: no split k and at least four row units per workgroup (the wide feed-forward projections); split
-// k pays for its partial sums with memory round trips that cost more than the better balance gains. Tuning
-// overrides (read at each call): QN_GEMV_OFF=1 always takes the general kernel, QN_GEMV_NK=<k-chunks> takes the
-// decode kernel with that cut whenever it fits.
+// general kernel: with no split k, at least four row units per workgroup (the wide feed-forward projections); with
+// a split k, only where the whole k does not fit in LDS (long rows, such as the feed-forward down projection: the
+// general kernel would read the activations from L2 once per wave there). For short rows the split-k partial sums
+// cost more memory round trips than the better balance gains. Tuning overrides (read at each call): QN_GEMV_OFF=1
+// always takes the general kernel, QN_GEMV_NK=<k-chunks> takes the decode kernel with that cut whenever it fits,
+// QN_GEMV_DEPTH=<2|3> sets the weight tiles in flight per wave.
 inline bool gemv_on(int64_t m) {
   if (m < 1 || m > 32) return false;
   const char* off = std::getenv("QN_GEMV_OFF");
   return !(off && off[0] == '1');
 }
-inline bool gemv_pick(const GemvCut& cut, int64_t nu) {
+inline bool gemv_pick(const GemvCut& cut, int64_t nu, int64_t KT, int tmt, int nr) {
   if (cut.nbr <= 0) return false;
   if (std::getenv("QN_GEMV_NK")) return true;
-  return cut.nk == 1 && ceil_div(nu, cut.nbr) >= 4;
+  if (cut.nk > 1) return KT > gemv_act_cap(tmt, nr);
+  return ceil_div(nu, cut.nbr) >= 4;
 }
 
 size_t gemv_pbuf_bytes(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj) {
@@ -2045,7 +2071,7 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
     const int tmt = (int)ceil_div(m, 16);
     const int64_t nu = silu ? ceil_div(projs[0].n, 16) : rg_total;
     const GemvCut cut = gemv_cut(nu, KT, tmt, silu ? 2 : 1);
-    if (gemv_pick(cut, nu)) {
+    if (gemv_pick(cut, nu, KT, tmt, silu ? 2 : 1)) {
       GemvArgs ga{};
       ga.L = la;
       ga.L.tok0 = 0;
@@ -2058,11 +2084,17 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
       ga.pbuf = reinterpret_cast<float*>(ws + wl.pbuf);
       ga.cnt = reinterpret_cast<uint32_t*>(ws + wl.cnt);
       const dim3 grid((unsigned)(cut.nbr * cut.nk)), block(kGWaves * kWave);
-      if (tmt == 1 && !silu) hipLaunchKernelGGL((k_gemv<1, false>), grid, block, 0, s, ga);
-      else if (tmt == 1) hipLaunchKernelGGL((k_gemv<1, true>), grid, block, 0, s, ga);
-      else if (!silu) hipLaunchKernelGGL((k_gemv<2, false>), grid, block, 0, s, ga);
-      else hipLaunchKernelGGL((k_gemv<2, true>), grid, block, 0, s, ga);
-      return hipGetLastError() == hipSuccess ? QN_OK : QN_ERR_HIP;
+      int depth = 3;  // weight tiles in flight per wave
+      if (const char* ov = std::getenv("QN_GEMV_DEPTH")) depth = std::atoi(ov);
+#define QN_GEMV(T_, S_, D_)                                                            \
+  if (tmt == T_ && silu == S_ && depth == D_) {                                       \
+    hipLaunchKernelGGL((k_gemv<T_, S_, D_>), grid, block, 0, s, ga);                  \
+    return hipGetLastError() == hipSuccess ? QN_OK : QN_ERR_HIP;                       \
+  }
+      QN_GEMV(1, false, 2) QN_GEMV(1, false, 3) QN_GEMV(1, true, 2) QN_GEMV(1, true, 3)
+      QN_GEMV(2, false, 2) QN_GEMV(2, false, 3) QN_GEMV(2, true, 2) QN_GEMV(2, true, 3)
+#undef QN_GEMV
+      return QN_ERR_UNSUPPORTED;  // (a tuning override asked for a depth that is not built)
     }
   }
   for (int64_t t0 = 0; t0 < m; t0 += kMaxTokensPerLaunch) {

@@ -24,11 +24,12 @@ __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + 
 __device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // f32 -> bf16 bits, round to nearest even (NaN kept quiet).
+// (written as a select, not an early return, so that it compiles to straight-line code without exec-mask branches)
 __device__ inline uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t quiet = (u >> 16) | 0x40u;
+  return (uint16_t)(((u & 0x7fffffffu) > 0x7f800000u) ? quiet : rounded);
 }
 
 __device__ inline bool bf16_finite(uint16_t b) { return ((b >> 7) & 0xffu) != 0xffu; }
