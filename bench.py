@@ -10,6 +10,11 @@ sigma = 1e-2.
 
 Prints one JSON line. `value` is 28-layer-equivalent decode tokens/s: M / (28 * layer step time), i.e. the rate of
 a 28-layer linear stack of this layer with attention scores excluded.
+
+`--workload prefill` instead times the prefill / log-prob forward GEMM: 8192 tokens (8 prompts x 8 responses x 128
+tokens, x ~ N(0,1) bf16) through the 7B gate|up NVFP4 weights (18944 x 3584 each) with rank-32 LoRA and the
+SiLU(gate) * up epilogue on the MFMA path, followed by the group advantages of 8 groups of 8 Bernoulli(0.3) rewards;
+`value` is TFLOP/s of the whole step and the roofline is the MFMA kernel's against the 2.5 PFLOP/s dense f16/bf16 peak.
 """
 from __future__ import annotations
 
@@ -23,21 +28,24 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense f16 / bf16 matrix peak, published
 PROFILE = os.path.join(ROOT, "profiles", "decode_layer_7b_m16.md")
+PREFILL_PROFILE = os.path.join(ROOT, "profiles", "prefill_gateup_7b_m8192.md")
 KERNEL_SOURCE = os.path.join(ROOT, "nvfp4_weight_only_amd", "csrc", "linear.hip")
 
 
-def measured_traffic():
-    """HBM bytes per launch of the gate|up kernel from the committed rocprofv3 counter summary (FETCH_SIZE and
+def measured_traffic(profile=PROFILE, tag="k_gemv gate|up"):
+    """HBM bytes per launch of the tagged kernel from a committed rocprofv3 counter summary (FETCH_SIZE and
     WRITE_SIZE, scaled by a plain copy's readings), or None when the kernel source has changed since it was taken."""
     import hashlib
     import re
     try:
-        text = open(PROFILE).read()
+        text = open(profile).read()
         sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
     except OSError:
         return None
-    mt = re.search(r"traffic_bytes_per_launch\[k_gemv gate\|up\] = (\d+) \(linear\.hip sha256 ([0-9a-f]{64})\)", text)
+    mt = re.search(r"traffic_bytes_per_launch\[" + re.escape(tag) + r"\] = (\d+) \(linear\.hip sha256 ([0-9a-f]{64})\)",
+                   text)
     if not mt or mt.group(2) != sha:
         return None
     return int(mt.group(1))
@@ -134,9 +142,126 @@ def cpu_baseline(shape, m, sigma, row_stride=4, repeats=2):
             "layer_step_s": t_layer}
 
 
+def prefill_flops(shape, m):
+    """gate and up: 2 M N K each, plus the rank-r LoRA of each (down 2 M r K, up 2 M r N)."""
+    n, k, r = shape.inter, shape.hidden, shape.rank
+    return 2 * (2 * m * n * k + 2 * m * r * (n + k))
+
+
+def prefill_cpu_baseline(shape, rows=2048, tokens=64):
+    """The oracle (single-threaded fp64 C++) on a sample of the prefill GEMM: `tokens` tokens through `rows` output rows
+    of gate and of up (quantization of those rows included, as the GPU step excludes it: reported separately),
+    scaled to FLOP/s and so to the full step's time."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    s = lambda t: synth.seed_for(5, 0, t)
+    n, k, r = shape.inter, shape.hidden, shape.rank
+    x = synth.normal_bf16(s("x"), (tokens, k))
+    ws = {nm: synth.normal_bf16(s("w_" + nm), (n, k), std=0.02)[:rows] for nm in ("gate", "up")}
+    lo = {nm: (synth.normal_bf16(s("a_" + nm), (r, k), std=0.02),
+               np.ascontiguousarray(synth.normal_bf16(s("b_" + nm), (n, r), std=0.02)[:rows])) for nm in ("gate", "up")}
+    q = {nm: oracle.nvfp4_quantize(w) for nm, w in ws.items()}
+    t0 = time.perf_counter()
+    yg = oracle.lora_linear(x, *q["gate"][:3], lo["gate"][0], lo["gate"][1], 2.0)
+    yu = oracle.lora_linear(x, *q["up"][:3], lo["up"][0], lo["up"][1], 2.0)
+    oracle.silu_mul(yg, yu)
+    dt = time.perf_counter() - t0
+    flop = 2 * (2 * tokens * rows * k + 2 * tokens * r * (rows + k))
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{tokens} tokens x {rows} rows of gate and of up (fp64, single thread), SiLU*up; TFLOP/s of "
+                      f"that sample, i.e. the full step would take {prefill_flops(shape, 8192) / (flop / dt):.0f} s"}
+
+
+def run_prefill(args):
+    import numpy as np
+    import torch
+
+    import nvfp4_weight_only_amd as qn
+    import synth
+    from nvfp4_weight_only_amd.layer import QWEN25_7B
+
+    shape = QWEN25_7B
+    m, n, k, r = 8192, shape.inter, shape.hidden, shape.rank
+    dev = torch.device("cuda:0")
+
+    def bf16_dev(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    s = lambda t: synth.seed_for(5, 0, t)
+    print("[bench] building the prefill gate|up weights, M=8192", file=sys.stderr, flush=True)
+    wq = {nm: qn.quantize(bf16_dev(synth.normal_bf16(s("w_" + nm), (n, k), std=0.02)), qn.LAYOUT_TILED)
+          for nm in ("gate", "up")}
+    lora = {nm: (bf16_dev(synth.normal_bf16(s("a_" + nm), (r, k), std=0.02)),
+                 bf16_dev(synth.normal_bf16(s("b_" + nm), (n, r), std=0.02))) for nm in ("gate", "up")}
+    x = bf16_dev(synth.normal_bf16(s("x"), (m, k)))
+    y = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+    rewards = torch.from_numpy(synth.bernoulli_f32(s("rewards"), (8, 8), 0.3)).to(dev)
+    call = qn.LinearCall(x, [qn.Projection(wq["gate"], y, *lora["gate"], 2.0),
+                             qn.Projection(wq["up"], None, *lora["up"], 2.0)], None, qn.EPI_SILU_MUL)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+
+    def step(i, timed):
+        call(phases=qn.RUN_PROLOGUE_ONLY)
+        if timed:
+            ev[i][0].record(stream)
+        call(phases=qn.RUN_MAIN_ONLY)
+        if timed:
+            ev[i][1].record(stream)
+        qn.group_advantage(rewards)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    if args.calib_copy:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        torch.empty_like(a).copy_(a)
+        torch.cuda.synchronize()
+    ms_step = elapsed * 1e3 / args.steps
+    main_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / args.steps
+    fl = prefill_flops(shape, m)
+    achieved = fl / (main_ms * 1e-3) / 1e12
+    result = {
+        "metric": "prefill TFLOP/s (% of dense MFMA peak), 7B gate|up NVFP4+LoRA, 8192 tokens",
+        "value": fl / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 weights x bf16 activations (f16 MFMA operands), f32 accumulate",
+        "data": "synthetic (seeded; W ~ N(0,0.02) quantized on device, x ~ N(0,1), R ~ Bernoulli(0.3))",
+        "config": {"workload": "prefill / log-prob forward GEMM: 8192 tokens through the 7B gate|up NVFP4 weights "
+                               "(18944 x 3584 each) + rank-32 bf16 LoRA, SiLU(gate)*up, then group advantages "
+                               "(8 groups of 8)", "global_batch": m, "hidden": k, "intermediate": n, "lora_rank": r},
+        "prefill_tokens_per_s": m / (ms_step * 1e-3),
+        "roofline": {"kernel": "k_gemm (prefill MFMA GEMM, SiLU epilogue)", "bound": "mfma", "achieved": achieved,
+                     "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MFMA_PEAK_TFLOPS,
+                     "traffic": measured_traffic(PREFILL_PROFILE, "k_gemm gate|up"), "launch_us": main_ms * 1e3,
+                     "flops_per_launch": fl},
+    }
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = prefill_cpu_baseline(shape)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--workload", choices=["decode", "prefill"], default="decode",
+                    help="decode: one 7B layer at M tokens (the headline); prefill: the 8192-token gate|up GEMM")
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--batch", type=int, default=16, help="decode tokens per step (M)")
@@ -148,6 +273,11 @@ def main():
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "prefill":
+        if args.steps == ap.get_default("steps"):
+            args.steps, args.warmup = 20, 3
+        return run_prefill(args)
 
     import torch
 
