@@ -27,6 +27,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 
 #include "qn_device.hpp"
 #include "qn_norm.hpp"
@@ -1523,18 +1524,19 @@ constexpr int kMTT = 8;                              // token tiles per workgrou
 constexpr int kMRG = 32;                             // row groups per workgroup
 constexpr int kMTBGroup = 4;                         // token blocks per group of the workgroup order
 constexpr int kMAct = kMTT * 4 * kWave * 16;         // activation fragments per stage (32 KB)
-// loads per k-tile and wave: 4 fragment pieces into LDS, 4 x (codes + scales) into registers
-constexpr int kMActLoads = 4, kMWLoads = 8;
+// 16-byte activation loads into LDS per k-tile and wave
+constexpr int kMActLoads = 4;
 
 struct GemmArgs {
   LinearArgs L;
   const u32x4* t_fin;       // LoRA t fragments from k_lora_tsum
   int32_t KT, ntiles, nrg;  // k-tiles; token tiles; row groups (flattened; with SILU: pairs x 2)
   int32_t nrb, ntb;         // row blocks and token blocks of the grid
+  int32_t fast_store;       // outputs and residuals allow 16-byte accesses and no output is broadcast
 };
 
 struct MW {
-  u32x4 c[4];
+  uint32_t c[4][4];  // [row-group slot][32-wide slice]
   uint32_t sc[4];
 };
 
@@ -1554,10 +1556,11 @@ __device__ __forceinline__ f16x8 dequant_frag(uint32_t cw, uint32_t scale_byte) 
 
 template <bool SILU>
 __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_st0[kMAct];
-  __shared__ __attribute__((aligned(16))) uint8_t s_st1[kMAct];
-  __shared__ __attribute__((aligned(16))) uint8_t s_st2[kMAct];
-  __shared__ __attribute__((aligned(16))) uint8_t s_st3[kMAct];
+  __shared__ __attribute__((aligned(16))) uint8_t s_st[4 * kMAct];  // four stages; after the loop the output tile
+  uint8_t* const s_st0 = s_st;
+  uint8_t* const s_st1 = s_st + kMAct;
+  uint8_t* const s_st2 = s_st + 2 * kMAct;
+  uint8_t* const s_st3 = s_st + 3 * kMAct;
   __shared__ ProjEpi s_pe[kMaxProj];
   const LinearArgs& a = g.L;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
@@ -1579,22 +1582,23 @@ __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
   const int tile0 = tb * kMTT;
   const int ntl = g.ntiles - tile0 < kMTT ? g.ntiles - tile0 : kMTT;
 
-  // the wave's four row-group slots: SILU slot s = (pair rb*16 + s/2, projection s%2); else flattened group rb*32 + s
+  // the wave's four row-group slots; slots 2p and 2p + 1 of every wave form epilogue pass p, which covers
+  // contiguous rows: SILU slot jj = (pair rb*16 + (jj/2)*8 + wave, projection jj%2); else flattened row group
+  // rb*32 + (jj/2)*16 + 2*wave + jj%2
   rsrc_t cd[4], sd[4];
   int pj[4];
   int64_t rgl[4];
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
-    const int slot = wave * 4 + jj;
     int p;
     int64_t rl;
     bool live;
     if (SILU) {
-      p = slot & 1;
-      rl = (int64_t)rb * (kMRG / 2) + slot / 2;
+      p = jj & 1;
+      rl = (int64_t)rb * (kMRG / 2) + (jj / 2) * kMWaves + wave;
       live = rl * 16 < a.p[0].n;
     } else {
-      const int64_t gf = (int64_t)rb * kMRG + slot;
+      const int64_t gf = (int64_t)rb * kMRG + (jj / 2) * (2 * kMWaves) + 2 * wave + (jj & 1);
       p = 0;
       for (int q = 1; q < a.nproj; ++q)
         if (gf >= a.p[q].rg_begin) p = q;
@@ -1623,15 +1627,22 @@ __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
                                                (in && tt < ntl) ? lane * 16 : kOutOfRange, so, 0, 0);
     }
   };
-  auto w_load = [&](MW& w, int kt) {
+  // weights of k-tile kt: half h = slices 2h, 2h + 1 of the four slots (8 bytes per lane), or the scales
+  auto w_load_half = [&](MW& w, int kt, int h) {
     const bool in = kt < KT;
     const int kc = __builtin_amdgcn_readfirstlane(in ? kt * kTileCodeBytes : 0);
-    const int ks = __builtin_amdgcn_readfirstlane(in ? kt * kTileScaleBytes : 0);
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      w.c[jj] = __builtin_amdgcn_raw_buffer_load_b128(cd[jj], in ? c_off : kOutOfRange, kc, 0);
-      w.sc[jj] = __builtin_amdgcn_raw_buffer_load_b32(sd[jj], in ? s_off : kOutOfRange, ks, 0);
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(cd[jj], in ? c_off + 8 * h : kOutOfRange, kc, 0);
+      w.c[jj][2 * h] = v[0];
+      w.c[jj][2 * h + 1] = v[1];
     }
+  };
+  auto w_load_sc = [&](MW& w, int kt) {
+    const bool in = kt < KT;
+    const int ks = __builtin_amdgcn_readfirstlane(in ? kt * kTileScaleBytes : 0);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) w.sc[jj] = __builtin_amdgcn_raw_buffer_load_b32(sd[jj], in ? s_off : kOutOfRange, ks, 0);
   };
 
   f32x4 acc[4][kMTT];
@@ -1640,55 +1651,70 @@ __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < kMTT; ++i) acc[jj][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // one k-tile: per 32-wide slice, the wave's four weight fragments, then the 8 token tiles' activation fragments
-  // from LDS, 4 MFMAs each
-  auto compute = [&](const uint8_t* st, const MW& w) {
+  // one k-tile: per 32-wide slice, the 8 token tiles' activation fragments from LDS (all eight reads issued
+  // first), the wave's four weight fragments unpacked, then 32 MFMAs in groups of four; the weights of the next
+  // k-tile are requested as the slices that held them are unpacked
+  auto compute = [&](const uint8_t* st, MW& w, int kt_next) {
+    const uint8_t* const stl = st + lane * 16;  // (one address per stage; the rest are instruction offsets)
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      u32x4 bq[kMTT];
+#pragma unroll
+      for (int i = 0; i < kMTT; ++i) bq[i] = *reinterpret_cast<const u32x4*>(stl + (i * 4 + s) * kWave * 16);
       f16x8 wv[4];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) wv[jj] = dequant_frag(w.c[jj][s], (w.sc[jj] >> (8 * s)) & 0xFFu);
+      if (s == 1) w_load_half(w, kt_next, 0);
+      if (s == 3) {
+        w_load_half(w, kt_next, 1);
+        w_load_sc(w, kt_next);
+      }
 #pragma unroll
       for (int i = 0; i < kMTT; ++i) {
-        const f16x8 bf = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(st + ((i * 4 + s) * kWave + lane) * 16));
+        const f16x8 bf = __builtin_bit_cast(f16x8, bq[i]);
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
           acc[jj][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv[jj], bf, acc[jj][i], 0, 0, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x002, 40, 0);  // the unpack
+      __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);  // the next k-tile's weight requests
+#pragma unroll
+      for (int q = 0; q < 8; ++q) __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
   };
 
-  // pipeline, step kt: wait for the wave's own activation loads of kt (what was issued after them may stay in
-  // flight), barrier (every wave is done with stage (kt + 3) % 4 = (kt - 1) % 4 and every wave's part of stage kt
-  // has landed), issue the weights of kt + 1 and the activations of kt + 3, compute kt. Activations: four LDS
-  // stages; weights: two register sets. Loads issued in the order act 0, act 1, W 0, act 2, then per step W, act:
-  // before step kt > 0 the loads after act kt are W kt-1, act kt+1, W kt, act kt+2; before step 0, act 1, W 0, act 2.
-  MW W0, W1;
+  // pipeline, step kt: wait for the wave's own activation loads of kt, barrier (every wave is done with stage
+  // (kt + 3) % 4 = (kt - 1) % 4 and every wave's part of stage kt has landed), issue the activations of kt + 3,
+  // compute kt (which requests the weights of kt + 1). Loads in order: act 0, act 1, act 2, W 0, then per step
+  // act kt+3, W kt+1 (12 loads). Before step kt the loads issued after act kt that may be outstanding are at most
+  // act kt+1, W kt-1 (landed: used in step kt-1), act kt+2, W kt, i.e. 32.
+  MW W;
   act_load(s_st0, 0);
   act_load(s_st1, 1);
-  w_load(W0, 0);
   act_load(s_st2, 2);
+  w_load_half(W, 0, 0);
+  w_load_half(W, 0, 1);
+  w_load_sc(W, 0);
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(kMActLoads + kMWLoads + kMActLoads));
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kMActLoads + 12));
   asm volatile("s_barrier" ::: "memory");
-  constexpr int kWaitAct = vmcnt_imm(2 * (kMWLoads + kMActLoads));
+  constexpr int kWaitAct = vmcnt_imm(2 * (kMActLoads + 12));
   // A plain s_barrier (a compiler barrier for memory, no fence): a workgroup fence would also wait for the next
   // stages' loads into LDS, which are meant to stay in flight.
-  auto step = [&](const uint8_t* st_use, uint8_t* st_next, const MW& w_use, MW& w_next, int kt)
-                  __attribute__((always_inline)) {
+  auto step = [&](const uint8_t* st_use, uint8_t* st_next, int kt) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(kWaitAct);
     asm volatile("s_barrier" ::: "memory");
-    w_load(w_next, kt + 1);
     act_load(st_next, kt + 3);
     __builtin_amdgcn_sched_barrier(0);
-    compute(st_use, w_use);  // (a k-tile past KT has zero weights and zero activations: adds exactly zero)
+    compute(st_use, W, kt + 1);  // (a k-tile past KT has zero weights and zero activations: adds exactly zero)
     __builtin_amdgcn_sched_barrier(0);
   };
   for (int kt = 0; kt < KT; kt += 4) {
-    step(s_st0, s_st3, W0, W1, kt);
-    step(s_st1, s_st0, W1, W0, kt + 1);
-    step(s_st2, s_st1, W0, W1, kt + 2);
-    step(s_st3, s_st2, W1, W0, kt + 3);
+    step(s_st0, s_st3, kt);
+    step(s_st1, s_st0, kt + 1);
+    step(s_st2, s_st1, kt + 2);
+    step(s_st3, s_st2, kt + 3);
   }
   __builtin_amdgcn_s_waitcnt(0);
 
@@ -1762,24 +1788,58 @@ __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
         }
       }
     }
+    // Pass j0 / 2: slots j0 and j0 + 1 of the eight waves cover the output columns [n0, n0 + kC) of one
+    // projection (with SILU the product's columns). When the outputs allow 16-byte accesses, the results (before
+    // the residual) go to an f32 tile in LDS (16-byte units swizzled by token % 16 against bank conflicts) and are
+    // then written row by row, 16 bytes per thread; otherwise each element is stored where it is computed.
+    constexpr int kC = SILU ? 16 * kMWaves : 32 * kMWaves;
+    const int pass = j0 / 2;
+    int pp = 0;
+    int64_t n0;
+    bool fast = g.fast_store != 0;
+    if (SILU) {
+      n0 = ((int64_t)rb * (kMRG / 2) + pass * kMWaves) * 16;
+    } else {
+      const int64_t gf0 = (int64_t)rb * kMRG + pass * (2 * kMWaves);
+      int p1 = 0;
+      for (int q = 1; q < a.nproj; ++q) {
+        if (gf0 >= a.p[q].rg_begin) pp = q;
+        if (gf0 + 2 * kMWaves - 1 >= a.p[q].rg_begin) p1 = q;
+      }
+      n0 = (gf0 - a.p[pp].rg_begin) * 16;
+      fast = fast && pp == p1;
+    }
+    float* const otile = reinterpret_cast<float*>(s_st);
 #pragma unroll
     for (int u = 0; u < (SILU ? 1 : 2); ++u) {
       const int jj = j0 + u;
       const ProjEpi& E = s_pe[pj[jj]];
+      const int cb = SILU ? wave * 16 : (2 * wave + u) * 16;  // the slot's first column in the pass
 #pragma unroll
       for (int i = 0; i < kMTT; ++i) {
         const int64_t tok = ((int64_t)tile0 + i) * 16 + lane % 16;
-        if (tok >= a.m) continue;
+        float o4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int64_t n = rgl[jj] * 16 + (lane / 16) * 4 + e;
-          if (n >= E.n) continue;
           float out = E.sg * (acc[jj][i][e] * tsc[i]) + E.lambda * la[u][i][e];
           if (SILU) {
             const ProjEpi& F = s_pe[pj[jj + 1]];
             const float up = F.sg * (acc[jj + 1][i][e] * tsc[i]) + F.lambda * la[1][i][e];
             out = out / (1.0f + __expf(-out)) * up;
           }
+          o4[e] = out;
+        }
+        if (fast) {
+          const int tl = i * 16 + lane % 16, unit = (cb / 4 + lane / 16) ^ (lane % 16);
+          *reinterpret_cast<f32x4*>(otile + tl * kC + unit * 4) = f32x4{o4[0], o4[1], o4[2], o4[3]};
+          continue;
+        }
+        if (tok >= a.m) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t n = rgl[jj] * 16 + (lane / 16) * 4 + e;
+          if (n >= E.n) continue;
+          float out = o4[e];
           if (E.res) out += bf16_to_f32(E.res[tok * E.ld_res + n]);
           const int rep = E.y_repeat > 1 ? E.y_repeat : 1;
           for (int gi = 0; gi < rep; ++gi) {
@@ -1790,6 +1850,66 @@ __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
           }
         }
       }
+    }
+    if (fast) {
+      __syncthreads();
+      const ProjEpi& E = s_pe[pp];
+      const bool f32o = E.y_dtype == QN_F32;
+      const int per_row = f32o ? kC / 4 : kC / 8;  // 16-byte output pieces per token row
+      for (int c = threadIdx.x; c < kMTT * 16 * per_row; c += kMWaves * kWave) {
+        const int tl = c / per_row, pc = c % per_row;
+        const int64_t tok = (int64_t)tile0 * 16 + tl;
+        if (tok >= a.m) continue;
+        const int nu = f32o ? 1 : 2;  // 16-byte tile units per piece
+        const int64_t n = n0 + (int64_t)pc * 4 * nu;
+        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (h >= nu) continue;
+          const f32x4 t4 = *reinterpret_cast<const f32x4*>(otile + tl * kC + ((pc * nu + h) ^ (tl % 16)) * 4);
+          v[4 * h] = t4[0];
+          v[4 * h + 1] = t4[1];
+          v[4 * h + 2] = t4[2];
+          v[4 * h + 3] = t4[3];
+        }
+        const int cnt = 4 * nu;
+        const bool whole = n + cnt <= E.n;
+        if (E.res) {
+          const uint16_t* rp = E.res + tok * E.ld_res + n;
+          if (whole && !f32o) {
+            const u32x4 r8 = *reinterpret_cast<const u32x4*>(rp);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] += bf16_to_f32((uint16_t)(r8[q / 2] >> (16 * (q % 2))));
+          } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+              if (q < cnt && n + q < E.n) v[q] += bf16_to_f32(rp[q]);
+          }
+        }
+        if (f32o) {
+          float* yp = reinterpret_cast<float*>(E.y) + tok * E.ldy + n;
+          if (whole) {
+            *reinterpret_cast<f32x4*>(yp) = f32x4{v[0], v[1], v[2], v[3]};
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (n + q < E.n) yp[q] = v[q];
+          }
+        } else {
+          uint16_t* yp = reinterpret_cast<uint16_t*>(E.y) + tok * E.ldy + n;
+          if (whole) {
+            u32x4 w8;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) w8[q] = (uint32_t)f32_to_bf16(v[2 * q]) | ((uint32_t)f32_to_bf16(v[2 * q + 1]) << 16);
+            *reinterpret_cast<u32x4*>(yp) = w8;
+          } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+              if (n + q < E.n) yp[q] = f32_to_bf16(v[q]);
+          }
+        }
+      }
+      __syncthreads();
     }
   };
   epilogue_pair(0);
@@ -2061,6 +2181,17 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
     ga.nrg = (int32_t)nrg;
     ga.nrb = (int32_t)(silu ? ceil_div(ceil_div(projs[0].n, 16), kMRG / 2) : ceil_div(rg_total, kMRG));
     ga.ntb = (int32_t)ceil_div(ntiles, kMTT);
+    // 16-byte output (and residual) accesses through an LDS tile where the buffers allow them (QN_GEMM_STORE=elem
+    // keeps the per-element stores, for comparisons)
+    bool fast = true;
+    for (int p = 0; p < (silu ? 1 : nproj); ++p) {
+      const qn_proj& P = projs[p];
+      const int64_t esz = P.y_dtype == QN_F32 ? 4 : 2;
+      fast = fast && P.y && (uintptr_t)P.y % 16 == 0 && (P.ldy * esz) % 16 == 0 && P.y_repeat <= 1;
+      if (P.residual) fast = fast && (uintptr_t)P.residual % 16 == 0 && (P.ld_res * 2) % 16 == 0;
+    }
+    if (const char* st = std::getenv("QN_GEMM_STORE")) fast = fast && std::strcmp(st, "elem") != 0;
+    ga.fast_store = fast ? 1 : 0;
     if ((int64_t)ga.nrb * ga.ntb >= ((int64_t)1 << 31)) return QN_ERR_UNSUPPORTED;
     const dim3 grid((unsigned)(ga.nrb * ga.ntb)), block(kMWaves * kWave);
     if (silu) hipLaunchKernelGGL((k_gemm<true>), grid, block, 0, s, ga);

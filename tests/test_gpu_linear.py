@@ -232,7 +232,7 @@ def test_linear_kernel_paths(qn, monkeypatch, path, m, ns, k, silu, residual, r,
 
 # Many tokens (more than 128): the MFMA kernel with one activation exponent per token, and the general kernel in
 # 128-token launches (its override), on shapes that leave ragged token blocks, ragged row blocks and mixed ranks.
-MANY_PATHS = {"mfma": {}, "general": {"QN_GEMM_OFF": "1"}}
+MANY_PATHS = {"mfma": {}, "mfma-elem-store": {"QN_GEMM_STORE": "elem"}, "general": {"QN_GEMM_OFF": "1"}}
 
 
 @pytest.mark.parametrize("path", list(MANY_PATHS))
@@ -243,9 +243,12 @@ MANY_PATHS = {"mfma": {}, "general": {"QN_GEMM_OFF": "1"}}
     (200, [96], 3584, False, True, 12, 1, False),
     (513, [272, 272], 640, True, False, 0, 1, True),
     (1000, [48], 256, False, False, 33, 1, True),
+    (150, [256, 256, 72], 256, False, True, 16, 1, True),
+    (160, [200, 72, 40], 512, False, False, 16, 1, False),
 ])
 def test_linear_many_tokens(qn, monkeypatch, path, m, ns, k, silu, residual, r, gqa, aqn):
     monkeypatch.delenv("QN_GEMM_OFF", raising=False)
+    monkeypatch.delenv("QN_GEMM_STORE", raising=False)
     for key, val in MANY_PATHS[path].items():
         monkeypatch.setenv(key, val)
     c = Case(m, ns, k, r=r, seed=m * 5 + k, aqn=aqn)
@@ -276,6 +279,45 @@ def test_linear_many_tokens(qn, monkeypatch, path, m, ns, k, silu, residual, r, 
         if rep > 1:
             ref = oracle.gqa_broadcast(ref, rep, 16)
         assert rel_err(ys[p].cpu().numpy(), ref) <= LINEAR_TOL, (path, p)
+
+
+@pytest.mark.parametrize("m,ns,k,silu,residual", [
+    (300, [512, 512], 640, True, False),
+    (200, [520], 1024, False, True),
+    (129, [256, 256], 384, False, True),
+])
+def test_linear_many_tokens_bf16_store_paths(qn, monkeypatch, m, ns, k, silu, residual):
+    """Many tokens with bf16 outputs: the 16-byte stores through the LDS tile and the per-element stores give the
+    same bits (same f32 values, residual added before the one rounding), and both meet the bar against the oracle
+    with one bf16 rounding on top (ragged row blocks and token blocks included)."""
+    monkeypatch.delenv("QN_GEMM_OFF", raising=False)
+    c = Case(m, ns, k, r=16, seed=m + 3 * k, aqn=True)
+    wq = [qn.quantize(dev_bf16(w), qn.LAYOUT_TILED) for w in c.w]
+    res = synth.normal_bf16(91, (m, ns[0])) if residual else None
+    outs = {}
+    for store in ("fast", "elem"):
+        if store == "elem":
+            monkeypatch.setenv("QN_GEMM_STORE", "elem")
+        else:
+            monkeypatch.delenv("QN_GEMM_STORE", raising=False)
+        ys, projs = [], []
+        for p, n in enumerate(ns):
+            y = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=DEV)
+            ys.append(y)
+            projs.append(qn.Projection(wq[p], None if (silu and p == 1) else y, dev_bf16(c.A[p]), dev_bf16(c.B[p]),
+                                       c.lam, residual=dev_bf16(res) if (residual and p == 0) else None))
+        qn.lora_linear(dev_bf16(c.x), projs, qn.make_aqn(dev_bf16(c.gamma), dev_f32(c.noise), c.sigma, 1e-6),
+                       qn.EPI_SILU_MUL if silu else qn.EPI_NONE)
+        torch.cuda.synchronize()
+        outs[store] = [host_bf16(y) for y in (ys[:1] if silu else ys)]
+    for a, b in zip(outs["fast"], outs["elem"]):
+        assert np.array_equal(a, b)
+    refs = [oracle.silu_mul(c.oracle_y(0), c.oracle_y(1))] if silu else [c.oracle_y(p) for p in range(len(ns))]
+    if residual:
+        refs[0] = refs[0] + bf16_bits_to_f64(res)
+    for got, ref in zip(outs["fast"], refs):
+        g = bf16_bits_to_f64(got)
+        assert np.all(np.abs(g - ref) <= 2.0 ** -8 * np.abs(ref) + LINEAR_TOL * np.abs(ref).max())
 
 
 def test_linear_many_tokens_row_scales(qn):
