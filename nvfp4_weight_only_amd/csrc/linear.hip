@@ -1533,6 +1533,7 @@ struct GemmArgs {
   int32_t KT, ntiles, nrg;  // k-tiles; token tiles; row groups (flattened; with SILU: pairs x 2)
   int32_t nrb, ntb;         // row blocks and token blocks of the grid
   int32_t fast_store;       // outputs and residuals allow 16-byte accesses and no output is broadcast
+  int32_t t_lds;            // SILU with both ranks <= 32: the LoRA t fragments are staged in LDS for the epilogue
 };
 
 struct MW {
@@ -1562,6 +1563,7 @@ __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
   uint8_t* const s_st2 = s_st + 2 * kMAct;
   uint8_t* const s_st3 = s_st + 3 * kMAct;
   __shared__ ProjEpi s_pe[kMaxProj];
+  __shared__ float s_tsc[kMTT * 16];  // the tokens' 2^-p
   const LinearArgs& a = g.L;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
   const int KT = g.KT;
@@ -1625,6 +1627,19 @@ __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
       const int so = __builtin_amdgcn_readfirstlane(in ? ((tt * KT + kt) * 4 * kWave + rem) * 16 : 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xsrc, (__attribute__((address_space(3))) void*)(st + q0 * 16), 16,
                                                (in && tt < ntl) ? lane * 16 : kOutOfRange, so, 0, 0);
+    }
+  };
+  // LoRA t fragments of the workgroup's token tiles for both projections (rank chunk 0: hi and lo parts), as
+  // 32 pieces of 1 KB [projection][token tile][hi/lo]; four pieces per wave, like one k-tile's activations
+  auto t_load = [&](uint8_t* st) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = wave * 4 + i, p = q >> 4, tt = (q >> 1) & 7, hl = q & 1;
+      const rsrc_t tsrc = make_rsrc(g.t_fin + (int64_t)(p * g.ntiles + tile0) * kRankChunks * 2 * kWave,
+                                    (int64_t)ntl * kRankChunks * 2 * kWave * 16);
+      const int so = __builtin_amdgcn_readfirstlane((tt * kRankChunks * 2 + hl) * kWave * 16);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(tsrc, (__attribute__((address_space(3))) void*)(st + q * kWave * 16), 16,
+                                               tt < ntl ? lane * 16 : kOutOfRange, so, 0, 0);
     }
   };
   // weights of k-tile kt: half h = slices 2h, 2h + 1 of the four slots (8 bytes per lane), or the scales
@@ -1696,9 +1711,23 @@ __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
   w_load_half(W, 0, 0);
   w_load_half(W, 0, 1);
   w_load_sc(W, 0);
+  // the epilogue's per-projection parameters and the tokens' 2^-p, fetched now (their latency overlaps that of the
+  // first loads) and kept in LDS
+  if (threadIdx.x < kMaxProj) {
+#pragma unroll
+    for (int q = 0; q < kMaxProj; ++q)
+      if (threadIdx.x == q && q < a.nproj) {
+        const ProjArgs& P = a.p[q];
+        s_pe[q] = ProjEpi{P.y, P.res, P.n, P.ldy, P.ld_res, gload(P.s_g), P.lambda, P.y_dtype, P.y_repeat,
+                          P.head_dim, P.rg_begin, P.r};
+      }
+  }
+  if (threadIdx.x < kMTT * 16) {
+    const int i = threadIdx.x / 16;
+    s_tsc[threadIdx.x] = i < ntl ? gload(a.xsc + (int64_t)(tile0 + i) * KT * 16 + threadIdx.x % 16) : 0.f;
+  }
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kMActLoads + 12));
-  asm volatile("s_barrier" ::: "memory");
+  __syncthreads();
   constexpr int kWaitAct = vmcnt_imm(2 * (kMActLoads + 12));
   // A plain s_barrier (a compiler barrier for memory, no fence): a workgroup fence would also wait for the next
   // stages' loads into LDS, which are meant to stay in flight.
@@ -1717,23 +1746,49 @@ __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
     step(s_st3, s_st2, kt + 3);
   }
   __builtin_amdgcn_s_waitcnt(0);
-
-  if (threadIdx.x < kMaxProj) {
-#pragma unroll
-    for (int q = 0; q < kMaxProj; ++q)
-      if (threadIdx.x == q && q < a.nproj) {
-        const ProjArgs& P = a.p[q];
-        s_pe[q] = ProjEpi{P.y, P.res, P.n, P.ldy, P.ld_res, gload(P.s_g), P.lambda, P.y_dtype, P.y_repeat,
-                          P.head_dim, P.rg_begin, P.r};
-      }
-  }
-  __syncthreads();
+  __syncthreads();  // every wave is done with the stages
 
   // the token's 2^-p (exact), per token tile: D column = token = lane % 16
   float tsc[kMTT];
 #pragma unroll
-  for (int i = 0; i < kMTT; ++i)
-    tsc[i] = i < ntl ? gload(a.xsc + (int64_t)(tile0 + i) * KT * 16 + lane % 16) : 0.f;
+  for (int i = 0; i < kMTT; ++i) tsc[i] = s_tsc[i * 16 + lane % 16];
+  // With SILU and both ranks <= 32, the LoRA t fragments go to stage 3 (the output tile takes stages 0 and 1) and
+  // the B rows of all four slots are requested with them: one memory round trip for the whole LoRA-up.
+  const bool t_lds = SILU && g.t_lds != 0;
+  const u32x4* const t_st = reinterpret_cast<const u32x4*>(s_st + 3 * kMAct);
+  uint8_t* const otile_base = s_st;
+  u32x4 bfr4[4];
+  if (t_lds) {
+    t_load(s_st + 3 * kMAct);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const ProjEpi& E = s_pe[pj[jj]];
+      const uint16_t* Bm = nullptr;
+#pragma unroll
+      for (int q = 0; q < kMaxProj; ++q)
+        if (q == pj[jj]) Bm = a.p[q].B;
+      const rsrc_t bsrc = make_rsrc(Bm, E.n * E.r * 2);
+      const int64_t n = rgl[jj] * 16 + lane % 16;
+      const int jr = (lane / 16) * 8;
+      if (E.r % 8 == 0) {
+        bfr4[jj] = bload16(bsrc, (E.r > 0 && n < E.n && jr < E.r) ? (uint32_t)((n * E.r + jr) * 2) : kOutOfRange);
+      } else {
+        uint32_t wv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t off = (n * E.r + jr + 2 * e) * 2;
+          const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(
+              bsrc, (n < E.n && jr + 2 * e < E.r) ? (uint32_t)off : kOutOfRange, 0, 0);
+          const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(
+              bsrc, (n < E.n && jr + 2 * e + 1 < E.r) ? (uint32_t)(off + 2) : kOutOfRange, 0, 0);
+          wv[e] = lo | (hi << 16);
+        }
+        bfr4[jj] = u32x4{wv[0], wv[1], wv[2], wv[3]};
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // the staged t fragments have landed
+  }
 
   // LoRA-up and epilogue, two slots at a time (with SILU the gate and up slots of one pair): rows of B (bf16)
   // against the t fragments (hi and lo bf16 parts), then D lane l holds rows 4 (l/16) .. + 3 for token l % 16
@@ -1748,6 +1803,19 @@ __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
       const int jj = j0 + u;
       const ProjEpi& E = s_pe[pj[jj]];
       const int r = E.r;
+      if (t_lds) {
+        if (r == 0) continue;
+#pragma unroll
+        for (int i = 0; i < kMTT; ++i) {
+          const u32x4 thi = t_st[((pj[jj] * kMTT + i) * 2) * kWave + lane];
+          const u32x4 tlo = t_st[((pj[jj] * kMTT + i) * 2 + 1) * kWave + lane];
+          la[u][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bfr4[jj]),
+                                                             __builtin_bit_cast(bf16x8, thi), la[u][i], 0, 0, 0);
+          la[u][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bfr4[jj]),
+                                                             __builtin_bit_cast(bf16x8, tlo), la[u][i], 0, 0, 0);
+        }
+        continue;
+      }
 #pragma unroll
       for (int jc = 0; jc < kRankChunks; ++jc) {
         if (jc * 32 >= r) continue;
@@ -1809,7 +1877,7 @@ __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
       n0 = (gf0 - a.p[pp].rg_begin) * 16;
       fast = fast && pp == p1;
     }
-    float* const otile = reinterpret_cast<float*>(s_st);
+    float* const otile = reinterpret_cast<float*>(otile_base);
 #pragma unroll
     for (int u = 0; u < (SILU ? 1 : 2); ++u) {
       const int jj = j0 + u;
@@ -2192,6 +2260,7 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
     }
     if (const char* st = std::getenv("QN_GEMM_STORE")) fast = fast && std::strcmp(st, "elem") != 0;
     ga.fast_store = fast ? 1 : 0;
+    ga.t_lds = silu && projs[0].r <= 32 && projs[1].r <= 32 ? 1 : 0;
     if ((int64_t)ga.nrb * ga.ntb >= ((int64_t)1 << 31)) return QN_ERR_UNSUPPORTED;
     const dim3 grid((unsigned)(ga.nrb * ga.ntb)), block(kMWaves * kWave);
     if (silu) hipLaunchKernelGGL((k_gemm<true>), grid, block, 0, s, ga);
