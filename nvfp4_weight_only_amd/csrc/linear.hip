@@ -28,6 +28,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 
 #include "qn_device.hpp"
 #include "qn_norm.hpp"
@@ -1922,61 +1923,67 @@ __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
     if (fast) {
       __syncthreads();
       const ProjEpi& E = s_pe[pp];
-      const bool f32o = E.y_dtype == QN_F32;
-      const int per_row = f32o ? kC / 4 : kC / 8;  // 16-byte output pieces per token row
-      for (int c = threadIdx.x; c < kMTT * 16 * per_row; c += kMWaves * kWave) {
-        const int tl = c / per_row, pc = c % per_row;
-        const int64_t tok = (int64_t)tile0 * 16 + tl;
-        if (tok >= a.m) continue;
-        const int nu = f32o ? 1 : 2;  // 16-byte tile units per piece
-        const int64_t n = n0 + (int64_t)pc * 4 * nu;
-        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      // 16-byte output pieces: 8 bf16 (two tile units) or 4 f32 (one unit); consecutive threads take consecutive
+      // pieces of a token row
+      auto store_phase = [&](auto f32_tag) __attribute__((always_inline)) {
+        constexpr bool F32O = decltype(f32_tag)::value;
+        constexpr int kNu = F32O ? 1 : 2, kCnt = 4 * kNu, kPerRow = kC / kCnt;
+        constexpr int kIters = kMTT * 16 * kPerRow / (kMWaves * kWave);
+        static_assert(kMTT * 16 * kPerRow % (kMWaves * kWave) == 0, "pieces per thread");
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          if (h >= nu) continue;
-          const f32x4 t4 = *reinterpret_cast<const f32x4*>(otile + tl * kC + ((pc * nu + h) ^ (tl % 16)) * 4);
-          v[4 * h] = t4[0];
-          v[4 * h + 1] = t4[1];
-          v[4 * h + 2] = t4[2];
-          v[4 * h + 3] = t4[3];
-        }
-        const int cnt = 4 * nu;
-        const bool whole = n + cnt <= E.n;
-        if (E.res) {
-          const uint16_t* rp = E.res + tok * E.ld_res + n;
-          if (whole && !f32o) {
-            const u32x4 r8 = *reinterpret_cast<const u32x4*>(rp);
+        for (int it = 0; it < kIters; ++it) {
+          const int c = it * kMWaves * kWave + (int)threadIdx.x;
+          const int tl = c / kPerRow, pc = c % kPerRow;
+          const int64_t tok = (int64_t)tile0 * 16 + tl;
+          if (tok >= a.m) continue;
+          const int64_t n = n0 + (int64_t)pc * kCnt;
+          float v[kCnt];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] += bf16_to_f32((uint16_t)(r8[q / 2] >> (16 * (q % 2))));
+          for (int h = 0; h < kNu; ++h) {
+            const f32x4 t4 = *reinterpret_cast<const f32x4*>(otile + tl * kC + ((pc * kNu + h) ^ (tl % 16)) * 4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[4 * h + q] = t4[q];
+          }
+          const bool whole = n + kCnt <= E.n;
+          if (E.res) {
+            const uint16_t* rp = E.res + tok * E.ld_res + n;
+            if (whole && !F32O) {
+              const u32x4 r8 = *reinterpret_cast<const u32x4*>(rp);
+#pragma unroll
+              for (int q = 0; q < kCnt; ++q) v[q] += bf16_to_f32((uint16_t)(r8[q / 2] >> (16 * (q % 2))));
+            } else {
+#pragma unroll
+              for (int q = 0; q < kCnt; ++q)
+                if (n + q < E.n) v[q] += bf16_to_f32(rp[q]);
+            }
+          }
+          if (F32O) {
+            float* yp = reinterpret_cast<float*>(E.y) + tok * E.ldy + n;
+            if (whole) {
+              *reinterpret_cast<f32x4*>(yp) = f32x4{v[0], v[1], v[2], v[3]};
+            } else {
+#pragma unroll
+              for (int q = 0; q < kCnt; ++q)
+                if (n + q < E.n) yp[q] = v[q];
+            }
           } else {
+            uint16_t* yp = reinterpret_cast<uint16_t*>(E.y) + tok * E.ldy + n;
+            if (whole) {
+              u32x4 w8;
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
-              if (q < cnt && n + q < E.n) v[q] += bf16_to_f32(rp[q]);
+              for (int q = 0; q < 4; ++q)
+                w8[q] = (uint32_t)f32_to_bf16(v[2 * q]) | ((uint32_t)f32_to_bf16(v[2 * q + 1]) << 16);
+              *reinterpret_cast<u32x4*>(yp) = w8;
+            } else {
+#pragma unroll
+              for (int q = 0; q < kCnt; ++q)
+                if (n + q < E.n) yp[q] = f32_to_bf16(v[q]);
+            }
           }
         }
-        if (f32o) {
-          float* yp = reinterpret_cast<float*>(E.y) + tok * E.ldy + n;
-          if (whole) {
-            *reinterpret_cast<f32x4*>(yp) = f32x4{v[0], v[1], v[2], v[3]};
-          } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              if (n + q < E.n) yp[q] = v[q];
-          }
-        } else {
-          uint16_t* yp = reinterpret_cast<uint16_t*>(E.y) + tok * E.ldy + n;
-          if (whole) {
-            u32x4 w8;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) w8[q] = (uint32_t)f32_to_bf16(v[2 * q]) | ((uint32_t)f32_to_bf16(v[2 * q + 1]) << 16);
-            *reinterpret_cast<u32x4*>(yp) = w8;
-          } else {
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-              if (n + q < E.n) yp[q] = f32_to_bf16(v[q]);
-          }
-        }
-      }
+      };
+      if (E.y_dtype == QN_F32) store_phase(std::true_type{});
+      else store_phase(std::false_type{});
       __syncthreads();
     }
   };
