@@ -48,6 +48,7 @@ def lib():
             "orc_nvfp4_code": ([u16, dbl], i32),
             "orc_nvfp4_bytes": ([i64, i64], i64),
             "orc_nvfp4_quantize": ([P, i64, i64, i64, i32, P, P, P, P], None),
+            "orc_nvfp4_quantize_rows": ([P, i64, i64, i64, P, i64, P, P, P, P], None),
             "orc_nvfp4_dequantize": ([P, P, f32, i64, i64, P, P], None),
             "orc_aqn_sigma": ([i32, dbl, dbl], dbl),
             "orc_aqn_rmsnorm": ([P, i64, i64, i64, P, P, i64, f32, f32, P, P], None),
@@ -120,6 +121,22 @@ def nvfp4_quantize(w: np.ndarray, scale_mode: int = 0, s_b: np.ndarray | None = 
     sg = np.array([0.0 if s_g is None else s_g], dtype=np.float32)
     flags = np.zeros(1, dtype=np.int32)
     lib().orc_nvfp4_quantize(_p(w), n, k, k, int(scale_mode), _p(codes), _p(sb), _p(sg), _p(flags))
+    return codes, sb, float(sg[0]), int(flags[0])
+
+
+def nvfp4_quantize_rows(w: np.ndarray, rows) -> tuple:
+    """The amax-rule quantization of the given rows of W bf16 [n, k]: s_g from the whole tensor, then block scales and
+    codes of those rows only -> (codes u8 [len(rows), k/2], s_b u8 [len(rows), k/16], s_g float, flags int)."""
+    w = _c(w, np.uint16)
+    n, k = w.shape
+    assert k % 16 == 0
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    assert rows.ndim == 1 and (rows.size == 0 or (rows.min() >= 0 and rows.max() < n))
+    codes = np.zeros((rows.size, k // 2), dtype=np.uint8)
+    sb = np.zeros((rows.size, k // 16), dtype=np.uint8)
+    sg = np.zeros(1, dtype=np.float32)
+    flags = np.zeros(1, dtype=np.int32)
+    lib().orc_nvfp4_quantize_rows(_p(w), n, k, k, _p(rows), rows.size, _p(codes), _p(sb), _p(sg), _p(flags))
     return codes, sb, float(sg[0]), int(flags[0])
 
 

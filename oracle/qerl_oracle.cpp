@@ -99,7 +99,7 @@ bool bf16_is_finite(uint16_t b) { return ((b >> 7) & 0xffu) != 0xffu; }
 // NVFP4 scales. The pages leave the choice of s_g and s_b to calibration [review §3.1]; the reading used here is
 // the amax rule: the tensor scale maps the tensor's largest magnitude onto (E2M1 max 6) x (E4M3 max 448), and each
 // 16-weight block's E4M3 scale maps that block's largest magnitude onto 6. Both divisions are IEEE f32.
-void nvfp4_scales(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, float* s_g_out, uint8_t* s_b, int* flags) {
+float nvfp4_tensor_scale(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, int* flags) {
   float amax = 0.0f;
   for (int64_t i = 0; i < n; ++i)
     for (int64_t j = 0; j < k; ++j) {
@@ -108,21 +108,29 @@ void nvfp4_scales(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, float* s
       float a = (float)std::fabs(bf16_value(b));
       if (a > amax) amax = a;
     }
-  float s_g = (amax > 0.0f) ? amax / 2688.0f : 1.0f;  // 2688 = 6 * 448
+  return (amax > 0.0f) ? amax / 2688.0f : 1.0f;  // 2688 = 6 * 448
+}
+
+// the block scales of one row (k / 16 blocks) under the tensor scale s_g
+void nvfp4_row_block_scales(const uint16_t* row, int64_t k, float s_g, uint8_t* s_b_row) {
   float denom = 6.0f * s_g;
-  *s_g_out = s_g;
-  for (int64_t i = 0; i < n; ++i)
-    for (int64_t b = 0; b < k / 16; ++b) {
-      float amax_b = 0.0f;
-      for (int64_t j = 0; j < 16; ++j) {
-        uint16_t v = w[i * ldw + b * 16 + j];
-        if (!bf16_is_finite(v)) continue;
-        float a = (float)std::fabs(bf16_value(v));
-        if (a > amax_b) amax_b = a;
-      }
-      float t = amax_b / denom;
-      s_b[i * (k / 16) + b] = (uint8_t)e4m3_encode_satfinite((double)t);
+  for (int64_t b = 0; b < k / 16; ++b) {
+    float amax_b = 0.0f;
+    for (int64_t j = 0; j < 16; ++j) {
+      uint16_t v = row[b * 16 + j];
+      if (!bf16_is_finite(v)) continue;
+      float a = (float)std::fabs(bf16_value(v));
+      if (a > amax_b) amax_b = a;
     }
+    float t = amax_b / denom;
+    s_b_row[b] = (uint8_t)e4m3_encode_satfinite((double)t);
+  }
+}
+
+void nvfp4_scales(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, float* s_g_out, uint8_t* s_b, int* flags) {
+  float s_g = nvfp4_tensor_scale(w, n, k, ldw, flags);
+  *s_g_out = s_g;
+  for (int64_t i = 0; i < n; ++i) nvfp4_row_block_scales(w + i * ldw, k, s_g, s_b + i * (k / 16));
 }
 
 // Exact three-way comparison of the distances |a - x| and |a - y| (a, x, y >= 0 exact doubles, x and y candidate
@@ -196,6 +204,25 @@ void orc_nvfp4_quantize(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, in
       uint8_t& byte = codes[i * (k / 2) + j / 2];
       if ((j & 1) == 0) byte = (uint8_t)c; else byte = (uint8_t)(byte | (c << 4));
     }
+}
+
+// The amax-rule quantization of selected rows of W: s_g from the whole tensor (as orc_nvfp4_quantize computes it),
+// block scales and codes for rows[0 .. nrows) only, written as consecutive rows of codes / s_b. Rows are independent
+// given s_g, so each output row equals that row of the whole tensor's quantization.
+void orc_nvfp4_quantize_rows(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, const int64_t* rows,
+                             int64_t nrows, uint8_t* codes, uint8_t* s_b, float* s_g, int* flags) {
+  *s_g = nvfp4_tensor_scale(w, n, k, ldw, flags);
+  for (int64_t r = 0; r < nrows; ++r) {
+    const uint16_t* row = w + rows[r] * ldw;
+    uint8_t* sb_row = s_b + r * (k / 16);
+    nvfp4_row_block_scales(row, k, *s_g, sb_row);
+    for (int64_t j = 0; j < k; ++j) {
+      double S = (double)(*s_g) * e4m3_value(sb_row[j / 16]);  // exact product
+      unsigned c = nvfp4_code(row[j], S);
+      uint8_t& byte = codes[r * (k / 2) + j / 2];
+      if ((j & 1) == 0) byte = (uint8_t)c; else byte = (uint8_t)(byte | (c << 4));
+    }
+  }
 }
 
 // Reconstruction w_hat = s_g * s_b * q [review §3.1, reconstruction equation], exact in fp64 (at most 30

@@ -42,10 +42,11 @@ class Case:
         return oracle.aqn_rmsnorm(self.x, self.gamma, self.noise, self.sigma, 1e-6)[1]
 
     def oracle_y(self, p, rows=None):
-        c, sb, sg, _ = oracle.nvfp4_quantize(self.w[p])
         B = self.B[p]
-        if rows is not None:
-            c, sb = c[rows], sb[rows]
+        if rows is None:
+            c, sb, sg, _ = oracle.nvfp4_quantize(self.w[p])
+        else:  # s_g from the whole tensor, codes of the sampled rows only
+            c, sb, sg, _ = oracle.nvfp4_quantize_rows(self.w[p], rows)
             B = None if B is None else B[rows]
         return oracle.lora_linear(self.oracle_h(), c, sb, sg, self.A[p], B, self.lam)
 
@@ -393,6 +394,60 @@ def test_linear_full_size_sampled(qn, m, n, k, aqn):
     rows = sampled_rows(n)
     ref = c.oracle_y(0, rows)
     assert rel_err(y[:, rows], ref) <= LINEAR_TOL
+
+
+# 32B-shaped projections (config 4) at decode batch 32 (decode kernel) and 128 (general kernel), heavy-tailed
+# weights whose 16-blocks carry exponents 2^e, e in -14..0: sampled output rows against the oracle.
+@pytest.mark.parametrize("m", [32, 128])
+def test_32b_gate_up_full_size_sampled(qn, m):
+    n, k = 27648, 5120
+    c = Case(m, [n, n], k, seed=32, r=32, wdist="t4")
+    wq = [qn.quantize(dev_bf16(w), qn.LAYOUT_TILED) for w in c.w]
+    y = torch.full((m, n), float("nan"), dtype=torch.float32, device=DEV)
+    projs = [qn.Projection(wq[0], y, dev_bf16(c.A[0]), dev_bf16(c.B[0]), c.lam),
+             qn.Projection(wq[1], None, dev_bf16(c.A[1]), dev_bf16(c.B[1]), c.lam)]
+    qn.lora_linear(dev_bf16(c.x), projs, qn.make_aqn(dev_bf16(c.gamma), dev_f32(c.noise), c.sigma, 1e-6),
+                   qn.EPI_SILU_MUL)
+    torch.cuda.synchronize()
+    rows = sampled_rows(n, 48)
+    ref = oracle.silu_mul(c.oracle_y(0, rows), c.oracle_y(1, rows))
+    assert rel_err(y.cpu().numpy()[:, rows], ref) <= LINEAR_TOL
+
+
+@pytest.mark.parametrize("m", [32, 128])
+def test_32b_down_full_size_sampled(qn, m):
+    n, k = 5120, 27648
+    c = Case(m, [n], k, seed=33, r=32, wdist="t4", aqn=False)
+    res = synth.normal_bf16(34, (m, n))
+    y = c.gpu(qn, residual=dev_bf16(res))[0].cpu().numpy()
+    rows = sampled_rows(n, 48)
+    ref = c.oracle_y(0, rows) + bf16_bits_to_f64(res)[:, rows]
+    assert rel_err(y[:, rows], ref) <= LINEAR_TOL
+
+
+def test_32b_qkv_gqa_full_size_sampled(qn):
+    """32B q|k|v (5,120 + 1,024 + 1,024 rows) sharing one AQN-RMSNorm at batch 128, v broadcast to its 5 query
+    heads per kv head (head_dim 128)."""
+    m, k = 128, 5120
+    ns = [5120, 1024, 1024]
+    c = Case(m, ns, k, seed=35, r=32, wdist="t4")
+    wq = [qn.quantize(dev_bf16(w), qn.LAYOUT_TILED) for w in c.w]
+    ys = [torch.full((m, n * (5 if p == 2 else 1)), float("nan"), dtype=torch.float32, device=DEV)
+          for p, n in enumerate(ns)]
+    projs = [qn.Projection(wq[p], ys[p], dev_bf16(c.A[p]), dev_bf16(c.B[p]), c.lam,
+                           y_repeat=5 if p == 2 else 1, head_dim=128) for p in range(3)]
+    qn.lora_linear(dev_bf16(c.x), projs, qn.make_aqn(dev_bf16(c.gamma), dev_f32(c.noise), c.sigma, 1e-6))
+    torch.cuda.synchronize()
+    for p, n in enumerate(ns):
+        rows = sampled_rows(n, 32)
+        ref = c.oracle_y(p, rows)
+        got = ys[p].cpu().numpy()
+        if p == 2:  # every copy of a sampled v row: head h's copies sit at (h*5 + g)*128 + row % 128
+            for g in range(5):
+                cols = (rows // 128 * 5 + g) * 128 + rows % 128
+                assert rel_err(got[:, cols], ref) <= LINEAR_TOL, g
+        else:
+            assert rel_err(got[:, rows], ref) <= LINEAR_TOL, p
 
 
 def test_prefill_gate_up_full_size_sampled(qn):

@@ -194,3 +194,25 @@ def test_zero_and_tiny_blocks(orc):
 def test_all_zero_tensor(orc):
     codes, s_b, s_g, flags = orc.nvfp4_quantize(np.zeros((4, 64), dtype=np.uint16))
     assert s_g == 1.0 and np.all(s_b == 0) and np.all(codes == 0) and flags == 0
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_quantize_rows_equals_rows_of_whole_quantization(orc, syn, seed):
+    """The row-subset quantizer (used for sampled full-size parity) gives exactly the selected rows of the whole
+    tensor's amax-rule quantization, with the same tensor scale; heavy-tailed blocks put the largest magnitude in
+    rows that are not selected, so s_g must come from the whole tensor."""
+    n, k = 96, 256
+    w = syn.student_t4_bf16(syn.seed_for(9, seed, "w_q"), (n, k), 0.02, 16, syn.seed_for(9, seed, "block_exp"), -14)
+    codes, sb, sg, flags = orc.nvfp4_quantize(w)
+    rows = np.array([0, 5, 17, 17, 40, n - 1], dtype=np.int64)
+    c2, sb2, sg2, f2 = orc.nvfp4_quantize_rows(w, rows)
+    assert sg2 == sg and f2 == flags
+    assert np.array_equal(c2, codes[rows]) and np.array_equal(sb2, sb[rows])
+    # all rows in order: the whole quantization
+    c3, sb3, sg3, _ = orc.nvfp4_quantize_rows(w, np.arange(n))
+    assert sg3 == sg and np.array_equal(c3, codes) and np.array_equal(sb3, sb)
+    # the tensor scale is not the subset's own: quantizing the subset as a tensor gives a different s_g
+    amax_rows = np.abs(syn.bf16_to_f32(w[rows])).max()
+    amax_all = np.abs(syn.bf16_to_f32(w)).max()
+    if amax_rows < amax_all:
+        assert orc.nvfp4_quantize(w[rows])[2] != sg
