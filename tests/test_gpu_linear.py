@@ -510,3 +510,66 @@ def test_decoder_layer_small(qn, m):
     for name in ("q", "k", "attn", "x2", "a", "out"):
         got = host_bf16(getattr(bound, name))
         assert bf16_chain_ok(got, ref[name]), name
+
+
+def test_decoder_chain_28_layers_m64(qn):
+    """28 Qwen2.5-7B-shaped layers chained at M = 64 with sigma_3 = 0.01 * 0.05^(1/4) in all 56 norms, a fresh noise
+    vector per norm, two weight sets alternating (layer l uses set l % 2). The chain runs on the GPU end to end; the
+    last layer is then checked op by op, each op fed the bf16 tensors the GPU consumed (teacher forcing), on sampled
+    output columns: q, k, v (all seven broadcast copies), o + residual, SiLU(gate) * up, down + residual."""
+    from nvfp4_weight_only_amd.layer import QWEN25_7B, DecoderLayer
+    shape, m, nl = QWEN25_7B, 64, 28
+    sigma = float(np.float32(oracle.aqn_sigma(3)))
+    assert abs(sigma - 4.728708e-3) < 1e-9
+    sets = []
+    for ws in range(2):
+        w, lora, _, g1, g2, _, _, _ = make_layer_inputs(shape, 1, 40 + ws, sigma)
+        layer = DecoderLayer.from_bf16(shape, {k: dev_bf16(v) for k, v in w.items()},
+                                       {k: (dev_bf16(a), dev_bf16(b)) for k, (a, b) in lora.items()},
+                                       dev_bf16(g1), dev_bf16(g2), None, None, sigma, 2.0)
+        sets.append((w if ws == (nl - 1) % 2 else None, lora, layer))
+    noise = [[synth.normal_f32(synth.seed_for(3, l, t), (shape.hidden,)) for t in ("eps_norm1", "eps_norm2")]
+             for l in range(nl)]
+    x0 = synth.normal_bf16(synth.seed_for(3, 0, "x"), (m, shape.hidden))
+    ws_buf = qn.Workspace(DEV)
+    bound, x = [], dev_bf16(x0)
+    for l in range(nl):
+        base = sets[l % 2][2]
+        layer = DecoderLayer(shape, base.w, base.lora, base.gamma1, base.gamma2, dev_f32(noise[l][0]),
+                             dev_f32(noise[l][1]), sigma, 2.0)
+        b = layer.bind(x, ws_buf)
+        bound.append(b)
+        x = b.out
+    for b in bound:
+        b()
+    torch.cuda.synchronize()
+    last = bound[-1]
+    w, lora, base = sets[(nl - 1) % 2]
+    g = {name: host_bf16(getattr(last, name)) for name in ("x", "attn", "x2", "a", "out", "q", "k")}
+    assert np.all(np.isfinite(bf16_bits_to_f64(g["out"])))
+    gamma1, gamma2 = host_bf16(base.gamma1), host_bf16(base.gamma2)
+
+    def lin(h, name, rows):
+        c, sb, sg, _ = oracle.nvfp4_quantize_rows(w[name], rows)
+        A, B = lora[name]
+        return oracle.lora_linear(h, c, sb, sg, A, B[rows], 2.0)
+
+    def check(got, ref):  # bf16 outputs: one rounding on top of the linear bar
+        gf = bf16_bits_to_f64(got)
+        assert np.all(np.abs(gf - ref) <= 2.0 ** -8 * np.abs(ref) + LINEAR_TOL * np.abs(ref).max())
+
+    h1 = oracle.aqn_rmsnorm(g["x"], gamma1, noise[nl - 1][0], sigma, 1e-6)[1]
+    for name, key in (("q", "q"), ("k", "k")):
+        rows = sampled_rows(w[name].shape[0], 32)
+        check(g[key][:, rows], lin(h1, name, rows))
+    rows = sampled_rows(shape.kv_dim, 32)
+    vref = lin(h1, "v", rows)
+    for gi in range(shape.group):
+        check(g["attn"][:, (rows // 128 * shape.group + gi) * 128 + rows % 128], vref)
+    rows = sampled_rows(shape.hidden, 32)
+    check(g["x2"][:, rows], lin(g["attn"], "o", rows) + bf16_bits_to_f64(g["x"])[:, rows])
+    h2 = oracle.aqn_rmsnorm(g["x2"], gamma2, noise[nl - 1][1], sigma, 1e-6)[1]
+    rows = sampled_rows(shape.inter, 32)
+    check(g["a"][:, rows], oracle.silu_mul(lin(h2, "gate", rows), lin(h2, "up", rows)))
+    rows = sampled_rows(shape.hidden, 32)
+    check(g["out"][:, rows], lin(g["a"], "down", rows) + bf16_bits_to_f64(g["x2"])[:, rows])
