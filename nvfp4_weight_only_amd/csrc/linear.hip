@@ -166,6 +166,7 @@ struct PrologueArgs {
   float* t_part;
   uint32_t* cnt;  // arrival counters of the linear kernel, zeroed here
   int32_t ncnt;
+  int32_t tgs;    // tokens per workgroup: 16 (a whole token tile) or 4 (the tile split over four workgroups)
 };
 
 // Sum of squares of one row by one wave, in the summation order of the standalone norm with NT threads (as
@@ -357,7 +358,12 @@ __global__ void __launch_bounds__(kProWaves * kWave) k_prologue(PrologueArgs a) 
   __shared__ __attribute__((aligned(16))) uint16_t s_h[16][kHRow];
   __shared__ f32x4 s_red[kProWaves][2][kWave];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
-  const int tile = blockIdx.x, ntiles = gridDim.x;
+  // workgroup x = (token tile, token group): tokens [tlo, tlo + tgs) of the tile are this workgroup's (their
+  // statistics, h, fragments and LoRA-down partials); the other tokens' h stays zero
+  const int ngpt = 16 / a.tgs;
+  const int tile = blockIdx.x / ngpt, tgrp = blockIdx.x % ngpt, ntiles = gridDim.x / ngpt;
+  const int tlo = tgrp * a.tgs;
+  auto mine = [&](int t) { return t >= tlo && t < tlo + a.tgs; };
   const int c = blockIdx.y, pg = blockIdx.z;
   const int KT = (int)a.KT, k = (int)a.k, m = (int)a.m;
   const int kt0 = c * a.CT;
@@ -380,12 +386,12 @@ __global__ void __launch_bounds__(kProWaves * kWave) k_prologue(PrologueArgs a) 
     base += nq;
   }
   const bool lora = p >= 0;
-  if (tile == 0 && c == 0 && pg == 0 && (int)threadIdx.x < a.ncnt) a.cnt[threadIdx.x] = 0u;
+  if (tile == 0 && tgrp == 0 && c == 0 && pg == 0 && (int)threadIdx.x < a.ncnt) a.cnt[threadIdx.x] = 0u;
 
   // Loads, in the order they are needed (each wait then covers its own loads only): the first batch of the
   // statistics row, the inputs of h, the LoRA-down A fragments.
   const rsrc_t xsrc = make_rsrc(a.x + (int64_t)tile * 16 * a.ldx, ((int64_t)(rows - 1) * a.ldx + k) * 2);
-  const bool own_stats = AQN && !a.rstd_in && wave < rows;  // wave w <-> token w of the tile
+  const bool own_stats = AQN && !a.rstd_in && wave < rows && mine(wave);  // wave w <-> token w of the tile
   const uint32_t stats_row = (uint32_t)((int64_t)wave * a.ldx * 2);
   uint32_t sq[8][4];
   if (AQN) row_sumsq_load<NT, VEC>(xsrc, own_stats ? stats_row : kOutOfRange, own_stats ? k : 0, sq);
@@ -405,7 +411,7 @@ __global__ void __launch_bounds__(kProWaves * kWave) k_prologue(PrologueArgs a) 
     const int g = threadIdx.x + ps * kProWaves * kWave;
     const int t = g / (ctn * 16), kg = g % (ctn * 16);
     const int kk = kc0 + kg * 8;
-    const bool ok = g < ngroups && t < rows && kk < k;
+    const bool ok = g < ngroups && t < rows && kk < k && mine(t);
     bload_bf16x8<VEC>(xsrc, ok ? (uint32_t)(((int64_t)t * a.ldx + kk) * 2) : kOutOfRange, hx[ps]);
     if (AQN) {
       bload_bf16x8<VEC>(gsrc, ok ? (uint32_t)kk * 2 : kOutOfRange, hg[ps]);
@@ -434,7 +440,7 @@ __global__ void __launch_bounds__(kProWaves * kWave) k_prologue(PrologueArgs a) 
   // statistics: wave w <-> token w of the tile
   if (AQN) {
     float rstd = 0.f;
-    if (wave < rows)
+    if (wave < rows && mine(wave))
       rstd = a.rstd_in ? gload(a.rstd_in + tile * 16 + wave)
                        : rms_rstd(row_sumsq_buf<NT, VEC>(xsrc, stats_row, k, sq), k, a.eps);
     if (lane == 0) s_rstd[wave] = rstd;
@@ -488,8 +494,10 @@ __global__ void __launch_bounds__(kProWaves * kWave) k_prologue(PrologueArgs a) 
       }
       const int64_t kt = kt0 + ktl;
       const int s = jj / 4, lhi = jj % 4;
-      a.xs[((tile * a.KT + kt) * 4 + s) * kWave + lhi * 16 + t] = u32x4{packed[0], packed[1], packed[2], packed[3]};
-      if (jj == 0) a.xsc[(tile * a.KT + kt) * 16 + t] = __uint_as_float((uint32_t)(127 - pw) << 23);
+      if (mine(t)) {
+        a.xs[((tile * a.KT + kt) * 4 + s) * kWave + lhi * 16 + t] = u32x4{packed[0], packed[1], packed[2], packed[3]};
+        if (jj == 0) a.xsc[(tile * a.KT + kt) * 16 + t] = __uint_as_float((uint32_t)(127 - pw) << 23);
+      }
     }
   }
   __syncthreads();
@@ -519,7 +527,8 @@ __global__ void __launch_bounds__(kProWaves * kWave) k_prologue(PrologueArgs a) 
     for (int w = 0; w < kProWaves; ++w) v += s_red[w][g][src][q];
     const int jl = g * 16 + jr;  // rank within the 32-rank chunk
     const int L = (jl / 8) * 16 + tc;
-    a.t_part[((((int64_t)p * ntiles + tile) * kRankChunks + jc) * a.ks + c) * kWave * 8 + L * 8 + jl % 8] = v;
+    if (mine(tc))
+      a.t_part[((((int64_t)p * ntiles + tile) * kRankChunks + jc) * a.ks + c) * kWave * 8 + L * 8 + jl % 8] = v;
   }
 }
 
@@ -2165,7 +2174,10 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
     const bool big = m > kMaxTokensPerLaunch;
     pa.rstd_in = big && aqn ? rstd : nullptr;
     pa.tok_p = big && gemm_path ? tok_p : nullptr;
-    const dim3 grid((unsigned)ntiles, (unsigned)ks, (unsigned)(npg > 0 ? npg : 1));
+    // with the norm at decode, each token tile's statistics rows are split over four workgroups (a workgroup
+    // reads 4 rows in full instead of 16)
+    pa.tgs = aqn && !big ? 4 : 16;
+    const dim3 grid((unsigned)(ntiles * (16 / pa.tgs)), (unsigned)ks, (unsigned)(npg > 0 ? npg : 1));
     const dim3 block(kProWaves * kWave);
     const bool vec = pa.vec_x && (!aqn || (pa.vec_g && (!aqn->noise || pa.vec_z)));
 #define QN_PRO(NT_, AQN_)                                                                  \
