@@ -167,6 +167,7 @@ struct PrologueArgs {
   uint32_t* cnt;  // arrival counters of the linear kernel, zeroed here
   int32_t ncnt;
   int32_t tgs;    // tokens per workgroup: 16 (a whole token tile) or 4 (the tile split over four workgroups)
+  int32_t pgm;    // pair groups per workgroup: 1, or 2 (h computed once for both, many tokens)
 };
 
 // Sum of squares of one row by one wave, in the summation order of the standalone norm with NT threads (as
@@ -348,7 +349,7 @@ __global__ void __launch_bounds__(16 * kWave) k_rowstats(PrologueArgs a, float* 
 }
 
 // VEC: x rows, gamma and the noise rows start 16-byte aligned at every 8-element group (all loads 16 bytes wide).
-template <int NT, bool AQN, bool VEC>
+template <int NT, bool AQN, bool VEC, int PGM>
 __global__ void __launch_bounds__(kProWaves * kWave) k_prologue(PrologueArgs a) {
   constexpr int kCT = kMaxChunkTiles;                              // k-tiles per chunk (at most)
   constexpr int kProSlices = kCT * 4 / kProWaves;                // 32-wide k-slices per wave (at most)
@@ -364,29 +365,39 @@ __global__ void __launch_bounds__(kProWaves * kWave) k_prologue(PrologueArgs a) 
   const int tile = blockIdx.x / ngpt, tgrp = blockIdx.x % ngpt, ntiles = gridDim.x / ngpt;
   const int tlo = tgrp * a.tgs;
   auto mine = [&](int t) { return t >= tlo && t < tlo + a.tgs; };
-  const int c = blockIdx.y, pg = blockIdx.z;
+  const int c = blockIdx.y, pz = blockIdx.z;  // pair groups pz * pgm .. + pgm - 1
   const int KT = (int)a.KT, k = (int)a.k, m = (int)a.m;
   const int kt0 = c * a.CT;
   const int ctn = KT - kt0 < a.CT ? KT - kt0 : a.CT;  // k-tiles in this chunk
   const int kc0 = kt0 * kKTile;
   const int rows = m - tile * 16 < 16 ? m - tile * 16 : 16;  // tokens of this tile
-  // pair group -> (projection p, 32-rank chunk jc), from the adapter ranks (constant-index argument reads)
-  int p = -1, jc = 0, base = 0;
-  const uint16_t* Ap = nullptr;
-  int r = 0;
+  // pair groups -> (projection p, 32-rank chunk jc), from the adapter ranks (constant-index argument reads)
+  constexpr int kPgm = PGM;  // pair groups per workgroup (at most)
+  int pgp[kPgm], pgjc[kPgm], pgr[kPgm];
+  const uint16_t* pgA[kPgm];
 #pragma unroll
-  for (int q = 0; q < kMaxProj; ++q) {
-    const int nq = q < a.nproj ? (a.r[q] + 31) / 32 : 0;
-    if (p < 0 && pg < base + nq) {
-      p = q;
-      jc = pg - base;
-      Ap = a.A[q];
-      r = a.r[q];
+  for (int gi = 0; gi < kPgm; ++gi) {
+    const int pg = pz * a.pgm + gi;
+    int p = -1, jc = 0, base = 0, r = 0;
+    const uint16_t* Ap = nullptr;
+#pragma unroll
+    for (int q = 0; q < kMaxProj; ++q) {
+      const int nq = q < a.nproj ? (a.r[q] + 31) / 32 : 0;
+      if (gi < a.pgm && p < 0 && pg < base + nq) {
+        p = q;
+        jc = pg - base;
+        Ap = a.A[q];
+        r = a.r[q];
+      }
+      base += nq;
     }
-    base += nq;
+    pgp[gi] = p;
+    pgjc[gi] = jc;
+    pgr[gi] = r;
+    pgA[gi] = Ap;
   }
-  const bool lora = p >= 0;
-  if (tile == 0 && tgrp == 0 && c == 0 && pg == 0 && (int)threadIdx.x < a.ncnt) a.cnt[threadIdx.x] = 0u;
+  const bool lora = pgp[0] >= 0;
+  if (tile == 0 && tgrp == 0 && c == 0 && pz == 0 && (int)threadIdx.x < a.ncnt) a.cnt[threadIdx.x] = 0u;
 
   // Loads, in the order they are needed (each wait then covers its own loads only): the first batch of the
   // statistics row, the inputs of h, the LoRA-down A fragments.
@@ -422,9 +433,11 @@ __global__ void __launch_bounds__(kProWaves * kWave) k_prologue(PrologueArgs a) 
   // LoRA-down A fragments of this wave's slices, issued last (needed last). Fragment (g, slice s): ranks
   // jc*32 + g*16 + lane%16, k = kc0 + 32 s + 8 (lane/16) .. + 8; ranks past r and k past the row read as 0.
   const int nsl = ctn * 4;
-  u32x4 af[2][kProSlices];
-  {
-    const rsrc_t asrc = make_rsrc(Ap, lora ? (int64_t)r * k * 2 : 0);
+  u32x4 af[kPgm][2][kProSlices];
+#pragma unroll
+  for (int gi = 0; gi < kPgm; ++gi) {
+    const int jc = pgjc[gi], r = pgr[gi];
+    const rsrc_t asrc = make_rsrc(pgA[gi], pgp[gi] >= 0 ? (int64_t)r * k * 2 : 0);
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
@@ -432,8 +445,8 @@ __global__ void __launch_bounds__(kProWaves * kWave) k_prologue(PrologueArgs a) 
         const int s = wave + i * kProWaves;
         const int j = jc * 32 + g * 16 + lane % 16;
         const int kk = kc0 + s * 32 + (lane / 16) * 8;
-        const bool ok = s < nsl && j < r && kk < k;
-        af[g][i] = bload16(asrc, ok ? (uint32_t)(((int64_t)j * k + kk) * 2) : kOutOfRange);
+        const bool ok = pgp[gi] >= 0 && s < nsl && j < r && kk < k;
+        af[gi][g][i] = bload16(asrc, ok ? (uint32_t)(((int64_t)j * k + kk) * 2) : kOutOfRange);
       }
   }
 
@@ -469,7 +482,7 @@ __global__ void __launch_bounds__(kProWaves * kWave) k_prologue(PrologueArgs a) 
       }
     }
     *reinterpret_cast<u32x4*>(&s_h[t][kg * 8]) = u32x4{hv[0], hv[1], hv[2], hv[3]};
-    if (pg == 0) {
+    if (pz == 0) {
       // tile amax over the 16 lanes of this (token, k-tile), then 2^p with amax * 2^p in [2^14, 2^15), read off the
       // exponent field and kept within the normal range so 2^p and 2^-p are plain f32 powers of two
       int pw;
@@ -503,32 +516,38 @@ __global__ void __launch_bounds__(kProWaves * kWave) k_prologue(PrologueArgs a) 
   __syncthreads();
   if (!lora) return;
 
-  // LoRA-down over the chunk: B-fragment (token lane%16, k = 32 s + 8 (lane/16) .. + 8) from LDS
-  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  // LoRA-down over the chunk, per pair group: B-fragment (token lane%16, k = 32 s + 8 (lane/16) .. + 8) from LDS
 #pragma unroll
-  for (int i = 0; i < kProSlices; ++i) {
-    const int s = wave + i * kProWaves;
-    if (s >= nsl) break;
-    const u32x4 b = *reinterpret_cast<const u32x4*>(&s_h[lane % 16][s * 32 + (lane / 16) * 8]);
+  for (int gi = 0; gi < kPgm; ++gi) {
+    const int p = pgp[gi], jc = pgjc[gi];
+    if (p < 0) break;
+    if (gi > 0) __syncthreads();  // the previous group's reduction is done with s_red
+    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
-      acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[g][i]),
-                                                       __builtin_bit_cast(bf16x8, b), acc[g], 0, 0, 0);
-  }
-  s_red[wave][0][lane] = acc[0];
-  s_red[wave][1][lane] = acc[1];
-  __syncthreads();
-  if (threadIdx.x < 512) {
-    // thread (rank group g, rank row jr, token column tc); D lane (jr/4)*16 + tc, element jr%4; waves in order
-    const int g = threadIdx.x / 256, jr = (threadIdx.x % 256) / 16, tc = threadIdx.x % 16;
-    const int src = (jr / 4) * 16 + tc, q = jr % 4;
-    float v = 0.f;
+    for (int i = 0; i < kProSlices; ++i) {
+      const int s = wave + i * kProWaves;
+      if (s >= nsl) break;
+      const u32x4 b = *reinterpret_cast<const u32x4*>(&s_h[lane % 16][s * 32 + (lane / 16) * 8]);
 #pragma unroll
-    for (int w = 0; w < kProWaves; ++w) v += s_red[w][g][src][q];
-    const int jl = g * 16 + jr;  // rank within the 32-rank chunk
-    const int L = (jl / 8) * 16 + tc;
-    if (mine(tc))
-      a.t_part[((((int64_t)p * ntiles + tile) * kRankChunks + jc) * a.ks + c) * kWave * 8 + L * 8 + jl % 8] = v;
+      for (int g = 0; g < 2; ++g)
+        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[gi][g][i]),
+                                                         __builtin_bit_cast(bf16x8, b), acc[g], 0, 0, 0);
+    }
+    s_red[wave][0][lane] = acc[0];
+    s_red[wave][1][lane] = acc[1];
+    __syncthreads();
+    if (threadIdx.x < 512) {
+      // thread (rank group g, rank row jr, token column tc); D lane (jr/4)*16 + tc, element jr%4; waves in order
+      const int g = threadIdx.x / 256, jr = (threadIdx.x % 256) / 16, tc = threadIdx.x % 16;
+      const int src = (jr / 4) * 16 + tc, q = jr % 4;
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kProWaves; ++w) v += s_red[w][g][src][q];
+      const int jl = g * 16 + jr;  // rank within the 32-rank chunk
+      const int L = (jl / 8) * 16 + tc;
+      if (mine(tc))
+        a.t_part[((((int64_t)p * ntiles + tile) * kRankChunks + jc) * a.ks + c) * kWave * 8 + L * 8 + jl % 8] = v;
+    }
   }
 }
 
@@ -2177,13 +2196,16 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
     // with the norm at decode, each token tile's statistics rows are split over four workgroups (a workgroup
     // reads 4 rows in full instead of 16)
     pa.tgs = aqn && !big ? 4 : 16;
-    const dim3 grid((unsigned)(ntiles * (16 / pa.tgs)), (unsigned)ks, (unsigned)(npg > 0 ? npg : 1));
+    // with many tokens, two pair groups share a workgroup (h of the chunk is computed once for both)
+    pa.pgm = big && norm_threads(k) == 256 ? 2 : 1;
+    const int npz = npg > 0 ? (npg + pa.pgm - 1) / pa.pgm : 1;
+    const dim3 grid((unsigned)(ntiles * (16 / pa.tgs)), (unsigned)ks, (unsigned)npz);
     const dim3 block(kProWaves * kWave);
     const bool vec = pa.vec_x && (!aqn || (pa.vec_g && (!aqn->noise || pa.vec_z)));
-#define QN_PRO(NT_, AQN_)                                                                  \
-  do {                                                                                     \
-    if (vec) hipLaunchKernelGGL((k_prologue<NT_, AQN_, true>), grid, block, 0, s, pa);  \
-    else hipLaunchKernelGGL((k_prologue<NT_, AQN_, false>), grid, block, 0, s, pa);     \
+#define QN_PRO(NT_, AQN_, PGM_)                                                                    \
+  do {                                                                                             \
+    if (vec) hipLaunchKernelGGL((k_prologue<NT_, AQN_, true, PGM_>), grid, block, 0, s, pa);    \
+    else hipLaunchKernelGGL((k_prologue<NT_, AQN_, false, PGM_>), grid, block, 0, s, pa);       \
   } while (0)
 #define QN_STATS(NT_, AQN_)                                                                                   \
   do {                                                                                                        \
@@ -2194,13 +2216,15 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
   } while (0)
     if (!aqn) {
       if (big) QN_STATS(256, false);
-      QN_PRO(256, false);
+      if (pa.pgm == 2) QN_PRO(256, false, 2);
+      else QN_PRO(256, false, 1);
     } else if (norm_threads(k) == 256) {
       if (big) QN_STATS(256, true);
-      QN_PRO(256, true);
+      if (pa.pgm == 2) QN_PRO(256, true, 2);
+      else QN_PRO(256, true, 1);
     } else {
       if (big) QN_STATS(1024, true);
-      QN_PRO(1024, true);
+      QN_PRO(1024, true, 1);
     }
 #undef QN_STATS
 #undef QN_PRO

@@ -321,6 +321,30 @@ def test_linear_many_tokens_bf16_store_paths(qn, monkeypatch, m, ns, k, silu, re
         assert np.all(np.abs(g - ref) <= 2.0 ** -8 * np.abs(ref) + LINEAR_TOL * np.abs(ref).max())
 
 
+@pytest.mark.parametrize("m,n,k", [(200, 520, 640), (129, 256, 384)])
+def test_linear_many_tokens_residual_aliases_output(qn, monkeypatch, m, n, k):
+    """Many tokens, bf16 output with the residual read from the output buffer itself (the one aliasing the API
+    allows): the same bits as with a separate residual buffer, on both store paths."""
+    monkeypatch.delenv("QN_GEMM_OFF", raising=False)
+    c = Case(m, [n], k, r=16, seed=m + k, aqn=True)
+    wq = qn.quantize(dev_bf16(c.w[0]), qn.LAYOUT_TILED)
+    res = synth.normal_bf16(93, (m, n))
+    aqn = qn.make_aqn(dev_bf16(c.gamma), dev_f32(c.noise), c.sigma, 1e-6)
+    for store in ("fast", "elem"):
+        if store == "elem":
+            monkeypatch.setenv("QN_GEMM_STORE", "elem")
+        else:
+            monkeypatch.delenv("QN_GEMM_STORE", raising=False)
+        y_sep = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=DEV)
+        qn.lora_linear(dev_bf16(c.x), [qn.Projection(wq, y_sep, dev_bf16(c.A[0]), dev_bf16(c.B[0]), c.lam,
+                                                     residual=dev_bf16(res))], aqn)
+        y_alias = dev_bf16(res)
+        qn.lora_linear(dev_bf16(c.x), [qn.Projection(wq, y_alias, dev_bf16(c.A[0]), dev_bf16(c.B[0]), c.lam,
+                                                     residual=y_alias)], aqn)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bf16(y_sep), host_bf16(y_alias)), store
+
+
 def test_linear_many_tokens_row_scales(qn):
     """One exponent per token: rows whose magnitudes differ by 2^40 across the batch, and a row of zeros, keep their
     own relative accuracy (each token is checked against its own scale)."""
