@@ -956,6 +956,10 @@ constexpr int kGFragLoads = 10;                     // 16-byte activation loads 
 __host__ __device__ constexpr int gemv_lred_bytes(int nr, int tmt) { return kGMaxUnits * nr * tmt * kWave * 16; }
 __host__ __device__ constexpr int64_t gemv_block_floats(int nr, int tmt) { return (int64_t)kGMaxUnits * nr * tmt * 256; }
 
+__host__ __device__ constexpr int vmcnt_imm(int n) {  // s_waitcnt immediate: vmcnt = n, expcnt and lgkmcnt not waited
+  return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+}
+
 struct GemvArgs {
   LinearArgs L;
   int32_t nu, nbr, nk;
@@ -1009,8 +1013,8 @@ __global__ void __launch_bounds__(kGWaves * kWave) k_gemv(GemvArgs g) {
   uint8_t* const lred = s_lds + kGLds - gemv_lred_bytes(NR, TMT);
   const int fr_bytes = TMT * T * 4 * kWave * 16;
 
-  // 1. stream waves: unit u, k-part j of h. Their first two weight tiles are requested before anything else (they
-  //    come from HBM); the preamble is kept short because every instruction of it is fetched cold at each launch.
+  // 1. stream waves: unit u, k-part j of h. The preamble is kept short because every instruction of it is fetched
+  //    cold at each launch.
   constexpr unsigned char kParts[kGMaxUnits + 1] = {1, 15, 7, 5, 3, 3, 2, 2, 1};  // kGStream / U
   static_assert(kGStream == 15 && kGMaxUnits == 8, "parts table");
   const int h = kParts[U];
@@ -1048,11 +1052,6 @@ __global__ void __launch_bounds__(kGWaves * kWave) k_gemv(GemvArgs g) {
     }
   };
   GTile<NR> Bt[D];
-#pragma unroll
-  for (int j = 0; j < D - 1; ++j) {
-    load(Bt[j], ta + j);
-    __builtin_amdgcn_sched_barrier(0);  // issue order of the first tiles: the loop's wait counts rely on it
-  }
 
   // 2. the chunk's activation fragments ([tt][lt][s][lane], 16 bytes) and tile scales ([tt][lt][16] f32), loaded
   //    straight into LDS (1 KB per wave and step; a chunk never straddles token tiles: T * 256 is a multiple of 64)
@@ -1108,7 +1107,16 @@ __global__ void __launch_bounds__(kGWaves * kWave) k_gemv(GemvArgs g) {
     const bool ok = rb && u < U && tok < mt && n < nl;
     res[i] = gload(ok ? rb + tok * ld + n : reinterpret_cast<const uint16_t*>(a.xsc));
   }
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's loads have landed (loads to LDS are counted by vmcnt)
+  // the first D - 1 weight tiles (from HBM) are requested after the activation copies and residuals: loads return
+  // in order, so the wait below covers those (loads to LDS are counted by vmcnt) and not these tiles, which stay in
+  // flight across the barrier (requested first, they held up every wave's copy: measured 0.6-0.8 us slower)
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < D - 1; ++j) {
+    load(Bt[j], ta + j);
+    __builtin_amdgcn_sched_barrier(0);  // issue order of the first tiles: the loop's wait counts rely on it
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((D - 1) * NR * 2));
 #pragma unroll
   for (int i = 0; i < kOut; ++i) s_res[threadIdx.x + i * kGWaves * kWave] = res[i];
   __syncthreads();
@@ -1569,10 +1577,6 @@ struct MW {
   uint32_t c[4][4];  // [row-group slot][32-wide slice]
   uint32_t sc[4];
 };
-
-__host__ __device__ constexpr int vmcnt_imm(int n) {  // s_waitcnt immediate: vmcnt = n, expcnt and lgkmcnt not waited
-  return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
-}
 
 // E2M1 codes (8 per dword) of one 32-wide slice times the E4M3 block scale, exactly, as the f16 A-fragment
 __device__ __forceinline__ f16x8 dequant_frag(uint32_t cw, uint32_t scale_byte) {
