@@ -36,8 +36,8 @@ def lib():
         if not os.path.exists(_LIB):
             build()
         L = ctypes.CDLL(_LIB)
-        P, i64, i32, dbl, f32, u16 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double,
-                                      ctypes.c_float, ctypes.c_uint16)
+        P, i64, i32, dbl, f32, u16, u64 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double,
+                                           ctypes.c_float, ctypes.c_uint16, ctypes.c_uint64)
         sig = {
             "orc_bf16_value": ([u16], dbl),
             "orc_bf16_round": ([dbl], u16),
@@ -52,6 +52,8 @@ def lib():
             "orc_nvfp4_dequantize": ([P, P, f32, i64, i64, P, P], None),
             "orc_aqn_sigma": ([i32, dbl, dbl], dbl),
             "orc_aqn_rmsnorm": ([P, i64, i64, i64, P, P, i64, f32, f32, P, P], None),
+            "orc_philox4x64_10": ([P, P, P], None),
+            "orc_aqn_noise": ([u64, u64, u64, i64, i64, i64, P, i64], None),
             "orc_lora_linear": ([P, i64, i64, i64, P, P, f32, i64, P, P, i32, dbl, P], None),
             "orc_dense_linear": ([P, i64, i64, P, i64, P], None),
             "orc_group_advantage": ([P, i32, i32, dbl, P], None),
@@ -169,6 +171,22 @@ def aqn_rmsnorm(x: np.ndarray, gamma: np.ndarray, noise: np.ndarray | None, sigm
     hb = np.empty((m, d), dtype=np.uint16)
     lib().orc_aqn_rmsnorm(_p(x), m, d, d, _p(gamma), _p(nz), noise_ld, float(sigma), float(eps), _p(he), _p(hb))
     return he, hb
+
+
+def philox4x64_10(counter, key) -> np.ndarray:
+    """One Philox4x64-10 block: counter (4 words) and key (2 words) -> 4 uint64 words."""
+    c = np.ascontiguousarray(np.asarray(counter, dtype=np.uint64))
+    k = np.ascontiguousarray(np.asarray(key, dtype=np.uint64))
+    out = np.empty(4, dtype=np.uint64)
+    lib().orc_philox4x64_10(_p(c), _p(k), _p(out))
+    return out
+
+
+def aqn_noise(seed: int, stream: int, row_offset: int, draw_rows: int, m: int, d: int) -> np.ndarray:
+    """Seeded standard-normal noise eps [m, d] f32 (Philox4x64-10 + Box-Muller; see orc_aqn_noise)."""
+    out = np.empty((m, d), dtype=np.float32)
+    lib().orc_aqn_noise(int(seed), int(stream), int(row_offset), int(draw_rows), m, d, _p(out), d)
+    return out
 
 
 # ---- linear ------------------------------------------------------------------------------------------------------

@@ -267,6 +267,63 @@ void orc_aqn_rmsnorm(const uint16_t* x, int64_t m, int64_t d, int64_t ldx, const
   }
 }
 
+// ---- AQN noise drawn from a seed -------------------------------------------------------------------------------
+// The pages add Gaussian noise z = sigma * eps, eps ~ N(0, 1), to the norm's clean scale at every call and say
+// neither how it is drawn nor how wide its scope is [review §5.1 and §9.1]. This draw is one concrete choice, fixed
+// here so that a device implementation can be checked against it: a counter-based generator (Philox4x64 with 10
+// rounds, Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011) keyed by
+// (seed, stream), one block per 8 consecutive columns of one draw, and the Box-Muller transform (Box and Muller,
+// 1958) on pairs of its 32-bit words.
+
+// One Philox4x64 block: 10 rounds of the 4-word S-box (two 64x64 -> 128-bit multiplications, the high halves
+// XOR-ed with the other two words and the round key, words permuted), the key advanced by the Weyl constants
+// between rounds. Constants as published for Philox4x64.
+void orc_philox4x64_10(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4]) {
+  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+  uint64_t x0 = ctr[0], x1 = ctr[1], x2 = ctr[2], x3 = ctr[3], k0 = key[0], k1 = key[1];
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) { k0 += W0; k1 += W1; }
+    const unsigned __int128 p0 = (unsigned __int128)M0 * x0, p1 = (unsigned __int128)M1 * x2;
+    const uint64_t hi0 = (uint64_t)(p0 >> 64), lo0 = (uint64_t)p0, hi1 = (uint64_t)(p1 >> 64), lo1 = (uint64_t)p1;
+    const uint64_t y0 = hi1 ^ x1 ^ k0, y1 = lo1, y2 = hi0 ^ x3 ^ k1, y3 = lo0;
+    x0 = y0; x1 = y1; x2 = y2; x3 = y3;
+  }
+  out[0] = x0; out[1] = x1; out[2] = x2; out[3] = x3;
+}
+
+// A 32-bit word as a uniform in (0, 1): its top 23 bits b, u = (b + 1/2) / 2^23, exactly representable in f32 and
+// f64 alike (so both sides of a comparison start from the same u), never 0 or 1.
+double word_uniform(uint32_t w) { return ((double)(w >> 9) + 0.5) / 8388608.0; }
+
+// eps[i][j] (f32, row stride ld) for rows i of a call: row i takes draw index row_offset + i / draw_rows (draw_rows
+// > 0: that many consecutive rows share a draw, e.g. the tokens of one response), or draw row_offset for every row
+// (draw_rows == 0). Columns 8c .. 8c+7 of draw r come from the block at counter (c, r, 0, 0) under key (seed,
+// stream); its words w_0..w_7 (w_2q = low half of output q, w_2q+1 = high half) pair as (w_2p, w_2p+1) -> columns
+// 8c+2p, 8c+2p+1: rho = sqrt(-2 ln u(w_2p)), eps = rho cos(2 pi u(w_2p+1)), rho sin(2 pi u(w_2p+1)). fp64, then
+// rounded to f32 (the precision the norm reads its noise in).
+void orc_aqn_noise(uint64_t seed, uint64_t stream, uint64_t row_offset, int64_t draw_rows, int64_t m, int64_t d,
+                   float* eps, int64_t ld) {
+  const double two_pi = 6.283185307179586476925286766559;
+  const uint64_t key[2] = {seed, stream};
+  for (int64_t i = 0; i < m; ++i) {
+    const uint64_t r = row_offset + (draw_rows > 0 ? (uint64_t)(i / draw_rows) : 0);
+    for (int64_t c = 0; c * 8 < d; ++c) {
+      const uint64_t ctr[4] = {(uint64_t)c, r, 0, 0};
+      uint64_t o[4];
+      orc_philox4x64_10(ctr, key, o);
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t wa = (uint32_t)o[p], wb = (uint32_t)(o[p] >> 32);
+        const double rho = std::sqrt(-2.0 * std::log(word_uniform(wa)));
+        const double th = two_pi * word_uniform(wb);
+        const int64_t j = c * 8 + 2 * p;
+        if (j < d) eps[i * ld + j] = (float)(rho * std::cos(th));
+        if (j + 1 < d) eps[i * ld + j + 1] = (float)(rho * std::sin(th));
+      }
+    }
+  }
+}
+
 // LoRA-adapted linear with an NVFP4 base [review §2.1, forward map y = W_hat x + lambda B (A x)], row-batched:
 //   y[i][o] = sum_c W_hat[o][c] h[i][c] + lambda * sum_j B[o][j] * t[i][j],   t[i][j] = sum_c A[j][c] h[i][c]
 // h [m x k] bf16 (row stride ldh), W_hat from the canonical NVFP4 layout [n x k], A [r x k] bf16, B [n x r] bf16.
