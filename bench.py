@@ -19,6 +19,7 @@ SiLU(gate) * up epilogue on the MFMA path, followed by the group advantages of 8
 from __future__ import annotations
 
 import argparse
+import functools
 import json
 import os
 import sys
@@ -69,7 +70,9 @@ def flops(shape, m):
     return sum(2 * m * n * k + 2 * m * shape.rank * (n + k) for n, k in shape.projections().values())
 
 
-def build_layers(shape, m, copies, sigma, dev):
+def build_layers(shape, m, copies, sigma, dev, noise="input"):
+    """noise: "input" (each norm reads a seeded noise vector shared by the batch) or "device" (each norm draws one
+    noise row per response on the device: Philox4x64-10 + Box-Muller, a key per layer copy and norm)."""
     import numpy as np
     import torch
 
@@ -89,14 +92,22 @@ def build_layers(shape, m, copies, sigma, dev):
     e1 = torch.from_numpy(synth.normal_f32(s("eps_norm1"), (shape.hidden,))).to(dev)
     e2 = torch.from_numpy(synth.normal_f32(s("eps_norm2"), (shape.hidden,))).to(dev)
     x = bf16_dev(synth.normal_bf16(s("x"), (m, shape.hidden)))
+    from nvfp4_weight_only_amd import NoiseDraw
+
+    def draws(i):
+        if noise != "device":
+            return None
+        return (NoiseDraw(s("eps_norm1"), i, 0, 1), NoiseDraw(s("eps_norm2"), i, 0, 1))
+
     base = DecoderLayer.from_bf16(shape, w, lora, g1, g2, e1, e2, sigma, 2.0)
+    base.draws = draws(0)
     del w
     layers = [base]
-    for _ in range(copies - 1):  # distinct copies of the packed weights and adapters (same values, new addresses)
+    for i in range(1, copies):  # distinct copies of the packed weights and adapters (same values, new addresses)
         wq = {nm: type(q)(q.codes.clone(), q.scales.clone(), q.tensor_scale.clone(), q.n, q.k, q.layout)
               for nm, q in base.w.items()}
         lo = {nm: (a.clone(), b.clone()) for nm, (a, b) in lora.items()}
-        layers.append(DecoderLayer(shape, wq, lo, g1, g2, e1, e2, sigma, 2.0))
+        layers.append(DecoderLayer(shape, wq, lo, g1, g2, e1, e2, sigma, 2.0, draws=draws(i)))
     torch.cuda.synchronize()
     return layers, x
 
@@ -269,6 +280,10 @@ def main():
     ap.add_argument("--event-every", type=int, default=8,
                     help="decode: put HIP events around the gate|up kernel on every n-th timed step")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--noise", choices=["input", "device", "standalone"], default="input",
+                    help="decode: the norms read a fixed noise vector (input), draw one row per response inside the "
+                         "norm prologues (device), or read rows written by the standalone generator before each "
+                         "norm (standalone: the same draws, one more launch per norm)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 256 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -291,7 +306,17 @@ def main():
     sigma = float(qn.aqn_sigma(1))
     dev = torch.device("cuda:0")
     print(f"[bench] building {args.copies} layer copies, M={m}", file=sys.stderr, flush=True)
-    layers, x = build_layers(shape, m, args.copies, sigma, dev)
+    layers, x = build_layers(shape, m, args.copies, sigma, dev, "device" if args.noise == "device" else "input")
+    if args.noise == "standalone":
+        # per-response rows written by aqn_noise before each norm, read by the norm (noise_per_row)
+        for i, L in enumerate(layers):
+            L.noise1 = torch.empty(m, shape.hidden, dtype=torch.float32, device=dev)
+            L.noise2 = torch.empty(m, shape.hidden, dtype=torch.float32, device=dev)
+            L.noise_rows = True
+            # the generator calls with their arguments bound once (a step's host work stays below its GPU time)
+            sh = qn._stream(torch.cuda.current_stream())
+            L.fresh = tuple(functools.partial(qn.lib.aqn_noise, j + 1, i, 0, 1, m, shape.hidden, qn._ptr(buf),
+                                              shape.hidden, sh) for j, buf in enumerate((L.noise1, L.noise2)))
     ws = qn.Workspace(dev)
     bound = [L.bind(x, ws) for L in layers]
     stream = torch.cuda.current_stream()
@@ -304,8 +329,13 @@ def main():
     def step(i, timed):
         b = bound[i % len(bound)]
         c = b.calls
+        if args.noise == "standalone":
+            L = layers[i % len(layers)]
+            L.fresh[0]()
         c[0]()
         c[1]()
+        if args.noise == "standalone":
+            L.fresh[1]()
         if timed and i in ev:
             c[2](phases=qn.RUN_PROLOGUE_ONLY)
             ev[i][0].record(stream)
@@ -352,7 +382,11 @@ def main():
         "config": {"workload": "Qwen2.5-7B-shaped decoder layer at decode, NVFP4 + rank-32 bf16 LoRA on every "
                                "projection, two AQN-RMSNorms (sigma 1e-2), attention scores excluded",
                    "global_batch": m, "hidden": shape.hidden, "intermediate": shape.inter, "lora_rank": shape.rank,
-                   "layer_copies_rotated": args.copies, "tokens_per_s_basis": "M / (28 x layer step time)"},
+                   "layer_copies_rotated": args.copies, "tokens_per_s_basis": "M / (28 x layer step time)",
+                   "noise": {"input": "read: one seeded N(0,1) vector per norm, shared by the batch",
+                             "device": "drawn in the norm prologues: Philox4x64-10 + Box-Muller, one row per response",
+                             "standalone": "one row per response, written by aqn_noise before each norm and read"
+                             }[args.noise]},
         "layer_step_us": ms_step * 1e3,
         "step_algorithmic_bytes": step_bytes,
         "step_achieved_GBps": step_bytes / (ms_step * 1e-3) / 1e9,

@@ -86,6 +86,12 @@ typedef struct {
   int64_t noise_ld;
   float sigma;           /* noise standard deviation for this stage, >= 0 (see aqn_sigma); 0 gives plain RMSNorm */
   float eps;             /* >= 0, added to the mean square */
+  /* Noise drawn on the device instead of read (draw != 0; noise must then be NULL): the same values aqn_noise
+   * writes for (seed, subseed, row_offset, draw_rows), generated where the norm consumes them. */
+  int32_t draw;
+  uint64_t seed, subseed;
+  uint64_t row_offset;   /* draw index of row 0 */
+  int64_t draw_rows;     /* >= 0: rows per draw (e.g. the tokens of one response); 0 = one draw for every row */
 } qn_aqn;
 
 /* One projection consuming the shared activation: y = s_g * W_hat(codes, scales) x + lambda * B (A x)
@@ -141,6 +147,17 @@ qn_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* block_scales, co
  * per row, f32 arithmetic, round-to-nearest-even to bf16.  x [m][ldx] bf16, h [m][ldh] bf16 (device). */
 qn_status aqn_rmsnorm(const uint16_t* x, int64_t m, int64_t d, int64_t ldx, const qn_aqn* aqn, uint16_t* h,
                       int64_t ldh, void* stream);
+
+/* Standard-normal noise for AQN drawn from a seed [review §5.1 and §9.1: Gaussian noise on the norm scale at every
+ * call; the pages leave the generator and the scope of a draw open]. Row i (0 <= i < m) takes draw index
+ * r = row_offset + i / draw_rows (draw_rows > 0), or r = row_offset for every row (draw_rows == 0). Columns 8c .. 8c+7
+ * of draw r come from one Philox4x64-10 block (Salmon, Moraes, Dror and Shaw, SC 2011) at counter (c, r, 0, 0)
+ * under key (seed, subseed); its eight 32-bit words w0..w7 (w2q, w2q+1 = low, high half of output word q) give
+ * columns 8c+2p, 8c+2p+1 by the Box-Muller transform: u(w) = ((w >> 9) + 1/2) 2^-23, rho = sqrt(-2 ln u(w2p)),
+ * eps = rho cos(2 pi u(w2p+1)), rho sin(2 pi u(w2p+1)), in f32 (a few ulp from the exactly rounded values).
+ * eps: [m][ld] f32 (device), ld >= d. Errors: QN_ERR_SHAPE (m, d < 0, ld < d, draw_rows < 0), QN_ERR_NULL. */
+qn_status aqn_noise(uint64_t seed, uint64_t subseed, uint64_t row_offset, int64_t draw_rows, int64_t m, int64_t d,
+                    float* eps, int64_t ld, void* stream);
 
 /* Workspace bytes nvfp4_lora_linear needs for these arguments (host, pure). */
 size_t nvfp4_lora_linear_workspace(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj);

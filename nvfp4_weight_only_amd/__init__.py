@@ -22,6 +22,7 @@ EPI_NONE, EPI_SILU_MUL = 0, 1
 RUN_PROLOGUE_ONLY, RUN_MAIN_ONLY = 0x100, 0x200
 
 EXPORTS = ["nvfp4_quantize", "nvfp4_tiled_codes_bytes", "nvfp4_tiled_scales_bytes", "nvfp4_dequantize", "aqn_rmsnorm",
+           "aqn_noise",
            "nvfp4_lora_linear_workspace", "nvfp4_lora_linear", "aqn_sigma", "grpo_group_advantage",
            "qn_status_string"]
 
@@ -34,7 +35,9 @@ class QnError(RuntimeError):
 
 class QnAqn(ctypes.Structure):
     _fields_ = [("gamma", ctypes.c_void_p), ("noise", ctypes.c_void_p), ("noise_ld", ctypes.c_int64),
-                ("sigma", ctypes.c_float), ("eps", ctypes.c_float)]
+                ("sigma", ctypes.c_float), ("eps", ctypes.c_float), ("draw", ctypes.c_int32),
+                ("seed", ctypes.c_uint64), ("subseed", ctypes.c_uint64), ("row_offset", ctypes.c_uint64),
+                ("draw_rows", ctypes.c_int64)]
 
 
 class QnProj(ctypes.Structure):
@@ -57,6 +60,7 @@ def _load():
         "nvfp4_tiled_scales_bytes": ([i64, i64], sz),
         "nvfp4_dequantize": ([P, P, P, i64, i64, i32, P, i64, P], i32),
         "aqn_rmsnorm": ([P, i64, i64, i64, ctypes.POINTER(QnAqn), P, i64, P], i32),
+        "aqn_noise": ([ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64, i64, i64, i64, P, i64, P], i32),
         "nvfp4_lora_linear_workspace": ([i64, i64, ctypes.POINTER(QnProj), i32], sz),
         "nvfp4_lora_linear": ([P, i64, i64, i64, ctypes.POINTER(QnAqn), ctypes.POINTER(QnProj), i32, i32, P, sz, P],
                               i32),
@@ -145,11 +149,23 @@ def aqn_sigma(stage: int, start: float = 1e-2, end: float = 5e-4) -> float:
     return float(lib.aqn_sigma(stage, start, end))
 
 
+@dataclass
+class NoiseDraw:
+    """Noise drawn on the device (see aqn_noise): key (seed, subseed); row i takes draw row_offset + i // draw_rows
+    (draw_rows > 0) or row_offset (draw_rows == 0)."""
+    seed: int
+    subseed: int = 0
+    row_offset: int = 0
+    draw_rows: int = 1
+
+
 class AqnParams:
     """AQN-RMSNorm parameters: keeps the device tensors alive for as long as the C struct that points at them."""
 
     def __init__(self, gamma: torch.Tensor, noise: Optional[torch.Tensor], sigma: float, eps: float = 1e-6,
-                 noise_per_row: bool = False):
+                 noise_per_row: bool = False, draw: Optional[NoiseDraw] = None):
+        if draw is not None and noise is not None:
+            raise ValueError("AQN noise is either read (noise) or drawn on the device (draw), not both")
         self.gamma, self.noise = gamma, noise
         self.c = QnAqn()
         self.c.gamma = gamma.data_ptr()
@@ -157,18 +173,31 @@ class AqnParams:
         self.c.noise_ld = noise.shape[-1] if (noise is not None and noise_per_row) else 0
         self.c.sigma = sigma
         self.c.eps = eps
+        if draw is not None:
+            self.c.draw = 1
+            self.c.seed, self.c.subseed = draw.seed, draw.subseed
+            self.c.row_offset, self.c.draw_rows = draw.row_offset, draw.draw_rows
 
 
 def make_aqn(gamma: torch.Tensor, noise: Optional[torch.Tensor], sigma: float, eps: float = 1e-6,
-             noise_per_row: bool = False) -> AqnParams:
-    return AqnParams(gamma, noise, sigma, eps, noise_per_row)
+             noise_per_row: bool = False, draw: Optional[NoiseDraw] = None) -> AqnParams:
+    return AqnParams(gamma, noise, sigma, eps, noise_per_row, draw)
+
+
+def aqn_noise(draw: NoiseDraw, m: int, d: int, device, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Seeded standard-normal noise [m, d] f32 on the device (Philox4x64-10 + Box-Muller)."""
+    eps = out if out is not None else torch.empty(m, d, dtype=torch.float32, device=device)
+    _check(lib.aqn_noise(draw.seed, draw.subseed, draw.row_offset, draw.draw_rows, m, d, _ptr(eps), eps.stride(0),
+                         _stream(stream)), "aqn_noise")
+    return eps
 
 
 def aqn_rmsnorm(x: torch.Tensor, gamma: torch.Tensor, noise: Optional[torch.Tensor], sigma: float, eps: float = 1e-6,
-                noise_per_row: bool = False, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                noise_per_row: bool = False, out: Optional[torch.Tensor] = None, stream=None,
+                draw: Optional[NoiseDraw] = None) -> torch.Tensor:
     m, d = x.shape
     h = out if out is not None else torch.empty(m, d, dtype=torch.bfloat16, device=x.device)
-    a = make_aqn(gamma, noise, sigma, eps, noise_per_row)
+    a = make_aqn(gamma, noise, sigma, eps, noise_per_row, draw)
     _check(lib.aqn_rmsnorm(_ptr(x), m, d, x.stride(0), ctypes.byref(a.c), _ptr(h), h.stride(0), _stream(stream)),
            "aqn_rmsnorm")
     return h

@@ -168,6 +168,7 @@ struct PrologueArgs {
   int32_t ncnt;
   int32_t tgs;    // tokens per workgroup: 16 (a whole token tile) or 4 (the tile split over four workgroups)
   int32_t pgm;    // pair groups per workgroup: 1, or 2 (h computed once for both, many tokens)
+  QnDraw draw;    // noise drawn on the device (draw.on) instead of read from `noise`
 };
 
 // Sum of squares of one row by one wave, in the summation order of the standalone norm with NT threads (as
@@ -323,7 +324,16 @@ __global__ void __launch_bounds__(16 * kWave) k_rowstats(PrologueArgs a, float* 
       bload_bf16x8<VEC>(xsrc, c < nch ? row + (uint32_t)c * 16 : kOutOfRange, hx[u]);
       if (AQN) {
         bload_bf16x8<VEC>(gsrc, c < nch ? (uint32_t)c * 16 : kOutOfRange, hg[u]);
-        bload_f32x8<VEC>(zsrc, c < nch ? (uint32_t)((wave * nld + c * 8) * 4) : kOutOfRange, hz[u]);
+        if (!a.draw.on) bload_f32x8<VEC>(zsrc, c < nch ? (uint32_t)((wave * nld + c * 8) * 4) : kOutOfRange, hz[u]);
+      }
+    }
+    if (AQN && a.draw.on) {
+      // drawn noise of this token's chunks, computed while the loads are in flight
+      const uint64_t r = draw_index(a.draw, (int64_t)tile * 16 + wave);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = c0 + u * kWave + lane;
+        if (c < nch) aqn_noise8(a.draw, r, (uint64_t)c, hz[u]);
       }
     }
 #pragma unroll
@@ -426,7 +436,7 @@ __global__ void __launch_bounds__(kProWaves * kWave) k_prologue(PrologueArgs a) 
     bload_bf16x8<VEC>(xsrc, ok ? (uint32_t)(((int64_t)t * a.ldx + kk) * 2) : kOutOfRange, hx[ps]);
     if (AQN) {
       bload_bf16x8<VEC>(gsrc, ok ? (uint32_t)kk * 2 : kOutOfRange, hg[ps]);
-      bload_f32x8<VEC>(zsrc, ok ? (uint32_t)((t * nld + kk) * 4) : kOutOfRange, hz[ps]);
+      if (!a.draw.on) bload_f32x8<VEC>(zsrc, ok ? (uint32_t)((t * nld + kk) * 4) : kOutOfRange, hz[ps]);
     }
   }
 
@@ -448,6 +458,22 @@ __global__ void __launch_bounds__(kProWaves * kWave) k_prologue(PrologueArgs a) 
         const bool ok = pgp[gi] >= 0 && s < nsl && j < r && kk < k;
         af[gi][g][i] = bload16(asrc, ok ? (uint32_t)(((int64_t)j * k + kk) * 2) : kOutOfRange);
       }
+  }
+
+  // drawn noise of this thread's groups, computed while the loads above are in flight
+  if (AQN && a.draw.on) {
+#pragma unroll
+    for (int ps = 0; ps < kPasses; ++ps) {
+      const int g = threadIdx.x + ps * kProWaves * kWave;
+      const int t = g / (ctn * 16), kg = g % (ctn * 16);
+      const int kk = kc0 + kg * 8;
+      if (g < ngroups && t < rows && kk < k && mine(t)) {
+        aqn_noise8(a.draw, draw_index(a.draw, (int64_t)tile * 16 + t), (uint64_t)(kk / 8), hz[ps]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hz[ps][e] = 0.0f;  // as an out-of-range load would give (h of x = 0 stays 0)
+      }
+    }
   }
 
   // statistics: wave w <-> token w of the tile
@@ -2127,6 +2153,8 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
     if (!(aqn->sigma >= 0.0f) || !std::isfinite(aqn->sigma) || !(aqn->eps >= 0.0f) || !std::isfinite(aqn->eps))
       return QN_ERR_VALUE;
     if (aqn->noise && aqn->noise_ld < 0) return QN_ERR_SHAPE;
+    if (aqn->draw && aqn->noise) return QN_ERR_VALUE;  // noise is either read or drawn
+    if (aqn->draw && aqn->draw_rows < 0) return QN_ERR_SHAPE;
     if (aqn->noise && aqn->noise_ld > 0 && aqn->noise_ld < k) return QN_ERR_SHAPE;
   }
   const Workspace wl = workspace_layout(m, k, projs, nproj);
@@ -2175,6 +2203,7 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
       pa.eps = aqn->eps;
       pa.vec_g = (uintptr_t)aqn->gamma % 16 == 0;
       pa.vec_z = aqn->noise && (uintptr_t)aqn->noise % 16 == 0 && pa.noise_ld % 4 == 0;
+      pa.draw = QnDraw{aqn->draw ? 1 : 0, aqn->seed, aqn->subseed, aqn->row_offset, aqn->draw_rows};
     }
     int npg = 0;
     for (int p = 0; p < nproj; ++p) {

@@ -12,15 +12,16 @@ namespace {
 template <int NT, int CPT>
 __global__ void __launch_bounds__(NT) k_aqn_rmsnorm(const uint16_t* __restrict__ x, int64_t d, int64_t ldx,
                                                      const uint16_t* __restrict__ gamma, const float* __restrict__ noise,
-                                                     int64_t noise_ld, float sigma, float eps, uint16_t* __restrict__ h,
-                                                     int64_t ldh, int vec_in, int vec_out, int vec_g, int vec_z) {
+                                                     int64_t noise_ld, QnDraw q, float sigma, float eps,
+                                                     uint16_t* __restrict__ h, int64_t ldh, int vec_in, int vec_out,
+                                                     int vec_g, int vec_z) {
   __shared__ float red[NT / kWave];
   const int64_t row = blockIdx.x;
   RowRegs<CPT> r;
   ScaleRegs<CPT> sr;
   const float* nz = noise ? noise + row * noise_ld : nullptr;
   load_row<NT, CPT>(x + row * ldx, d, vec_in != 0, r);
-  load_scales<NT, CPT>(gamma, nz, d, vec_g != 0, vec_z != 0, sr);
+  load_scales<NT, CPT>(gamma, nz, d, vec_g != 0, vec_z != 0, q, row, sr);
   const float rstd = rms_rstd(row_sumsq<NT, CPT>(r, red), d, eps);
   apply_aqn<NT, CPT>(r, sr, d, rstd, sigma);
   uint16_t* hr = h + row * ldh;
@@ -41,8 +42,24 @@ void launch_norm(int64_t m, hipStream_t s, const uint16_t* x, int64_t d, int64_t
                  int64_t ldh, int vec_in, int vec_out) {
   const int vec_g = (uintptr_t)a->gamma % 16 == 0;
   const int vec_z = a->noise && (uintptr_t)a->noise % 16 == 0 && a->noise_ld % 4 == 0;
+  const QnDraw q{a->draw ? 1 : 0, a->seed, a->subseed, a->row_offset, a->draw_rows};
   hipLaunchKernelGGL((k_aqn_rmsnorm<NT, CPT>), dim3((unsigned)m), dim3(NT), 0, s, x, d, ldx, a->gamma, a->noise,
-                     a->noise_ld, a->sigma, a->eps, h, ldh, vec_in, vec_out, vec_g, vec_z);
+                     a->noise_ld, q, a->sigma, a->eps, h, ldh, vec_in, vec_out, vec_g, vec_z);
+}
+
+// aqn_noise: one thread per 8-column block of a row.
+__global__ void __launch_bounds__(256) k_aqn_noise(QnDraw q, int64_t m, int64_t d, float* __restrict__ eps,
+                                                   int64_t ld) {
+  const int64_t nb = (d + 7) / 8;
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= m * nb) return;
+  const int64_t row = id / nb, c = id % nb;
+  float z[8];
+  aqn_noise8(q, draw_index(q, row), (uint64_t)c, z);
+  float* out = eps + row * ld + c * 8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (c * 8 + e < d) out[e] = z[e];
 }
 
 }  // namespace
@@ -61,6 +78,8 @@ extern "C" qn_status aqn_rmsnorm(const uint16_t* x, int64_t m, int64_t d, int64_
   if (!x || !h || !aqn->gamma) return QN_ERR_NULL;
   if (ldx < d || ldh < d) return QN_ERR_SHAPE;
   if (aqn->noise && (aqn->noise_ld < 0 || (aqn->noise_ld > 0 && aqn->noise_ld < d))) return QN_ERR_SHAPE;
+  if (aqn->draw && aqn->noise) return QN_ERR_VALUE;  // noise is either read or drawn
+  if (aqn->draw && aqn->draw_rows < 0) return QN_ERR_SHAPE;
   if (((uintptr_t)x % 2) || ((uintptr_t)h % 2)) return QN_ERR_ALIGN;
   const int vec_in = ((uintptr_t)x % 16 == 0) && (ldx % 8 == 0);
   const int vec_out = ((uintptr_t)h % 16 == 0) && (ldh % 8 == 0);
@@ -76,5 +95,18 @@ extern "C" qn_status aqn_rmsnorm(const uint16_t* x, int64_t m, int64_t d, int64_
   } else {
     launch_norm<1024, 16>(m, s, x, d, ldx, aqn, h, ldh, vec_in, vec_out);
   }
+  return hipGetLastError() == hipSuccess ? QN_OK : QN_ERR_HIP;
+}
+
+extern "C" qn_status aqn_noise(uint64_t seed, uint64_t subseed, uint64_t row_offset, int64_t draw_rows, int64_t m,
+                               int64_t d, float* eps, int64_t ld, void* stream) {
+  if (m < 0 || d < 0 || draw_rows < 0) return QN_ERR_SHAPE;
+  if (m == 0 || d == 0) return QN_OK;
+  if (!eps) return QN_ERR_NULL;
+  if (ld < d) return QN_ERR_SHAPE;
+  const int64_t blocks = ceil_div(m * ceil_div(d, 8), 256);
+  if (blocks > 0x7fffffff) return QN_ERR_UNSUPPORTED;
+  const QnDraw q{1, seed, subseed, row_offset, draw_rows};
+  hipLaunchKernelGGL(k_aqn_noise, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, q, m, d, eps, ld);
   return hipGetLastError() == hipSuccess ? QN_OK : QN_ERR_HIP;
 }

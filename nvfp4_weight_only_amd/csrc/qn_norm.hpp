@@ -10,6 +10,7 @@
 // waves in order), so every kernel using these routines with the same NT gets the same bits.
 #pragma once
 #include "qn_device.hpp"
+#include "qn_rng.hpp"
 
 namespace qn {
 
@@ -131,7 +132,8 @@ __device__ inline uint16_t aqn_value(float x, float rstd, uint16_t gb, float noi
 }
 
 // The norm scale and noise of this thread's chunks, fetched together with the row so that one memory round trip
-// serves all three. vec_g / vec_z: gamma / the noise row are 16-byte aligned at chunk starts.
+// serves all three. vec_g / vec_z: gamma / the noise row are 16-byte aligned at chunk starts. With a draw (q.on) the
+// noise of row `row` is generated instead of read.
 template <int CPT>
 struct ScaleRegs {
   uint32_t g[CPT][4];  // gamma, bf16 pairs
@@ -140,7 +142,7 @@ struct ScaleRegs {
 
 template <int NT, int CPT>
 __device__ inline void load_scales(const uint16_t* __restrict__ gamma, const float* __restrict__ noise, int64_t d,
-                                   bool vec_g, bool vec_z, ScaleRegs<CPT>& sr) {
+                                   bool vec_g, bool vec_z, const QnDraw& q, int64_t row, ScaleRegs<CPT>& sr) {
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int64_t j0 = ((int64_t)threadIdx.x + (int64_t)i * NT) * 8;
@@ -155,7 +157,12 @@ __device__ inline void load_scales(const uint16_t* __restrict__ gamma, const flo
         sr.g[i][e] = lo | (hi << 16);
       }
     }
-    if (noise && vec_z && j0 + 8 <= d) {
+    if (q.on) {
+      if (j0 < d) aqn_noise8(q, draw_index(q, row), (uint64_t)(j0 / 8), sr.z[i]);
+      else
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sr.z[i][e] = 0.0f;
+    } else if (noise && vec_z && j0 + 8 <= d) {
       typedef float f32x4_t __attribute__((ext_vector_type(4)));
       const f32x4_t a = *reinterpret_cast<const f32x4_t*>(noise + j0);
       const f32x4_t b = *reinterpret_cast<const f32x4_t*>(noise + j0 + 4);

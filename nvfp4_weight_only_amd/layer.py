@@ -52,10 +52,15 @@ class DecoderLayer:
 
     def __init__(self, shape: LayerShape, weights: Dict[str, NVFP4Weight], lora: Dict[str, tuple],
                  gamma1: torch.Tensor, gamma2: torch.Tensor, noise1: Optional[torch.Tensor],
-                 noise2: Optional[torch.Tensor], sigma: float, lam: float = 2.0, eps: float = 1e-6):
+                 noise2: Optional[torch.Tensor], sigma: float, lam: float = 2.0, eps: float = 1e-6,
+                 draws: Optional[tuple] = None, noise_rows: bool = False):
+        """draws: None (the norms read noise1, noise2: one vector for every row, or with noise_rows one row per token),
+        or a pair of NoiseDraw: the two norms draw their noise on the device instead (noise1, noise2 not read)."""
         self.shape, self.w, self.lora = shape, weights, lora
         self.gamma1, self.gamma2, self.noise1, self.noise2 = gamma1, gamma2, noise1, noise2
         self.sigma, self.lam, self.eps = sigma, lam, eps
+        self.draws = draws
+        self.noise_rows = noise_rows
 
     @staticmethod
     def from_bf16(shape: LayerShape, w_bf16: Dict[str, torch.Tensor], lora: Dict[str, tuple], gamma1, gamma2,
@@ -87,8 +92,12 @@ class BoundLayer:
             A, B = L.lora.get(name, (None, None))
             return Projection(L.w[name], y, A, B, L.lam, **kw)
 
-        aqn1 = make_aqn(L.gamma1, L.noise1, L.sigma, L.eps)
-        aqn2 = make_aqn(L.gamma2, L.noise2, L.sigma, L.eps)
+        if L.draws is None:
+            aqn1 = make_aqn(L.gamma1, L.noise1, L.sigma, L.eps, noise_per_row=L.noise_rows)
+            aqn2 = make_aqn(L.gamma2, L.noise2, L.sigma, L.eps, noise_per_row=L.noise_rows)
+        else:
+            aqn1 = make_aqn(L.gamma1, None, L.sigma, L.eps, draw=L.draws[0])
+            aqn2 = make_aqn(L.gamma2, None, L.sigma, L.eps, draw=L.draws[1])
         self.calls = [
             LinearCall(x, [proj("q", self.q), proj("k", self.k),
                            proj("v", self.attn, y_repeat=S.group, head_dim=S.head_dim)], aqn1, EPI_NONE, ws),
