@@ -412,8 +412,12 @@ __global__ void __launch_bounds__(kProWaves * kWave) k_prologue(PrologueArgs a) 
   // Loads, in the order they are needed (each wait then covers its own loads only): the first batch of the
   // statistics row, the inputs of h, the LoRA-down A fragments.
   const rsrc_t xsrc = make_rsrc(a.x + (int64_t)tile * 16 * a.ldx, ((int64_t)(rows - 1) * a.ldx + k) * 2);
-  const bool own_stats = AQN && !a.rstd_in && wave < rows && mine(wave);  // wave w <-> token w of the tile
-  const uint32_t stats_row = (uint32_t)((int64_t)wave * a.ldx * 2);
+  // statistics: wave w <-> token w ^ 8 of the tile. The h groups of a token lie in the waves from about its own
+  // index on (one wave per token at 4 k-tiles per chunk), so the waves that sum a workgroup's rows are not the ones
+  // that draw its noise (with a seeded draw) and the two run side by side.
+  const int st = wave ^ 8;
+  const bool own_stats = AQN && !a.rstd_in && st < rows && mine(st);
+  const uint32_t stats_row = (uint32_t)((int64_t)st * a.ldx * 2);
   uint32_t sq[8][4];
   if (AQN) row_sumsq_load<NT, VEC>(xsrc, own_stats ? stats_row : kOutOfRange, own_stats ? k : 0, sq);
 
@@ -476,13 +480,13 @@ __global__ void __launch_bounds__(kProWaves * kWave) k_prologue(PrologueArgs a) 
     }
   }
 
-  // statistics: wave w <-> token w of the tile
+  // statistics of token st = wave ^ 8 (every token of the tile has exactly one wave)
   if (AQN) {
     float rstd = 0.f;
-    if (wave < rows && mine(wave))
-      rstd = a.rstd_in ? gload(a.rstd_in + tile * 16 + wave)
+    if (st < rows && mine(st))
+      rstd = a.rstd_in ? gload(a.rstd_in + tile * 16 + st)
                        : rms_rstd(row_sumsq_buf<NT, VEC>(xsrc, stats_row, k, sq), k, a.eps);
-    if (lane == 0) s_rstd[wave] = rstd;
+    if (lane == 0) s_rstd[st] = rstd;
   }
   __syncthreads();
 
