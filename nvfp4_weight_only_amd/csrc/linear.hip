@@ -2091,12 +2091,20 @@ void pick_shape(int tmt, int64_t mt, bool silu, int64_t nrg, int64_t KT, int* R_
   const int64_t want_waves = 2048;
   // fewer row groups than workgroups worth having: drop towards one row group (one gate/up pair) per workgroup
   while (R > rmin && ceil_div(nrg, R) * 16 < want_waves) R /= 2;
-  const int64_t nwg = ceil_div(nrg, R);
   // register budget: wider tiles leave room for fewer waves per workgroup
-  const int wmax = tmt >= 8 ? 4 : (tmt >= 4 ? (R == 1 ? 8 : 4) : (tmt == 2 || R == 4 ? 8 : 16));
+  int wmax = tmt >= 8 ? 4 : (tmt >= 4 ? (R == 1 ? 8 : 4) : (tmt == 2 || R == 4 ? 8 : 16));
+  int Rf = R;
+  if (tmt == 1 && !silu) {
+    // measured at 1-16 tokens on the 7B/8B shapes (q|k|v 4,608 x 3,584; o 3,584 x 3,584; 4,096 x 4,096): one row
+    // group per workgroup while the row groups fit one per CU, two beyond; at most eight waves (sixteen leave each
+    // wave 1-2 k-tiles and cost 0.5-1.9 us more per call)
+    Rf = nrg > 256 ? 2 : 1;
+    wmax = 8;
+  }
+  const int64_t nwgf = ceil_div(nrg, Rf);
   int W = 4;
-  while (W < wmax && nwg * W < want_waves && KT >= 2 * W) W *= 2;
-  *R_out = R;
+  while (W < wmax && nwgf * W < want_waves && KT >= 2 * W) W *= 2;
+  *R_out = Rf;
   *W_out = W;
 }
 
