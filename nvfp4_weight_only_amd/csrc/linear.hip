@@ -1488,8 +1488,8 @@ inline GemvCut gemv_cut(int64_t nu, int64_t KT, int tmt, int nr) {
 
 // Decode kernel use: up to 32 tokens and a cut that fits. By default it is taken where it measured faster than the
 // general kernel: with no split k, at least four row units per workgroup (the wide feed-forward projections); with
-// a split k, only where the whole k does not fit in LDS (long rows, such as the feed-forward down projection: the
-// general kernel would read the activations from L2 once per wave there). For short rows the split-k partial sums
+// a split k, only at up to 16 tokens and where the whole k does not fit in LDS (long rows, such as the feed-forward
+// down projection: the general kernel would read the activations from L2 once per wave there). For short rows the split-k partial sums
 // cost more memory round trips than the better balance gains. Tuning overrides (read at each call): QN_GEMV_OFF=1
 // always takes the general kernel, QN_GEMV_NK=<k-chunks> takes the decode kernel with that cut whenever it fits,
 // QN_GEMV_DEPTH=<2|3> sets the weight tiles in flight per wave.
@@ -1501,6 +1501,10 @@ inline bool gemv_on(int64_t m) {
 inline bool gemv_pick(const GemvCut& cut, int64_t nu, int64_t KT, int tmt, int nr) {
   if (cut.nbr <= 0) return false;
   if (std::getenv("QN_GEMV_NK")) return true;
+  // two token tiles halve the k-tiles a workgroup holds in LDS, so every 7B/32B row length takes the split-k form,
+  // which measured slower than the general kernel at 17-32 tokens (7B q|k|v 31.8 vs 17.7 us, o 18.5 vs 13.1 us,
+  // down 32.0 vs 31.6 us; 32B q|k|v 21.2 vs 17.8 us)
+  if (cut.nk > 1 && tmt >= 2) return false;
   if (cut.nk > 1) return KT > gemv_act_cap(tmt, nr);
   return ceil_div(nu, cut.nbr) >= 4;
 }
