@@ -93,6 +93,22 @@ def test_validation_errors(qn):
     p.lambda_ = float("inf")
     arr[0] = p
     assert call() == qn.QN_ERR_VALUE
+    p.lambda_ = 2.0
+    arr[0] = p
+    # noise drawn on the device: not together with a noise buffer, draws per row >= 0 (norm and linear)
+    a = qn.QnAqn(gamma=256, noise=256, noise_ld=0, sigma=0.01, eps=1e-6, draw=1, seed=1, subseed=0, row_offset=0,
+                 draw_rows=1)
+    assert L.aqn_rmsnorm(fake, 2, 32, 32, ctypes.byref(a), fake, 32, None) == qn.QN_ERR_VALUE
+    assert call(aqn=ctypes.byref(a)) == qn.QN_ERR_VALUE
+    a.noise, a.draw_rows = None, -1
+    assert L.aqn_rmsnorm(fake, 2, 32, 32, ctypes.byref(a), fake, 32, None) == qn.QN_ERR_SHAPE
+    assert call(aqn=ctypes.byref(a)) == qn.QN_ERR_SHAPE
+    # standalone noise: shapes, row stride, draws per row, NULL output; empty is a no-op
+    assert L.aqn_noise(1, 0, 0, 1, -1, 32, fake, 32, None) == qn.QN_ERR_SHAPE
+    assert L.aqn_noise(1, 0, 0, 1, 2, 32, fake, 16, None) == qn.QN_ERR_SHAPE
+    assert L.aqn_noise(1, 0, 0, -1, 2, 32, fake, 32, None) == qn.QN_ERR_SHAPE
+    assert L.aqn_noise(1, 0, 0, 1, 2, 32, None, 32, None) == qn.QN_ERR_NULL
+    assert L.aqn_noise(1, 0, 0, 1, 0, 32, None, 32, None) == qn.QN_OK
     # advantage
     assert L.grpo_group_advantage(fake, 8, 8, -1.0, fake, None) == qn.QN_ERR_VALUE
     assert L.grpo_group_advantage(None, 8, 8, 1e-6, fake, None) == qn.QN_ERR_NULL
