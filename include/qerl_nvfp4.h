@@ -155,7 +155,8 @@ qn_status aqn_rmsnorm(const uint16_t* x, int64_t m, int64_t d, int64_t ldx, cons
  * under key (seed, subseed); its eight 32-bit words w0..w7 (w2q, w2q+1 = low, high half of output word q) give
  * columns 8c+2p, 8c+2p+1 by the Box-Muller transform: u(w) = ((w >> 9) + 1/2) 2^-23, rho = sqrt(-2 ln u(w2p)),
  * eps = rho cos(2 pi u(w2p+1)), rho sin(2 pi u(w2p+1)), in f32 (a few ulp from the exactly rounded values).
- * eps: [m][ld] f32 (device), ld >= d. Errors: QN_ERR_SHAPE (m, d < 0, ld < d, draw_rows < 0), QN_ERR_NULL. */
+ * eps: [m][ld] f32 (device, 4-byte aligned), ld >= d. Errors: QN_ERR_SHAPE (m, d < 0, ld < d, draw_rows < 0),
+ * QN_ERR_NULL, QN_ERR_ALIGN; nothing is launched on an error. */
 qn_status aqn_noise(uint64_t seed, uint64_t subseed, uint64_t row_offset, int64_t draw_rows, int64_t m, int64_t d,
                     float* eps, int64_t ld, void* stream);
 

@@ -104,6 +104,7 @@ extern "C" qn_status aqn_noise(uint64_t seed, uint64_t subseed, uint64_t row_off
   if (m == 0 || d == 0) return QN_OK;
   if (!eps) return QN_ERR_NULL;
   if (ld < d) return QN_ERR_SHAPE;
+  if ((uintptr_t)eps % 4) return QN_ERR_ALIGN;
   const int64_t blocks = ceil_div(m * ceil_div(d, 8), 256);
   if (blocks > 0x7fffffff) return QN_ERR_UNSUPPORTED;
   const QnDraw q{1, seed, subseed, row_offset, draw_rows};

@@ -108,6 +108,7 @@ def test_validation_errors(qn):
     assert L.aqn_noise(1, 0, 0, 1, 2, 32, fake, 16, None) == qn.QN_ERR_SHAPE
     assert L.aqn_noise(1, 0, 0, -1, 2, 32, fake, 32, None) == qn.QN_ERR_SHAPE
     assert L.aqn_noise(1, 0, 0, 1, 2, 32, None, 32, None) == qn.QN_ERR_NULL
+    assert L.aqn_noise(1, 0, 0, 1, 2, 32, P(258), 32, None) == qn.QN_ERR_ALIGN
     assert L.aqn_noise(1, 0, 0, 1, 0, 32, None, 32, None) == qn.QN_OK
     # advantage
     assert L.grpo_group_advantage(fake, 8, 8, -1.0, fake, None) == qn.QN_ERR_VALUE
