@@ -288,7 +288,7 @@ def main():
                     help="also run one plain 256 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported", file=sys.stderr)
+        print(f"bench.py: this benchmark runs on one GPU; --gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
 
     if args.workload == "prefill":

@@ -33,7 +33,7 @@ typedef enum {
   QN_ERR_ALIGN = 3,       /* a pointer is not aligned as documented */
   QN_ERR_VALUE = 4,       /* a scalar is out of range (negative or non-finite sigma/eps/lambda, bad enum) */
   QN_ERR_WORKSPACE = 5,   /* workspace is NULL or smaller than nvfp4_lora_linear_workspace() */
-  QN_ERR_UNSUPPORTED = 6, /* a valid request this build does not implement (e.g. LoRA rank > 64, > 4 projections) */
+  QN_ERR_UNSUPPORTED = 6, /* a valid request this library does not implement (e.g. LoRA rank > 64, > 4 projections) */
   QN_ERR_HIP = 7          /* a HIP launch failed */
 } qn_status;
 

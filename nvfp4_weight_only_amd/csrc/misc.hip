@@ -57,7 +57,7 @@ extern "C" const char* qn_status_string(qn_status s) {
     case QN_ERR_ALIGN: return "pointer not aligned as required";
     case QN_ERR_VALUE: return "scalar argument out of range";
     case QN_ERR_WORKSPACE: return "workspace missing or too small";
-    case QN_ERR_UNSUPPORTED: return "request not supported by this build";
+    case QN_ERR_UNSUPPORTED: return "request not supported by this library";
     case QN_ERR_HIP: return "HIP launch failed";
   }
   return "unknown status";
