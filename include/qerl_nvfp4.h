@@ -174,6 +174,43 @@ qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx
                             const qn_proj* projs, int32_t nproj, int32_t epilogue, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/* Kernel choice for nvfp4_lora_linear_opts. A call runs one of three streaming kernels; the library picks one from
+ * the token count and the shapes (QN_KERNEL_AUTO, what nvfp4_lora_linear does). Naming another one runs the same
+ * computation, to the same accuracy bound, on that kernel: for checks of each kernel on the same inputs and for
+ * timing them side by side. */
+typedef enum {
+  QN_KERNEL_AUTO = 0,    /* the library's choice */
+  QN_KERNEL_GENERAL = 1, /* the general streaming kernel, one launch per 128 tokens; any m */
+  QN_KERNEL_DECODE = 2,  /* the decode streaming kernel (activations held in LDS, optional split k); m <= 32 and a
+                            split of the rows and k that fits its LDS, else QN_ERR_UNSUPPORTED */
+  QN_KERNEL_MANY = 3     /* the many-token MFMA kernel; m > 128, else QN_ERR_UNSUPPORTED */
+} qn_kernel;
+
+/* Explicit options of one nvfp4_lora_linear_opts call. Zero-initialised, it asks for the library's defaults. These
+ * are the only inputs besides the arguments that change which kernel a call runs: the library reads no environment
+ * variables and keeps no settings between calls. */
+typedef struct {
+  int32_t kernel;         /* qn_kernel */
+  int32_t decode_kchunks; /* QN_KERNEL_DECODE: k-chunks of the split-k cut, 1..64 (0 = the library's cut) */
+  int32_t decode_depth;   /* QN_KERNEL_DECODE: weight tiles in flight per wave: 0 (the default, 3), 2 or 3 */
+  int32_t general_rows;   /* QN_KERNEL_GENERAL: row groups per workgroup and waves per workgroup, both 0 (the */
+  int32_t general_waves;  /* library's shape) or both > 0 naming a built pair (else QN_ERR_UNSUPPORTED) */
+  int32_t elem_store;     /* 0 or 1; many-token kernel: 1 stores outputs element by element instead of in 16-byte
+                             pieces through LDS (same values) */
+} qn_linear_opts;
+
+/* Workspace bytes of nvfp4_lora_linear_opts with these options (host, pure); 0 if the options are invalid or name
+ * a kernel that cannot serve the call. NULL opts = nvfp4_lora_linear_workspace. */
+size_t nvfp4_lora_linear_workspace_opts(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj,
+                                        const qn_linear_opts* opts);
+
+/* nvfp4_lora_linear with explicit options (NULL = defaults, identical to nvfp4_lora_linear). Errors besides those of
+ * nvfp4_lora_linear: QN_ERR_VALUE for an option out of range, QN_ERR_UNSUPPORTED when the named kernel or shape cannot
+ * serve the call; in both cases nothing is launched. */
+qn_status nvfp4_lora_linear_opts(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const qn_aqn* aqn,
+                                 const qn_proj* projs, int32_t nproj, int32_t epilogue, const qn_linear_opts* opts,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* Exponential AQN noise schedule [review §5.2]: sigma_0 = 0, sigma_k = start * (end/start)^((k-1)/8), k = 1..9
  * (stages beyond 9 continue the same geometric decay). Host, pure, fp64. */
 double aqn_sigma(int32_t stage, double sigma_start, double sigma_end);

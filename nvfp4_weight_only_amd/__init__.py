@@ -21,10 +21,12 @@ BF16, F32 = 0, 1
 EPI_NONE, EPI_SILU_MUL = 0, 1
 RUN_PROLOGUE_ONLY, RUN_MAIN_ONLY = 0x100, 0x200
 
+KERNEL_AUTO, KERNEL_GENERAL, KERNEL_DECODE, KERNEL_MANY = range(4)
+
 EXPORTS = ["nvfp4_quantize", "nvfp4_tiled_codes_bytes", "nvfp4_tiled_scales_bytes", "nvfp4_dequantize", "aqn_rmsnorm",
            "aqn_noise",
-           "nvfp4_lora_linear_workspace", "nvfp4_lora_linear", "aqn_sigma", "grpo_group_advantage",
-           "qn_status_string"]
+           "nvfp4_lora_linear_workspace", "nvfp4_lora_linear", "nvfp4_lora_linear_workspace_opts",
+           "nvfp4_lora_linear_opts", "aqn_sigma", "grpo_group_advantage", "qn_status_string"]
 
 
 class QnError(RuntimeError):
@@ -48,6 +50,26 @@ class QnProj(ctypes.Structure):
                 ("y_repeat", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
 
 
+class QnLinearOpts(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("decode_kchunks", ctypes.c_int32), ("decode_depth", ctypes.c_int32),
+                ("general_rows", ctypes.c_int32), ("general_waves", ctypes.c_int32), ("elem_store", ctypes.c_int32)]
+
+
+@dataclass
+class LinearOpts:
+    """Explicit kernel choice of one linear call (qn_linear_opts); the defaults are the library's own choice."""
+    kernel: int = KERNEL_AUTO
+    decode_kchunks: int = 0
+    decode_depth: int = 0
+    general_rows: int = 0
+    general_waves: int = 0
+    elem_store: int = 0
+
+    def to_c(self) -> QnLinearOpts:
+        return QnLinearOpts(self.kernel, self.decode_kchunks, self.decode_depth, self.general_rows,
+                            self.general_waves, self.elem_store)
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() (hipcc for gfx950) first")
@@ -64,6 +86,10 @@ def _load():
         "nvfp4_lora_linear_workspace": ([i64, i64, ctypes.POINTER(QnProj), i32], sz),
         "nvfp4_lora_linear": ([P, i64, i64, i64, ctypes.POINTER(QnAqn), ctypes.POINTER(QnProj), i32, i32, P, sz, P],
                               i32),
+        "nvfp4_lora_linear_workspace_opts": ([i64, i64, ctypes.POINTER(QnProj), i32, ctypes.POINTER(QnLinearOpts)],
+                                             sz),
+        "nvfp4_lora_linear_opts": ([P, i64, i64, i64, ctypes.POINTER(QnAqn), ctypes.POINTER(QnProj), i32, i32,
+                                    ctypes.POINTER(QnLinearOpts), P, sz, P], i32),
         "aqn_sigma": ([i32, f64, f64], f64),
         "grpo_group_advantage": ([P, i32, i32, f32, P, P], i32),
         "qn_status_string": ([i32], ctypes.c_char_p),
@@ -134,6 +160,8 @@ def quantize(w: torch.Tensor, layout: int = LAYOUT_TILED, scale_mode: int = 0, o
         out = alloc_weight(n, k, layout, w.device)
     _check(lib.nvfp4_quantize(_ptr(w), n, k, w.stride(0), scale_mode, out.layout, _ptr(out.codes), _ptr(out.scales),
                               _ptr(out.tensor_scale), _ptr(flags), _stream(stream)), "nvfp4_quantize")
+    for t in (out.codes, out.scales, out.tensor_scale):
+        _keep_for(t, stream)
     return out
 
 
@@ -141,6 +169,7 @@ def dequantize(wq: NVFP4Weight, stream=None) -> torch.Tensor:
     out = torch.empty(wq.n, wq.k, dtype=torch.float32, device=wq.codes.device)
     _check(lib.nvfp4_dequantize(_ptr(wq.codes), _ptr(wq.scales), _ptr(wq.tensor_scale), wq.n, wq.k, wq.layout,
                                 _ptr(out), wq.k, _stream(stream)), "nvfp4_dequantize")
+    _keep_for(out, stream)
     return out
 
 
@@ -189,6 +218,7 @@ def aqn_noise(draw: NoiseDraw, m: int, d: int, device, out: Optional[torch.Tenso
     eps = out if out is not None else torch.empty(m, d, dtype=torch.float32, device=device)
     _check(lib.aqn_noise(draw.seed, draw.subseed, draw.row_offset, draw.draw_rows, m, d, _ptr(eps), eps.stride(0),
                          _stream(stream)), "aqn_noise")
+    _keep_for(eps, stream)
     return eps
 
 
@@ -200,6 +230,7 @@ def aqn_rmsnorm(x: torch.Tensor, gamma: torch.Tensor, noise: Optional[torch.Tens
     a = make_aqn(gamma, noise, sigma, eps, noise_per_row, draw)
     _check(lib.aqn_rmsnorm(_ptr(x), m, d, x.stride(0), ctypes.byref(a.c), _ptr(h), h.stride(0), _stream(stream)),
            "aqn_rmsnorm")
+    _keep_for(h, stream)
     return h
 
 
@@ -233,6 +264,13 @@ class Projection:
         return p
 
 
+def _keep_for(t: Optional[torch.Tensor], stream) -> None:
+    """A tensor that kernels on `stream` use while the caller's current stream runs ahead: the caching allocator must
+    not hand its memory out again before that stream is done with it."""
+    if t is not None and stream is not None and stream != torch.cuda.current_stream(t.device):
+        t.record_stream(stream)
+
+
 class Workspace:
     """Grow-only device workspace for nvfp4_lora_linear (allocated by torch, outside the timed calls)."""
 
@@ -242,41 +280,48 @@ class Workspace:
 
     def get(self, nbytes: int) -> torch.Tensor:
         if self.buf.numel() < nbytes:
+            # the old buffer's memory is recycled only after every stream it was used on reaches this point
+            # (LinearCall records those streams on it)
             self.buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
         return self.buf
 
 
-def linear_workspace_bytes(m: int, k: int, projs: Sequence[Projection]) -> int:
+def linear_workspace_bytes(m: int, k: int, projs: Sequence[Projection], opts: Optional[LinearOpts] = None) -> int:
     arr = (QnProj * len(projs))(*[p.to_c() for p in projs])
-    return int(lib.nvfp4_lora_linear_workspace(m, k, arr, len(projs)))
+    oc = opts.to_c() if opts is not None else None
+    return int(lib.nvfp4_lora_linear_workspace_opts(m, k, arr, len(projs), ctypes.byref(oc) if oc else None))
 
 
 class LinearCall:
-    """A prepared nvfp4_lora_linear call: the C structs are built once, so repeated launches only cross ctypes."""
+    """A prepared nvfp4_lora_linear call: the C structs are built once, so repeated launches only cross ctypes.
+    opts: an explicit kernel choice (LinearOpts), None for the library's own."""
 
     def __init__(self, x: torch.Tensor, projs: Sequence[Projection], aqn: Optional[AqnParams] = None,
-                 epilogue: int = EPI_NONE, workspace: Optional[Workspace] = None):
+                 epilogue: int = EPI_NONE, workspace: Optional[Workspace] = None, opts: Optional[LinearOpts] = None):
         self.x = x
         self.m, self.k = x.shape
         self.projs = list(projs)
         self.arr = (QnProj * len(projs))(*[p.to_c() for p in projs])
         self.aqn = aqn
         self.epilogue = epilogue
-        need = int(lib.nvfp4_lora_linear_workspace(self.m, self.k, self.arr, len(projs)))
+        self.opts = opts.to_c() if opts is not None else None
+        self.opts_ref = ctypes.byref(self.opts) if self.opts is not None else None
+        need = int(lib.nvfp4_lora_linear_workspace_opts(self.m, self.k, self.arr, len(projs), self.opts_ref))
         self.ws = (workspace or Workspace(x.device)).get(need)
         self.ws_bytes = self.ws.numel()
 
     def __call__(self, stream=None, phases: int = 0):
-        _check(lib.nvfp4_lora_linear(_ptr(self.x), self.m, self.k, self.x.stride(0),
-                                     ctypes.byref(self.aqn.c) if self.aqn is not None else None, self.arr,
-                                     len(self.projs), self.epilogue | phases, _ptr(self.ws), self.ws_bytes,
-                                     _stream(stream)),
+        _check(lib.nvfp4_lora_linear_opts(_ptr(self.x), self.m, self.k, self.x.stride(0),
+                                          ctypes.byref(self.aqn.c) if self.aqn is not None else None, self.arr,
+                                          len(self.projs), self.epilogue | phases, self.opts_ref, _ptr(self.ws),
+                                          self.ws_bytes, _stream(stream)),
                "nvfp4_lora_linear")
+        _keep_for(self.ws, stream)
 
 
 def lora_linear(x: torch.Tensor, projs: Sequence[Projection], aqn: Optional[AqnParams] = None, epilogue: int = EPI_NONE,
-                workspace: Optional[Workspace] = None, stream=None):
-    LinearCall(x, projs, aqn, epilogue, workspace)(stream)
+                workspace: Optional[Workspace] = None, stream=None, opts: Optional[LinearOpts] = None):
+    LinearCall(x, projs, aqn, epilogue, workspace, opts)(stream)
 
 
 def group_advantage(rewards: torch.Tensor, eps: float = 1e-6, stream=None) -> torch.Tensor:
@@ -284,4 +329,5 @@ def group_advantage(rewards: torch.Tensor, eps: float = 1e-6, stream=None) -> to
     adv = torch.empty_like(rewards)
     _check(lib.grpo_group_advantage(_ptr(rewards), groups, g, eps, _ptr(adv), _stream(stream)),
            "grpo_group_advantage")
+    _keep_for(adv, stream)
     return adv

@@ -90,9 +90,10 @@ inline int64_t lora_chunks(int64_t k) {
   return ceil_div(KT, chunk_tiles(KT));
 }
 
-size_t gemv_pbuf_bytes(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj);
+struct Opts;
+size_t gemv_pbuf_bytes(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj, const Opts& o);
 
-Workspace workspace_layout(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj) {
+Workspace workspace_layout(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj, const Opts& o) {
   const int64_t KT = ceil_div(k, kKTile), kp = KT * kKTile;
   const int64_t mp = ceil_div(m, 16) * 16;
   Workspace w;
@@ -103,7 +104,7 @@ Workspace workspace_layout(int64_t m, int64_t k, const qn_proj* projs, int32_t n
   w.tok_p = off;  off = align256(off + (size_t)mp * 4);
   w.t_part = off; off = align256(off + (size_t)nproj * (mp / 16) * kRankChunks * lora_chunks(k) * kWave * 32);
   w.t_fin = off;  off = align256(off + (m > kMaxTokensPerLaunch ? (size_t)nproj * (mp / 16) * kRankChunks * 2 * kWave * 16 : 0));
-  w.pbuf = off;   off = align256(off + gemv_pbuf_bytes(m, k, projs, nproj));
+  w.pbuf = off;   off = align256(off + gemv_pbuf_bytes(m, k, projs, nproj, o));
   w.cnt = off;    off = align256(off + 256 * 4);
   w.total = off;
   return w;
@@ -1459,12 +1460,11 @@ struct GemvCut {
 // k-tiles of activations a workgroup of the decode kernel can hold in LDS
 inline int64_t gemv_act_cap(int tmt, int nr) { return (kGLds - gemv_lred_bytes(nr, tmt)) / ((int64_t)tmt * kGTileAct); }
 
-inline GemvCut gemv_cut(int64_t nu, int64_t KT, int tmt, int nr) {
+// nk_only > 0: only that many k-chunks (a cut asked for by the caller's options).
+inline GemvCut gemv_cut(int64_t nu, int64_t KT, int tmt, int nr, int nk_only) {
   const int64_t act_cap = gemv_act_cap(tmt, nr);
   GemvCut best{0, 0};
   double best_t = 1e30;
-  int nk_only = 0;  // tuning override: QN_GEMV_NK=<k-chunks>
-  if (const char* ov = std::getenv("QN_GEMV_NK")) nk_only = std::atoi(ov);
   for (int64_t nk = 1; nk <= KT && nk <= 64; ++nk) {
     if (nk_only > 0 && nk != nk_only) continue;
     const int64_t tmax = ceil_div(KT, nk);
@@ -1489,18 +1489,10 @@ inline GemvCut gemv_cut(int64_t nu, int64_t KT, int tmt, int nr) {
 // Decode kernel use: up to 32 tokens and a cut that fits. By default it is taken where it measured faster than the
 // general kernel: with no split k, at least four row units per workgroup (the wide feed-forward projections); with
 // a split k, only at up to 16 tokens and where the whole k does not fit in LDS (long rows, such as the feed-forward
-// down projection: the general kernel would read the activations from L2 once per wave there). For short rows the split-k partial sums
-// cost more memory round trips than the better balance gains. Tuning overrides (read at each call): QN_GEMV_OFF=1
-// always takes the general kernel, QN_GEMV_NK=<k-chunks> takes the decode kernel with that cut whenever it fits,
-// QN_GEMV_DEPTH=<2|3> sets the weight tiles in flight per wave.
-inline bool gemv_on(int64_t m) {
-  if (m < 1 || m > 32) return false;
-  const char* off = std::getenv("QN_GEMV_OFF");
-  return !(off && off[0] == '1');
-}
-inline bool gemv_pick(const GemvCut& cut, int64_t nu, int64_t KT, int tmt, int nr) {
+// down projection: the general kernel would read the activations from L2 once per wave there). For short rows the
+// split-k partial sums cost more memory round trips than the better balance gains.
+inline bool gemv_default(const GemvCut& cut, int64_t nu, int64_t KT, int tmt, int nr) {
   if (cut.nbr <= 0) return false;
-  if (std::getenv("QN_GEMV_NK")) return true;
   // two token tiles halve the k-tiles a workgroup holds in LDS, so every 7B/32B row length takes the split-k form,
   // which measured slower than the general kernel at 17-32 tokens (7B q|k|v 31.8 vs 17.7 us, o 18.5 vs 13.1 us,
   // down 32.0 vs 31.6 us; 32B q|k|v 21.2 vs 17.8 us)
@@ -1509,21 +1501,76 @@ inline bool gemv_pick(const GemvCut& cut, int64_t nu, int64_t KT, int tmt, int n
   return ceil_div(nu, cut.nbr) >= 4;
 }
 
-size_t gemv_pbuf_bytes(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj) {
-  if (!gemv_on(m) || !projs || nproj < 1) return 0;
+// Options of one call (qn_linear_opts, zero = defaults).
+struct Opts {
+  int kernel = QN_KERNEL_AUTO, nk = 0, depth = 0, rows = 0, waves = 0, elem = 0;
+};
+
+inline bool opts_valid(const Opts& o) {
+  return o.kernel >= QN_KERNEL_AUTO && o.kernel <= QN_KERNEL_MANY && o.nk >= 0 && o.nk <= 64 &&
+         (o.depth == 0 || o.depth == 2 || o.depth == 3) && o.rows >= 0 && o.waves >= 0 && (o.rows > 0) == (o.waves > 0) &&
+         (o.elem == 0 || o.elem == 1);
+}
+
+inline Opts opts_of(const qn_linear_opts* p) {
+  Opts o;
+  if (p) {
+    o.kernel = p->kernel;
+    o.nk = p->decode_kchunks;
+    o.depth = p->decode_depth;
+    o.rows = p->general_rows;
+    o.waves = p->general_waves;
+    o.elem = p->elem_store;
+  }
+  return o;
+}
+
+// Which streaming kernel serves a call: the many-token MFMA kernel, the decode kernel (with its cut) or the general
+// kernel. Decided on the host before anything is launched; QN_ERR_UNSUPPORTED if the options name a kernel that
+// cannot serve the call.
+enum MainPath { kPathGeneral = 0, kPathDecode = 1, kPathMany = 2 };
+struct Plan {
+  MainPath path = kPathGeneral;
+  GemvCut cut{0, 0};
+  int depth = 3;
+};
+
+inline qn_status plan_main(int64_t m, int64_t KT, int64_t nu, bool silu, const Opts& o, Plan* out) {
+  Plan pl;
+  const int nr = silu ? 2 : 1;
+  if (o.kernel == QN_KERNEL_MANY || (o.kernel == QN_KERNEL_AUTO && m > kMaxTokensPerLaunch)) {
+    if (m <= kMaxTokensPerLaunch) return QN_ERR_UNSUPPORTED;
+    pl.path = kPathMany;
+  } else if (o.kernel == QN_KERNEL_DECODE || (o.kernel == QN_KERNEL_AUTO && m >= 1 && m <= 32)) {
+    bool take = false;
+    if (m >= 1 && m <= 32) {
+      const int tmt = (int)ceil_div(m, 16);
+      pl.cut = gemv_cut(nu, KT, tmt, nr, o.kernel == QN_KERNEL_DECODE ? o.nk : 0);
+      take = o.kernel == QN_KERNEL_DECODE ? pl.cut.nbr > 0 : gemv_default(pl.cut, nu, KT, tmt, nr);
+    }
+    if (o.kernel == QN_KERNEL_DECODE && !take) return QN_ERR_UNSUPPORTED;
+    pl.path = take ? kPathDecode : kPathGeneral;
+    pl.depth = o.depth ? o.depth : 3;
+  }
+  *out = pl;
+  return QN_OK;
+}
+
+// Split-k part sums of the decode kernel (none without a split).
+size_t gemv_pbuf_bytes(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj, const Opts& o) {
+  if (!projs || nproj < 1 || m < 1 || m > 32) return 0;
   const int tmt = (int)ceil_div(m, 16);
   const int64_t KT = ceil_div(k, kKTile);
   int64_t nu_flat = 0;
   for (int p = 0; p < nproj; ++p) nu_flat += ceil_div(projs[p].n, 16);
+  // the workspace query does not know the epilogue: size for both readings of a two-projection call
   size_t bytes = 0;
-  const GemvCut cf = gemv_cut(nu_flat, KT, tmt, 1);
-  if (cf.nk > 1) bytes = (size_t)cf.nbr * (cf.nk + 1) * gemv_block_floats(1, tmt) * 4;
-  if (nproj == 2) {
-    const GemvCut cp = gemv_cut(ceil_div(projs[0].n, 16), KT, tmt, 2);
-    if (cp.nk > 1) {
-      const size_t bp = (size_t)cp.nbr * (cp.nk + 1) * gemv_block_floats(2, tmt) * 4;
-      bytes = bp > bytes ? bp : bytes;
-    }
+  for (int silu = 0; silu <= (nproj == 2 ? 1 : 0); ++silu) {
+    Plan pl;
+    if (plan_main(m, KT, silu ? ceil_div(projs[0].n, 16) : nu_flat, silu, o, &pl) != QN_OK) continue;
+    if (pl.path != kPathDecode || pl.cut.nk <= 1) continue;
+    const size_t b = (size_t)pl.cut.nbr * (pl.cut.nk + 1) * gemv_block_floats(silu ? 2 : 1, tmt) * 4;
+    bytes = b > bytes ? b : bytes;
   }
   return bytes;
 }
@@ -2062,11 +2109,12 @@ void launch_linear(const LinearArgs& a, int64_t nwg, hipStream_t s) {
   hipLaunchKernelGGL((k_linear<TMT, R, W, SILU>), dim3((unsigned)nwg), dim3(W * kWave), 0, s, a);
 }
 
-// The instantiated (TMT, R, W, SILU) combinations; returns false if the combination is not built.
-bool dispatch_linear(int tmt, int R, int W, bool silu, const LinearArgs& a, int64_t nwg, hipStream_t s) {
+// The instantiated (TMT, R, W, SILU) combinations; returns false if the combination is not built. With a null
+// `a` it only answers whether the combination is built.
+bool dispatch_linear(int tmt, int R, int W, bool silu, const LinearArgs* a, int64_t nwg, hipStream_t s) {
 #define QN_CASE(T_, R_, W_, S_)                         \
   if (tmt == T_ && R == R_ && W == W_ && silu == S_) { \
-    launch_linear<T_, R_, W_, S_>(a, nwg, s);          \
+    if (a) launch_linear<T_, R_, W_, S_>(*a, nwg, s);  \
     return true;                                       \
   }
   QN_CASE(1, 1, 4, false) QN_CASE(1, 1, 8, false) QN_CASE(1, 1, 16, false)
@@ -2119,20 +2167,25 @@ void pick_shape(int tmt, int64_t mt, bool silu, int64_t nrg, int64_t KT, int* R_
 
 inline bool aligned(const void* p, size_t al) { return ((uintptr_t)p % al) == 0; }
 
-}  // namespace
-}  // namespace qn
-
-using namespace qn;
-
-extern "C" size_t nvfp4_lora_linear_workspace(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj) {
-  if (m <= 0 || k <= 0 || nproj <= 0) return 0;
-  return workspace_layout(m, k, projs, nproj).total;
+// Launch shape of the general kernel for the launch of `mt` tokens starting at token t0 (tmt token tiles, rounded
+// up to a built tile count); false if the options name a shape that is not built.
+bool general_shape(int64_t mt, bool silu, int64_t nrg, int64_t KT, const Opts& o, int* tmt_out, int* R, int* W) {
+  int tmt = (int)ceil_div(mt, 16);
+  tmt = tmt <= 2 ? tmt : (tmt <= 4 ? 4 : 8);
+  pick_shape(tmt, mt, silu, nrg, KT, R, W);
+  if (o.rows > 0) {
+    *R = o.rows;
+    *W = o.waves;
+  }
+  *tmt_out = tmt;
+  return dispatch_linear(tmt, *R, *W, silu, nullptr, 0, nullptr);
 }
 
-extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const qn_aqn* aqn,
-                                       const qn_proj* projs, int32_t nproj, int32_t epilogue, void* workspace,
-                                       size_t workspace_bytes, void* stream) {
-  // ---- host-side validation (nothing is launched on failure)
+// All host-side validation of a call (nothing is launched on failure); on success the plan of its main kernel.
+qn_status validate_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const qn_aqn* aqn,
+                          const qn_proj* projs, int32_t nproj, int32_t epilogue, const Opts& o, void* workspace,
+                          size_t workspace_bytes, Plan* plan, bool check_workspace) {
+  if (!opts_valid(o)) return QN_ERR_VALUE;
   if (m < 0 || k < 0 || k % 16 != 0) return QN_ERR_SHAPE;
   if (!projs) return QN_ERR_NULL;
   if (nproj < 1) return QN_ERR_SHAPE;
@@ -2140,7 +2193,6 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
   const int32_t phases = epilogue & (QN_RUN_PROLOGUE_ONLY | QN_RUN_MAIN_ONLY);
   epilogue &= ~(QN_RUN_PROLOGUE_ONLY | QN_RUN_MAIN_ONLY);
   if (phases == (QN_RUN_PROLOGUE_ONLY | QN_RUN_MAIN_ONLY)) return QN_ERR_VALUE;
-  const bool run_prologue = phases != QN_RUN_MAIN_ONLY, run_main = phases != QN_RUN_PROLOGUE_ONLY;
   if (epilogue != QN_EPI_NONE && epilogue != QN_EPI_SILU_MUL) return QN_ERR_VALUE;
   if (epilogue == QN_EPI_SILU_MUL && (nproj != 2 || projs[0].n != projs[1].n)) return QN_ERR_SHAPE;
   for (int p = 0; p < nproj; ++p) {
@@ -2178,18 +2230,48 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
     if (aqn->draw && aqn->draw_rows < 0) return QN_ERR_SHAPE;
     if (aqn->noise && aqn->noise_ld > 0 && aqn->noise_ld < k) return QN_ERR_SHAPE;
   }
-  const Workspace wl = workspace_layout(m, k, projs, nproj);
-  if (!workspace || workspace_bytes < wl.total) return QN_ERR_WORKSPACE;
-  if (!aligned(workspace, 256)) return QN_ERR_ALIGN;
   if (k > 131072) return QN_ERR_UNSUPPORTED;
   // 32-bit buffer offsets: 16 rows of x or of the noise, the LoRA-down partials and every LoRA-B matrix stay below 2 GiB
   if (ldx >= ((int64_t)1 << 26)) return QN_ERR_UNSUPPORTED;
   if (aqn && aqn->noise && aqn->noise_ld >= ((int64_t)1 << 25)) return QN_ERR_UNSUPPORTED;
-  if (wl.total - wl.t_part >= ((size_t)1 << 31)) return QN_ERR_UNSUPPORTED;
   for (int p = 0; p < nproj; ++p)
     if ((int64_t)projs[p].n * projs[p].r * 2 >= ((int64_t)1 << 31)) return QN_ERR_UNSUPPORTED;
+  // the main kernel's plan (and, for the general kernel, that every launch's shape is built)
+  const bool silu = epilogue == QN_EPI_SILU_MUL;
+  const int64_t KT = ceil_div(k, kKTile);
+  int64_t rg_total = 0;
+  for (int p = 0; p < nproj; ++p) rg_total += ceil_div(projs[p].n, 16);
+  const int64_t nrg = silu ? 2 * ceil_div(projs[0].n, 16) : rg_total;
+  const qn_status ps = plan_main(m, KT, silu ? ceil_div(projs[0].n, 16) : rg_total, silu, o, plan);
+  if (ps != QN_OK) return ps;
+  if (plan->path == kPathGeneral && nrg > 0) {
+    for (int64_t t0 = 0; t0 < m; t0 += kMaxTokensPerLaunch) {
+      const int64_t mt = (m - t0) < kMaxTokensPerLaunch ? (m - t0) : kMaxTokensPerLaunch;
+      int tmt, R, W;
+      if (!general_shape(mt, silu, nrg, KT, o, &tmt, &R, &W)) return QN_ERR_UNSUPPORTED;
+    }
+  }
+  if (plan->path == kPathMany) {
+    const int64_t nrb = silu ? ceil_div(ceil_div(projs[0].n, 16), kMRG / 2) : ceil_div(rg_total, kMRG);
+    if (nrb * ceil_div(ceil_div(m, 16), kMTT) >= ((int64_t)1 << 31)) return QN_ERR_UNSUPPORTED;
+  }
+  if (check_workspace) {
+    const Workspace wl = workspace_layout(m, k, projs, nproj, o);
+    if (!workspace || workspace_bytes < wl.total) return QN_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return QN_ERR_ALIGN;
+    if (wl.total - wl.t_part >= ((size_t)1 << 31)) return QN_ERR_UNSUPPORTED;
+  }
+  return QN_OK;
+}
 
-  hipStream_t s = (hipStream_t)stream;
+// The launches of a validated call.
+qn_status run_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const qn_aqn* aqn, const qn_proj* projs,
+                     int32_t nproj, int32_t epilogue, const Opts& o, const Plan& plan, void* workspace,
+                     hipStream_t s) {
+  const int32_t phases = epilogue & (QN_RUN_PROLOGUE_ONLY | QN_RUN_MAIN_ONLY);
+  epilogue &= ~(QN_RUN_PROLOGUE_ONLY | QN_RUN_MAIN_ONLY);
+  const bool run_prologue = phases != QN_RUN_MAIN_ONLY, run_main = phases != QN_RUN_PROLOGUE_ONLY;
+  const Workspace wl = workspace_layout(m, k, projs, nproj, o);
   char* ws = static_cast<char*>(workspace);
   const int64_t KT = ceil_div(k, kKTile), kp = KT * kKTile;
   const int64_t ntiles = ceil_div(m, 16);
@@ -2197,9 +2279,7 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
   float* xsc = reinterpret_cast<float*>(ws + wl.xsc);
   float* rstd = reinterpret_cast<float*>(ws + wl.rstd);
   int32_t* tok_p = reinterpret_cast<int32_t*>(ws + wl.tok_p);
-  // many tokens go to the MFMA kernel (QN_GEMM_OFF=1 takes the general kernel, for comparisons)
-  const char* gemm_off = std::getenv("QN_GEMM_OFF");
-  const bool gemm_path = m > kMaxTokensPerLaunch && !(gemm_off && gemm_off[0] == '1');
+  const bool gemm_path = plan.path == kPathMany;
   float* t_part = reinterpret_cast<float*>(ws + wl.t_part);
   const int CT = (int)chunk_tiles(KT);
   const int ks = (int)lora_chunks(k);
@@ -2323,7 +2403,6 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
   if (nrg == 0 || !run_main) return hipGetLastError() == hipSuccess ? QN_OK : QN_ERR_HIP;
   // many tokens: LoRA t sums, then the MFMA kernel
   if (gemm_path) {
-    const int64_t ntiles = ceil_div(m, 16);
     u32x4* t_fin = reinterpret_cast<u32x4*>(ws + wl.t_fin);
     int max_r = 0;
     for (int p = 0; p < nproj; ++p) max_r = projs[p].r > max_r ? projs[p].r : max_r;
@@ -2346,71 +2425,90 @@ extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, 
     ga.nrg = (int32_t)nrg;
     ga.nrb = (int32_t)(silu ? ceil_div(ceil_div(projs[0].n, 16), kMRG / 2) : ceil_div(rg_total, kMRG));
     ga.ntb = (int32_t)ceil_div(ntiles, kMTT);
-    // 16-byte output (and residual) accesses through an LDS tile where the buffers allow them (QN_GEMM_STORE=elem
-    // keeps the per-element stores, for comparisons)
-    bool fast = true;
+    // 16-byte output (and residual) accesses through an LDS tile where the buffers allow them and the options do not
+    // ask for per-element stores
+    bool fast = o.elem == 0;
     for (int p = 0; p < (silu ? 1 : nproj); ++p) {
       const qn_proj& P = projs[p];
       const int64_t esz = P.y_dtype == QN_F32 ? 4 : 2;
       fast = fast && P.y && (uintptr_t)P.y % 16 == 0 && (P.ldy * esz) % 16 == 0 && P.y_repeat <= 1;
       if (P.residual) fast = fast && (uintptr_t)P.residual % 16 == 0 && (P.ld_res * 2) % 16 == 0;
     }
-    if (const char* st = std::getenv("QN_GEMM_STORE")) fast = fast && std::strcmp(st, "elem") != 0;
     ga.fast_store = fast ? 1 : 0;
     ga.t_lds = silu && projs[0].r <= 32 && projs[1].r <= 32 ? 1 : 0;
-    if ((int64_t)ga.nrb * ga.ntb >= ((int64_t)1 << 31)) return QN_ERR_UNSUPPORTED;
     const dim3 grid((unsigned)(ga.nrb * ga.ntb)), block(kMWaves * kWave);
     if (silu) hipLaunchKernelGGL((k_gemm<true>), grid, block, 0, s, ga);
     else hipLaunchKernelGGL((k_gemm<false>), grid, block, 0, s, ga);
     return hipGetLastError() == hipSuccess ? QN_OK : QN_ERR_HIP;
   }
-  if (gemv_on(m)) {
+  if (plan.path == kPathDecode) {
     const int tmt = (int)ceil_div(m, 16);
     const int64_t nu = silu ? ceil_div(projs[0].n, 16) : rg_total;
-    const GemvCut cut = gemv_cut(nu, KT, tmt, silu ? 2 : 1);
-    if (gemv_pick(cut, nu, KT, tmt, silu ? 2 : 1)) {
-      GemvArgs ga{};
-      ga.L = la;
-      ga.L.tok0 = 0;
-      ga.KT = (int32_t)KT;
-      ga.ntiles = (int32_t)ceil_div(m, 16);
-      ga.mt = (int32_t)m;
-      ga.nu = (int32_t)nu;
-      ga.nbr = cut.nbr;
-      ga.nk = cut.nk;
-      ga.pbuf = reinterpret_cast<float*>(ws + wl.pbuf);
-      ga.cnt = reinterpret_cast<uint32_t*>(ws + wl.cnt);
-      const dim3 grid((unsigned)(cut.nbr * cut.nk)), block(kGWaves * kWave);
-      int depth = 3;  // weight tiles in flight per wave
-      if (const char* ov = std::getenv("QN_GEMV_DEPTH")) depth = std::atoi(ov);
+    GemvArgs ga{};
+    ga.L = la;
+    ga.L.tok0 = 0;
+    ga.KT = (int32_t)KT;
+    ga.ntiles = (int32_t)ceil_div(m, 16);
+    ga.mt = (int32_t)m;
+    ga.nu = (int32_t)nu;
+    ga.nbr = plan.cut.nbr;
+    ga.nk = plan.cut.nk;
+    ga.pbuf = reinterpret_cast<float*>(ws + wl.pbuf);
+    ga.cnt = reinterpret_cast<uint32_t*>(ws + wl.cnt);
+    const dim3 grid((unsigned)(plan.cut.nbr * plan.cut.nk)), block(kGWaves * kWave);
+    const int depth = plan.depth;  // weight tiles in flight per wave
 #define QN_GEMV(T_, S_, D_)                                                            \
   if (tmt == T_ && silu == S_ && depth == D_) {                                       \
     hipLaunchKernelGGL((k_gemv<T_, S_, D_>), grid, block, 0, s, ga);                  \
     return hipGetLastError() == hipSuccess ? QN_OK : QN_ERR_HIP;                       \
   }
-      QN_GEMV(1, false, 2) QN_GEMV(1, false, 3) QN_GEMV(1, true, 2) QN_GEMV(1, true, 3)
-      QN_GEMV(2, false, 2) QN_GEMV(2, false, 3) QN_GEMV(2, true, 2) QN_GEMV(2, true, 3)
+    QN_GEMV(1, false, 2) QN_GEMV(1, false, 3) QN_GEMV(1, true, 2) QN_GEMV(1, true, 3)
+    QN_GEMV(2, false, 2) QN_GEMV(2, false, 3) QN_GEMV(2, true, 2) QN_GEMV(2, true, 3)
 #undef QN_GEMV
-      return QN_ERR_UNSUPPORTED;  // (a tuning override asked for a depth that is not built)
-    }
+    return QN_ERR_UNSUPPORTED;  // (not reached: every (tmt <= 2, silu, depth 2 or 3) is built)
   }
   for (int64_t t0 = 0; t0 < m; t0 += kMaxTokensPerLaunch) {
     la.tok0 = t0;
     const int64_t mt = (m - t0) < kMaxTokensPerLaunch ? (m - t0) : kMaxTokensPerLaunch;
-    int tmt = (int)ceil_div(mt, 16);
-    tmt = tmt <= 2 ? tmt : (tmt <= 4 ? 4 : 8);
-    int R, W;
-    pick_shape(tmt, mt, silu, nrg, KT, &R, &W);
-    // tuning override "R,W" (row groups and waves per workgroup); ignored unless that kernel variant is built
-    if (const char* ov = std::getenv("QN_LINEAR_SHAPE")) {
-      int r2 = 0, w2 = 0;
-      if (std::sscanf(ov, "%d,%d", &r2, &w2) == 2 && r2 > 0 && w2 > 0 && (!silu || r2 % 2 == 0)) {
-        R = r2;
-        W = w2;
-      }
-    }
-    const int64_t nwg = ceil_div(nrg, R);
-    if (!dispatch_linear(tmt, R, W, silu, la, nwg, s)) return QN_ERR_UNSUPPORTED;
+    int tmt, R, W;
+    general_shape(mt, silu, nrg, KT, o, &tmt, &R, &W);  // (built: checked in validation)
+    dispatch_linear(tmt, R, W, silu, &la, ceil_div(nrg, R), s);
   }
   return hipGetLastError() == hipSuccess ? QN_OK : QN_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace qn
+
+using namespace qn;
+
+extern "C" size_t nvfp4_lora_linear_workspace_opts(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj,
+                                                   const qn_linear_opts* opts) {
+  if (m <= 0 || k <= 0 || nproj <= 0 || !projs) return 0;
+  const Opts o = opts_of(opts);
+  if (!opts_valid(o)) return 0;
+  return workspace_layout(m, k, projs, nproj, o).total;
+}
+
+extern "C" size_t nvfp4_lora_linear_workspace(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj) {
+  return nvfp4_lora_linear_workspace_opts(m, k, projs, nproj, nullptr);
+}
+
+extern "C" qn_status nvfp4_lora_linear_opts(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const qn_aqn* aqn,
+                                            const qn_proj* projs, int32_t nproj, int32_t epilogue,
+                                            const qn_linear_opts* opts, void* workspace, size_t workspace_bytes,
+                                            void* stream) {
+  const Opts o = opts_of(opts);
+  Plan plan;
+  const qn_status st =
+      validate_linear(x, m, k, ldx, aqn, projs, nproj, epilogue, o, workspace, workspace_bytes, &plan, true);
+  if (st != QN_OK || m == 0 || k == 0) return st;
+  return run_linear(x, m, k, ldx, aqn, projs, nproj, epilogue, o, plan, workspace, (hipStream_t)stream);
+}
+
+extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const qn_aqn* aqn,
+                                       const qn_proj* projs, int32_t nproj, int32_t epilogue, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  return nvfp4_lora_linear_opts(x, m, k, ldx, aqn, projs, nproj, epilogue, nullptr, workspace, workspace_bytes,
+                                stream);
 }

@@ -124,3 +124,57 @@ def test_host_helpers(qn):
     assert cb == 2 * 2 * 1024 and sb == 2 * 2 * 128
     for s in range(8):
         assert qn.status_string(s)
+
+
+def test_library_reads_no_environment():
+    """Which kernel a call runs depends on its arguments and its explicit options only: no source of the library
+    reads an environment variable."""
+    csrc = os.path.join(ROOT, "nvfp4_weight_only_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        text = open(os.path.join(csrc, name)).read()
+        assert "getenv" not in text and "environ" not in text, name
+
+
+def test_linear_options_validation(qn):
+    """Options out of range are QN_ERR_VALUE; a kernel that cannot serve the call is QN_ERR_UNSUPPORTED; both are
+    decided on the host before any launch (every call here returns without touching a GPU)."""
+    L = qn.lib
+    P = ctypes.c_void_p
+    fake = P(256)
+    p = qn.QnProj(codes=256, block_scales=256, tensor_scale=256, n=64, lora_a=256, lora_b=256, r=32, lambda_=2.0,
+                  y=256, y_dtype=0, ldy=64)
+    arr = (qn.QnProj * 1)(p)
+
+    def call(m, o, k=128, ws_bytes=None):
+        oc = o.to_c()
+        need = L.nvfp4_lora_linear_workspace_opts(m, k, arr, 1, ctypes.byref(oc))
+        return L.nvfp4_lora_linear_opts(fake, m, k, k, None, arr, 1, 0, ctypes.byref(oc), P(1 << 20),
+                                        need if ws_bytes is None else ws_bytes, None)
+
+    bad = [qn.LinearOpts(kernel=4), qn.LinearOpts(kernel=-1), qn.LinearOpts(decode_kchunks=65),
+           qn.LinearOpts(decode_depth=4), qn.LinearOpts(general_rows=2), qn.LinearOpts(general_waves=8),
+           qn.LinearOpts(elem_store=2)]
+    for o in bad:
+        assert call(4, o) == qn.QN_ERR_VALUE, o
+        oc = o.to_c()
+        assert L.nvfp4_lora_linear_workspace_opts(4, 128, arr, 1, ctypes.byref(oc)) == 0, o
+    assert call(64, qn.LinearOpts(kernel=qn.KERNEL_DECODE)) == qn.QN_ERR_UNSUPPORTED  # decode kernel: m <= 32
+    assert call(100, qn.LinearOpts(kernel=qn.KERNEL_MANY)) == qn.QN_ERR_UNSUPPORTED  # MFMA kernel: m > 128
+    assert call(4, qn.LinearOpts(kernel=qn.KERNEL_GENERAL, general_rows=3, general_waves=5)) == qn.QN_ERR_UNSUPPORTED
+    # a decode cut whose k-chunk does not fit the kernel's LDS: 32 tokens over a 40960-long row in one chunk
+    assert call(32, qn.LinearOpts(kernel=qn.KERNEL_DECODE, decode_kchunks=1), k=40960) == qn.QN_ERR_UNSUPPORTED
+    # the workspace check still applies with options
+    assert call(4, qn.LinearOpts(kernel=qn.KERNEL_GENERAL), ws_bytes=16) == qn.QN_ERR_WORKSPACE
+    # the plain entry point is the options entry point with the library's defaults
+    assert L.nvfp4_lora_linear_workspace(4, 128, arr, 1) == L.nvfp4_lora_linear_workspace_opts(4, 128, arr, 1, None)
+
+
+def test_sigma_schedule_matches_oracle(qn, orc):
+    """The library's sigma_k for every stage of the ten-stage schedule (0.01 -> 5e-4) equals the oracle's; stage 3 is
+    the value the 28-layer configuration uses."""
+    for k in range(10):
+        assert qn.aqn_sigma(k) == orc.aqn_sigma(k), k
+    assert abs(qn.aqn_sigma(3) - 4.728708e-3) < 5e-10
+    # another start/end pair, and stages past 9 continuing the decay
+    for k in range(12):
+        assert qn.aqn_sigma(k, 0.05, 5e-4) == orc.aqn_sigma(k, 0.05, 5e-4), k

@@ -50,7 +50,7 @@ class Case:
             B = None if B is None else B[rows]
         return oracle.lora_linear(self.oracle_h(), c, sb, sg, self.A[p], B, self.lam)
 
-    def gpu(self, qn, y_dtype=torch.float32, epilogue=0, residual=None):
+    def gpu(self, qn, y_dtype=torch.float32, epilogue=0, residual=None, opts=None):
         self.wq = [qn.quantize(dev_bf16(w), qn.LAYOUT_TILED) for w in self.w]
         ys, projs = [], []
         for p, n in enumerate(self.ns):
@@ -61,7 +61,7 @@ class Case:
             projs.append(qn.Projection(self.wq[p], y, A, B, self.lam, residual=residual))
         aqn = qn.make_aqn(dev_bf16(self.gamma), dev_f32(self.noise), self.sigma, 1e-6) if self.aqn else None
         self.xd = dev_bf16(self.x)
-        qn.lora_linear(self.xd, projs, aqn, epilogue)
+        qn.lora_linear(self.xd, projs, aqn, epilogue, opts=opts)
         torch.cuda.synchronize()
         return ys
 
@@ -178,14 +178,36 @@ def test_fused_norm_matches_standalone_norm(qn, m, k, per_row):
     assert torch.equal(y1, y2)
 
 
-# The two streaming kernels and the split-k form of the decode kernel, each forced through the library's tuning
-# overrides (read at every call), on the same cases: default choice, the general kernel, the decode kernel without
-# and with a split k.
-KERNEL_PATHS = {"default": {}, "general": {"QN_GEMV_OFF": "1"}, "decode": {"QN_GEMV_NK": "1"},
-                "decode-splitk": {"QN_GEMV_NK": "3"}}
+# The two streaming kernels and the split-k form of the decode kernel, each named through the call's options, on the
+# same cases: default choice, the general kernel, the decode kernel without and with a split k, and the decode kernel
+# with two weight tiles in flight.
+def kernel_paths(qn):
+    return {"default": None, "general": qn.LinearOpts(kernel=qn.KERNEL_GENERAL),
+            "decode": qn.LinearOpts(kernel=qn.KERNEL_DECODE, decode_kchunks=1),
+            "decode-splitk": qn.LinearOpts(kernel=qn.KERNEL_DECODE, decode_kchunks=3),
+            "decode-depth2": qn.LinearOpts(kernel=qn.KERNEL_DECODE, decode_depth=2)}
 
 
-@pytest.mark.parametrize("path", list(KERNEL_PATHS))
+KERNEL_PATHS = ["default", "general", "decode", "decode-splitk", "decode-depth2"]
+
+
+def decode_fits(m, nu, k, nchunks, nr):
+    """Whether the decode kernel can take a call with a cut of `nchunks` k-chunks (0: any cut): the rule the library
+    documents for QN_KERNEL_DECODE, restated from its limits (144 KiB of activations and LoRA slots in LDS, at most 8
+    row units per workgroup, about 256 workgroups)."""
+    if m > 32:
+        return False
+    tmt, KT = -(-m // 16), -(-k // 128)
+    cap = (147456 - 8 * nr * tmt * 64 * 16) // (tmt * (4 * 64 * 16 + 64))
+    for nk in ([nchunks] if nchunks else range(1, min(KT, 64) + 1)):
+        tmax = -(-KT // nk)
+        nbr = min(256 // nk, nu)
+        if tmax <= cap and tmax * tmt <= 40 and nbr >= 1 and -(-nu // nbr) <= 8:
+            return True
+    return False
+
+
+@pytest.mark.parametrize("path", KERNEL_PATHS)
 @pytest.mark.parametrize("m,ns,k,silu,residual,r,gqa", [
     (1, [200], 1024, False, False, 32, 1),
     (16, [520, 64, 64], 1040, False, False, 64, 1),
@@ -196,11 +218,8 @@ KERNEL_PATHS = {"default": {}, "general": {"QN_GEMV_OFF": "1"}, "decode": {"QN_G
     (32, [128, 128], 1024, True, False, 0, 1),
     (9, [512, 128, 128], 640, False, False, 32, 4),
 ])
-def test_linear_kernel_paths(qn, monkeypatch, path, m, ns, k, silu, residual, r, gqa):
-    for key in ("QN_GEMV_OFF", "QN_GEMV_NK"):
-        monkeypatch.delenv(key, raising=False)
-    for key, val in KERNEL_PATHS[path].items():
-        monkeypatch.setenv(key, val)
+def test_linear_kernel_paths(qn, path, m, ns, k, silu, residual, r, gqa):
+    opts = kernel_paths(qn)[path]
     c = Case(m, ns, k, r=r, seed=m * 7 + k)
     wq = [qn.quantize(dev_bf16(w), qn.LAYOUT_TILED) for w in c.w]
     res = synth.normal_bf16(56, (m, ns[0])) if residual else None
@@ -215,7 +234,13 @@ def test_linear_kernel_paths(qn, monkeypatch, path, m, ns, k, silu, residual, r,
                                    residual=dev_bf16(res) if (residual and p == 0) else None,
                                    y_repeat=rep, head_dim=64))
     aqn = qn.make_aqn(dev_bf16(c.gamma), dev_f32(c.noise), c.sigma, 1e-6)
-    qn.lora_linear(dev_bf16(c.x), projs, aqn, qn.EPI_SILU_MUL if silu else qn.EPI_NONE)
+    nu = -(-ns[0] // 16) if silu else sum(-(-n // 16) for n in ns)
+    if path.startswith("decode") and not decode_fits(m, nu, k, opts.decode_kchunks, 2 if silu else 1):
+        with pytest.raises(qn.QnError) as e:  # refused on the host, nothing launched
+            qn.lora_linear(dev_bf16(c.x), projs, aqn, qn.EPI_SILU_MUL if silu else qn.EPI_NONE, opts=opts)
+        assert e.value.status == qn.QN_ERR_UNSUPPORTED
+        return
+    qn.lora_linear(dev_bf16(c.x), projs, aqn, qn.EPI_SILU_MUL if silu else qn.EPI_NONE, opts=opts)
     torch.cuda.synchronize()
     if silu:
         ref = oracle.silu_mul(c.oracle_y(0), c.oracle_y(1))
@@ -232,11 +257,14 @@ def test_linear_kernel_paths(qn, monkeypatch, path, m, ns, k, silu, residual, r,
 
 
 # Many tokens (more than 128): the MFMA kernel with one activation exponent per token, and the general kernel in
-# 128-token launches (its override), on shapes that leave ragged token blocks, ragged row blocks and mixed ranks.
-MANY_PATHS = {"mfma": {}, "mfma-elem-store": {"QN_GEMM_STORE": "elem"}, "general": {"QN_GEMM_OFF": "1"}}
+# 128-token launches (named through the options), on shapes that leave ragged token blocks, ragged row blocks and
+# mixed ranks.
+def many_paths(qn):
+    return {"mfma": None, "mfma-elem-store": qn.LinearOpts(kernel=qn.KERNEL_MANY, elem_store=1),
+            "general": qn.LinearOpts(kernel=qn.KERNEL_GENERAL)}
 
 
-@pytest.mark.parametrize("path", list(MANY_PATHS))
+@pytest.mark.parametrize("path", ["mfma", "mfma-elem-store", "general"])
 @pytest.mark.parametrize("m,ns,k,silu,residual,r,gqa,aqn", [
     (129, [200], 1024, False, False, 32, 1, True),
     (300, [384, 384], 512, True, False, 8, 1, True),
@@ -247,11 +275,8 @@ MANY_PATHS = {"mfma": {}, "mfma-elem-store": {"QN_GEMM_STORE": "elem"}, "general
     (150, [256, 256, 72], 256, False, True, 16, 1, True),
     (160, [200, 72, 40], 512, False, False, 16, 1, False),
 ])
-def test_linear_many_tokens(qn, monkeypatch, path, m, ns, k, silu, residual, r, gqa, aqn):
-    monkeypatch.delenv("QN_GEMM_OFF", raising=False)
-    monkeypatch.delenv("QN_GEMM_STORE", raising=False)
-    for key, val in MANY_PATHS[path].items():
-        monkeypatch.setenv(key, val)
+def test_linear_many_tokens(qn, path, m, ns, k, silu, residual, r, gqa, aqn):
+    opts = many_paths(qn)[path]
     c = Case(m, ns, k, r=r, seed=m * 5 + k, aqn=aqn)
     wq = [qn.quantize(dev_bf16(w), qn.LAYOUT_TILED) for w in c.w]
     res = synth.normal_bf16(57, (m, ns[0])) if residual else None
@@ -266,7 +291,7 @@ def test_linear_many_tokens(qn, monkeypatch, path, m, ns, k, silu, residual, r, 
                                    residual=dev_bf16(res) if (residual and p == 0) else None,
                                    y_repeat=rep, head_dim=16))
     norm = qn.make_aqn(dev_bf16(c.gamma), dev_f32(c.noise), c.sigma, 1e-6) if aqn else None
-    qn.lora_linear(dev_bf16(c.x), projs, norm, qn.EPI_SILU_MUL if silu else qn.EPI_NONE)
+    qn.lora_linear(dev_bf16(c.x), projs, norm, qn.EPI_SILU_MUL if silu else qn.EPI_NONE, opts=opts)
     torch.cuda.synchronize()
     if silu:
         ref = oracle.silu_mul(c.oracle_y(0), c.oracle_y(1))
@@ -287,20 +312,16 @@ def test_linear_many_tokens(qn, monkeypatch, path, m, ns, k, silu, residual, r, 
     (200, [520], 1024, False, True),
     (129, [256, 256], 384, False, True),
 ])
-def test_linear_many_tokens_bf16_store_paths(qn, monkeypatch, m, ns, k, silu, residual):
+def test_linear_many_tokens_bf16_store_paths(qn, m, ns, k, silu, residual):
     """Many tokens with bf16 outputs: the 16-byte stores through the LDS tile and the per-element stores give the
     same bits (same f32 values, residual added before the one rounding), and both meet the bar against the oracle
     with one bf16 rounding on top (ragged row blocks and token blocks included)."""
-    monkeypatch.delenv("QN_GEMM_OFF", raising=False)
     c = Case(m, ns, k, r=16, seed=m + 3 * k, aqn=True)
     wq = [qn.quantize(dev_bf16(w), qn.LAYOUT_TILED) for w in c.w]
     res = synth.normal_bf16(91, (m, ns[0])) if residual else None
     outs = {}
     for store in ("fast", "elem"):
-        if store == "elem":
-            monkeypatch.setenv("QN_GEMM_STORE", "elem")
-        else:
-            monkeypatch.delenv("QN_GEMM_STORE", raising=False)
+        opts = qn.LinearOpts(elem_store=1) if store == "elem" else None
         ys, projs = [], []
         for p, n in enumerate(ns):
             y = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=DEV)
@@ -308,7 +329,7 @@ def test_linear_many_tokens_bf16_store_paths(qn, monkeypatch, m, ns, k, silu, re
             projs.append(qn.Projection(wq[p], None if (silu and p == 1) else y, dev_bf16(c.A[p]), dev_bf16(c.B[p]),
                                        c.lam, residual=dev_bf16(res) if (residual and p == 0) else None))
         qn.lora_linear(dev_bf16(c.x), projs, qn.make_aqn(dev_bf16(c.gamma), dev_f32(c.noise), c.sigma, 1e-6),
-                       qn.EPI_SILU_MUL if silu else qn.EPI_NONE)
+                       qn.EPI_SILU_MUL if silu else qn.EPI_NONE, opts=opts)
         torch.cuda.synchronize()
         outs[store] = [host_bf16(y) for y in (ys[:1] if silu else ys)]
     for a, b in zip(outs["fast"], outs["elem"]):
@@ -322,25 +343,21 @@ def test_linear_many_tokens_bf16_store_paths(qn, monkeypatch, m, ns, k, silu, re
 
 
 @pytest.mark.parametrize("m,n,k", [(200, 520, 640), (129, 256, 384)])
-def test_linear_many_tokens_residual_aliases_output(qn, monkeypatch, m, n, k):
+def test_linear_many_tokens_residual_aliases_output(qn, m, n, k):
     """Many tokens, bf16 output with the residual read from the output buffer itself (the one aliasing the API
     allows): the same bits as with a separate residual buffer, on both store paths."""
-    monkeypatch.delenv("QN_GEMM_OFF", raising=False)
     c = Case(m, [n], k, r=16, seed=m + k, aqn=True)
     wq = qn.quantize(dev_bf16(c.w[0]), qn.LAYOUT_TILED)
     res = synth.normal_bf16(93, (m, n))
     aqn = qn.make_aqn(dev_bf16(c.gamma), dev_f32(c.noise), c.sigma, 1e-6)
     for store in ("fast", "elem"):
-        if store == "elem":
-            monkeypatch.setenv("QN_GEMM_STORE", "elem")
-        else:
-            monkeypatch.delenv("QN_GEMM_STORE", raising=False)
+        opts = qn.LinearOpts(elem_store=1) if store == "elem" else None
         y_sep = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=DEV)
         qn.lora_linear(dev_bf16(c.x), [qn.Projection(wq, y_sep, dev_bf16(c.A[0]), dev_bf16(c.B[0]), c.lam,
-                                                     residual=dev_bf16(res))], aqn)
+                                                     residual=dev_bf16(res))], aqn, opts=opts)
         y_alias = dev_bf16(res)
         qn.lora_linear(dev_bf16(c.x), [qn.Projection(wq, y_alias, dev_bf16(c.A[0]), dev_bf16(c.B[0]), c.lam,
-                                                     residual=y_alias)], aqn)
+                                                     residual=y_alias)], aqn, opts=opts)
         torch.cuda.synchronize()
         assert np.array_equal(host_bf16(y_sep), host_bf16(y_alias)), store
 
