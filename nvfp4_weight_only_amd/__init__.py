@@ -5,6 +5,7 @@ package without the built library raises, and calls never fall back to anything 
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from dataclasses import dataclass
@@ -122,6 +123,12 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on(stream):
+    """Allocations the binding makes for a call on `stream` come from that stream's pool of the caching allocator, so
+    they never alias memory another stream still has work pending on."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 # ---- NVFP4 weights ------------------------------------------------------------------------------------------------
 @dataclass
 class NVFP4Weight:
@@ -157,7 +164,8 @@ def quantize(w: torch.Tensor, layout: int = LAYOUT_TILED, scale_mode: int = 0, o
     assert w.dtype == torch.bfloat16 and w.dim() == 2
     n, k = w.shape
     if out is None:
-        out = alloc_weight(n, k, layout, w.device)
+        with _on(stream):
+            out = alloc_weight(n, k, layout, w.device)
     _check(lib.nvfp4_quantize(_ptr(w), n, k, w.stride(0), scale_mode, out.layout, _ptr(out.codes), _ptr(out.scales),
                               _ptr(out.tensor_scale), _ptr(flags), _stream(stream)), "nvfp4_quantize")
     for t in (out.codes, out.scales, out.tensor_scale):
@@ -166,7 +174,8 @@ def quantize(w: torch.Tensor, layout: int = LAYOUT_TILED, scale_mode: int = 0, o
 
 
 def dequantize(wq: NVFP4Weight, stream=None) -> torch.Tensor:
-    out = torch.empty(wq.n, wq.k, dtype=torch.float32, device=wq.codes.device)
+    with _on(stream):
+        out = torch.empty(wq.n, wq.k, dtype=torch.float32, device=wq.codes.device)
     _check(lib.nvfp4_dequantize(_ptr(wq.codes), _ptr(wq.scales), _ptr(wq.tensor_scale), wq.n, wq.k, wq.layout,
                                 _ptr(out), wq.k, _stream(stream)), "nvfp4_dequantize")
     _keep_for(out, stream)
@@ -215,7 +224,8 @@ def make_aqn(gamma: torch.Tensor, noise: Optional[torch.Tensor], sigma: float, e
 
 def aqn_noise(draw: NoiseDraw, m: int, d: int, device, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Seeded standard-normal noise [m, d] f32 on the device (Philox4x64-10 + Box-Muller)."""
-    eps = out if out is not None else torch.empty(m, d, dtype=torch.float32, device=device)
+    with _on(stream):
+        eps = out if out is not None else torch.empty(m, d, dtype=torch.float32, device=device)
     _check(lib.aqn_noise(draw.seed, draw.subseed, draw.row_offset, draw.draw_rows, m, d, _ptr(eps), eps.stride(0),
                          _stream(stream)), "aqn_noise")
     _keep_for(eps, stream)
@@ -226,7 +236,8 @@ def aqn_rmsnorm(x: torch.Tensor, gamma: torch.Tensor, noise: Optional[torch.Tens
                 noise_per_row: bool = False, out: Optional[torch.Tensor] = None, stream=None,
                 draw: Optional[NoiseDraw] = None) -> torch.Tensor:
     m, d = x.shape
-    h = out if out is not None else torch.empty(m, d, dtype=torch.bfloat16, device=x.device)
+    with _on(stream):
+        h = out if out is not None else torch.empty(m, d, dtype=torch.bfloat16, device=x.device)
     a = make_aqn(gamma, noise, sigma, eps, noise_per_row, draw)
     _check(lib.aqn_rmsnorm(_ptr(x), m, d, x.stride(0), ctypes.byref(a.c), _ptr(h), h.stride(0), _stream(stream)),
            "aqn_rmsnorm")
@@ -294,7 +305,9 @@ def linear_workspace_bytes(m: int, k: int, projs: Sequence[Projection], opts: Op
 
 class LinearCall:
     """A prepared nvfp4_lora_linear call: the C structs are built once, so repeated launches only cross ctypes.
-    opts: an explicit kernel choice (LinearOpts), None for the library's own."""
+    opts: an explicit kernel choice (LinearOpts), None for the library's own. The workspace belongs to the stream
+    current when it was allocated; a call on another stream is recorded on it, so its memory is not recycled while
+    that stream may still use it."""
 
     def __init__(self, x: torch.Tensor, projs: Sequence[Projection], aqn: Optional[AqnParams] = None,
                  epilogue: int = EPI_NONE, workspace: Optional[Workspace] = None, opts: Optional[LinearOpts] = None):
@@ -321,12 +334,17 @@ class LinearCall:
 
 def lora_linear(x: torch.Tensor, projs: Sequence[Projection], aqn: Optional[AqnParams] = None, epilogue: int = EPI_NONE,
                 workspace: Optional[Workspace] = None, stream=None, opts: Optional[LinearOpts] = None):
-    LinearCall(x, projs, aqn, epilogue, workspace, opts)(stream)
+    """One call. Without a workspace, the call's own comes from `stream`'s allocator pool and is released on return
+    (its memory is reused only by later work on that stream). The caller orders `stream` after any work on its tensors
+    (torch's usual rule for tensors shared between streams)."""
+    with _on(stream):
+        LinearCall(x, projs, aqn, epilogue, workspace, opts)(stream)
 
 
 def group_advantage(rewards: torch.Tensor, eps: float = 1e-6, stream=None) -> torch.Tensor:
     groups, g = rewards.shape
-    adv = torch.empty_like(rewards)
+    with _on(stream):
+        adv = torch.empty_like(rewards)
     _check(lib.grpo_group_advantage(_ptr(rewards), groups, g, eps, _ptr(adv), _stream(stream)),
            "grpo_group_advantage")
     _keep_for(adv, stream)

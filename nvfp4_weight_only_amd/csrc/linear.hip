@@ -564,6 +564,8 @@ __global__ void __launch_bounds__(kProWaves * kWave) k_prologue(PrologueArgs a) 
         acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[gi][g][i]),
                                                          __builtin_bit_cast(bf16x8, b), acc[g], 0, 0, 0);
     }
+    mfma_settle(acc[0]);  // (the loop's exit separates the MFMAs from these stores)
+    mfma_settle(acc[1]);
     s_red[wave][0][lane] = acc[0];
     s_red[wave][1][lane] = acc[1];
     __syncthreads();
@@ -912,6 +914,8 @@ __global__ void __launch_bounds__(W * kWave) k_linear(LinearArgs a) {
       if (!kEarlyLora) issue_lora<TMT>(lops[q], lraw[q], a.p[pj[rr]], pj[rr], rg[rr], lane, a, tile0, ntiles);
       finish_lora<TMT>(lops[q], lraw[q], a.p[pj[rr]], pj[rr], lane, a, tile0, ntiles);
       lora_mfma<TMT>(lops[q], la);
+#pragma unroll
+      for (int tt = 0; tt < TMT; ++tt) mfma_settle(la[tt]);  // (read past the end of this branch)
     }
 #pragma unroll
     for (int tt = 0; tt < TMT; ++tt) red[W][rr][tt][lane] = la[tt];
@@ -1307,6 +1311,7 @@ __global__ void __launch_bounds__(kGWaves * kWave) k_gemv(GemvArgs g) {
                                                            __builtin_bit_cast(bf16x8, thi), la, 0, 0, 0);
               la = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bfr[u]),
                                                            __builtin_bit_cast(bf16x8, tlo), la, 0, 0, 0);
+              mfma_settle(la);  // (the store below sits behind a branch on one of its paths)
               f32x4* slot = reinterpret_cast<f32x4*>(lred + ((((u * NR + nr) * TMT + tt) * kWave) + lane) * 16);
               *slot = jc == 0 ? la : *slot + la;
             }

@@ -47,6 +47,14 @@ __device__ inline float e4m3_to_f32(uint32_t byte) {
   return (byte & 0x80u) ? -mag : mag;
 }
 
+// An MFMA's result registers may be read by a non-MFMA instruction (a VALU operation, an LDS or memory store) only
+// once the matrix core has written every pass of them; the program must place enough independent instructions in
+// between. Within a basic block the compiler counts them; across a branch or a loop exit it has been seen to count
+// too few (an LDS store one instruction after the MFMA on a taken branch, which then stored stale lanes). This waits
+// the passes out explicitly: the assembly statement takes the registers as an operand, so it stays between the MFMA
+// and every reader on every path, and its no-ops give 16 wait states, more than any 16x16x32 MFMA here needs.
+__device__ __forceinline__ void mfma_settle(f32x4& v) { asm volatile("s_nop 7\n\ts_nop 7" : "+v"(v)); }
+
 // Wave-wide reductions (wave64) through ds_swizzle-free shuffles.
 __device__ inline float wave_max(float v) {
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
