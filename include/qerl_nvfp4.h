@@ -7,13 +7,15 @@
  * Conventions for every entry point:
  *   - Buffer pointers are DEVICE pointers (hipMalloc / torch CUDA tensors) unless a comment says "host".
  *     bf16 tensors are passed as uint16_t bit patterns, E2M1 codes and E4M3 scales as uint8_t.
- *   - The caller owns every buffer. The library allocates no device memory; scratch space comes from `workspace`.
+ *   - The caller owns every buffer. The library allocates no device memory; scratch space comes from `workspace`
+ *     (nvfp4_lora_linear_noalloc uses one device array of the library instead, see there).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Calls only enqueue work on it and
  *     return; results are ready when the stream reaches that point.
  *   - Errors: arguments are validated on the host before anything is launched; a failed validation returns a
  *     status other than QN_OK and enqueues nothing. QN_ERR_HIP reports a failed launch. Nothing is printed and
  *     nothing aborts. Conditions seen on the device are reported through an optional device flag word.
- *   - Thread safety: calls on different streams may run concurrently; the library keeps no mutable global state.
+ *   - Thread safety: calls on different streams may run concurrently; the library keeps no mutable global state
+ *     (except nvfp4_lora_linear_noalloc's shared scratch array, see there).
  *   - Empty inputs (m == 0 or n == 0) are valid and enqueue nothing.
  */
 #ifndef QERL_NVFP4_H
@@ -210,6 +212,22 @@ size_t nvfp4_lora_linear_workspace_opts(int64_t m, int64_t k, const qn_proj* pro
 qn_status nvfp4_lora_linear_opts(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const qn_aqn* aqn,
                                  const qn_proj* projs, int32_t nproj, int32_t epilogue, const qn_linear_opts* opts,
                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* nvfp4_lora_linear for callers that cannot allocate memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same computation and kernels, with the scratch space taken from a device
+ * array inside the library instead of a caller's workspace. It calls no allocator. The array holds
+ * nvfp4_lora_linear_noalloc_max_bytes() bytes (32 MiB) on each GPU the library runs on, for as long as the process
+ * lives; it serves every decode-sized call of the configurations here (up to 128 tokens at the 7B and 32B shapes).
+ * A call needing more (nvfp4_lora_linear_workspace above the maximum) returns QN_ERR_WORKSPACE and launches nothing.
+ * Every call on one GPU shares that GPU's array, so calls that overlap on one GPU (on different streams, or from
+ * different threads without ordering) race; calls ordered on one stream are safe. The array keeps the last call's
+ * contents; what a call needs zeroed it clears itself. Errors: as nvfp4_lora_linear, plus QN_ERR_HIP if the array's
+ * device address cannot be looked up. */
+qn_status nvfp4_lora_linear_noalloc(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const qn_aqn* aqn,
+                                    const qn_proj* projs, int32_t nproj, int32_t epilogue, void* stream);
+
+/* Bytes of the scratch array behind nvfp4_lora_linear_noalloc (host, pure). */
+size_t nvfp4_lora_linear_noalloc_max_bytes(void);
 
 /* Exponential AQN noise schedule [review §5.2]: sigma_0 = 0, sigma_k = start * (end/start)^((k-1)/8), k = 1..9
  * (stages beyond 9 continue the same geometric decay). Host, pure, fp64. */

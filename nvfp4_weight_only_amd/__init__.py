@@ -27,7 +27,8 @@ KERNEL_AUTO, KERNEL_GENERAL, KERNEL_DECODE, KERNEL_MANY = range(4)
 EXPORTS = ["nvfp4_quantize", "nvfp4_tiled_codes_bytes", "nvfp4_tiled_scales_bytes", "nvfp4_dequantize", "aqn_rmsnorm",
            "aqn_noise",
            "nvfp4_lora_linear_workspace", "nvfp4_lora_linear", "nvfp4_lora_linear_workspace_opts",
-           "nvfp4_lora_linear_opts", "aqn_sigma", "grpo_group_advantage", "qn_status_string"]
+           "nvfp4_lora_linear_opts", "nvfp4_lora_linear_noalloc", "nvfp4_lora_linear_noalloc_max_bytes",
+           "aqn_sigma", "grpo_group_advantage", "qn_status_string"]
 
 
 class QnError(RuntimeError):
@@ -91,6 +92,9 @@ def _load():
                                              sz),
         "nvfp4_lora_linear_opts": ([P, i64, i64, i64, ctypes.POINTER(QnAqn), ctypes.POINTER(QnProj), i32, i32,
                                     ctypes.POINTER(QnLinearOpts), P, sz, P], i32),
+        "nvfp4_lora_linear_noalloc": ([P, i64, i64, i64, ctypes.POINTER(QnAqn), ctypes.POINTER(QnProj), i32, i32, P],
+                                      i32),
+        "nvfp4_lora_linear_noalloc_max_bytes": ([], sz),
         "aqn_sigma": ([i32, f64, f64], f64),
         "grpo_group_advantage": ([P, i32, i32, f32, P, P], i32),
         "qn_status_string": ([i32], ctypes.c_char_p),
@@ -339,6 +343,16 @@ def lora_linear(x: torch.Tensor, projs: Sequence[Projection], aqn: Optional[AqnP
     (torch's usual rule for tensors shared between streams)."""
     with _on(stream):
         LinearCall(x, projs, aqn, epilogue, workspace, opts)(stream)
+
+
+def lora_linear_noalloc(x: torch.Tensor, projs: Sequence[Projection], aqn: Optional[AqnParams] = None,
+                        epilogue: int = EPI_NONE, stream=None):
+    """nvfp4_lora_linear_noalloc: the same call with the library's own scratch array (no workspace, no allocation).
+    Calls that overlap on one GPU share that array and must not run concurrently."""
+    arr = (QnProj * len(projs))(*[p.to_c() for p in projs])
+    m, k = x.shape
+    _check(lib.nvfp4_lora_linear_noalloc(_ptr(x), m, k, x.stride(0), ctypes.byref(aqn.c) if aqn is not None else None,
+                                         arr, len(projs), epilogue, _stream(stream)), "nvfp4_lora_linear_noalloc")
 
 
 def group_advantage(rewards: torch.Tensor, eps: float = 1e-6, stream=None) -> torch.Tensor:

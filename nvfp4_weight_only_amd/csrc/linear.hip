@@ -28,6 +28,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "qn_device.hpp"
@@ -2509,6 +2510,46 @@ extern "C" qn_status nvfp4_lora_linear_opts(const uint16_t* x, int64_t m, int64_
       validate_linear(x, m, k, ldx, aqn, projs, nproj, epilogue, o, workspace, workspace_bytes, &plan, true);
   if (st != QN_OK || m == 0 || k == 0) return st;
   return run_linear(x, m, k, ldx, aqn, projs, nproj, epilogue, o, plan, workspace, (hipStream_t)stream);
+}
+
+// ---- the entry point that allocates nothing ---------------------------------------------------------------------
+// Its scratch space is one file-scope device array per GPU, held until the process ends. Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in symbol): the device address of each GPU's copy is looked
+// up once per device with hipGetSymbolAddress and used instead.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once looked up
+
+// The current device's copy of the scratch array (looked up on its first use on that device, with it current).
+static qn_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QN_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return QN_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return QN_OK;
+}
+
+extern "C" size_t nvfp4_lora_linear_noalloc_max_bytes(void) { return kScratchBytes; }
+
+extern "C" qn_status nvfp4_lora_linear_noalloc(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const qn_aqn* aqn,
+                                               const qn_proj* projs, int32_t nproj, int32_t epilogue, void* stream) {
+  Plan plan;
+  const Opts o;
+  qn_status st = validate_linear(x, m, k, ldx, aqn, projs, nproj, epilogue, o, nullptr, 0, &plan, false);
+  if (st != QN_OK || m == 0 || k == 0) return st;
+  if (workspace_layout(m, k, projs, nproj, o).total > kScratchBytes) return QN_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != QN_OK) return st;
+  return run_linear(x, m, k, ldx, aqn, projs, nproj, epilogue, o, plan, ws, (hipStream_t)stream);
 }
 
 extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const qn_aqn* aqn,
