@@ -237,6 +237,12 @@ double aqn_sigma(int32_t stage, double sigma_start, double sigma_end);
  * rewards. rewards, adv: [groups][g] f32 (device); fp64 arithmetic on the device, rounded to f32. */
 qn_status grpo_group_advantage(const float* rewards, int32_t groups, int32_t g, float eps, float* adv, void* stream);
 
+/* Measurement helper, not part of the method: reads [src, src + bytes) from device memory once, as a plain streaming
+ * kernel (16-byte non-temporal loads, 2048 workgroups of 256 threads), and XORs what it read into *sink (device, the
+ * caller zeroes it), so that the rate a memory-bound kernel reaches can be compared with the rate plain streaming
+ * reads reach on the same device. bytes % 16 == 0 (QN_ERR_SHAPE), src 16-byte and sink 4-byte aligned (QN_ERR_ALIGN). */
+qn_status qn_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 /* Static description of a status code (host). */
 const char* qn_status_string(qn_status s);
 

@@ -28,7 +28,7 @@ EXPORTS = ["nvfp4_quantize", "nvfp4_tiled_codes_bytes", "nvfp4_tiled_scales_byte
            "aqn_noise",
            "nvfp4_lora_linear_workspace", "nvfp4_lora_linear", "nvfp4_lora_linear_workspace_opts",
            "nvfp4_lora_linear_opts", "nvfp4_lora_linear_noalloc", "nvfp4_lora_linear_noalloc_max_bytes",
-           "aqn_sigma", "grpo_group_advantage", "qn_status_string"]
+           "aqn_sigma", "grpo_group_advantage", "qn_stream_read", "qn_status_string"]
 
 
 class QnError(RuntimeError):
@@ -96,6 +96,7 @@ def _load():
                                       i32),
         "nvfp4_lora_linear_noalloc_max_bytes": ([], sz),
         "aqn_sigma": ([i32, f64, f64], f64),
+        "qn_stream_read": ([P, sz, P, P], i32),
         "grpo_group_advantage": ([P, i32, i32, f32, P, P], i32),
         "qn_status_string": ([i32], ctypes.c_char_p),
     }
@@ -353,6 +354,12 @@ def lora_linear_noalloc(x: torch.Tensor, projs: Sequence[Projection], aqn: Optio
     m, k = x.shape
     _check(lib.nvfp4_lora_linear_noalloc(_ptr(x), m, k, x.stride(0), ctypes.byref(aqn.c) if aqn is not None else None,
                                          arr, len(projs), epilogue, _stream(stream)), "nvfp4_lora_linear_noalloc")
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """qn_stream_read over the whole of `buf` (a measurement helper: plain streaming reads)."""
+    _check(lib.qn_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)),
+           "qn_stream_read")
 
 
 def group_advantage(rewards: torch.Tensor, eps: float = 1e-6, stream=None) -> torch.Tensor:

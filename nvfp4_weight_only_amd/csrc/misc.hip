@@ -28,10 +28,40 @@ __global__ void k_group_advantage(const float* __restrict__ rewards, int groups,
   for (int i = 0; i < g; ++i) adv[(int64_t)q * g + i] = (float)(((double)R[i] - mean) / denom);
 }
 
+// Plain streaming read: every 16-byte piece of [src, src + 16 n16) loaded once (non-temporal), four loads in flight per
+// thread, folded into an XOR that one lane per wave publishes (so the loads cannot be dropped).
+__global__ void __launch_bounds__(256) k_stream_read(const u32x4* __restrict__ src, int64_t n16,
+                                                     uint32_t* __restrict__ sink) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4 a = __builtin_nontemporal_load(src + i);
+    const u32x4 b = __builtin_nontemporal_load(src + i + stride);
+    const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
+    const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
+    acc ^= a ^ b ^ c ^ d;
+  }
+  for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(src + i);
+  uint32_t v = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  for (int off = 32; off > 0; off >>= 1) v ^= (uint32_t)__shfl_xor((int)v, off, kWave);
+  if (threadIdx.x % kWave == 0) atomicXor(sink, v);
+}
+
 }  // namespace
 }  // namespace qn
 
 using namespace qn;
+
+extern "C" qn_status qn_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (bytes % 16 != 0) return QN_ERR_SHAPE;
+  if (bytes == 0) return QN_OK;
+  if (!src || !sink) return QN_ERR_NULL;
+  if ((uintptr_t)src % 16 != 0 || (uintptr_t)sink % 4 != 0) return QN_ERR_ALIGN;
+  hipLaunchKernelGGL(k_stream_read, dim3(256 * 8), dim3(256), 0, (hipStream_t)stream,
+                     static_cast<const u32x4*>(src), (int64_t)(bytes / 16), sink);
+  return hipGetLastError() == hipSuccess ? QN_OK : QN_ERR_HIP;
+}
 
 extern "C" double aqn_sigma(int32_t stage, double sigma_start, double sigma_end) {
   if (stage <= 0) return 0.0;
