@@ -58,6 +58,7 @@ def lib():
             "orc_dense_linear": ([P, i64, i64, P, i64, P], None),
             "orc_group_advantage": ([P, i32, i32, dbl, P], None),
             "orc_silu_mul": ([P, P, i64, P], None),
+            "orc_grpo_surrogate": ([P, P, i64, P, P, i32, i32, dbl, dbl, i32, P, P, P], None),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -235,6 +236,24 @@ def silu_mul(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
     out = np.empty_like(g)
     lib().orc_silu_mul(_p(g), _p(u), g.size, _p(out))
     return out
+
+
+def grpo_surrogate(logp: np.ndarray, logp_old: np.ndarray, lengths, adv, clip_low: float = 0.2,
+                   clip_high: float = 0.2, agg: int = 0):
+    """GRPO token ratios and clipped surrogate (see orc_grpo_surrogate). logp, logp_old f32 [n_seq, t_max];
+    lengths int [n_seq]; adv f32 [n_seq] -> (surrogate fp64 [n_seq, t_max], grad fp64 [n_seq, t_max], stats dict)."""
+    lp = _c(logp, np.float32)
+    lo = _c(logp_old, np.float32)
+    n_seq, t_max = lp.shape
+    ln = _c(lengths, np.int32)
+    A = _c(adv, np.float32)
+    sur = np.empty((n_seq, t_max), dtype=np.float64)
+    g = np.empty((n_seq, t_max), dtype=np.float64)
+    st = np.empty(6, dtype=np.float64)
+    lib().orc_grpo_surrogate(_p(lp), _p(lo), t_max, _p(ln), _p(A), n_seq, t_max, float(clip_low), float(clip_high),
+                             int(agg), _p(sur), _p(g), _p(st))
+    keys = ("loss", "ratio_mean", "ratio_min", "ratio_max", "tokens", "clipped")
+    return sur, g, dict(zip(keys, st.tolist()))
 
 
 # ---- decoder layer at decode (composition of the functions above) -------------------------------------------------

@@ -387,6 +387,62 @@ void orc_group_advantage(const float* rewards, int groups, int g, double eps, do
   }
 }
 
+// GRPO token ratio and clipped surrogate [review §2.3]: for token t of response i, sampled by the behavior policy
+// pi_b,  rho = exp(log pi_theta - log pi_b)  and the surrogate  s = min(rho A_i, clip(rho, 1 - clip_low, 1 + clip_high) A_i).
+// The pages fix neither the clip widths nor how token surrogates are combined; the readings here: both widths are
+// arguments, and the loss is -(sum_i,t w_i,t s_i,t) with w = 1 / (all valid tokens) (agg 0, a token mean over the
+// batch) or w = 1 / (responses with tokens x tokens of response i) (agg 1, each response's token mean, averaged over
+// responses). Response i has lengths[i] valid tokens (clamped to [0, t_max]) at logp[i * ld + t].
+// Per token: surrogate s (0 past the length) and grad = d loss / d log pi_theta = -w rho A where the unclipped term
+// is the smaller (ties included: inside the clip range both terms are equal), else 0 (the clipped term is constant).
+// stats: [0] loss, [1] mean ratio over valid tokens, [2] min ratio, [3] max ratio, [4] valid tokens, [5] tokens whose
+// clipped term is strictly smaller. fp64 throughout, from the f32 inputs.
+void orc_grpo_surrogate(const float* logp, const float* logp_old, int64_t ld, const int* lengths, const float* adv,
+                        int n_seq, int t_max, double clip_low, double clip_high, int agg, double* surrogate,
+                        double* grad, double* stats) {
+  int64_t n_tok = 0;
+  int n_nonempty = 0;
+  for (int i = 0; i < n_seq; ++i) {
+    int L = lengths[i] < 0 ? 0 : (lengths[i] > t_max ? t_max : lengths[i]);
+    n_tok += L;
+    if (L > 0) ++n_nonempty;
+  }
+  double loss = 0.0, rsum = 0.0, rmin = INFINITY, rmax = -INFINITY;
+  int64_t clipped = 0;
+  for (int i = 0; i < n_seq; ++i) {
+    int L = lengths[i] < 0 ? 0 : (lengths[i] > t_max ? t_max : lengths[i]);
+    const double A = (double)adv[i];
+    const double w = agg == 0 ? (n_tok > 0 ? 1.0 / (double)n_tok : 0.0)
+                              : (L > 0 ? 1.0 / ((double)n_nonempty * (double)L) : 0.0);
+    for (int t = 0; t < t_max; ++t) {
+      const int64_t k = (int64_t)i * ld + t;
+      if (t >= L) {
+        if (surrogate) surrogate[k] = 0.0;
+        if (grad) grad[k] = 0.0;
+        continue;
+      }
+      const double rho = std::exp((double)logp[k] - (double)logp_old[k]);
+      const double lo = 1.0 - clip_low, hi = 1.0 + clip_high;
+      const double unclipped = rho * A;
+      const double clipped_term = (rho < lo ? lo : (rho > hi ? hi : rho)) * A;
+      const double sur = unclipped <= clipped_term ? unclipped : clipped_term;
+      if (surrogate) surrogate[k] = sur;
+      if (grad) grad[k] = unclipped <= clipped_term ? -w * rho * A : 0.0;
+      if (clipped_term < unclipped) ++clipped;
+      loss -= w * sur;
+      rsum += rho;
+      rmin = rho < rmin ? rho : rmin;
+      rmax = rho > rmax ? rho : rmax;
+    }
+  }
+  stats[0] = loss;
+  stats[1] = n_tok > 0 ? rsum / (double)n_tok : 0.0;
+  stats[2] = n_tok > 0 ? rmin : 0.0;
+  stats[3] = n_tok > 0 ? rmax : 0.0;
+  stats[4] = (double)n_tok;
+  stats[5] = (double)clipped;
+}
+
 // SwiGLU gating of the feed-forward block (the "gating multiplication and nonlinearity" before Down,
 // [review §5.1]): a = SiLU(g) * u with SiLU(v) = v / (1 + exp(-v)). fp64, element-wise.
 void orc_silu_mul(const double* gate, const double* up, int64_t count, double* out) {
