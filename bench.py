@@ -19,6 +19,7 @@ cache):
                       down 5120x27648), heavy-tailed weights (Student-t nu = 4 x 0.02 x 2^e per 16-block)
   c5_prefill_m8192    8192 tokens through the 7B gate|up with LoRA and SiLU*up on the MFMA kernel, then the group
                       advantages of 8 groups of 8 Bernoulli(0.3) rewards
+  f4_grpo_surrogate_8192  GRPO token ratios and clipped surrogate over the same 64 responses x 128 tokens
 plus `hbm_stream_read` (a plain streaming-read kernel over 4 GiB: the achievable read rate, the second roofline
 denominator) and `cpu_baseline` (the fp64 oracle on the host, all threads and one thread).
 
@@ -294,6 +295,34 @@ def run_c5(base, shape, dev, steps, warmup):
     return r
 
 
+def run_f4(dev, steps, warmup):
+    """GRPO token ratios and clipped surrogate over 8 prompts x 8 responses x 128 tokens (the prefill batch): seeded
+    log-probabilities (log pi_b = -Exponential(2) per token, log pi_theta = log pi_b + N(0, 0.3)), advantages of
+    Bernoulli(0.3) rewards from the device's group advantage."""
+    import numpy as np
+    import torch
+    import nvfp4_weight_only_amd as qn
+    import synth
+    n_seq, t = 64, 128
+    rng = np.random.default_rng(20251013)
+    lp_old = torch.from_numpy((-rng.exponential(2.0, (n_seq, t))).astype(np.float32)).to(dev)
+    lp = lp_old + torch.from_numpy(rng.normal(0.0, 0.3, (n_seq, t)).astype(np.float32)).to(dev)
+    lengths = torch.from_numpy(rng.integers(1, t + 1, n_seq).astype(np.int32)).to(dev)
+    rewards = torch.from_numpy(synth.bernoulli_f32(synth.seed_for(5, 0, "rewards"), (8, 8), 0.3)).to(dev)
+    adv = qn.group_advantage(rewards).reshape(-1)
+    out = {}
+
+    def step(i):
+        out["r"] = qn.grpo_surrogate(lp, lp_old, lengths, adv)
+
+    tm = time_steps(step, max(steps, 20), warmup)
+    nbytes = n_seq * t * 4 * 4 + n_seq * 8  # logp, logp_old in; surrogate, grad out; lengths, advantages
+    st = qn.grpo_stats(out["r"][2])
+    return {"us_per_call": tm * 1e6, "tokens": int(st["tokens"]), "algorithmic_bytes": nbytes,
+            "GBps": nbytes / tm / 1e9, "bound": "latency (one workgroup; 128 KB moved)",
+            "loss": st["loss"], "clipped_tokens": int(st["clipped"])}
+
+
 # ---- the oracle on the host ----------------------------------------------------------------------------------------
 def cpu_threads():
     try:
@@ -539,6 +568,9 @@ def main():
         if want("c5"):
             log("config 5: prefill 8192 tokens")
             cfg["c5_prefill_m8192"] = run_c5(base, shape, dev, args.steps, args.warmup)
+        if want("f4"):
+            log("GRPO ratio and clipped surrogate, 8192 tokens")
+            cfg["f4_grpo_surrogate_8192"] = run_f4(dev, args.steps, args.warmup)
         del layers
         torch.cuda.empty_cache()
         if want("c4"):

@@ -243,6 +243,30 @@ qn_status grpo_group_advantage(const float* rewards, int32_t groups, int32_t g, 
  * reads reach on the same device. bytes % 16 == 0 (QN_ERR_SHAPE), src 16-byte and sink 4-byte aligned (QN_ERR_ALIGN). */
 qn_status qn_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
+/* Statistics of one grpo_clipped_surrogate call (device struct, written by the call). */
+typedef struct {
+  double loss;       /* -(sum over valid tokens of w * surrogate), w as set by `agg` */
+  double ratio_mean; /* mean token ratio over valid tokens (0 if none) */
+  float ratio_min, ratio_max;
+  int64_t tokens;    /* valid tokens */
+  int64_t clipped;   /* tokens whose clipped term is strictly the smaller (their gradient is zero) */
+} qn_grpo_stats;
+
+/* GRPO token ratio and clipped surrogate [review §2.3]: for token t of response i (sampled by the behavior policy),
+ *   rho = exp(logp[i][t] - logp_old[i][t]),  s = min(rho A_i, clip(rho, 1 - clip_low, 1 + clip_high) A_i),
+ * with A_i the response's group-relative advantage (grpo_group_advantage). loss = -(sum w s) with w = 1 / (valid
+ * tokens of the batch) (agg 0) or w = 1 / (responses with tokens x tokens of response i) (agg 1). The pages fix
+ * neither the widths nor the combination; both are arguments here. Per token (optional outputs, [n_seq][ld] f32, 0 past
+ * the response's length): the surrogate and grad = d loss / d logp = -w rho A where the unclipped term is the smaller
+ * (ties included), else 0.
+ *   logp, logp_old [n_seq][ld] f32; lengths [n_seq] int32 (valid tokens, clamped to [0, t_max]); adv [n_seq] f32; all
+ *   device. fp64 arithmetic from the f32 inputs; one workgroup, statistics summed in a fixed order (deterministic).
+ * Errors: QN_ERR_SHAPE (negative sizes, ld < t_max with n_seq > 0), QN_ERR_VALUE (clip_low outside [0, 1), clip_high < 0, bad agg,
+ * non-finite widths), QN_ERR_NULL. */
+qn_status grpo_clipped_surrogate(const float* logp, const float* logp_old, int64_t ld, const int32_t* lengths,
+                                 const float* adv, int32_t n_seq, int32_t t_max, float clip_low, float clip_high,
+                                 int32_t agg, float* surrogate, float* grad, qn_grpo_stats* stats, void* stream);
+
 /* Static description of a status code (host). */
 const char* qn_status_string(qn_status s);
 

@@ -28,7 +28,7 @@ EXPORTS = ["nvfp4_quantize", "nvfp4_tiled_codes_bytes", "nvfp4_tiled_scales_byte
            "aqn_noise",
            "nvfp4_lora_linear_workspace", "nvfp4_lora_linear", "nvfp4_lora_linear_workspace_opts",
            "nvfp4_lora_linear_opts", "nvfp4_lora_linear_noalloc", "nvfp4_lora_linear_noalloc_max_bytes",
-           "aqn_sigma", "grpo_group_advantage", "qn_stream_read", "qn_status_string"]
+           "aqn_sigma", "grpo_group_advantage", "grpo_clipped_surrogate", "qn_stream_read", "qn_status_string"]
 
 
 class QnError(RuntimeError):
@@ -97,6 +97,7 @@ def _load():
         "nvfp4_lora_linear_noalloc_max_bytes": ([], sz),
         "aqn_sigma": ([i32, f64, f64], f64),
         "qn_stream_read": ([P, sz, P, P], i32),
+        "grpo_clipped_surrogate": ([P, P, i64, P, P, i32, i32, f32, f32, i32, P, P, P, P], i32),
         "grpo_group_advantage": ([P, i32, i32, f32, P, P], i32),
         "qn_status_string": ([i32], ctypes.c_char_p),
     }
@@ -354,6 +355,33 @@ def lora_linear_noalloc(x: torch.Tensor, projs: Sequence[Projection], aqn: Optio
     m, k = x.shape
     _check(lib.nvfp4_lora_linear_noalloc(_ptr(x), m, k, x.stride(0), ctypes.byref(aqn.c) if aqn is not None else None,
                                          arr, len(projs), epilogue, _stream(stream)), "nvfp4_lora_linear_noalloc")
+
+
+GRPO_STATS_DTYPE = [("loss", "f8"), ("ratio_mean", "f8"), ("ratio_min", "f4"), ("ratio_max", "f4"),
+                    ("tokens", "i8"), ("clipped", "i8")]
+GRPO_STATS_BYTES = 40
+
+
+def grpo_surrogate(logp: torch.Tensor, logp_old: torch.Tensor, lengths: torch.Tensor, adv: torch.Tensor,
+                   clip_low: float = 0.2, clip_high: float = 0.2, agg: int = 0, stream=None):
+    """grpo_clipped_surrogate: logp, logp_old [n_seq, t_max] f32; lengths int32 [n_seq]; adv f32 [n_seq] (device) ->
+    (surrogate [n_seq, t_max] f32, grad [n_seq, t_max] f32, stats: a 40-byte device buffer, see grpo_stats)."""
+    n_seq, t_max = logp.shape
+    with _on(stream):
+        sur = torch.empty(n_seq, t_max, dtype=torch.float32, device=logp.device)
+        grad = torch.empty_like(sur)
+        stats = torch.zeros(GRPO_STATS_BYTES, dtype=torch.uint8, device=logp.device)
+    _check(lib.grpo_clipped_surrogate(_ptr(logp), _ptr(logp_old), logp.stride(0), _ptr(lengths), _ptr(adv), n_seq,
+                                      t_max, clip_low, clip_high, agg, _ptr(sur), _ptr(grad), _ptr(stats),
+                                      _stream(stream)), "grpo_clipped_surrogate")
+    return sur, grad, stats
+
+
+def grpo_stats(stats: torch.Tensor) -> dict:
+    """The device statistics buffer of grpo_surrogate as a dict (copies to the host)."""
+    import numpy as np
+    rec = np.frombuffer(stats.cpu().numpy().tobytes(), dtype=np.dtype(GRPO_STATS_DTYPE))[0]
+    return {k: rec[k].item() for k, _ in GRPO_STATS_DTYPE}
 
 
 def stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:

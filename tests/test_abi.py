@@ -110,6 +110,16 @@ def test_validation_errors(qn):
     assert L.aqn_noise(1, 0, 0, 1, 2, 32, None, 32, None) == qn.QN_ERR_NULL
     assert L.aqn_noise(1, 0, 0, 1, 2, 32, P(258), 32, None) == qn.QN_ERR_ALIGN
     assert L.aqn_noise(1, 0, 0, 1, 0, 32, None, 32, None) == qn.QN_OK
+    # GRPO surrogate: shapes, widths, aggregation, NULL statistics
+    gs = L.grpo_clipped_surrogate
+    assert gs(fake, fake, 8, fake, fake, -1, 8, 0.2, 0.2, 0, None, None, fake, None) == qn.QN_ERR_SHAPE
+    assert gs(fake, fake, 4, fake, fake, 2, 8, 0.2, 0.2, 0, None, None, fake, None) == qn.QN_ERR_SHAPE
+    assert gs(fake, fake, 8, fake, fake, 2, 8, 1.0, 0.2, 0, None, None, fake, None) == qn.QN_ERR_VALUE
+    assert gs(fake, fake, 8, fake, fake, 2, 8, 0.2, -0.1, 0, None, None, fake, None) == qn.QN_ERR_VALUE
+    assert gs(fake, fake, 8, fake, fake, 2, 8, 0.2, float("nan"), 0, None, None, fake, None) == qn.QN_ERR_VALUE
+    assert gs(fake, fake, 8, fake, fake, 2, 8, 0.2, 0.2, 2, None, None, fake, None) == qn.QN_ERR_VALUE
+    assert gs(fake, fake, 8, fake, fake, 2, 8, 0.2, 0.2, 0, None, None, None, None) == qn.QN_ERR_NULL
+    assert gs(None, fake, 8, fake, fake, 2, 8, 0.2, 0.2, 0, None, None, fake, None) == qn.QN_ERR_NULL
     # advantage
     assert L.grpo_group_advantage(fake, 8, 8, -1.0, fake, None) == qn.QN_ERR_VALUE
     assert L.grpo_group_advantage(None, 8, 8, 1e-6, fake, None) == qn.QN_ERR_NULL
