@@ -59,6 +59,7 @@ def lib():
             "orc_group_advantage": ([P, i32, i32, dbl, P], None),
             "orc_silu_mul": ([P, P, i64, P], None),
             "orc_grpo_surrogate": ([P, P, i64, P, P, i32, i32, dbl, dbl, i32, P, P, P], None),
+            "orc_lora_linear_backward": ([P, i64, i64, P, i64, P, P, f32, P, P, i32, dbl, P, P, P], None),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -209,6 +210,28 @@ def lora_linear(h: np.ndarray, codes: np.ndarray, s_b: np.ndarray, s_g: float, A
     y = np.empty((m, n), dtype=np.float64)
     lib().orc_lora_linear(_p(h), m, k, k, _p(codes), _p(s_b), float(s_g), n, _p(A), _p(B), r, float(lam), _p(y))
     return y
+
+
+def lora_linear_backward(g: np.ndarray, h: np.ndarray, codes: np.ndarray, s_b: np.ndarray, s_g: float,
+                         A: np.ndarray | None, B: np.ndarray | None, lam: float, want=("dh", "dA", "dB")):
+    """Backward of lora_linear through the frozen NVFP4 weight. g bf16 [m, n] (dL/dy), h bf16 [m, k], NVFP4 W [n, k]
+    canonical, A bf16 [r, k], B bf16 [n, r] -> dict of fp64 dh [m, k], dA [r, k], dB [n, r] (those in `want`)."""
+    g = _c(g, np.uint16)
+    h = _c(h, np.uint16)
+    m, n = g.shape
+    k = h.shape[1]
+    assert h.shape[0] == m and codes.shape == (n, k // 2)
+    r = 0
+    if A is not None:
+        A = _c(A, np.uint16)
+        B = _c(B, np.uint16)
+        r = A.shape[0]
+        assert A.shape == (r, k) and B.shape == (n, r)
+    out = {"dh": np.empty((m, k)) if "dh" in want else None, "dA": np.empty((r, k)) if "dA" in want else None,
+           "dB": np.empty((n, r)) if "dB" in want else None}
+    lib().orc_lora_linear_backward(_p(g), m, n, _p(h), k, _p(_c(codes, np.uint8)), _p(_c(s_b, np.uint8)), float(s_g),
+                                   _p(A), _p(B), r, float(lam), _p(out["dh"]), _p(out["dA"]), _p(out["dB"]))
+    return {key: v for key, v in out.items() if v is not None}
 
 
 def dense_linear(h: np.ndarray, w: np.ndarray) -> np.ndarray:

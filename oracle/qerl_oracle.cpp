@@ -362,6 +362,72 @@ void orc_lora_linear(const uint16_t* h, int64_t m, int64_t k, int64_t ldh, const
   delete[] t;
 }
 
+// Backward of the LoRA-adapted linear through the frozen NVFP4 base [review §2.1: the backbone is frozen, gradients
+// update A and B, and may need to pass through the frozen projection to reach an earlier adapter; §6, steps 8-10].
+// With the upstream gradient g = dL/dy [m x n] (bf16) of y = W_hat h + lambda B (A h):
+//   u = B^T g per token   (u[i][j] = sum_o B[o][j] g[i][o]),   t = A h per token (t[i][j] = sum_c A[j][c] h[i][c]),
+//   dh[i][c] = sum_o W_hat[o][c] g[i][o] + lambda sum_j A[j][c] u[i][j],
+//   dA[j][c] = lambda sum_i u[i][j] h[i][c],     dB[o][j] = lambda sum_i g[i][o] t[i][j].
+// Everything in fp64 from the exact inputs (W_hat exact); any output pointer may be null.
+void orc_lora_linear_backward(const uint16_t* g, int64_t m, int64_t n, const uint16_t* h, int64_t k,
+                              const uint8_t* codes, const uint8_t* s_b, float s_g, const uint16_t* A,
+                              const uint16_t* B, int r, double lambda, double* dh, double* dA, double* dB) {
+  const bool lora = A && B && r > 0;
+  double* u = new double[(size_t)(m * (r > 0 ? r : 1))];
+  double* t = new double[(size_t)(m * (r > 0 ? r : 1))];
+  if (lora)
+    for (int64_t i = 0; i < m; ++i)
+      for (int j = 0; j < r; ++j) {
+        double su = 0.0, st = 0.0;
+        for (int64_t o = 0; o < n; ++o) su += bf16_value(B[o * r + j]) * bf16_value(g[i * n + o]);
+        for (int64_t c = 0; c < k; ++c) st += bf16_value(A[(int64_t)j * k + c]) * bf16_value(h[i * k + c]);
+        u[i * r + j] = su;
+        t[i * r + j] = st;
+      }
+  if (dh) {
+    for (int64_t x = 0; x < m * k; ++x) dh[x] = 0.0;
+    double* wrow = new double[(size_t)k];
+    for (int64_t o = 0; o < n; ++o) {
+      for (int64_t c = 0; c < k; ++c) {
+        uint8_t byte = codes[o * (k / 2) + c / 2];
+        unsigned q = (c & 1) ? (byte >> 4) : (byte & 15u);
+        wrow[c] = (double)s_g * (e4m3_value(s_b[o * (k / 16) + c / 16]) * e2m1_value(q));
+      }
+      for (int64_t i = 0; i < m; ++i) {
+        const double gi = bf16_value(g[i * n + o]);
+        if (gi == 0.0) continue;
+        for (int64_t c = 0; c < k; ++c) dh[i * k + c] += wrow[c] * gi;
+      }
+    }
+    delete[] wrow;
+    if (lora)
+      for (int64_t i = 0; i < m; ++i)
+        for (int64_t c = 0; c < k; ++c) {
+          double acc = 0.0;
+          for (int j = 0; j < r; ++j) acc += bf16_value(A[(int64_t)j * k + c]) * u[i * r + j];
+          dh[i * k + c] += lambda * acc;
+        }
+  }
+  if (dA)
+    for (int j = 0; j < r; ++j)
+      for (int64_t c = 0; c < k; ++c) {
+        double acc = 0.0;
+        if (lora)
+          for (int64_t i = 0; i < m; ++i) acc += u[i * r + j] * bf16_value(h[i * k + c]);
+        dA[(int64_t)j * k + c] = lambda * acc;
+      }
+  if (dB)
+    for (int64_t o = 0; o < n; ++o)
+      for (int j = 0; j < r; ++j) {
+        double acc = 0.0;
+        if (lora)
+          for (int64_t i = 0; i < m; ++i) acc += bf16_value(g[i * n + o]) * t[i * r + j];
+        dB[o * r + j] = lambda * acc;
+      }
+  delete[] u;
+  delete[] t;
+}
+
 // Dense bf16 linear y = x W^T (no quantization), used by the tests as the "BF16 LoRA" comparison baseline.
 void orc_dense_linear(const uint16_t* h, int64_t m, int64_t k, const uint16_t* w, int64_t n, double* y) {
   for (int64_t o = 0; o < n; ++o)
