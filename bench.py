@@ -19,6 +19,7 @@ cache):
                       down 5120x27648), heavy-tailed weights (Student-t nu = 4 x 0.02 x 2^e per 16-block)
   c5_prefill_m8192    8192 tokens through the 7B gate|up with LoRA and SiLU*up on the MFMA kernel, then the group
                       advantages of 8 groups of 8 Bernoulli(0.3) rewards
+  f2_backward_gate_m8192  backward of the 7B gate projection at 8192 tokens: dh through the frozen NVFP4 weight, dA, dB
   f4_grpo_surrogate_8192  GRPO token ratios and clipped surrogate over the same 64 responses x 128 tokens
 plus `hbm_stream_read` (a plain streaming-read kernel over 4 GiB: the achievable read rate, the second roofline
 denominator) and `cpu_baseline` (the fp64 oracle on the host, all threads and one thread).
@@ -323,6 +324,36 @@ def run_f4(dev, steps, warmup):
             "loss": st["loss"], "clipped_tokens": int(st["clipped"])}
 
 
+def run_f2(base, shape, dev, steps, warmup):
+    """Backward of the 7B gate projection (18944 x 3584, rank-32 LoRA) at the 8192-token prefill batch: dh through
+    the frozen NVFP4 weight, dA and dB. The upstream gradient is seeded N(0, 1) bf16, h the prefill's input."""
+    import torch
+    import nvfp4_weight_only_amd as qn
+    import synth
+    m, n, k = 8192, shape.inter, shape.hidden
+    s = lambda t: synth.seed_for(5, 1, t)
+    g = bf16_dev(synth.normal_bf16(s("eps_norm1"), (m, n)), dev)
+    h = bf16_dev(synth.normal_bf16(s("x"), (m, k)), dev)
+    A, B = base.lora["gate"]
+    w = base.w["gate"]
+    stream = torch.cuda.current_stream()
+    out = {}
+
+    def run(want):
+        out["r"] = qn.lora_linear_backward(g, h, w, A, B, 2.0, torch.float32, want)
+
+    nsteps = max(5, steps // 2)
+    t_all = time_steps(lambda i: run(("dh", "dA", "dB")), nsteps, max(1, warmup // 2))
+    t_dh = time_steps(lambda i: run(("dh",)), nsteps, 1)
+    fl_dh = 2 * m * n * k + 2 * m * shape.rank * (n + k)  # W^T g, and u = B^T g with A^T u
+    fl_all = 2 * m * n * k + 2 * m * shape.rank * (2 * n + 2 * k)  # + t = A h, dA, dB
+    return {"us_per_step": t_all * 1e6, "flops_per_step": fl_all, "step_TFLOPs": fl_all / t_all / 1e12,
+            "dh_us": t_dh * 1e6, "dh_TFLOPs": fl_dh / t_dh / 1e12,
+            "dh_frac_of_mfma_peak": fl_dh / t_dh / 1e12 / MFMA_PEAK_TFLOPS,
+            "kernels": "k_bt + k_skinny (u) + k_dh (dh, bf16 MFMA, weight dequantized to LDS transposed); "
+                       "k_skinny (t) + k_outer/k_outer_sum (dA, dB)"}
+
+
 # ---- the oracle on the host ----------------------------------------------------------------------------------------
 def cpu_threads():
     try:
@@ -568,6 +599,9 @@ def main():
         if want("c5"):
             log("config 5: prefill 8192 tokens")
             cfg["c5_prefill_m8192"] = run_c5(base, shape, dev, args.steps, args.warmup)
+        if want("f2"):
+            log("backward through the 7B gate weight, 8192 tokens")
+            cfg["f2_backward_gate_m8192"] = run_f2(base, shape, dev, args.steps, args.warmup)
         if want("f4"):
             log("GRPO ratio and clipped surrogate, 8192 tokens")
             cfg["f4_grpo_surrogate_8192"] = run_f4(dev, args.steps, args.warmup)

@@ -229,6 +229,28 @@ qn_status nvfp4_lora_linear_noalloc(const uint16_t* x, int64_t m, int64_t k, int
 /* Bytes of the scratch array behind nvfp4_lora_linear_noalloc (host, pure). */
 size_t nvfp4_lora_linear_noalloc_max_bytes(void);
 
+/* Backward of nvfp4_lora_linear (one projection, no norm) through the frozen NVFP4 weight [review §2.1: the backbone is
+ * frozen and the gradients update A and B, but may pass through the frozen projection to reach an earlier adapter;
+ * §6, steps 8-10]. For y = s_g W_hat h + lambda B (A h) and the upstream gradient g = dL/dy:
+ *   dh = s_g W_hat^T g + lambda A^T (B^T g)       [m][lddh], bf16 or f32 (dh_dtype), NULL = not computed
+ *   d_a = lambda (B^T g)^T h                      [r][k] f32 row-major, NULL = not computed
+ *   d_b = lambda g^T (A h)                        [n][r] f32 row-major, NULL = not computed
+ * g [m][ldg] bf16 and h [m][ldh] bf16 (the forward's input; needed for d_a and d_b), 2-byte aligned (16-byte aligned
+ * rows are read 16 bytes at a time); the weight in QN_LAYOUT_TILED as for the forward; lora_a [r][k], lora_b [n][r] bf16 (r <= 64; r == 0: no
+ * adapter, only dh). bf16 MFMAs with f32 accumulation; the rank-r intermediates are kept in f32 and enter the MFMAs as
+ * bf16 hi + lo parts. The weight is read transposed from the tiled layout (dequantized exactly to bf16 in LDS).
+ * Results do not depend on scheduling (fixed summation orders). Workspace: nvfp4_lora_linear_backward_workspace
+ * (256-byte aligned; none needed when r == 0). Errors: QN_ERR_SHAPE, QN_ERR_ALIGN, QN_ERR_NULL, QN_ERR_VALUE (bad
+ * dh_dtype, non-finite lambda), QN_ERR_WORKSPACE, QN_ERR_UNSUPPORTED (r > 64); nothing is launched on an error. */
+qn_status nvfp4_lora_linear_backward(const uint16_t* g, int64_t m, int64_t n, int64_t ldg, const uint16_t* h, int64_t k,
+                                     int64_t ldh, const uint8_t* codes, const uint8_t* block_scales,
+                                     const float* tensor_scale, const uint16_t* lora_a, const uint16_t* lora_b,
+                                     int32_t r, float lambda, void* dh, int32_t dh_dtype, int64_t lddh, float* d_a,
+                                     float* d_b, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of nvfp4_lora_linear_backward (host, pure). */
+size_t nvfp4_lora_linear_backward_workspace(int64_t m, int64_t n, int64_t k, int32_t r);
+
 /* Exponential AQN noise schedule [review §5.2]: sigma_0 = 0, sigma_k = start * (end/start)^((k-1)/8), k = 1..9
  * (stages beyond 9 continue the same geometric decay). Host, pure, fp64. */
 double aqn_sigma(int32_t stage, double sigma_start, double sigma_end);

@@ -28,7 +28,8 @@ EXPORTS = ["nvfp4_quantize", "nvfp4_tiled_codes_bytes", "nvfp4_tiled_scales_byte
            "aqn_noise",
            "nvfp4_lora_linear_workspace", "nvfp4_lora_linear", "nvfp4_lora_linear_workspace_opts",
            "nvfp4_lora_linear_opts", "nvfp4_lora_linear_noalloc", "nvfp4_lora_linear_noalloc_max_bytes",
-           "aqn_sigma", "grpo_group_advantage", "grpo_clipped_surrogate", "qn_stream_read", "qn_status_string"]
+           "aqn_sigma", "grpo_group_advantage", "grpo_clipped_surrogate", "qn_stream_read", "qn_status_string",
+           "nvfp4_lora_linear_backward", "nvfp4_lora_linear_backward_workspace"]
 
 
 class QnError(RuntimeError):
@@ -97,6 +98,9 @@ def _load():
         "nvfp4_lora_linear_noalloc_max_bytes": ([], sz),
         "aqn_sigma": ([i32, f64, f64], f64),
         "qn_stream_read": ([P, sz, P, P], i32),
+        "nvfp4_lora_linear_backward": ([P, i64, i64, i64, P, i64, i64, P, P, P, P, P, i32, f32, P, i32, i64, P, P, P, sz,
+                                        P], i32),
+        "nvfp4_lora_linear_backward_workspace": ([i64, i64, i64, i32], sz),
         "grpo_clipped_surrogate": ([P, P, i64, P, P, i32, i32, f32, f32, i32, P, P, P, P], i32),
         "grpo_group_advantage": ([P, i32, i32, f32, P, P], i32),
         "qn_status_string": ([i32], ctypes.c_char_p),
@@ -388,6 +392,31 @@ def stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
     """qn_stream_read over the whole of `buf` (a measurement helper: plain streaming reads)."""
     _check(lib.qn_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)),
            "qn_stream_read")
+
+
+def lora_linear_backward(g: torch.Tensor, h: Optional[torch.Tensor], weight: NVFP4Weight,
+                         lora_a: Optional[torch.Tensor], lora_b: Optional[torch.Tensor], lam: float = 1.0,
+                         dh_dtype=torch.float32, want=("dh", "dA", "dB"), stream=None):
+    """Backward of one projection through the frozen tiled NVFP4 weight: g = dL/dy bf16 [m, n], h = the forward's
+    input bf16 [m, k] -> dict with dh [m, k] (dh_dtype), dA f32 [r, k], dB f32 [n, r] (those in `want`)."""
+    m, n = g.shape
+    k = weight.k
+    r = 0 if lora_a is None else lora_a.shape[0]
+    need = int(lib.nvfp4_lora_linear_backward_workspace(m, n, k, r))
+    with _on(stream):
+        out = {"dh": torch.empty(m, k, dtype=dh_dtype, device=g.device) if "dh" in want else None,
+               "dA": torch.empty(r, k, dtype=torch.float32, device=g.device) if ("dA" in want and r) else None,
+               "dB": torch.empty(n, r, dtype=torch.float32, device=g.device) if ("dB" in want and r) else None}
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=g.device)
+    dh = out["dh"]
+    _check(lib.nvfp4_lora_linear_backward(_ptr(g), m, n, g.stride(0), _ptr(h), k, h.stride(0) if h is not None else k,
+                                          _ptr(weight.codes), _ptr(weight.scales), _ptr(weight.tensor_scale),
+                                          _ptr(lora_a), _ptr(lora_b), r, lam, _ptr(dh),
+                                          F32 if dh_dtype == torch.float32 else BF16, dh.stride(0) if dh is not None else k,
+                                          _ptr(out["dA"]), _ptr(out["dB"]), _ptr(ws), ws.numel(), _stream(stream)),
+           "nvfp4_lora_linear_backward")
+    _keep_for(ws, stream)
+    return {key: v for key, v in out.items() if v is not None}
 
 
 def group_advantage(rewards: torch.Tensor, eps: float = 1e-6, stream=None) -> torch.Tensor:

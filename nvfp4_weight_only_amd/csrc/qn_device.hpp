@@ -47,6 +47,38 @@ __device__ inline float e4m3_to_f32(uint32_t byte) {
   return (byte & 0x80u) ? -mag : mag;
 }
 
+// Loads. Every load issued ahead of the weight stream is a buffer load or a global-segment load, never a flat one:
+// a pending flat load may be an LDS access, which forces the compiler to drain all loads at every later wait and
+// so would serialize the double-buffered stream.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit data format (gfx9 family)
+constexpr int kNonTemporal = 2;                 // streamed once: do not keep in cache
+constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset past every num_records: the load returns 0
+
+// Wave-uniform copies (readfirstlane) of values the compiler cannot prove uniform on its own, so that buffer
+// descriptors built from them stay in SGPRs.
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Raw buffer descriptor over [base, base + bytes); bytes < 2^31 (checked on the host).
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)uniform64((uint64_t)base), (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane((uint32_t)bytes), kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// Load through a pointer known to address global memory.
+template <class T>
+__device__ __forceinline__ T gload(const T* p) {
+  return *reinterpret_cast<const __attribute__((address_space(1))) T*>(reinterpret_cast<uintptr_t>(p));
+}
+
 // An MFMA's result registers may be read by a non-MFMA instruction (a VALU operation, an LDS or memory store) only
 // once the matrix core has written every pass of them; the program must place enough independent instructions in
 // between. Within a basic block the compiler counts them; across a branch or a loop exit it has been seen to count

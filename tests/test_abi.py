@@ -120,6 +120,26 @@ def test_validation_errors(qn):
     assert gs(fake, fake, 8, fake, fake, 2, 8, 0.2, 0.2, 2, None, None, fake, None) == qn.QN_ERR_VALUE
     assert gs(fake, fake, 8, fake, fake, 2, 8, 0.2, 0.2, 0, None, None, None, None) == qn.QN_ERR_NULL
     assert gs(None, fake, 8, fake, fake, 2, 8, 0.2, 0.2, 0, None, None, fake, None) == qn.QN_ERR_NULL
+    # backward: shapes, rank, dtype, NULLs, workspace
+    order = ("g", "m", "n", "ldg", "h", "k", "ldh", "c", "s", "sg", "a", "b", "r", "lam", "dh", "dt", "lddh", "da", "db",
+             "ws", "wsb", "st")
+
+    def bw(**kw):
+        args = dict(g=fake, m=4, n=64, ldg=64, h=fake, k=128, ldh=128, c=fake, s=fake, sg=fake, a=fake, b=fake, r=32,
+                    lam=2.0, dh=fake, dt=1, lddh=128, da=fake, db=fake, ws=P(1 << 20), wsb=1 << 30, st=None)
+        args.update(kw)
+        return L.nvfp4_lora_linear_backward(*[args[key] for key in order])
+
+    assert bw(k=120) == qn.QN_ERR_SHAPE
+    assert bw(ldg=32) == qn.QN_ERR_SHAPE
+    assert bw(r=65) == qn.QN_ERR_UNSUPPORTED
+    assert bw(dt=5) == qn.QN_ERR_VALUE
+    assert bw(lam=float("inf")) == qn.QN_ERR_VALUE
+    assert bw(g=None) == qn.QN_ERR_NULL
+    assert bw(h=None) == qn.QN_ERR_NULL
+    assert bw(wsb=16) == qn.QN_ERR_WORKSPACE
+    assert bw(g=P(257)) == qn.QN_ERR_ALIGN
+    assert bw(m=0) == qn.QN_OK
     # advantage
     assert L.grpo_group_advantage(fake, 8, 8, -1.0, fake, None) == qn.QN_ERR_VALUE
     assert L.grpo_group_advantage(None, 8, 8, 1e-6, fake, None) == qn.QN_ERR_NULL
