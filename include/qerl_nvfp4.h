@@ -162,7 +162,11 @@ qn_status aqn_rmsnorm(const uint16_t* x, int64_t m, int64_t d, int64_t ldx, cons
 qn_status aqn_noise(uint64_t seed, uint64_t subseed, uint64_t row_offset, int64_t draw_rows, int64_t m, int64_t d,
                     float* eps, int64_t ld, void* stream);
 
-/* Workspace bytes nvfp4_lora_linear needs for these arguments (host, pure). */
+/* Workspace bytes nvfp4_lora_linear needs for these arguments (host, pure).
+ * The workspace must be zero-filled before its first use (hipMemset once, or allocated zeroed). Every call leaves
+ * its control words (split-k arrival counters, the fused decode kernel's counter and LoRA-down partials) zero again,
+ * so a workspace can be reused by any later call ordered after it; calls that may run at the same time need
+ * workspaces of their own. */
 size_t nvfp4_lora_linear_workspace(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj);
 
 /* The rollout-decode linear layer [review §2.1 forward map, §3.2, §5.1]:
@@ -185,7 +189,12 @@ typedef enum {
   QN_KERNEL_GENERAL = 1, /* the general streaming kernel, one launch per 128 tokens; any m */
   QN_KERNEL_DECODE = 2,  /* the decode streaming kernel (activations held in LDS, optional split k); m <= 32 and a
                             split of the rows and k that fits its LDS, else QN_ERR_UNSUPPORTED */
-  QN_KERNEL_MANY = 3     /* the many-token MFMA kernel; m > 128, else QN_ERR_UNSUPPORTED */
+  QN_KERNEL_MANY = 3,    /* the many-token MFMA kernel; m > 128, else QN_ERR_UNSUPPORTED */
+  QN_KERNEL_FUSED = 4    /* the decode kernel with the norm, the activation conversion and the LoRA-down folded in:
+                            one launch per call; m <= 16, a cut that fits its LDS (with the norm: the whole row in one
+                            k-chunk, k <= 3968), not with the phase flags, else QN_ERR_UNSUPPORTED. AUTO does not
+                            take it: on the 7B decode shapes it measured slower than the prologue and the other
+                            kernels at 1 to 16 tokens. */
 } qn_kernel;
 
 /* Explicit options of one nvfp4_lora_linear_opts call. Zero-initialised, it asks for the library's defaults. These
@@ -193,8 +202,9 @@ typedef enum {
  * variables and keeps no settings between calls. */
 typedef struct {
   int32_t kernel;         /* qn_kernel */
-  int32_t decode_kchunks; /* QN_KERNEL_DECODE: k-chunks of the split-k cut, 1..64 (0 = the library's cut) */
-  int32_t decode_depth;   /* QN_KERNEL_DECODE: weight tiles in flight per wave: 0 (the default, 3), 2 or 3 */
+  int32_t decode_kchunks; /* QN_KERNEL_DECODE / _FUSED: k-chunks of the split-k cut, 1..64 (0 = the library's cut) */
+  int32_t decode_depth;   /* QN_KERNEL_DECODE: weight tiles in flight per wave: 0 (the default, 3), 2 or 3;
+                             QN_KERNEL_FUSED takes 0 or 3; with AUTO, 2 rules the fused kernel out */
   int32_t general_rows;   /* QN_KERNEL_GENERAL: row groups per workgroup and waves per workgroup, both 0 (the */
   int32_t general_waves;  /* library's shape) or both > 0 naming a built pair (else QN_ERR_UNSUPPORTED) */
   int32_t elem_store;     /* 0 or 1; many-token kernel: 1 stores outputs element by element instead of in 16-byte
@@ -221,7 +231,8 @@ qn_status nvfp4_lora_linear_opts(const uint16_t* x, int64_t m, int64_t k, int64_
  * A call needing more (nvfp4_lora_linear_workspace above the maximum) returns QN_ERR_WORKSPACE and launches nothing.
  * Every call on one GPU shares that GPU's array, so calls that overlap on one GPU (on different streams, or from
  * different threads without ordering) race; calls ordered on one stream are safe. The array keeps the last call's
- * contents; what a call needs zeroed it clears itself. Errors: as nvfp4_lora_linear, plus QN_ERR_HIP if the array's
+ * contents; it starts zeroed (static device memory) and every call leaves its control words zero, as the workspace
+ * contract above asks. Errors: as nvfp4_lora_linear, plus QN_ERR_HIP if the array's
  * device address cannot be looked up. */
 qn_status nvfp4_lora_linear_noalloc(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const qn_aqn* aqn,
                                     const qn_proj* projs, int32_t nproj, int32_t epilogue, void* stream);

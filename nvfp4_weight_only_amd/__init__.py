@@ -22,7 +22,7 @@ BF16, F32 = 0, 1
 EPI_NONE, EPI_SILU_MUL = 0, 1
 RUN_PROLOGUE_ONLY, RUN_MAIN_ONLY = 0x100, 0x200
 
-KERNEL_AUTO, KERNEL_GENERAL, KERNEL_DECODE, KERNEL_MANY = range(4)
+KERNEL_AUTO, KERNEL_GENERAL, KERNEL_DECODE, KERNEL_MANY, KERNEL_FUSED = range(5)
 
 EXPORTS = ["nvfp4_quantize", "nvfp4_tiled_codes_bytes", "nvfp4_tiled_scales_bytes", "nvfp4_dequantize", "aqn_rmsnorm",
            "aqn_noise",
@@ -293,7 +293,8 @@ def _keep_for(t: Optional[torch.Tensor], stream) -> None:
 
 
 class Workspace:
-    """Grow-only device workspace for nvfp4_lora_linear (allocated by torch, outside the timed calls)."""
+    """Grow-only device workspace for nvfp4_lora_linear (allocated zero-filled by torch, outside the timed calls; the
+    library leaves its control words zero after every call)."""
 
     def __init__(self, device="cuda"):
         self.device = device
@@ -303,7 +304,7 @@ class Workspace:
         if self.buf.numel() < nbytes:
             # the old buffer's memory is recycled only after every stream it was used on reaches this point
             # (LinearCall records those streams on it)
-            self.buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
+            self.buf = torch.zeros(nbytes + 256, dtype=torch.uint8, device=self.device)
         return self.buf
 
 

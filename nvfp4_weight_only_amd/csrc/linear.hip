@@ -74,7 +74,7 @@ struct LinearArgs {
 
 // Workspace carve-up (256-byte aligned regions).
 struct Workspace {
-  size_t xs, xsc, rstd, tok_p, t_part, t_fin, pbuf, cnt, total;
+  size_t xs, xsc, rstd, tok_p, t_part, t_fin, pbuf, t_fused, cnt, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -91,6 +91,12 @@ inline int64_t lora_chunks(int64_t k) {
   return ceil_div(KT, chunk_tiles(KT));
 }
 
+// Control words of the workspace, zero between calls: 256 split-k arrival counters, then the fused decode kernel's
+// consumer counter (kCountWords in all). Every call that runs the prologue zeroes them. The fused kernel's LoRA-down
+// partials (kFusedItemsMax items) are zero between calls too: they are their own ready flags.
+constexpr int kFusedItemsMax = 192;
+constexpr int kCountWords = 256 + 1;
+
 struct Opts;
 size_t gemv_pbuf_bytes(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj, const Opts& o);
 
@@ -106,7 +112,8 @@ Workspace workspace_layout(int64_t m, int64_t k, const qn_proj* projs, int32_t n
   w.t_part = off; off = align256(off + (size_t)nproj * (mp / 16) * kRankChunks * lora_chunks(k) * kWave * 32);
   w.t_fin = off;  off = align256(off + (m > kMaxTokensPerLaunch ? (size_t)nproj * (mp / 16) * kRankChunks * 2 * kWave * 16 : 0));
   w.pbuf = off;   off = align256(off + gemv_pbuf_bytes(m, k, projs, nproj, o));
-  w.cnt = off;    off = align256(off + 256 * 4);
+  w.t_fused = off; off = align256(off + (m <= 16 ? (size_t)kFusedItemsMax * kWave * 8 * 4 : 0));
+  w.cnt = off;    off = align256(off + kCountWords * 4);  // split-k counters, then the fused kernel's control words
   w.total = off;
   return w;
 }
@@ -1424,6 +1431,717 @@ __global__ void __launch_bounds__(kGWaves * kWave) k_gemv(GemvArgs g) {
   }
 }
 
+// ------------------------------------------------------------------------------------------------------------------
+// F: fused decode kernel for up to 16 tokens: the decode kernel above with the prologue folded in, one launch per
+// call. Each workgroup builds the activation fragments of its own k-chunk in LDS from x, which it reads once into
+// registers. With the norm (then the chunk is the whole row), the row statistics come from those registers in the
+// standalone norm's summation order (running sums of the 256 stand-in threads kept in LDS, one round per 256 chunks of
+// 8 channels), so h is bit for bit the norm's; the per-(token, k-tile) power-of-two exponents are the prologue's. When
+// every token shares gamma + sigma * noise, the workgroup computes that scale once into LDS.
+// The one step that needs all of a row's channels, the LoRA-down t = A h, is cut into items (projection, 32-rank
+// chunk, k-chunk). Workgroup i computes item i from its LDS fragments (f16 * 2^-p gives back h exactly above 2^-32 of
+// the tile's largest value) with 8 waves; its wave 15 adds their sums and stores the partial past the per-XCD caches,
+// bit-inverted, so that a word of it reads zero until it is written: the partials are their own ready flags. Item i
+// lives in workgroup i, workgroups are dispatched in index order and a producer waits for nothing before its item is
+// out, so the waits below always end. The LoRA wave of a block's chunk-0 workgroup (a consumer) polls its projections'
+// partials until every word is written (a wait bounded by a poll count: should it ever expire, the LoRA term becomes
+// NaN, so the outputs show it, rather than the wave spinning on), adds them in k-chunk order and continues as in the
+// decode kernel. The last consumer to finish its reads clears the partials and its counter, so they are zero between
+// calls; they must be zero before the first.
+constexpr int kFLoraWaves = 8;                                // waves computing a LoRA-down item
+constexpr int kFRedBytes = kFLoraWaves * 2 * kWave * 16;      // their sums (top of LDS)
+constexpr int kFMaxItems = kFusedItemsMax;
+constexpr int kFItemTiles = 4;                                // k-tiles per LoRA-down item without a split k
+constexpr uint32_t kFSpin = 1u << 24;                         // polls before a wait gives up (about a second)
+constexpr int kCoherent = 16;                                 // cache policy sc1: device-coherent, past the XCD's L2
+__host__ __device__ constexpr int fused_lds_top(int nr) {     // LDS bytes above the fragments and tile scales
+  return gemv_lred_bytes(nr, 1) > kFRedBytes ? gemv_lred_bytes(nr, 1) : kFRedBytes;
+}
+
+struct FusedArgs {
+  GemvArgs G;
+  const uint16_t* x;
+  int64_t ldx;
+  const uint16_t* gamma;
+  const float* noise;
+  int64_t noise_ld;
+  float sigma, eps;
+  QnDraw draw;
+  int32_t g_shared;         // with the norm: every token has the same gamma + sigma * noise
+  int32_t ctl_k;            // k-tiles per LoRA-down item when nk == 1 (0 with a split k: an item is a whole chunk)
+  int32_t nkc;              // LoRA-down k-chunks per (projection, rank chunk)
+  int32_t nitems;           // items, in (projection, rank chunk, k-chunk) order; item i = workgroup i
+  int32_t pair0[kMaxProj];  // first (projection, rank chunk) pair of each projection
+  float* t_part;            // [item][lane][8] f32 partials, in the LoRA-up B-fragment lane order
+  uint32_t* ctl;            // consumers past their reads (one word)
+};
+
+// x * rstd * g rounded to bf16, g = gamma + sigma * noise already formed (the same operations as aqn_value).
+__device__ __forceinline__ uint32_t aqn_scaled(float x, float rstd, float g) {
+  return f32_to_bf16(__fmul_rn(__fmul_rn(x, rstd), g));
+}
+
+// GSH (with the norm): every token has the same gamma + sigma * noise (FusedArgs::g_shared).
+template <bool SILU, bool AQN, bool VEC, bool GSH>
+__global__ void __launch_bounds__(kGWaves * kWave) k_fgemv(FusedArgs f) {
+  constexpr int NR = SILU ? 2 : 1, D = 3;
+  constexpr int kOut = (kGMaxUnits * 16 * 16 + kGWaves * kWave - 1) / (kGWaves * kWave);
+  constexpr int kAPre = 2;  // A fragments per item wave requested up front (an item of 4 k-tiles needs 2)
+  __shared__ __attribute__((aligned(16))) uint8_t s_lds[kGLds];
+  __shared__ uint16_t s_res[kGMaxUnits * 16 * 16];
+  __shared__ ProjEpi s_pe[kMaxProj];
+  __shared__ float s_rstd[16];
+  __shared__ int s_last;
+  const GemvArgs& g = f.G;
+  const LinearArgs& a = g.L;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+  const unsigned bid = blockIdx.x, nbr = (unsigned)g.nbr, nk = (unsigned)g.nk;
+  const int b = (int)(bid / nk), c = (int)(bid % nk);  // chunks of a block adjacent: item i <-> workgroup i
+  const int KT = g.KT, mt = g.mt, k = (int)a.k;
+  const int u0 = (int)((unsigned)b * (unsigned)g.nu / nbr);
+  const int U = (int)((unsigned)(b + 1) * (unsigned)g.nu / nbr) - u0;
+  const int t0 = (int)((unsigned)c * (unsigned)KT / nk), T = (int)((unsigned)(c + 1) * (unsigned)KT / nk) - t0;
+  uint8_t* const lred = s_lds + kGLds - gemv_lred_bytes(NR, 1);
+  const int fr_bytes = T * 4 * kWave * 16;
+  const int kc0 = t0 * kKTile;   // first channel of the chunk
+  constexpr bool gsh = AQN && GSH;
+
+  // stream waves: unit su, k-part sj of the chunk (as in the decode kernel; here h = 15 / U is computed, not looked
+  // up: a table in memory is a load, and its wait would come after every load issued before it)
+  const int h = U > 0 ? kGStream / U : 1;
+  const bool streams = wave < U * h;
+  const int su = streams ? (int)((unsigned)wave / (unsigned)h) : 0, sj = streams ? wave - su * h : 0;
+  const int ta = __builtin_amdgcn_readfirstlane(t0 + (int)((unsigned)(sj * T) / (unsigned)h));
+  const int tb = __builtin_amdgcn_readfirstlane(streams ? t0 + (int)((unsigned)((sj + 1) * T) / (unsigned)h) : ta);
+  rsrc_t cd[NR], sd[NR];
+#pragma unroll
+  for (int nr = 0; nr < NR; ++nr) {
+    const int64_t gu = u0 + su;
+    int p = nr;
+    if (!SILU) {
+      p = 0;
+      for (int q = 1; q < a.nproj; ++q)
+        if (gu >= a.p[q].rg_begin) p = q;
+      p = __builtin_amdgcn_readfirstlane(p);
+    }
+    const ProjArgs& P = a.p[p];
+    const int64_t rg = SILU ? gu : gu - P.rg_begin;
+    const bool live = streams && rg * 16 < P.n;
+    cd[nr] = make_rsrc(P.codes + rg * KT * kTileCodeBytes, live ? KT * kTileCodeBytes : 0);
+    sd[nr] = make_rsrc(P.scales + rg * KT * kTileScaleBytes, live ? KT * kTileScaleBytes : 0);
+  }
+  const uint32_t c_off = lane * 16, s_off = ((lane % 16) * 2 + (lane / 16) / 2) * 4;
+  auto load = [&](GTile<NR>& tl, int kt) {
+    const bool in = kt < tb;
+    const int kc = __builtin_amdgcn_readfirstlane(in ? kt * kTileCodeBytes : 0);
+    const int ks = __builtin_amdgcn_readfirstlane(in ? kt * kTileScaleBytes : 0);
+#pragma unroll
+    for (int nr = 0; nr < NR; ++nr) {
+      tl.c[nr] = __builtin_amdgcn_raw_buffer_load_b128(cd[nr], in ? c_off : kOutOfRange, kc, kNonTemporal);
+      tl.sc[nr] = __builtin_amdgcn_raw_buffer_load_b32(sd[nr], in ? s_off : kOutOfRange, ks, kNonTemporal);
+    }
+  };
+  // tensor scales of the projections (threads 0..nproj-1), to LDS below
+  float sg_mine = 0.f;
+#pragma unroll
+  for (int q = 0; q < kMaxProj; ++q)
+    if (threadIdx.x == q && q < a.nproj) sg_mine = gload(a.p[q].s_g);
+  // ---- requests, in the order they are needed: the shared norm scale's inputs, x, residuals, the LoRA-down item's
+  //      A fragments, the first weight tiles (the waits for earlier ones then leave the later ones in flight)
+  const rsrc_t gsrc = make_rsrc(f.gamma, AQN ? (int64_t)k * 2 : 0);
+  const rsrc_t zsrc = make_rsrc(f.noise, (AQN && f.noise) ? ((int64_t)(mt - 1) * f.noise_ld + k) * 4 : 0);
+  uint32_t gw[4] = {0u, 0u, 0u, 0u};
+  float gz[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (gsh) {  // channels kc0 + 8 tid .. + 8 (one group per thread: a chunk has at most 31 * 16 groups)
+    const int kk = kc0 + (int)threadIdx.x * 8;
+    const bool ok = (int)threadIdx.x < T * 16 && kk < k;
+    bload_bf16x8<VEC>(gsrc, ok ? (uint32_t)kk * 2 : kOutOfRange, gw);
+    if (!f.draw.on) bload_f32x8<VEC>(zsrc, ok ? (uint32_t)kk * 4 : kOutOfRange, gz);
+  }
+  // unit (token t, local k-tile lt, channel quarter jq) of pass ps: t = lane % 16, jq = lane / 16, lt = wave + 16 ps; it
+  // holds channels 32 jq .. 32 jq + 31 of the k-tile, four groups of 8. A wave covers one k-tile of all 16 tokens, so a
+  // (token, k-tile) spans four lanes 16 apart, and its fragment stores go to 16 distinct LDS bank groups per 16 lanes.
+  const int ut = lane % 16, uq = lane / 16;
+  const rsrc_t xsrc = make_rsrc(f.x, ((int64_t)(mt - 1) * f.ldx + k) * 2);
+  uint32_t hx[2][4][4];
+#pragma unroll
+  for (int ps = 0; ps < 2; ++ps)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int lt = wave + 16 * ps, kk = kc0 + lt * kKTile + uq * 32 + i * 8;
+      const bool ok = ut < mt && lt < T && kk < k;
+      bload_bf16x8<VEC>(xsrc, ok ? (uint32_t)(((int64_t)ut * f.ldx + kk) * 2) : kOutOfRange, hx[ps][i]);
+    }
+  // residual of this thread's outputs (output e = (unit, token, row) = ((u * 16 + tok) * 16 + row)); outputs without
+  // one read a valid stand-in address (x)
+  uint16_t res[kOut];
+#pragma unroll
+  for (int i = 0; i < kOut; ++i) {
+    const int e = threadIdx.x + i * kGWaves * kWave;
+    const int u = e >> 8, tok = (e >> 4) & 15, row = e & 15;
+    const int64_t gu = u0 + u;
+    const uint16_t* rb = a.p[0].res;
+    int64_t rbeg = 0, nl = a.p[0].n, ld = a.p[0].ld_res;
+    if (!SILU) {
+#pragma unroll
+      for (int q = 1; q < kMaxProj; ++q)
+        if (q < a.nproj && gu >= a.p[q].rg_begin) {
+          rb = a.p[q].res;
+          rbeg = a.p[q].rg_begin;
+          nl = a.p[q].n;
+          ld = a.p[q].ld_res;
+        }
+    }
+    const int64_t n = (gu - rbeg) * 16 + row;
+    const bool ok = rb && u < U && tok < mt && n < nl;
+    res[i] = gload(ok ? rb + tok * ld + n : f.x);
+  }
+  // this workgroup's LoRA-down item, if it has one: (projection ip, rank chunk ijc), local k-tiles [lt0, lt0 + ltn)
+  const bool producer = (int)bid < f.nitems;
+  int ip = 0, ijc = 0, lt0 = 0, ltn = 0;
+  if (producer) {
+    const int pair = (int)bid / f.nkc, kc = (int)bid % f.nkc;
+#pragma unroll
+    for (int q = 1; q < kMaxProj; ++q)
+      if (q < a.nproj && pair >= f.pair0[q]) ip = q;
+    ijc = pair - f.pair0[ip];
+    lt0 = f.ctl_k > 0 ? kc * f.ctl_k : 0;
+    ltn = f.ctl_k > 0 ? (T - lt0 < f.ctl_k ? T - lt0 : f.ctl_k) : T;
+  }
+  const uint16_t* Ap = nullptr;
+  int ir = 0;
+#pragma unroll
+  for (int q = 0; q < kMaxProj; ++q)
+    if (q == ip) {
+      Ap = a.p[q].A;
+      ir = a.p[q].r;
+    }
+  const rsrc_t asrc = make_rsrc(Ap, producer ? (int64_t)ir * k * 2 : 0);
+  // A fragment of (slice sl, half gh) for waves 0..7: ranks jc*32 + 16 gh + lane%16, k of the slice + 8 (lane/16)
+  auto a_off = [&](int sl, int gh) -> uint32_t {
+    const int j = ijc * 32 + gh * 16 + lane % 16;
+    const int kk = (t0 + lt0 + sl / 4) * kKTile + (sl % 4) * 32 + (lane / 16) * 8;
+    const bool ok = producer && wave < kFLoraWaves && sl < ltn * 4 && j < ir && kk < k;
+    return ok ? (uint32_t)(((int64_t)j * k + kk) * 2) : kOutOfRange;
+  };
+  u32x4 apre[kAPre][2];
+#pragma unroll
+  for (int i = 0; i < kAPre; ++i)
+#pragma unroll
+    for (int gh = 0; gh < 2; ++gh) apre[i][gh] = bload16(asrc, a_off(wave + i * kFLoraWaves, gh));
+  // the first D - 1 weight tiles of the stream waves
+  GTile<NR> Bt[D];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < D - 1; ++j) {
+    load(Bt[j], ta + j);
+    __builtin_amdgcn_sched_barrier(0);  // issue order of the first tiles: the loop's wait counts rely on it
+  }
+
+  if (threadIdx.x < kMaxProj) {
+#pragma unroll
+    for (int q = 0; q < kMaxProj; ++q)
+      if (threadIdx.x == q && q < a.nproj) {
+        const ProjArgs& P = a.p[q];
+        s_pe[q] = ProjEpi{P.y, P.res, P.n, P.ldy, P.ld_res, sg_mine, P.lambda, P.y_dtype, P.y_repeat, P.head_dim,
+                          P.rg_begin, P.r};
+      }
+  }
+  // the shared norm scale g = gamma + sigma * noise of the chunk's channels, f32, at the top of LDS (below it the
+  // fragments; the LoRA-down sums and LoRA slots reuse it later)
+  float* const s_g = reinterpret_cast<float*>(s_lds + kGLds - T * kKTile * 4);
+  if (gsh && (int)threadIdx.x < T * 16) {
+    if (f.draw.on) aqn_noise8(f.draw, draw_index(f.draw, 0), (uint64_t)(kc0 / 8 + threadIdx.x), gz);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s_g[threadIdx.x * 8 + 2 * e] = __fadd_rn(lo_bf16(gw[e]), __fmul_rn(f.sigma, gz[2 * e]));
+      s_g[threadIdx.x * 8 + 2 * e + 1] = __fadd_rn(hi_bf16(gw[e]), __fmul_rn(f.sigma, gz[2 * e + 1]));
+    }
+  }
+
+  // 1. with the norm (the chunk is the whole row): per token, the standalone norm's sum of squares. Stand-in thread s
+  //    (of 256) adds the chunks c = s, s + 256, ... of 8 channels in order, elements in order; its running sum sits in
+  //    LDS slot [s][token] between rounds: round 0 is pass 0 (chunks 0..255), round 1 pass 1 (the rest; a row has at
+  //    most 31 * 16 chunks). Then wave t adds token t's 256 stand-ins as four wave sums taken in order.
+  if (AQN) {
+    float* const s_ss = reinterpret_cast<float*>(s_lds);  // [256][16] (in the fragment area, written later)
+    for (int i = threadIdx.x; i < 256 * 16; i += kGWaves * kWave)
+      if (i / 16 >= T * 16) s_ss[i] = 0.0f;  // stand-ins without a chunk
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps) {
+      const int lt = wave + 16 * ps;
+      if (ps == 1 && T <= 16) break;
+      if (lt < T) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int sl = (lt % 16) * 16 + uq * 4 + i;  // stand-in of chunk lt * 16 + uq * 4 + i
+          float s = ps == 0 ? 0.0f : s_ss[sl * 16 + ut];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x0 = lo_bf16(hx[ps][i][e]), x1 = hi_bf16(hx[ps][i][e]);
+            s = __fadd_rn(s, __fmul_rn(x0, x0));
+            s = __fadd_rn(s, __fmul_rn(x1, x1));
+          }
+          s_ss[sl * 16 + ut] = s;
+        }
+      }
+      __syncthreads();
+    }
+    if (wave < mt) {
+      float tot = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) tot = __fadd_rn(tot, wave_sum(s_ss[(v * kWave + lane) * 16 + wave]));
+      if (lane == 0) s_rstd[wave] = rms_rstd(tot, k, f.eps);
+    }
+    __syncthreads();
+  }
+
+  // 2. h of every unit (from the registers), the (token, k-tile) exponent (amax over the unit's 32 values and the
+  //    three other lanes of the token) and the fragments: [lt][s][lane] 16 bytes, then [lt][16] f32 tile scales 2^-p
+#pragma unroll
+  for (int ps = 0; ps < 2; ++ps) {
+    const int lt = wave + 16 * ps;
+    if (lt >= T) break;  // (uniform)
+    uint32_t hv[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hv[i][e] = hx[ps][i][e];
+    if (AQN && ut < mt) {
+      const float rstd = s_rstd[ut];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ch = lt * 16 + uq * 4 + i, kk = kc0 + ch * 8;
+        if (kk >= k) continue;
+        float gv[8];
+        if (gsh) {
+          const f32x4 g0 = *reinterpret_cast<const f32x4*>(s_g + ch * 8);
+          const f32x4 g1 = *reinterpret_cast<const f32x4*>(s_g + ch * 8 + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            gv[e] = g0[e];
+            gv[4 + e] = g1[e];
+          }
+        } else {  // a scale of its own per token: gamma and this token's noise (read or drawn), one group at a time
+          uint32_t gb[4];
+          float z[8];
+          __builtin_amdgcn_sched_barrier(0);
+          bload_bf16x8<VEC>(gsrc, (uint32_t)kk * 2, gb);
+          if (f.draw.on) aqn_noise8(f.draw, draw_index(f.draw, ut), (uint64_t)(kk / 8), z);
+          else bload_f32x8<VEC>(zsrc, (uint32_t)((ut * f.noise_ld + kk) * 4), z);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            gv[2 * e] = __fadd_rn(lo_bf16(gb[e]), __fmul_rn(f.sigma, z[2 * e]));
+            gv[2 * e + 1] = __fadd_rn(hi_bf16(gb[e]), __fmul_rn(f.sigma, z[2 * e + 1]));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          hv[i][e] = aqn_scaled(lo_bf16(hv[i][e]), rstd, gv[2 * e]) |
+                     (aqn_scaled(hi_bf16(hv[i][e]), rstd, gv[2 * e + 1]) << 16);
+      }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fmaxf(fabsf(lo_bf16(hv[i][e])), fabsf(hi_bf16(hv[i][e]))));
+    amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+    const int pw = act_exponent(amax);
+    const float up = __uint_as_float((uint32_t)(pw + 127) << 23);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t packed[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f16x2 v;
+        v[0] = (_Float16)__fmul_rn(lo_bf16(hv[i][e]), up);
+        v[1] = (_Float16)__fmul_rn(hi_bf16(hv[i][e]), up);
+        packed[e] = __builtin_bit_cast(uint32_t, v);
+      }
+      // group jj = 4 uq + i: slice s = uq, lane group i
+      *reinterpret_cast<u32x4*>(s_lds + ((lt * 4 + uq) * kWave + i * 16 + ut) * 16) =
+          u32x4{packed[0], packed[1], packed[2], packed[3]};
+    }
+    if (uq == 0)
+      *reinterpret_cast<float*>(s_lds + fr_bytes + (lt * 16 + ut) * 4) = __uint_as_float((uint32_t)(127 - pw) << 23);
+  }
+#pragma unroll
+  for (int i = 0; i < kOut; ++i) s_res[threadIdx.x + i * kGWaves * kWave] = res[i];
+  __syncthreads();
+
+  // 3. the LoRA-down item: waves 0..7 over its 32-wide k-slices (B-fragment = h back from the f16 fragment, token
+  //    lane%16), two bf16 MFMAs per slice, into LDS; wave 15 adds the eight waves' sums in wave order, stores the
+  //    partial past the caches in the LoRA-up's lane order
+  if (producer) {
+    f32x4* s_red = reinterpret_cast<f32x4*>(s_lds + kGLds - kFRedBytes);
+    if (wave < kFLoraWaves) {
+      f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      for (int i0 = 0; i0 * kFLoraWaves < ltn * 4; i0 += kAPre) {
+        u32x4 af[kAPre][2];
+        if (i0 == 0) {
+#pragma unroll
+          for (int i = 0; i < kAPre; ++i) af[i][0] = apre[i][0], af[i][1] = apre[i][1];
+        } else {
+#pragma unroll
+          for (int i = 0; i < kAPre; ++i)
+#pragma unroll
+            for (int gh = 0; gh < 2; ++gh) af[i][gh] = bload16(asrc, a_off(wave + (i0 + i) * kFLoraWaves, gh));
+        }
+#pragma unroll
+        for (int i = 0; i < kAPre; ++i) {
+          const int sl = wave + (i0 + i) * kFLoraWaves;
+          if (sl >= ltn * 4) break;
+          const int lt = lt0 + sl / 4, s = sl % 4;
+          const u32x4 fr = *reinterpret_cast<const u32x4*>(s_lds + ((lt * 4 + s) * kWave + lane) * 16);
+          const float dn = *reinterpret_cast<const float*>(s_lds + fr_bytes + (lt * 16 + lane % 16) * 4);
+          uint32_t hb[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const f16x2 v = as_f16x2(fr[e]);
+            hb[e] = (uint32_t)f32_to_bf16(__fmul_rn((float)v[0], dn)) |
+                    ((uint32_t)f32_to_bf16(__fmul_rn((float)v[1], dn)) << 16);
+          }
+          const bf16x8 bv = __builtin_bit_cast(bf16x8, u32x4{hb[0], hb[1], hb[2], hb[3]});
+#pragma unroll
+          for (int gh = 0; gh < 2; ++gh)
+            acc[gh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[i][gh]), bv, acc[gh], 0,
+                                                              0, 0);
+        }
+      }
+      mfma_settle(acc[0]);  // (the loop's exit separates the MFMAs from these stores)
+      mfma_settle(acc[1]);
+      s_red[(wave * 2 + 0) * kWave + lane] = acc[0];
+      s_red[(wave * 2 + 1) * kWave + lane] = acc[1];
+    }
+    __syncthreads();
+    if (wave == kGWaves - 1) {
+      // lane L = (jl / 8) * 16 + token holds ranks jl = 8 (L / 16) .. + 7 of the chunk; rank jl's sum sits in D lane
+      // ((jl % 16) / 4) * 16 + token, element jl % 4, of half jl / 16
+      const int tok = lane % 16;
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int jl = (lane / 16) * 8 + e, gh = jl / 16, jr = jl % 16;
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < kFLoraWaves; ++w) sum += s_red[(w * 2 + gh) * kWave + (jr / 4) * 16 + tok][jr % 4];
+        v[e] = sum;
+      }
+      // stored bit-inverted: a word reads 0 until written (an all-ones f32, a NaN no arithmetic produces, is the
+      // only value that would store as 0)
+      const rsrc_t tsrc = make_rsrc(f.t_part, (int64_t)f.nitems * kWave * 32);
+      const uint32_t off = (uint32_t)(((int64_t)bid * kWave + lane) * 32);
+      u32x4 w0, w1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w0[e] = ~__float_as_uint(v[e]);
+        w1[e] = ~__float_as_uint(v[4 + e]);
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(w0, tsrc, off, 0, kCoherent);
+      __builtin_amdgcn_raw_buffer_store_b128(w1, tsrc, off + 16, 0, kCoherent);
+    }
+  }
+
+  // 4. the weight stream (as in the decode kernel)
+  f32x4 acc[NR];
+#pragma unroll
+  for (int nr = 0; nr < NR; ++nr) acc[nr] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const GTile<NR>& tl, int kt) {
+    const int lt = (kt < tb ? kt : tb - 1) - t0;
+    f32x4 part[NR];
+#pragma unroll
+    for (int nr = 0; nr < NR; ++nr) part[nr] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const u32x4 bf = *reinterpret_cast<const u32x4*>(s_lds + ((lt * 4 + s) * kWave + lane) * 16);
+#pragma unroll
+      for (int nr = 0; nr < NR; ++nr) {
+        const uint32_t scv = ((tl.sc[nr] >> (8 * s)) & 0xFFu) * 0x00800080u;  // E4M3 byte << 7 = E4M3 * 2^-8 in f16
+        const f16x2 sh = __builtin_bit_cast(f16x2, scv);
+        const uint32_t cw = tl.c[nr][s];
+        const f16x2 q0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 256.0f, 0) * sh;
+        const f16x2 q1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 256.0f, 1) * sh;
+        const f16x2 q2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 256.0f, 2) * sh;
+        const f16x2 q3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 256.0f, 3) * sh;
+        const f16x8 wv = {q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
+        part[nr] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, __builtin_bit_cast(f16x8, bf), part[nr], 0, 0, 0);
+      }
+    }
+    const float u = *reinterpret_cast<const float*>(s_lds + fr_bytes + (lt * 16 + lane % 16) * 4);
+#pragma unroll
+    for (int nr = 0; nr < NR; ++nr)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[nr][e] = __builtin_fmaf(part[nr][e], u, acc[nr][e]);
+  };
+  if (streams) {
+    for (int kt = ta; kt < tb; kt += D) {
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        load(Bt[(j + D - 1) % D], kt + j + D - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(Bt[j], kt + j);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  // 5. LoRA-up of the block's rows (chunk-0 workgroup, wave 15): per projection and rank chunk, the partials of its
+  //    k-chunk items (polled until written) added in k-chunk order, split into bf16 hi and lo, two MFMAs per unit.
+  //    Past its reads the wave counts itself; the last consumer clears the partials and the count for the next call.
+  if (wave == kGWaves - 1 && c == 0) {
+    const rsrc_t tsrc = make_rsrc(f.t_part, (int64_t)f.nitems * kWave * 32);
+#pragma unroll
+    for (int nr = 0; nr < NR; ++nr) {
+      int pfirst = SILU ? nr : unit_proj(s_pe, a.nproj, u0), plast = SILU ? nr : unit_proj(s_pe, a.nproj, u0 + U - 1);
+      pfirst = __builtin_amdgcn_readfirstlane(pfirst);
+      plast = __builtin_amdgcn_readfirstlane(plast);
+      for (int p = pfirst; p <= plast; ++p) {
+        const ProjEpi& E = s_pe[p];
+        const uint16_t* Bm = nullptr;
+        int pr0 = 0;
+#pragma unroll
+        for (int q = 0; q < kMaxProj; ++q)
+          if (q == p) {
+            Bm = a.p[q].B;
+            pr0 = f.pair0[q];
+          }
+        const int r = E.r;
+        for (int jc = 0; jc * 32 < r; ++jc) {
+          const rsrc_t bsrc = make_rsrc(Bm, E.n * r * 2);
+          u32x4 bfr[kGMaxUnits];
+#pragma unroll
+          for (int u = 0; u < kGMaxUnits; ++u) {
+            const bool mine = u < U && (SILU || unit_proj(s_pe, a.nproj, u0 + u) == p);
+            const int64_t n = (SILU ? u0 + u : u0 + u - E.rg_begin) * 16 + lane % 16;
+            const int j0 = jc * 32 + (lane / 16) * 8;
+            if (r % 8 == 0) {
+              bfr[u] = bload16(bsrc, (mine && n < E.n && j0 < r) ? (uint32_t)((n * r + j0) * 2) : kOutOfRange);
+            } else {
+              uint32_t w[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int64_t off = (n * r + j0 + 2 * e) * 2;
+                const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(
+                    bsrc, (mine && n < E.n && j0 + 2 * e < r) ? (uint32_t)off : kOutOfRange, 0, 0);
+                const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(
+                    bsrc, (mine && n < E.n && j0 + 2 * e + 1 < r) ? (uint32_t)(off + 2) : kOutOfRange, 0, 0);
+                w[e] = lo | (hi << 16);
+              }
+              bfr[u] = u32x4{w[0], w[1], w[2], w[3]};
+            }
+          }
+          // the partials of (p, jc)'s k-chunk items i0 .. i0 + nkc - 1, four per batch of loads, polled until every word
+          // is written (non-zero) and added in item order; a batch that never completes within the poll limit gives NaN
+          const int i0 = (pr0 + jc) * f.nkc;
+          constexpr int kTB = 4;
+          bool ready = true;
+          f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+          for (int kc0 = 0; kc0 < f.nkc; kc0 += kTB) {
+            u32x4 q[kTB][2];
+            bool got = false;
+            for (uint32_t spins = 0; spins < kFSpin && !got; ++spins) {
+              if (spins > 0) __builtin_amdgcn_s_sleep(2);
+              bool all = true;
+#pragma unroll
+              for (int v = 0; v < kTB; ++v) {
+                const bool in = kc0 + v < f.nkc;
+                const uint32_t off = (uint32_t)(((int64_t)(i0 + kc0 + v) * kWave + lane) * 32);
+                q[v][0] = __builtin_amdgcn_raw_buffer_load_b128(tsrc, in ? off : kOutOfRange, 0, kCoherent);
+                q[v][1] = __builtin_amdgcn_raw_buffer_load_b128(tsrc, in ? off + 16 : kOutOfRange, 0, kCoherent);
+              }
+#pragma unroll
+              for (int v = 0; v < kTB; ++v)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  all = all && (kc0 + v >= f.nkc || (q[v][0][e] != 0u && q[v][1][e] != 0u));
+              got = __all(all) != 0;
+            }
+            ready = ready && got;
+#pragma unroll
+            for (int v = 0; v < kTB; ++v) {
+              if (kc0 + v >= f.nkc) break;
+              f32x4 a, b;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                a[e] = __uint_as_float(~q[v][0][e]);
+                b[e] = __uint_as_float(~q[v][1][e]);
+              }
+              s0 += a;
+              s1 += b;
+            }
+          }
+          uint32_t hi[4], lo[4];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float t = ready ? (e < 4 ? s0[e] : s1[e - 4]) : __uint_as_float(0x7fc00000u);
+            const uint32_t th = f32_to_bf16(t);
+            const uint32_t tl = f32_to_bf16(t - bf16_to_f32((uint16_t)th));  // t - th is exact in f32
+            if (e % 2 == 0) {
+              hi[e / 2] = th;
+              lo[e / 2] = tl;
+            } else {
+              hi[e / 2] |= th << 16;
+              lo[e / 2] |= tl << 16;
+            }
+          }
+          const u32x4 thi = u32x4{hi[0], hi[1], hi[2], hi[3]}, tlo = u32x4{lo[0], lo[1], lo[2], lo[3]};
+#pragma unroll
+          for (int u = 0; u < kGMaxUnits; ++u) {
+            if (u >= U) break;
+            if (!SILU && unit_proj(s_pe, a.nproj, u0 + u) != p) continue;
+            f32x4 la = {0.f, 0.f, 0.f, 0.f};
+            la = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bfr[u]),
+                                                         __builtin_bit_cast(bf16x8, thi), la, 0, 0, 0);
+            la = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bfr[u]),
+                                                         __builtin_bit_cast(bf16x8, tlo), la, 0, 0, 0);
+            mfma_settle(la);  // (the store below sits behind a branch on one of its paths)
+            f32x4* slot = reinterpret_cast<f32x4*>(lred + ((u * NR + nr) * kWave + lane) * 16);
+            *slot = jc == 0 ? la : *slot + la;
+          }
+        }
+      }
+    }
+    // every read of this consumer is done: count it; the last one clears the partials and the count
+    uint32_t done = 0;
+    if (lane == 0) done = __hip_atomic_fetch_add(f.ctl, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    done = __shfl(done, 0, kWave);
+    if (done == nbr - 1) {
+      for (int i = 0; i < f.nitems * 2; ++i)
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, tsrc, (uint32_t)((i * kWave + lane) * 16), 0,
+                                               kCoherent);
+      if (lane == 0) __hip_atomic_store(f.ctl, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();  // every wave is done with the activations in LDS
+
+  // 6. part sums of the stream waves into LDS (over the activation area), then the per-output sums
+  if (streams) {
+#pragma unroll
+    for (int nr = 0; nr < NR; ++nr)
+      *reinterpret_cast<f32x4*>(s_lds + (((su * h + sj) * NR + nr) * kWave + lane) * 16) = acc[nr];
+  }
+  __syncthreads();
+  const bool has_lora = c == 0;
+  const int nout = U * 256;
+  float vsum[kOut][NR], vlo[kOut][NR];
+#pragma unroll
+  for (int i = 0; i < kOut; ++i) {
+    const int e = threadIdx.x + i * kGWaves * kWave;
+    const int u = e >> 8, tok = (e >> 4) & 15, row = e & 15;
+    const int ln = (row / 4) * 16 + tok, ii = row % 4;
+#pragma unroll
+    for (int nr = 0; nr < NR; ++nr) {
+      float s = 0.f, lo = 0.f;
+      if (e < nout) {
+        for (int j = 0; j < h; ++j)
+          s += reinterpret_cast<const float*>(s_lds + (((u * h + j) * NR + nr) * kWave + ln) * 16)[ii];
+        if (has_lora && s_pe[SILU ? nr : unit_proj(s_pe, a.nproj, u0 + u)].r > 0)
+          lo = reinterpret_cast<const float*>(lred + ((u * NR + nr) * kWave + ln) * 16)[ii];
+      }
+      vsum[i][nr] = s;
+      vlo[i][nr] = lo;
+    }
+  }
+  // 7. split k: as in the decode kernel
+  bool epilogue = true;
+  if (g.nk > 1) {
+    const int64_t PB = gemv_block_floats(NR, 1);
+    float* pb = g.pbuf + (int64_t)b * (g.nk + 1) * PB;
+#pragma unroll
+    for (int i = 0; i < kOut; ++i) {
+      const int e = threadIdx.x + i * kGWaves * kWave;
+      if (e >= nout) break;
+#pragma unroll
+      for (int nr = 0; nr < NR; ++nr) {
+        __hip_atomic_store(pb + (int64_t)c * PB + (int64_t)e * NR + nr, vsum[i][nr], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        if (c == 0)
+          __hip_atomic_store(pb + (int64_t)g.nk * PB + (int64_t)e * NR + nr, vlo[i][nr], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0)
+      s_last = __hip_atomic_fetch_add(g.cnt + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               (uint32_t)(g.nk - 1);
+    __syncthreads();
+    epilogue = s_last != 0;
+    if (epilogue) {
+      constexpr int kRedBatch = 8;
+#pragma unroll
+      for (int i = 0; i < kOut; ++i)
+#pragma unroll
+        for (int nr = 0; nr < NR; ++nr) vsum[i][nr] = 0.f;
+      for (int c0 = 0; c0 < g.nk; c0 += kRedBatch) {
+        float q[kOut][NR][kRedBatch];
+#pragma unroll
+        for (int i = 0; i < kOut; ++i) {
+          const int e = threadIdx.x + i * kGWaves * kWave;
+#pragma unroll
+          for (int nr = 0; nr < NR; ++nr)
+#pragma unroll
+            for (int v = 0; v < kRedBatch; ++v)
+              q[i][nr][v] = (e < nout && c0 + v < g.nk)
+                                ? __hip_atomic_load(pb + (int64_t)(c0 + v) * PB + (int64_t)e * NR + nr,
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                : 0.f;
+          if (c0 == 0) {
+#pragma unroll
+            for (int nr = 0; nr < NR; ++nr)
+              vlo[i][nr] = e < nout ? __hip_atomic_load(pb + (int64_t)g.nk * PB + (int64_t)e * NR + nr,
+                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                    : 0.f;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < kOut; ++i)
+#pragma unroll
+          for (int nr = 0; nr < NR; ++nr)
+#pragma unroll
+            for (int v = 0; v < kRedBatch; ++v) {
+              if (c0 + v >= g.nk) break;
+              vsum[i][nr] = (c0 + v == 0) ? q[i][nr][v] : vsum[i][nr] + q[i][nr][v];
+            }
+      }
+      if (threadIdx.x == 0) __hip_atomic_store(g.cnt + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  // 8. epilogue: y = s_g * sum + lambda * lora (SILU: SiLU(gate) * up), + residual, broadcast, rounding
+  if (epilogue) {
+#pragma unroll
+    for (int i = 0; i < kOut; ++i) {
+      const int e = threadIdx.x + i * kGWaves * kWave;
+      if (e >= nout) break;
+      const int u = e >> 8, tok = (e >> 4) & 15, row = e & 15;
+      if (tok >= mt) continue;
+      const int64_t gu = u0 + u;
+      const int p0 = SILU ? 0 : unit_proj(s_pe, a.nproj, gu);
+      const ProjEpi& E = s_pe[p0];
+      const int64_t n = (SILU ? gu : gu - E.rg_begin) * 16 + row;
+      if (n >= E.n) continue;
+      float val[NR];
+#pragma unroll
+      for (int nr = 0; nr < NR; ++nr) {
+        const ProjEpi& F = s_pe[SILU ? nr : p0];
+        val[nr] = F.sg * vsum[i][nr] + F.lambda * vlo[i][nr];
+      }
+      float out = val[0];
+      if (SILU) out = val[0] / (1.0f + __expf(-val[0])) * val[NR - 1];
+      if (E.res) out += bf16_to_f32(s_res[e]);
+      const int rep = E.y_repeat > 1 ? E.y_repeat : 1;
+      for (int gi = 0; gi < rep; ++gi) {
+        const int64_t col_out = rep > 1 ? ((n / E.head_dim) * rep + gi) * E.head_dim + n % E.head_dim : n;
+        const int64_t off = (int64_t)tok * E.ldy + col_out;
+        if (E.y_dtype == QN_F32) reinterpret_cast<float*>(E.y)[off] = out;
+        else reinterpret_cast<uint16_t*>(E.y)[off] = f32_to_bf16(out);
+      }
+    }
+  }
+}
+
 // Row blocks x k-chunks of the decode kernel: about one workgroup per CU, at most kGMaxUnits units per block, the
 // chunk's activations within LDS; among those, the cut with the least estimated time (largest share streamed at
 // ~25 GB/s per CU, the activation copy at ~80 GB/s, ~1.5 us more for a split k).
@@ -1433,9 +2151,9 @@ struct GemvCut {
 // k-tiles of activations a workgroup of the decode kernel can hold in LDS
 inline int64_t gemv_act_cap(int tmt, int nr) { return (kGLds - gemv_lred_bytes(nr, tmt)) / ((int64_t)tmt * kGTileAct); }
 
-// nk_only > 0: only that many k-chunks (a cut asked for by the caller's options).
-inline GemvCut gemv_cut(int64_t nu, int64_t KT, int tmt, int nr, int nk_only) {
-  const int64_t act_cap = gemv_act_cap(tmt, nr);
+// nk_only > 0: only that many k-chunks (a cut asked for by the caller's options). act_cap: k-tiles of activations a
+// workgroup holds (at most).
+inline GemvCut gemv_cut(int64_t nu, int64_t KT, int tmt, int nr, int nk_only, int64_t act_cap) {
   GemvCut best{0, 0};
   double best_t = 1e30;
   for (int64_t nk = 1; nk <= KT && nk <= 64; ++nk) {
@@ -1480,7 +2198,7 @@ struct Opts {
 };
 
 inline bool opts_valid(const Opts& o) {
-  return o.kernel >= QN_KERNEL_AUTO && o.kernel <= QN_KERNEL_MANY && o.nk >= 0 && o.nk <= 64 &&
+  return o.kernel >= QN_KERNEL_AUTO && o.kernel <= QN_KERNEL_FUSED && o.nk >= 0 && o.nk <= 64 &&
          (o.depth == 0 || o.depth == 2 || o.depth == 3) && o.rows >= 0 && o.waves >= 0 && (o.rows > 0) == (o.waves > 0) &&
          (o.elem == 0 || o.elem == 1);
 }
@@ -1501,16 +2219,62 @@ inline Opts opts_of(const qn_linear_opts* p) {
 // Which streaming kernel serves a call: the many-token MFMA kernel, the decode kernel (with its cut) or the general
 // kernel. Decided on the host before anything is launched; QN_ERR_UNSUPPORTED if the options name a kernel that
 // cannot serve the call.
-enum MainPath { kPathGeneral = 0, kPathDecode = 1, kPathMany = 2 };
+enum MainPath { kPathGeneral = 0, kPathDecode = 1, kPathMany = 2, kPathFused = 3 };
 struct Plan {
   MainPath path = kPathGeneral;
   GemvCut cut{0, 0};
   int depth = 3;
+  int ctl_k = 0, nkc = 0, npairs = 0;  // fused decode kernel: LoRA-down items (see FusedArgs)
 };
 
-inline qn_status plan_main(int64_t m, int64_t KT, int64_t nu, bool silu, const Opts& o, Plan* out) {
+// The fused decode kernel's plan, if it can serve the call: up to 16 tokens, a cut whose chunk fits in LDS beside
+// the LoRA-down reduction, with the norm no split k (the row statistics come from the chunk), and LoRA-down items
+// (kFItemTiles k-tiles each without a split k; one per chunk with one) that are at most as many as the workgroups.
+inline bool plan_fused(int64_t m, int64_t KT, int64_t nu, bool silu, bool norm, const qn_proj* projs,
+                       int32_t nproj, int nk_only, Plan* out) {
+  if (m < 1 || m > 16 || nu < 1) return false;
+  const int nr = silu ? 2 : 1;
+  if (norm && nk_only > 1) return false;
+  const GemvCut cut = gemv_cut(nu, KT, 1, nr, norm ? 1 : nk_only, (kGLds - fused_lds_top(nr)) / kGTileAct);
+  if (cut.nbr <= 0) return false;
+  int npairs = 0;
+  for (int p = 0; p < nproj; ++p) npairs += (int)ceil_div(projs[p].r, 32);
+  const int64_t grid = (int64_t)cut.nbr * cut.nk;
+  int64_t nkc = 0, ctl_k = 0;
+  if (cut.nk == 1) {
+    nkc = ceil_div(KT, kFItemTiles);
+    if (npairs > 0 && nkc > grid / npairs) nkc = grid / npairs;
+    if (nkc > 64) nkc = 64;
+    if (nkc < 1) return false;
+    ctl_k = ceil_div(KT, nkc);
+    nkc = ceil_div(KT, ctl_k);
+  } else {
+    nkc = cut.nk;
+    if (npairs > cut.nbr) return false;
+  }
+  if ((int64_t)npairs * nkc > kFMaxItems || (int64_t)npairs * nkc > grid) return false;
+  Plan pl;
+  pl.path = kPathFused;
+  pl.cut = cut;
+  pl.ctl_k = (int)ctl_k;
+  pl.nkc = (int)nkc;
+  pl.npairs = npairs;
+  *out = pl;
+  return true;
+}
+
+// allow_fused: false for a call split into its phases (the fused kernel has no separate prologue). norm: the call
+// has the norm (unknown to a workspace query: then the larger of both cases is sized).
+inline qn_status plan_main(int64_t m, int64_t KT, int64_t nu, bool silu, bool norm, const qn_proj* projs,
+                           int32_t nproj, const Opts& o, bool allow_fused, Plan* out) {
   Plan pl;
   const int nr = silu ? 2 : 1;
+  if (o.kernel == QN_KERNEL_FUSED) {
+    if (!allow_fused || (o.depth != 0 && o.depth != 3) || !plan_fused(m, KT, nu, silu, norm, projs, nproj, o.nk, &pl))
+      return QN_ERR_UNSUPPORTED;
+    *out = pl;
+    return QN_OK;
+  }
   if (o.kernel == QN_KERNEL_MANY || (o.kernel == QN_KERNEL_AUTO && m > kMaxTokensPerLaunch)) {
     if (m <= kMaxTokensPerLaunch) return QN_ERR_UNSUPPORTED;
     pl.path = kPathMany;
@@ -1518,7 +2282,7 @@ inline qn_status plan_main(int64_t m, int64_t KT, int64_t nu, bool silu, const O
     bool take = false;
     if (m >= 1 && m <= 32) {
       const int tmt = (int)ceil_div(m, 16);
-      pl.cut = gemv_cut(nu, KT, tmt, nr, o.kernel == QN_KERNEL_DECODE ? o.nk : 0);
+      pl.cut = gemv_cut(nu, KT, tmt, nr, o.kernel == QN_KERNEL_DECODE ? o.nk : 0, gemv_act_cap(tmt, nr));
       take = o.kernel == QN_KERNEL_DECODE ? pl.cut.nbr > 0 : gemv_default(pl.cut, nu, KT, tmt, nr);
     }
     if (o.kernel == QN_KERNEL_DECODE && !take) return QN_ERR_UNSUPPORTED;
@@ -1537,14 +2301,19 @@ size_t gemv_pbuf_bytes(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj
   int64_t nu_flat = 0;
   for (int p = 0; p < nproj; ++p) nu_flat += ceil_div(projs[p].n, 16);
   // the workspace query does not know the epilogue: size for both readings of a two-projection call
+  // nor whether the call is split into phases (no fused kernel then): size for every case
   size_t bytes = 0;
-  for (int silu = 0; silu <= (nproj == 2 ? 1 : 0); ++silu) {
-    Plan pl;
-    if (plan_main(m, KT, silu ? ceil_div(projs[0].n, 16) : nu_flat, silu, o, &pl) != QN_OK) continue;
-    if (pl.path != kPathDecode || pl.cut.nk <= 1) continue;
-    const size_t b = (size_t)pl.cut.nbr * (pl.cut.nk + 1) * gemv_block_floats(silu ? 2 : 1, tmt) * 4;
-    bytes = b > bytes ? b : bytes;
-  }
+  for (int silu = 0; silu <= (nproj == 2 ? 1 : 0); ++silu)
+    for (int fused = 0; fused <= 1; ++fused)
+      for (int norm = 0; norm <= 1; ++norm) {
+        Plan pl;
+        if (plan_main(m, KT, silu ? ceil_div(projs[0].n, 16) : nu_flat, silu, norm != 0, projs, nproj, o, fused != 0,
+                      &pl) != QN_OK)
+          continue;
+        if ((pl.path != kPathDecode && pl.path != kPathFused) || pl.cut.nk <= 1) continue;
+        const size_t b = (size_t)pl.cut.nbr * (pl.cut.nk + 1) * gemv_block_floats(silu ? 2 : 1, tmt) * 4;
+        bytes = b > bytes ? b : bytes;
+      }
   return bytes;
 }
 
@@ -2215,7 +2984,9 @@ qn_status validate_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, 
   int64_t rg_total = 0;
   for (int p = 0; p < nproj; ++p) rg_total += ceil_div(projs[p].n, 16);
   const int64_t nrg = silu ? 2 * ceil_div(projs[0].n, 16) : rg_total;
-  const qn_status ps = plan_main(m, KT, silu ? ceil_div(projs[0].n, 16) : rg_total, silu, o, plan);
+  const qn_status ps =
+      plan_main(m, KT, silu ? ceil_div(projs[0].n, 16) : rg_total, silu, aqn != nullptr, projs, nproj, o, phases == 0,
+                plan);
   if (ps != QN_OK) return ps;
   if (plan->path == kPathGeneral && nrg > 0) {
     for (int64_t t0 = 0; t0 < m; t0 += kMaxTokensPerLaunch) {
@@ -2257,8 +3028,8 @@ qn_status run_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const
   const int CT = (int)chunk_tiles(KT);
   const int ks = (int)lora_chunks(k);
 
-  // P (and the statistics kernel for many tokens)
-  if (run_prologue) {
+  // P (and the statistics kernel for many tokens); the fused decode kernel does this work itself
+  if (run_prologue && plan.path != kPathFused) {
     PrologueArgs pa{};
     pa.x = x;
     pa.ldx = ldx;
@@ -2295,7 +3066,7 @@ qn_status run_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const
     pa.xsc = xsc;
     pa.t_part = t_part;
     pa.cnt = reinterpret_cast<uint32_t*>(ws + wl.cnt);
-    pa.ncnt = 256;
+    pa.ncnt = kCountWords;
     // many tokens: row statistics in a kernel of their own (rstd with the norm, and one exponent per token)
     const bool big = m > kMaxTokensPerLaunch;
     pa.rstd_in = big && aqn ? rstd : nullptr;
@@ -2413,6 +3184,60 @@ qn_status run_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const
     if (silu) hipLaunchKernelGGL((k_gemm<true>), grid, block, 0, s, ga);
     else hipLaunchKernelGGL((k_gemm<false>), grid, block, 0, s, ga);
     return hipGetLastError() == hipSuccess ? QN_OK : QN_ERR_HIP;
+  }
+  if (plan.path == kPathFused) {
+    FusedArgs fa{};
+    GemvArgs& ga = fa.G;
+    ga.L = la;
+    ga.L.tok0 = 0;
+    ga.KT = (int32_t)KT;
+    ga.ntiles = 1;
+    ga.mt = (int32_t)m;
+    ga.nu = (int32_t)(silu ? ceil_div(projs[0].n, 16) : rg_total);
+    ga.nbr = plan.cut.nbr;
+    ga.nk = plan.cut.nk;
+    ga.pbuf = reinterpret_cast<float*>(ws + wl.pbuf);
+    ga.cnt = reinterpret_cast<uint32_t*>(ws + wl.cnt);
+    fa.x = x;
+    fa.ldx = ldx;
+    bool vec = ((uintptr_t)x % 16 == 0) && (ldx % 8 == 0);
+    if (aqn) {
+      fa.gamma = aqn->gamma;
+      fa.noise = aqn->noise;
+      fa.noise_ld = aqn->noise ? aqn->noise_ld : 0;
+      fa.sigma = aqn->sigma;
+      fa.eps = aqn->eps;
+      fa.draw = QnDraw{aqn->draw ? 1 : 0, aqn->seed, aqn->subseed, aqn->row_offset, aqn->draw_rows};
+      vec = vec && (uintptr_t)aqn->gamma % 16 == 0 &&
+            (!aqn->noise || ((uintptr_t)aqn->noise % 16 == 0 && fa.noise_ld % 4 == 0));
+      // one gamma + sigma * noise for every token: noise read with a zero stride, one draw for all rows, or none
+      fa.g_shared = aqn->draw ? (aqn->draw_rows == 0 || aqn->draw_rows >= m) : (!aqn->noise || fa.noise_ld == 0);
+    }
+    fa.ctl_k = plan.ctl_k;
+    fa.nkc = plan.nkc;
+    fa.nitems = plan.npairs * plan.nkc;
+    int pair = 0;
+    for (int p = 0; p < nproj; ++p) {
+      fa.pair0[p] = pair;
+      pair += (int)ceil_div(projs[p].r, 32);
+    }
+    fa.t_part = reinterpret_cast<float*>(ws + wl.t_fused);
+    fa.ctl = reinterpret_cast<uint32_t*>(ws + wl.cnt) + 256;
+    const dim3 grid((unsigned)(plan.cut.nbr * plan.cut.nk)), block(kGWaves * kWave);
+    const bool gsh = aqn && fa.g_shared;
+#define QN_FGEMV(S_, A_, V_, G_)                                                                     \
+  if (silu == S_ && (aqn != nullptr) == A_ && vec == V_ && gsh == G_) {                             \
+    hipLaunchKernelGGL((k_fgemv<S_, A_, V_, G_>), grid, block, 0, s, fa);                           \
+    return hipGetLastError() == hipSuccess ? QN_OK : QN_ERR_HIP;                                    \
+  }
+    QN_FGEMV(false, false, false, false) QN_FGEMV(false, false, true, false)
+    QN_FGEMV(true, false, false, false) QN_FGEMV(true, false, true, false)
+    QN_FGEMV(false, true, false, false) QN_FGEMV(false, true, true, false)
+    QN_FGEMV(true, true, false, false) QN_FGEMV(true, true, true, false)
+    QN_FGEMV(false, true, false, true) QN_FGEMV(false, true, true, true)
+    QN_FGEMV(true, true, false, true) QN_FGEMV(true, true, true, true)
+#undef QN_FGEMV
+    return QN_ERR_UNSUPPORTED;  // (not reached)
   }
   if (plan.path == kPathDecode) {
     const int tmt = (int)ceil_div(m, 16);

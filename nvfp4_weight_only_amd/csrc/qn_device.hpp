@@ -73,6 +73,10 @@ __device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
+// A 32-bit word's bits as two f16. Taking the word as a by-value argument matters: applied directly to an element of
+// a vector (w[i] of a u32x4), __builtin_bit_cast has been seen to compile to a read of element 0 whatever i is.
+__device__ __forceinline__ f16x2 as_f16x2(uint32_t w) { return __builtin_bit_cast(f16x2, w); }
+
 // Load through a pointer known to address global memory.
 template <class T>
 __device__ __forceinline__ T gload(const T* p) {

@@ -175,13 +175,13 @@ def test_linear_options_validation(qn):
                   y=256, y_dtype=0, ldy=64)
     arr = (qn.QnProj * 1)(p)
 
-    def call(m, o, k=128, ws_bytes=None):
+    def call(m, o, k=128, ws_bytes=None, aqn=None):
         oc = o.to_c()
         need = L.nvfp4_lora_linear_workspace_opts(m, k, arr, 1, ctypes.byref(oc))
-        return L.nvfp4_lora_linear_opts(fake, m, k, k, None, arr, 1, 0, ctypes.byref(oc), P(1 << 20),
-                                        need if ws_bytes is None else ws_bytes, None)
+        return L.nvfp4_lora_linear_opts(fake, m, k, k, ctypes.byref(aqn) if aqn else None, arr, 1, 0, ctypes.byref(oc),
+                                        P(1 << 20), need if ws_bytes is None else ws_bytes, None)
 
-    bad = [qn.LinearOpts(kernel=4), qn.LinearOpts(kernel=-1), qn.LinearOpts(decode_kchunks=65),
+    bad = [qn.LinearOpts(kernel=5), qn.LinearOpts(kernel=-1), qn.LinearOpts(decode_kchunks=65),
            qn.LinearOpts(decode_depth=4), qn.LinearOpts(general_rows=2), qn.LinearOpts(general_waves=8),
            qn.LinearOpts(elem_store=2)]
     for o in bad:
@@ -190,6 +190,17 @@ def test_linear_options_validation(qn):
         assert L.nvfp4_lora_linear_workspace_opts(4, 128, arr, 1, ctypes.byref(oc)) == 0, o
     assert call(64, qn.LinearOpts(kernel=qn.KERNEL_DECODE)) == qn.QN_ERR_UNSUPPORTED  # decode kernel: m <= 32
     assert call(100, qn.LinearOpts(kernel=qn.KERNEL_MANY)) == qn.QN_ERR_UNSUPPORTED  # MFMA kernel: m > 128
+    # fused decode kernel: m <= 16, depth 0 or 3, not split into phases, with the norm the whole row in one k-chunk
+    norm = qn.QnAqn(gamma=256, noise=None, noise_ld=0, sigma=0.01, eps=1e-6)
+    assert call(17, qn.LinearOpts(kernel=qn.KERNEL_FUSED)) == qn.QN_ERR_UNSUPPORTED
+    assert call(4, qn.LinearOpts(kernel=qn.KERNEL_FUSED), k=32 * 128, aqn=norm) == qn.QN_ERR_UNSUPPORTED
+    assert call(4, qn.LinearOpts(kernel=qn.KERNEL_FUSED, decode_kchunks=2), aqn=norm) == qn.QN_ERR_UNSUPPORTED
+    assert call(4, qn.LinearOpts(kernel=qn.KERNEL_FUSED, decode_depth=2)) == qn.QN_ERR_UNSUPPORTED
+    oc = qn.LinearOpts(kernel=qn.KERNEL_FUSED).to_c()
+    need = L.nvfp4_lora_linear_workspace_opts(4, 128, arr, 1, ctypes.byref(oc))
+    for phase in (qn.RUN_PROLOGUE_ONLY, qn.RUN_MAIN_ONLY):
+        assert L.nvfp4_lora_linear_opts(fake, 4, 128, 128, None, arr, 1, phase, ctypes.byref(oc), P(1 << 20), need,
+                                        None) == qn.QN_ERR_UNSUPPORTED
     assert call(4, qn.LinearOpts(kernel=qn.KERNEL_GENERAL, general_rows=3, general_waves=5)) == qn.QN_ERR_UNSUPPORTED
     # a decode cut whose k-chunk does not fit the kernel's LDS: 32 tokens over a 40960-long row in one chunk
     assert call(32, qn.LinearOpts(kernel=qn.KERNEL_DECODE, decode_kchunks=1), k=40960) == qn.QN_ERR_UNSUPPORTED

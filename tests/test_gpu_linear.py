@@ -158,22 +158,28 @@ def test_linear_per_row_noise(qn):
     assert rel_err(y.cpu().numpy(), oracle.lora_linear(h, cc, sb, sg, c.A[0], c.B[0], c.lam)) <= LINEAR_TOL
 
 
-@pytest.mark.parametrize("m,k,per_row", [(16, 3584, False), (5, 272, True), (300, 1024, False), (17, 40960, True)])
+@pytest.mark.parametrize("m,k,per_row", [(16, 3584, False), (5, 272, True), (16, 2048, True), (1, 3968, False),
+                                         (300, 1024, False), (17, 40960, True)])
 def test_fused_norm_matches_standalone_norm(qn, m, k, per_row):
-    """The norm inside the linear call gives the bits of the standalone norm: y(fused) == y(norm, then plain linear).
+    """The norm inside the linear call gives the bits of the standalone norm: y(fused) == y(norm, then plain linear),
+    both calls on the same kernel and cut (without the norm the library may split k, which changes the summation
+    order of the product, not h).
 
-    Covers the one-wave statistics in both thread counts (k > 32768 uses 1024), per-row noise, a ragged k and the
-    separate statistics kernel taken from 256 tokens on."""
+    Covers the one-wave statistics in both thread counts (k > 32768 uses 1024), the fused decode kernel's statistics
+    from registers in one and two rounds of 256 chunks, per-row noise, a ragged k and the separate statistics kernel
+    taken from 256 tokens on."""
     c = Case(m, [96], k, seed=m + k)
     noise = synth.normal_f32(78, (m, k) if per_row else (k,))
     wq = qn.quantize(dev_bf16(c.w[0]), qn.LAYOUT_TILED)
     A, B = dev_bf16(c.A[0]), dev_bf16(c.B[0])
     g, z, x = dev_bf16(c.gamma), dev_f32(noise), dev_bf16(c.x)
+    opts = qn.LinearOpts(kernel=qn.KERNEL_FUSED, decode_kchunks=1) if m <= 16 and k <= 3968 else None
     y1 = torch.empty(m, 96, dtype=torch.float32, device=DEV)
-    qn.lora_linear(x, [qn.Projection(wq, y1, A, B, c.lam)], qn.make_aqn(g, z, c.sigma, 1e-6, noise_per_row=per_row))
+    qn.lora_linear(x, [qn.Projection(wq, y1, A, B, c.lam)], qn.make_aqn(g, z, c.sigma, 1e-6, noise_per_row=per_row),
+                   opts=opts)
     h = qn.aqn_rmsnorm(x, g, z, c.sigma, 1e-6, noise_per_row=per_row)
     y2 = torch.empty(m, 96, dtype=torch.float32, device=DEV)
-    qn.lora_linear(h, [qn.Projection(wq, y2, A, B, c.lam)])
+    qn.lora_linear(h, [qn.Projection(wq, y2, A, B, c.lam)], opts=opts)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
 
@@ -185,10 +191,12 @@ def kernel_paths(qn):
     return {"default": None, "general": qn.LinearOpts(kernel=qn.KERNEL_GENERAL),
             "decode": qn.LinearOpts(kernel=qn.KERNEL_DECODE, decode_kchunks=1),
             "decode-splitk": qn.LinearOpts(kernel=qn.KERNEL_DECODE, decode_kchunks=3),
-            "decode-depth2": qn.LinearOpts(kernel=qn.KERNEL_DECODE, decode_depth=2)}
+            "decode-depth2": qn.LinearOpts(kernel=qn.KERNEL_DECODE, decode_depth=2),
+            "fused": qn.LinearOpts(kernel=qn.KERNEL_FUSED),
+            "fused-splitk": qn.LinearOpts(kernel=qn.KERNEL_FUSED, decode_kchunks=3)}
 
 
-KERNEL_PATHS = ["default", "general", "decode", "decode-splitk", "decode-depth2"]
+KERNEL_PATHS = ["default", "general", "decode", "decode-splitk", "decode-depth2", "fused", "fused-splitk"]
 
 
 def decode_fits(m, nu, k, nchunks, nr):
@@ -204,6 +212,27 @@ def decode_fits(m, nu, k, nchunks, nr):
         nbr = min(256 // nk, nu)
         if tmax <= cap and tmax * tmt <= 40 and nbr >= 1 and -(-nu // nbr) <= 8:
             return True
+    return False
+
+
+def fused_fits(m, nu, k, nchunks, nr, npairs, norm=True):
+    """Whether the fused decode kernel can take a call: up to 16 tokens, a cut whose chunk fits in LDS under the LoRA
+    slots or the 16 KiB LoRA-down reduction (whichever is larger), with the norm a single k-chunk, at most 8 row units
+    per workgroup, and LoRA-down items (one per 4 k-tiles without a split, one per chunk with one) no more than the
+    workgroups. For a cut the caller names (nchunks > 0) this is exact; with the library's own cut the test cases are
+    ones where every feasible cut also has room for the items."""
+    if m > 16 or (norm and nchunks > 1):
+        return False
+    KT = -(-k // 128)
+    cap = (147456 - max(8 * nr * 64 * 16, 16384)) // (4 * 64 * 16 + 64)
+    for nk in ([1] if norm else [nchunks] if nchunks else range(1, min(KT, 64) + 1)):
+        tmax = -(-KT // nk)
+        nbr = min(256 // nk, nu)
+        if not (tmax <= cap and tmax <= 40 and nbr >= 1 and -(-nu // nbr) <= 8):
+            continue
+        if nk > 1 and npairs > nbr:
+            continue
+        return True
     return False
 
 
@@ -235,7 +264,9 @@ def test_linear_kernel_paths(qn, path, m, ns, k, silu, residual, r, gqa):
                                    y_repeat=rep, head_dim=64))
     aqn = qn.make_aqn(dev_bf16(c.gamma), dev_f32(c.noise), c.sigma, 1e-6)
     nu = -(-ns[0] // 16) if silu else sum(-(-n // 16) for n in ns)
-    if path.startswith("decode") and not decode_fits(m, nu, k, opts.decode_kchunks, 2 if silu else 1):
+    npairs = len(ns) * (-(-r // 32))
+    if (path.startswith("decode") and not decode_fits(m, nu, k, opts.decode_kchunks, 2 if silu else 1)) or \
+            (path.startswith("fused") and not fused_fits(m, nu, k, opts.decode_kchunks, 2 if silu else 1, npairs)):
         with pytest.raises(qn.QnError) as e:  # refused on the host, nothing launched
             qn.lora_linear(dev_bf16(c.x), projs, aqn, qn.EPI_SILU_MUL if silu else qn.EPI_NONE, opts=opts)
         assert e.value.status == qn.QN_ERR_UNSUPPORTED
@@ -254,6 +285,33 @@ def test_linear_kernel_paths(qn, path, m, ns, k, silu, residual, r, gqa):
         if rep > 1:
             ref = oracle.gqa_broadcast(ref, rep, 64)
         assert rel_err(ys[p].cpu().numpy(), ref) <= LINEAR_TOL, (path, p)
+
+
+# The fused decode kernel without the norm (the o and down projections of a layer): its split-k form, which the calls
+# with the norm never take, on rows too long for one chunk and on cuts named through the options, with residuals,
+# several projections, mixed and odd ranks; every output checked against the oracle.
+@pytest.mark.parametrize("m,ns,k,r,nchunks,residual", [
+    (16, [520], 4992, 32, 0, True),      # 39 k-tiles: more than one chunk holds
+    (1, [3584], 18944, 32, 0, True),     # the 7B down projection's row length
+    (7, [200, 72], 2048, 12, 3, False),
+    (16, [1040, 64, 64], 1040, 64, 2, False),
+    (3, [96], 640, 0, 4, True),
+    (16, [384], 3584, 33, 5, False),
+])
+def test_fused_split_k_without_norm(qn, m, ns, k, r, nchunks, residual):
+    c = Case(m, ns, k, r=r, seed=k + m, aqn=False)
+    res = synth.normal_bf16(57, (m, ns[0])) if residual else None
+    opts = qn.LinearOpts(kernel=qn.KERNEL_FUSED, decode_kchunks=nchunks)
+    nu = sum(-(-n // 16) for n in ns)
+    npairs = len(ns) * (-(-r // 32))
+    if not fused_fits(m, nu, k, nchunks, 1, npairs, norm=False):
+        pytest.skip("cut outside the fused kernel's limits")
+    ys = c.gpu(qn, residual=dev_bf16(res) if residual else None, opts=opts)
+    for p in range(len(ns)):
+        ref = c.oracle_y(p)
+        if residual:
+            ref = ref + bf16_bits_to_f64(res)
+        assert rel_err(ys[p].cpu().numpy(), ref) <= LINEAR_TOL, p
 
 
 # Many tokens (more than 128): the MFMA kernel with one activation exponent per token, and the general kernel in
