@@ -3,7 +3,7 @@
 TEST INFRASTRUCTURE ONLY: imported by tests/, the smoke check and the benchmark's CPU-baseline leg. The product
 library never imports this package, and this package never imports the product library.
 
-Arrays are numpy: bf16 tensors are uint16 bit patterns, NVFP4 codes and E4M3 scales are uint8.
+Arrays are numpy: bf16 tensors are uint16 bit patterns, NVFP4 and MXFP4 codes and their E4M3 and E8M0 scales are uint8.
 """
 from __future__ import annotations
 
@@ -55,6 +55,9 @@ def lib():
             "orc_philox4x64_10": ([P, P, P], None),
             "orc_aqn_noise": ([u64, u64, u64, i64, i64, i64, P, i64], None),
             "orc_lora_linear": ([P, i64, i64, i64, P, P, f32, i64, P, P, i32, dbl, P], None),
+            "orc_mxfp4_quantize": ([P, i64, i64, i64, P, P, P], None),
+            "orc_mxfp4_dequantize": ([P, P, i64, i64, P, P], None),
+            "orc_mxfp4_lora_linear": ([P, i64, i64, i64, P, P, i64, P, P, i32, dbl, P], None),
             "orc_dense_linear": ([P, i64, i64, P, i64, P], None),
             "orc_group_advantage": ([P, i32, i32, dbl, P], None),
             "orc_silu_mul": ([P, P, i64, P], None),
@@ -232,6 +235,52 @@ def lora_linear_backward(g: np.ndarray, h: np.ndarray, codes: np.ndarray, s_b: n
     lib().orc_lora_linear_backward(_p(g), m, n, _p(h), k, _p(_c(codes, np.uint8)), _p(_c(s_b, np.uint8)), float(s_g),
                                    _p(A), _p(B), r, float(lam), _p(out["dh"]), _p(out["dA"]), _p(out["dB"]))
     return {key: v for key, v in out.items() if v is not None}
+
+
+def mxfp4_quantize(w: np.ndarray):
+    """W bf16 [n, k] (k % 32 == 0) -> (codes u8 [n, k/2], E8M0 scales u8 [n, k/32], flags int); canonical MX layout
+    (OCP MX: one power-of-two scale per 32 weights, E2M1 elements)."""
+    w = _c(w, np.uint16)
+    n, k = w.shape
+    assert k % 32 == 0
+    codes = np.zeros((n, k // 2), dtype=np.uint8)
+    sc = np.zeros((n, k // 32), dtype=np.uint8)
+    flags = np.zeros(1, dtype=np.int32)
+    lib().orc_mxfp4_quantize(_p(w), n, k, k, _p(codes), _p(sc), _p(flags))
+    return codes, sc, int(flags[0])
+
+
+def mxfp4_dequantize(codes: np.ndarray, scales: np.ndarray):
+    """-> (exact fp64 [n, k], RNE f32 [n, k])."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    n, k2 = codes.shape
+    k = 2 * k2
+    assert scales.shape == (n, k // 32)
+    we = np.empty((n, k), dtype=np.float64)
+    wf = np.empty((n, k), dtype=np.float32)
+    lib().orc_mxfp4_dequantize(_p(codes), _p(scales), n, k, _p(we), _p(wf))
+    return we, wf
+
+
+def mxfp4_lora_linear(h: np.ndarray, codes: np.ndarray, scales: np.ndarray, A: np.ndarray | None,
+                      B: np.ndarray | None, lam: float) -> np.ndarray:
+    """h bf16 [m, k]; MXFP4 W [n, k] canonical; A bf16 [r, k]; B bf16 [n, r] -> y fp64 [m, n]."""
+    h = _c(h, np.uint16)
+    m, k = h.shape
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    n = codes.shape[0]
+    assert codes.shape[1] * 2 == k and scales.shape == (n, k // 32)
+    r = 0
+    if A is not None:
+        A = _c(A, np.uint16)
+        B = _c(B, np.uint16)
+        r = A.shape[0]
+        assert A.shape == (r, k) and B.shape == (n, r)
+    y = np.empty((m, n), dtype=np.float64)
+    lib().orc_mxfp4_lora_linear(_p(h), m, k, k, _p(codes), _p(scales), n, _p(A), _p(B), r, float(lam), _p(y))
+    return y
 
 
 def dense_linear(h: np.ndarray, w: np.ndarray) -> np.ndarray:

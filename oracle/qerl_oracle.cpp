@@ -167,6 +167,56 @@ unsigned nvfp4_code(uint16_t wb, double S) {
   return sign | best;
 }
 
+// ---------------------------------------------------------------------------------------------------------------
+// MXFP4, the OCP Microscaling FP4 format the papers calibrate and compare beside NVFP4 ["QeRL 阅读笔记" §3.1]. The pages
+// give it no further detail, so the reading is the OCP MX v1.0 definition: blocks of 32 consecutive weights along k
+// share one E8M0 scale X = 2^(E - 127) (E = 255 is NaN; no sign, no mantissa). The shared exponent is the block's
+// floor(log2(amax)) minus the largest exponent of the element format (2 for E2M1, whose largest value is
+// 6 = 1.5 * 2^2), kept within E8M0's range; each element is the E2M1 value nearest to w / X, ties to the even code,
+// values beyond 6 saturating to 6, with the sign of w. A block without a nonzero finite value takes E = 0.
+double e8m0_value(unsigned byte) {
+  return byte == 255u ? std::numeric_limits<double>::quiet_NaN() : std::ldexp(1.0, (int)byte - 127);
+}
+
+unsigned mxfp4_block_exponent(double amax) {
+  if (!(amax > 0.0)) return 0u;
+  int e;
+  std::frexp(amax, &e);  // amax = f 2^e with f in [0.5, 1): floor(log2(amax)) = e - 1
+  const int E = (e - 1) - 2 + 127;
+  return E < 0 ? 0u : (E > 254 ? 254u : (unsigned)E);
+}
+
+// y = W_hat h + lambda B (A h) in fp64, W_hat row o given by row(o, out[k]) (the shared body of the linear oracles).
+template <class RowFn>
+void lora_linear_rows(const uint16_t* h, int64_t m, int64_t k, int64_t ldh, int64_t n, RowFn row, const uint16_t* A,
+                      const uint16_t* B, int r, double lambda, double* y) {
+  double* t = new double[(size_t)(m * (r > 0 ? r : 1))];
+  bool lora = A && B && r > 0;
+  if (lora)
+    for (int64_t i = 0; i < m; ++i)
+      for (int j = 0; j < r; ++j) {
+        double acc = 0.0;
+        for (int64_t c = 0; c < k; ++c) acc += bf16_value(A[j * k + c]) * bf16_value(h[i * ldh + c]);
+        t[i * r + j] = acc;
+      }
+  double* wrow = new double[(size_t)k];
+  for (int64_t o = 0; o < n; ++o) {
+    row(o, wrow);
+    for (int64_t i = 0; i < m; ++i) {
+      double acc = 0.0;
+      for (int64_t c = 0; c < k; ++c) acc += wrow[c] * bf16_value(h[i * ldh + c]);
+      if (lora) {
+        double lr = 0.0;
+        for (int j = 0; j < r; ++j) lr += bf16_value(B[o * r + j]) * t[i * r + j];
+        acc += lambda * lr;
+      }
+      y[i * n + o] = acc;
+    }
+  }
+  delete[] wrow;
+  delete[] t;
+}
+
 }  // namespace
 
 // =================================================================================================================
@@ -331,35 +381,71 @@ void orc_aqn_noise(uint64_t seed, uint64_t stream, uint64_t row_offset, int64_t 
 void orc_lora_linear(const uint16_t* h, int64_t m, int64_t k, int64_t ldh, const uint8_t* codes,
                      const uint8_t* s_b, float s_g, int64_t n, const uint16_t* A, const uint16_t* B, int r,
                      double lambda, double* y) {
-  double* t = new double[(size_t)(m * (r > 0 ? r : 1))];
-  bool lora = A && B && r > 0;
-  if (lora)
-    for (int64_t i = 0; i < m; ++i)
-      for (int j = 0; j < r; ++j) {
-        double acc = 0.0;
-        for (int64_t c = 0; c < k; ++c) acc += bf16_value(A[j * k + c]) * bf16_value(h[i * ldh + c]);
-        t[i * r + j] = acc;
+  lora_linear_rows(
+      h, m, k, ldh, n,
+      [&](int64_t o, double* wrow) {
+        for (int64_t c = 0; c < k; ++c) {
+          uint8_t byte = codes[o * (k / 2) + c / 2];
+          unsigned q = (c & 1) ? (byte >> 4) : (byte & 15u);
+          wrow[c] = (double)s_g * (e4m3_value(s_b[o * (k / 16) + c / 16]) * e2m1_value(q));
+        }
+      },
+      A, B, r, lambda, y);
+}
+
+// MXFP4 quantization of W bf16 [n x k] (k % 32 == 0), canonical layout: codes [n][k/2] packed as for NVFP4 (element
+// 2j in bits 3:0 of byte j), E8M0 scales [n][k/32]. Non-finite weights are left out of the block amax, get code 0
+// and set bit 0 of *flags.
+void orc_mxfp4_quantize(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, uint8_t* codes, uint8_t* scales,
+                        int* flags) {
+  for (int64_t i = 0; i < n; ++i)
+    for (int64_t b = 0; b < k / 32; ++b) {
+      const uint16_t* blk = w + i * ldw + b * 32;
+      double amax = 0.0;
+      for (int j = 0; j < 32; ++j) {
+        if (!bf16_is_finite(blk[j])) {
+          if (flags) *flags |= 1;
+          continue;
+        }
+        amax = std::fmax(amax, std::fabs(bf16_value(blk[j])));
       }
-  double* wrow = new double[(size_t)k];
-  for (int64_t o = 0; o < n; ++o) {
-    for (int64_t c = 0; c < k; ++c) {
-      uint8_t byte = codes[o * (k / 2) + c / 2];
-      unsigned q = (c & 1) ? (byte >> 4) : (byte & 15u);
-      wrow[c] = (double)s_g * (e4m3_value(s_b[o * (k / 16) + c / 16]) * e2m1_value(q));
-    }
-    for (int64_t i = 0; i < m; ++i) {
-      double acc = 0.0;
-      for (int64_t c = 0; c < k; ++c) acc += wrow[c] * bf16_value(h[i * ldh + c]);
-      if (lora) {
-        double lr = 0.0;
-        for (int j = 0; j < r; ++j) lr += bf16_value(B[o * r + j]) * t[i * r + j];
-        acc += lambda * lr;
+      const unsigned E = mxfp4_block_exponent(amax);
+      scales[i * (k / 32) + b] = (uint8_t)E;
+      const double X = e8m0_value(E);
+      for (int j = 0; j < 32; j += 2) {
+        const unsigned lo = nvfp4_code(blk[j], X), hi = nvfp4_code(blk[j + 1], X);  // nearest E2M1 under scale X
+        codes[i * (k / 2) + (b * 32 + j) / 2] = (uint8_t)(lo | (hi << 4));
       }
-      y[i * n + o] = acc;
     }
-  }
-  delete[] wrow;
-  delete[] t;
+}
+
+// W_hat = X * q from the canonical MXFP4 layout: exact (fp64) and rounded once to f32.
+void orc_mxfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k, double* w_exact,
+                          float* w_f32) {
+  for (int64_t i = 0; i < n; ++i)
+    for (int64_t j = 0; j < k; ++j) {
+      uint8_t byte = codes[i * (k / 2) + j / 2];
+      unsigned c = (j & 1) ? (byte >> 4) : (byte & 15u);
+      double v = e8m0_value(scales[i * (k / 32) + j / 32]) * e2m1_value(c);
+      if (w_exact) w_exact[i * k + j] = v;
+      if (w_f32) w_f32[i * k + j] = (float)v;
+    }
+}
+
+// The LoRA-adapted linear of orc_lora_linear with an MXFP4 base (canonical layout).
+void orc_mxfp4_lora_linear(const uint16_t* h, int64_t m, int64_t k, int64_t ldh, const uint8_t* codes,
+                           const uint8_t* scales, int64_t n, const uint16_t* A, const uint16_t* B, int r,
+                           double lambda, double* y) {
+  lora_linear_rows(
+      h, m, k, ldh, n,
+      [&](int64_t o, double* wrow) {
+        for (int64_t c = 0; c < k; ++c) {
+          uint8_t byte = codes[o * (k / 2) + c / 2];
+          unsigned q = (c & 1) ? (byte >> 4) : (byte & 15u);
+          wrow[c] = e8m0_value(scales[o * (k / 32) + c / 32]) * e2m1_value(q);
+        }
+      },
+      A, B, r, lambda, y);
 }
 
 // Backward of the LoRA-adapted linear through the frozen NVFP4 base [review §2.1: the backbone is frozen, gradients
