@@ -220,6 +220,25 @@ def run_layer(layers, shape, m, dev, steps, warmup, stream_gbs, layers_equiv, x_
                       "copies_rotated": len(layers)})
 
 
+def run_f3(base, shape, dev, steps, warmup, stream_gbs):
+    """The 7B layer at M = 16 with MXFP4 weights (E8M0 scale per 32; the same seeded bf16 weights quantized by the MX
+    rule and written in the tiled form the kernels read), 5 copies rotated. The tiled form stores the MX scale once
+    per 16 weights, so the bytes read are NVFP4's."""
+    import torch
+    import nvfp4_weight_only_amd as qn
+    import synth
+    from nvfp4_weight_only_amd.layer import DecoderLayer
+    s = lambda t: synth.seed_for(2, 0, t)
+    w = {nm: qn.mxfp4_quantize(bf16_dev(synth.normal_bf16(s("w_" + nm), nk, std=0.02), dev), qn.LAYOUT_TILED)
+         for nm, nk in shape.projections().items()}
+    mx = DecoderLayer(shape, w, base.lora, base.gamma1, base.gamma2, base.noise1, base.noise2, base.sigma, base.lam)
+    torch.cuda.synchronize()
+    layers = copies_of(mx, 5)
+    out = run_layer(layers, shape, 16, dev, steps, warmup, stream_gbs, 28, synth.seed_for(2, 0, "x") + 16)
+    out["weights"] = "MXFP4 (OCP MX rule), tiled form with power-of-two NVFP4 block and tensor scales"
+    return out
+
+
 def run_c3(base, shape, dev, steps, warmup, stream_gbs):
     """28 chained layers (distinct weight copies), M = 64, sigma_3 in all 56 norms, a fresh noise vector per norm."""
     import torch
@@ -596,6 +615,9 @@ def main():
         if want("c3"):
             log("config 3: 28 chained 7B layers, M=64")
             cfg["c3_stack28_7b_m64"] = run_c3(base, shape, dev, args.steps, args.warmup, stream_gbs)
+        if want("f3"):
+            log("MXFP4 weights: 7B layer, M=16")
+            cfg["f3_mxfp4_layer7b_m16"] = run_f3(base, shape, dev, args.steps, args.warmup, stream_gbs)
         if want("c5"):
             log("config 5: prefill 8192 tokens")
             cfg["c5_prefill_m8192"] = run_c5(base, shape, dev, args.steps, args.warmup)

@@ -145,6 +145,33 @@ size_t nvfp4_tiled_scales_bytes(int64_t n, int64_t k);
 qn_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* block_scales, const float* tensor_scale, int64_t n,
                            int64_t k, int32_t layout, float* w_out, int64_t ldo, void* stream);
 
+/* MXFP4 quantizer, the OCP Microscaling FP4 format the papers calibrate and compare beside NVFP4 ["QeRL 阅读笔记" §3.1;
+ * the pages give no more detail, so the OCP MX v1.0 definition is the reading]: blocks of 32 consecutive weights along
+ * k share one E8M0 scale X = 2^(E - 127), E = floor(log2(block amax)) - 2 (2 = the largest E2M1 exponent) kept within
+ * 0..254 (0 for a block without a nonzero finite weight); each element is the E2M1 code nearest to w / X (ties to the
+ * even code, saturating at 6), with the sign of w. Non-finite weights are left out of the amax, get code 0 and set
+ * bit 0 of *d_flags (if not NULL; the caller zeroes it beforehand).
+ *   w [n][ldw] bf16 (device), k % 32 == 0, ldw >= k.
+ *   layout QN_LAYOUT_ROWMAJOR: the canonical MX layout, codes [n][k/2] (packed as for NVFP4) and E8M0 scales
+ *     [n][k/32] (mxfp4_scales_bytes); tensor_scale is not used (may be NULL).
+ *   layout QN_LAYOUT_TILED: the same weight written exactly in the NVFP4 tiled form that nvfp4_lora_linear and the
+ *     backward read (so every kernel serves MXFP4 weights): with E_ref = (largest E of the tensor) - 8, each 16-weight
+ *     half of a block gets the E4M3 block scale 2^(E - E_ref) and *tensor_scale = 2^(E_ref - 127), so that
+ *     s_g * s_b * q = X * q bit for bit. A block whose E is more than 17 below the largest cannot be written so: bit 1
+ *     of *d_flags is set and that block's values are wrong (an error for the caller). codes and block_scales sized by
+ *     nvfp4_tiled_codes_bytes / nvfp4_tiled_scales_bytes; tensor_scale is scratch until the last of four kernels.
+ * Errors: QN_ERR_SHAPE (k % 32 != 0, ldw < k, negative sizes), QN_ERR_VALUE (layout), QN_ERR_NULL, QN_ERR_ALIGN (codes
+ * 16-byte, tensor_scale and d_flags 4-byte aligned). */
+qn_status mxfp4_quantize(const uint16_t* w, int64_t n, int64_t k, int64_t ldw, int32_t layout, uint8_t* codes,
+                         uint8_t* scales, float* tensor_scale, int32_t* d_flags, void* stream);
+
+/* Bytes of the canonical MXFP4 scales of an [n x k] weight (host, pure; 0 unless k % 32 == 0). */
+size_t mxfp4_scales_bytes(int64_t n, int64_t k);
+
+/* W_hat = X * q from the canonical MXFP4 layout into f32 w_out [n][ldo] (exact, rounded once to f32). */
+qn_status mxfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k, float* w_out,
+                           int64_t ldo, void* stream);
+
 /* AQN-RMSNorm [review §5.1]: h = bf16(x * rstd * (gamma + sigma * noise)), rstd = 1 / sqrt(sum_j x_j^2 / d + eps),
  * per row, f32 arithmetic, round-to-nearest-even to bf16.  x [m][ldx] bf16, h [m][ldh] bf16 (device). */
 qn_status aqn_rmsnorm(const uint16_t* x, int64_t m, int64_t d, int64_t ldx, const qn_aqn* aqn, uint16_t* h,

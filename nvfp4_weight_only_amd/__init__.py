@@ -29,7 +29,8 @@ EXPORTS = ["nvfp4_quantize", "nvfp4_tiled_codes_bytes", "nvfp4_tiled_scales_byte
            "nvfp4_lora_linear_workspace", "nvfp4_lora_linear", "nvfp4_lora_linear_workspace_opts",
            "nvfp4_lora_linear_opts", "nvfp4_lora_linear_noalloc", "nvfp4_lora_linear_noalloc_max_bytes",
            "aqn_sigma", "grpo_group_advantage", "grpo_clipped_surrogate", "qn_stream_read", "qn_status_string",
-           "nvfp4_lora_linear_backward", "nvfp4_lora_linear_backward_workspace"]
+           "nvfp4_lora_linear_backward", "nvfp4_lora_linear_backward_workspace", "mxfp4_quantize",
+           "mxfp4_dequantize", "mxfp4_scales_bytes"]
 
 
 class QnError(RuntimeError):
@@ -84,6 +85,9 @@ def _load():
         "nvfp4_tiled_codes_bytes": ([i64, i64], sz),
         "nvfp4_tiled_scales_bytes": ([i64, i64], sz),
         "nvfp4_dequantize": ([P, P, P, i64, i64, i32, P, i64, P], i32),
+        "mxfp4_quantize": ([P, i64, i64, i64, i32, P, P, P, P, P], i32),
+        "mxfp4_dequantize": ([P, P, i64, i64, P, i64, P], i32),
+        "mxfp4_scales_bytes": ([i64, i64], sz),
         "aqn_rmsnorm": ([P, i64, i64, i64, ctypes.POINTER(QnAqn), P, i64, P], i32),
         "aqn_noise": ([ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64, i64, i64, i64, P, i64, P], i32),
         "nvfp4_lora_linear_workspace": ([i64, i64, ctypes.POINTER(QnProj), i32], sz),
@@ -188,6 +192,48 @@ def dequantize(wq: NVFP4Weight, stream=None) -> torch.Tensor:
         out = torch.empty(wq.n, wq.k, dtype=torch.float32, device=wq.codes.device)
     _check(lib.nvfp4_dequantize(_ptr(wq.codes), _ptr(wq.scales), _ptr(wq.tensor_scale), wq.n, wq.k, wq.layout,
                                 _ptr(out), wq.k, _stream(stream)), "nvfp4_dequantize")
+    _keep_for(out, stream)
+    return out
+
+
+# ---- MXFP4 weights ------------------------------------------------------------------------------------------------
+@dataclass
+class MXFP4Weight:
+    """A packed MXFP4 weight [n x k] in the canonical MX layout: codes [n][k/2] and E8M0 scales [n][k/32] (device)."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    n: int
+    k: int
+
+
+def mxfp4_quantize(w: torch.Tensor, layout: int = LAYOUT_TILED, flags: Optional[torch.Tensor] = None, stream=None):
+    """bf16 W [n, k] (device, k % 32 == 0) -> MXFP4 (OCP MX: E8M0 scale per 32 weights). LAYOUT_ROWMAJOR gives the
+    canonical MXFP4Weight; LAYOUT_TILED gives the same weight re-expressed exactly as an NVFP4Weight (power-of-two
+    block scales and tensor scale) for nvfp4_lora_linear and the other kernels; bit 1 of `flags` reports a block too
+    far below the tensor's largest for that form."""
+    assert w.dtype == torch.bfloat16 and w.dim() == 2
+    n, k = w.shape
+    with _on(stream):
+        if layout == LAYOUT_TILED:
+            out = alloc_weight(n, k, LAYOUT_TILED, w.device)
+            codes, scales, ts = out.codes, out.scales, out.tensor_scale
+        else:
+            codes = torch.zeros(max(n * k // 2, 16), dtype=torch.uint8, device=w.device)
+            scales = torch.zeros(max(int(lib.mxfp4_scales_bytes(n, k)), 4), dtype=torch.uint8, device=w.device)
+            ts = None
+            out = MXFP4Weight(codes, scales, n, k)
+    _check(lib.mxfp4_quantize(_ptr(w), n, k, w.stride(0), layout, _ptr(codes), _ptr(scales), _ptr(ts), _ptr(flags),
+                              _stream(stream)), "mxfp4_quantize")
+    for t in (codes, scales, ts):
+        _keep_for(t, stream)
+    return out
+
+
+def mxfp4_dequantize(wq: MXFP4Weight, stream=None) -> torch.Tensor:
+    with _on(stream):
+        out = torch.empty(wq.n, wq.k, dtype=torch.float32, device=wq.codes.device)
+    _check(lib.mxfp4_dequantize(_ptr(wq.codes), _ptr(wq.scales), wq.n, wq.k, _ptr(out), wq.k, _stream(stream)),
+           "mxfp4_dequantize")
     _keep_for(out, stream)
     return out
 

@@ -52,6 +52,16 @@ def test_validation_errors(qn):
     # dequantize
     assert L.nvfp4_dequantize(fake, fake, fake, 16, 20, 1, fake, 20, None) == qn.QN_ERR_SHAPE
     assert L.nvfp4_dequantize(fake, fake, None, 16, 32, 1, fake, 32, None) == qn.QN_ERR_NULL
+    # MXFP4 quantize / dequantize: k % 32 != 0, bad layout, NULL tensor scale for the tiled form, misaligned codes
+    assert L.mxfp4_quantize(fake, 16, 48, 48, 0, fake, fake, None, None, None) == qn.QN_ERR_SHAPE
+    assert L.mxfp4_quantize(fake, 16, 64, 32, 0, fake, fake, None, None, None) == qn.QN_ERR_SHAPE
+    assert L.mxfp4_quantize(fake, 16, 64, 64, 3, fake, fake, None, None, None) == qn.QN_ERR_VALUE
+    assert L.mxfp4_quantize(fake, 16, 64, 64, 1, fake, fake, None, None, None) == qn.QN_ERR_NULL
+    assert L.mxfp4_quantize(fake, 16, 64, 64, 0, P(264), fake, None, None, None) == qn.QN_ERR_ALIGN
+    assert L.mxfp4_quantize(fake, 0, 64, 64, 1, None, None, None, None, None) == qn.QN_OK  # empty
+    assert L.mxfp4_dequantize(fake, fake, 16, 48, fake, 48, None) == qn.QN_ERR_SHAPE
+    assert L.mxfp4_dequantize(fake, None, 16, 64, fake, 64, None) == qn.QN_ERR_NULL
+    assert L.mxfp4_scales_bytes(16, 64) == 32 and L.mxfp4_scales_bytes(16, 48) == 0
     # norm: negative sigma, NaN eps, NULL aqn
     a = qn.QnAqn(gamma=256, noise=None, noise_ld=0, sigma=-1.0, eps=1e-6)
     assert L.aqn_rmsnorm(fake, 2, 32, 32, ctypes.byref(a), fake, 32, None) == qn.QN_ERR_VALUE
