@@ -2413,11 +2413,17 @@ __device__ __forceinline__ f16x8 dequant_frag(uint32_t cw, uint32_t scale_byte) 
 
 template <bool SILU>
 __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_st[4 * kMAct];  // four stages; after the loop the output tile
+  // Four stages. Stages 2 and 3 are arrays of their own: the compiler then knows that a stage being read and one
+  // being filled by a load into LDS never overlap, and issues no wait for the in-flight fills before each stage's
+  // reads (with one array and wave-dependent fill offsets it drained every load before every k-tile). After the loop
+  // stages 0 and 1 hold the output tile and stage 3 the LoRA t fragments.
+  __shared__ __attribute__((aligned(16))) uint8_t s_st[2 * kMAct];
+  __shared__ __attribute__((aligned(16))) uint8_t s_st2a[kMAct];
+  __shared__ __attribute__((aligned(16))) uint8_t s_st3a[kMAct];
   uint8_t* const s_st0 = s_st;
   uint8_t* const s_st1 = s_st + kMAct;
-  uint8_t* const s_st2 = s_st + 2 * kMAct;
-  uint8_t* const s_st3 = s_st + 3 * kMAct;
+  uint8_t* const s_st2 = s_st2a;
+  uint8_t* const s_st3 = s_st3a;
   __shared__ ProjEpi s_pe[kMaxProj];
   __shared__ float s_tsc[kMTT * 16];  // the tokens' 2^-p
   const LinearArgs& a = g.L;
@@ -2478,7 +2484,9 @@ __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
     const bool in = kt < KT;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int q0 = i * kMWaves * kWave + wave * kWave;  // first 16-byte piece of this wave
+      // first 16-byte piece of this wave (wave masked: a bound the compiler can see, so the fill provably stays
+      // inside its stage)
+      const int q0 = i * kMWaves * kWave + (wave & (kMWaves - 1)) * kWave;
       const int tt = q0 >> 8, rem = q0 & 255;
       const int so = __builtin_amdgcn_readfirstlane(in ? ((tt * KT + kt) * 4 * kWave + rem) * 16 : 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xsrc, (__attribute__((address_space(3))) void*)(st + q0 * 16), 16,
@@ -2611,11 +2619,11 @@ __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
   // With SILU and both ranks <= 32, the LoRA t fragments go to stage 3 (the output tile takes stages 0 and 1) and
   // the B rows of all four slots are requested with them: one memory round trip for the whole LoRA-up.
   const bool t_lds = SILU && g.t_lds != 0;
-  const u32x4* const t_st = reinterpret_cast<const u32x4*>(s_st + 3 * kMAct);
+  const u32x4* const t_st = reinterpret_cast<const u32x4*>(s_st3);
   uint8_t* const otile_base = s_st;
   u32x4 bfr4[4];
   if (t_lds) {
-    t_load(s_st + 3 * kMAct);
+    t_load(s_st3);
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const ProjEpi& E = s_pe[pj[jj]];
@@ -2733,7 +2741,14 @@ __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
       n0 = (gf0 - a.p[pp].rg_begin) * 16;
       fast = fast && pp == p1;
     }
-    float* const otile = reinterpret_cast<float*>(otile_base);
+    // row tl (a token) of the output tile: the rows fill stages 0 and 1, then stage 2, then stage 3
+    auto orow = [&](int tl) __attribute__((always_inline)) -> float* {
+      constexpr int kRows01 = 2 * kMAct / (kC * 4), kRowsSt = kMAct / (kC * 4);
+      static_assert(kRows01 + 2 * kRowsSt >= kMTT * 16, "output tile rows");
+      if (tl < kRows01) return reinterpret_cast<float*>(otile_base) + tl * kC;
+      if (tl < kRows01 + kRowsSt) return reinterpret_cast<float*>(s_st2) + (tl - kRows01) * kC;
+      return reinterpret_cast<float*>(s_st3) + (tl - kRows01 - kRowsSt) * kC;
+    };
 #pragma unroll
     for (int u = 0; u < (SILU ? 1 : 2); ++u) {
       const int jj = j0 + u;
@@ -2755,7 +2770,7 @@ __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
         }
         if (fast) {
           const int tl = i * 16 + lane % 16, unit = (cb / 4 + lane / 16) ^ (lane % 16);
-          *reinterpret_cast<f32x4*>(otile + tl * kC + unit * 4) = f32x4{o4[0], o4[1], o4[2], o4[3]};
+          *reinterpret_cast<f32x4*>(orow(tl) + unit * 4) = f32x4{o4[0], o4[1], o4[2], o4[3]};
           continue;
         }
         if (tok >= a.m) continue;
@@ -2795,7 +2810,7 @@ __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
           float v[kCnt];
 #pragma unroll
           for (int h = 0; h < kNu; ++h) {
-            const f32x4 t4 = *reinterpret_cast<const f32x4*>(otile + tl * kC + ((pc * kNu + h) ^ (tl % 16)) * 4);
+            const f32x4 t4 = *reinterpret_cast<const f32x4*>(orow(tl) + ((pc * kNu + h) ^ (tl % 16)) * 4);
 #pragma unroll
             for (int q = 0; q < 4; ++q) v[4 * h + q] = t4[q];
           }
