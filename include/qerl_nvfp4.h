@@ -191,9 +191,10 @@ qn_status aqn_noise(uint64_t seed, uint64_t subseed, uint64_t row_offset, int64_
 
 /* Workspace bytes nvfp4_lora_linear needs for these arguments (host, pure).
  * The workspace must be zero-filled before its first use (hipMemset once, or allocated zeroed). Every call leaves
- * its control words (split-k arrival counters, the fused decode kernel's counter and LoRA-down partials) zero again,
- * so a workspace can be reused by any later call ordered after it; calls that may run at the same time need
- * workspaces of their own. */
+ * its control words (split-k arrival counters, the prologue's LoRA-down arrival counters, the fused decode kernel's
+ * counter and LoRA-down partials) zero again; they sit at the start of the workspace, at the same offsets for every
+ * call, so a workspace can be reused by any later call ordered after it, whatever its shapes; calls that may run at
+ * the same time need workspaces of their own. */
 size_t nvfp4_lora_linear_workspace(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj);
 
 /* The rollout-decode linear layer [review §2.1 forward map, §3.2, §5.1]:
@@ -217,11 +218,15 @@ typedef enum {
   QN_KERNEL_DECODE = 2,  /* the decode streaming kernel (activations held in LDS, optional split k); m <= 32 and a
                             split of the rows and k that fits its LDS, else QN_ERR_UNSUPPORTED */
   QN_KERNEL_MANY = 3,    /* the many-token MFMA kernel; m > 128, else QN_ERR_UNSUPPORTED */
-  QN_KERNEL_FUSED = 4    /* the decode kernel with the norm, the activation conversion and the LoRA-down folded in:
+  QN_KERNEL_FUSED = 4,   /* the decode kernel with the norm, the activation conversion and the LoRA-down folded in:
                             one launch per call; m <= 16, a cut that fits its LDS (with the norm: the whole row in one
                             k-chunk, k <= 3968), not with the phase flags, else QN_ERR_UNSUPPORTED. AUTO does not
                             take it: on the 7B decode shapes it measured slower than the prologue and the other
                             kernels at 1 to 16 tokens. */
+  QN_KERNEL_WIDE = 5     /* the decode streaming kernel for 17 to 64 tokens (activations streamed through LDS in
+                            passes, every activation tile shared by all row groups of a workgroup, optional split
+                            k); m in 17..64, else QN_ERR_UNSUPPORTED. AUTO takes it at 17 to 64 tokens for calls
+                            with at least 24 MB of packed weights (the wide feed-forward and long-row projections). */
 } qn_kernel;
 
 /* Explicit options of one nvfp4_lora_linear_opts call. Zero-initialised, it asks for the library's defaults. These
@@ -229,9 +234,10 @@ typedef enum {
  * variables and keeps no settings between calls. */
 typedef struct {
   int32_t kernel;         /* qn_kernel */
-  int32_t decode_kchunks; /* QN_KERNEL_DECODE / _FUSED: k-chunks of the split-k cut, 1..64 (0 = the library's cut) */
+  int32_t decode_kchunks; /* QN_KERNEL_DECODE / _FUSED / _WIDE: k-chunks of the split-k cut, 1..64 (0 = the
+                             library's cut) */
   int32_t decode_depth;   /* QN_KERNEL_DECODE: weight tiles in flight per wave: 0 (the default, 3), 2 or 3;
-                             QN_KERNEL_FUSED takes 0 or 3; with AUTO, 2 rules the fused kernel out */
+                             QN_KERNEL_FUSED and _WIDE take 0 or 3; with AUTO, 2 rules those two out */
   int32_t general_rows;   /* QN_KERNEL_GENERAL: row groups per workgroup and waves per workgroup, both 0 (the */
   int32_t general_waves;  /* library's shape) or both > 0 naming a built pair (else QN_ERR_UNSUPPORTED) */
   int32_t elem_store;     /* 0 or 1; many-token kernel: 1 stores outputs element by element instead of in 16-byte

@@ -22,7 +22,7 @@ BF16, F32 = 0, 1
 EPI_NONE, EPI_SILU_MUL = 0, 1
 RUN_PROLOGUE_ONLY, RUN_MAIN_ONLY = 0x100, 0x200
 
-KERNEL_AUTO, KERNEL_GENERAL, KERNEL_DECODE, KERNEL_MANY, KERNEL_FUSED = range(5)
+KERNEL_AUTO, KERNEL_GENERAL, KERNEL_DECODE, KERNEL_MANY, KERNEL_FUSED, KERNEL_WIDE = range(6)
 
 EXPORTS = ["nvfp4_quantize", "nvfp4_tiled_codes_bytes", "nvfp4_tiled_scales_bytes", "nvfp4_dequantize", "aqn_rmsnorm",
            "aqn_noise",

@@ -92,10 +92,14 @@ inline int64_t lora_chunks(int64_t k) {
 }
 
 // Control words of the workspace, zero between calls: 256 split-k arrival counters, then the fused decode kernel's
-// consumer counter (kCountWords in all). Every call that runs the prologue zeroes them. The fused kernel's LoRA-down
-// partials (kFusedItemsMax items) are zero between calls too: they are their own ready flags.
+// consumer counter (kCountWords in all; every call that runs the prologue zeroes them), then the prologue's own
+// arrival counters for summing the LoRA-down t (kTsumWords: one per pair group and token tile of up to 64 tokens;
+// each is reset by the last workgroup to arrive). The fused kernel's LoRA-down partials (kFusedItemsMax items) are
+// zero between calls too: they are their own ready flags.
 constexpr int kFusedItemsMax = 192;
 constexpr int kCountWords = 256 + 1;
+constexpr int kTsumWords = 4 * 2 * 4;  // kMaxPg x token tiles (kMaxPg = kMaxProj * kRankChunks)
+constexpr int kCoherent = 16;          // buffer-access cache policy sc1: device-coherent, past the XCD's L2
 
 struct Opts;
 size_t gemv_pbuf_bytes(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj, const Opts& o);
@@ -105,15 +109,17 @@ Workspace workspace_layout(int64_t m, int64_t k, const qn_proj* projs, int32_t n
   const int64_t mp = ceil_div(m, 16) * 16;
   Workspace w;
   size_t off = 0;
+  // Regions that must be zero between calls come first, at the same offsets in every call's layout, so that no other
+  // call sharing the workspace (with other shapes, hence other offsets for its data) writes over them.
+  w.cnt = off;     off = align256(off + (kCountWords + kTsumWords) * 4);  // (see kCountWords)
+  w.t_fused = off; off = align256(off + (size_t)kFusedItemsMax * kWave * 8 * 4);
   w.xs = off;     off = align256(off + (size_t)mp * kp * 2);
   w.xsc = off;    off = align256(off + (size_t)mp * KT * 4);
   w.rstd = off;   off = align256(off + (size_t)mp * 4);
   w.tok_p = off;  off = align256(off + (size_t)mp * 4);
   w.t_part = off; off = align256(off + (size_t)nproj * (mp / 16) * kRankChunks * lora_chunks(k) * kWave * 32);
-  w.t_fin = off;  off = align256(off + (m > kMaxTokensPerLaunch ? (size_t)nproj * (mp / 16) * kRankChunks * 2 * kWave * 16 : 0));
+  w.t_fin = off;  off = align256(off + (m > 16 ? (size_t)nproj * (mp / 16) * kRankChunks * 2 * kWave * 16 : 0));
   w.pbuf = off;   off = align256(off + gemv_pbuf_bytes(m, k, projs, nproj, o));
-  w.t_fused = off; off = align256(off + (m <= 16 ? (size_t)kFusedItemsMax * kWave * 8 * 4 : 0));
-  w.cnt = off;    off = align256(off + kCountWords * 4);  // split-k counters, then the fused kernel's control words
   w.total = off;
   return w;
 }
@@ -142,6 +148,8 @@ struct PrologueArgs {
   float* t_part;
   uint32_t* cnt;  // arrival counters of the linear kernel, zeroed here
   int32_t ncnt;
+  u32x4* t_fin;       // or null: the last workgroup of each (pair group, token tile) also sums the LoRA-down chunk
+  uint32_t* t_cnt;    // partials into bf16 hi/lo fragments ([p][tile][jc][hi, lo][lane]); t_cnt: their arrivals
   int32_t tgs;    // tokens per workgroup: 16 (a whole token tile) or 4 (the tile split over four workgroups)
   int32_t pgm;    // pair groups per workgroup: 1, or 2 (h computed once for both, many tokens)
   QnDraw draw;    // noise drawn on the device (draw.on) instead of read from `noise`
@@ -344,6 +352,7 @@ __global__ void __launch_bounds__(kProWaves * kWave) k_prologue(PrologueArgs a) 
   __shared__ float s_rstd[16];
   __shared__ __attribute__((aligned(16))) uint16_t s_h[16][kHRow];
   __shared__ f32x4 s_red[kProWaves][2][kWave];
+  __shared__ int s_tlast;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
   // workgroup x = (token tile, token group): tokens [tlo, tlo + tgs) of the tile are this workgroup's (their
   // statistics, h, fragments and LoRA-down partials); the other tokens' h stays zero
@@ -553,8 +562,62 @@ __global__ void __launch_bounds__(kProWaves * kWave) k_prologue(PrologueArgs a) 
       for (int w = 0; w < kProWaves; ++w) v += s_red[w][g][src][q];
       const int jl = g * 16 + jr;  // rank within the 32-rank chunk
       const int L = (jl / 8) * 16 + tc;
-      if (mine(tc))
-        a.t_part[((((int64_t)p * ntiles + tile) * kRankChunks + jc) * a.ks + c) * kWave * 8 + L * 8 + jl % 8] = v;
+      float* const dst = a.t_part + ((((int64_t)p * ntiles + tile) * kRankChunks + jc) * a.ks + c) * kWave * 8 + L * 8 +
+                         jl % 8;
+      if (mine(tc)) {
+        if (a.t_fin) __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // read back below
+        else *dst = v;
+      }
+    }
+  }
+
+  // With t_fin (one pair group per workgroup): the last of the ks * ngpt workgroups of this (pair group, token tile)
+  // to arrive adds the chunk partials in chunk order (the order of every other reader of them) and stores t as bf16
+  // hi and lo B-fragments. The partials were written with device-scope stores that completed before the arrival and
+  // are read with device-coherent loads, so no cache-wide fence is needed. Waves 0 and 1 take ranks 0-3 and 4-7 of
+  // each lane's eight.
+  if (PGM == 1 && a.t_fin) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    uint32_t* const ctr = a.t_cnt + pz * ntiles + tile;
+    if (threadIdx.x == 0)
+      s_tlast = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                (uint32_t)(a.ks * ngpt - 1);
+    __syncthreads();
+    if (s_tlast && wave < 2) {
+      const int p = pgp[0], jc = pgjc[0];
+      const int64_t slot = ((int64_t)p * ntiles + tile) * kRankChunks + jc;
+      const rsrc_t src = make_rsrc(a.t_part + slot * a.ks * kWave * 8, (int64_t)a.ks * kWave * 8 * 4);
+      constexpr int kB = 16;  // chunk partials loaded together
+      f32x4 t = {0.f, 0.f, 0.f, 0.f};
+      for (int c0 = 0; c0 < a.ks; c0 += kB) {
+        u32x4 q[kB];
+#pragma unroll
+        for (int v = 0; v < kB; ++v)
+          q[v] = __builtin_amdgcn_raw_buffer_load_b128(
+              src, c0 + v < a.ks ? (uint32_t)((((c0 + v) * kWave + lane) * 8 + wave * 4) * 4) : kOutOfRange, 0,
+              kCoherent);
+#pragma unroll
+        for (int v = 0; v < kB; ++v)
+          if (c0 + v < a.ks) t = (c0 + v == 0) ? __builtin_bit_cast(f32x4, q[v]) : t + __builtin_bit_cast(f32x4, q[v]);
+      }
+      uint32_t hi[2], lo[2];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t th = f32_to_bf16(t[e]);
+        const uint32_t tl = f32_to_bf16(t[e] - bf16_to_f32((uint16_t)th));  // t - th is exact in f32
+        if (e % 2 == 0) {
+          hi[e / 2] = th;
+          lo[e / 2] = tl;
+        } else {
+          hi[e / 2] |= th << 16;
+          lo[e / 2] |= tl << 16;
+        }
+      }
+      uint32_t* const d = reinterpret_cast<uint32_t*>(a.t_fin + slot * 2 * kWave + lane) + wave * 2;
+      *reinterpret_cast<u32x2*>(d) = u32x2{hi[0], hi[1]};
+      *reinterpret_cast<u32x2*>(d + kWave * 4) = u32x2{lo[0], lo[1]};
+      if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -1001,6 +1064,117 @@ __device__ __forceinline__ int unit_proj(const ProjEpi* pe, int nproj, int64_t g
   return p;
 }
 
+// Split-k reduction and epilogue of the decode kernels. Thread t of the NTHR holds the sums (vsum) and LoRA terms
+// (vlo, valid in chunk 0) of outputs e = t + i * NTHR, i < KOUT, e = (unit * TMT*16 + token) * 16 + row, e < nout.
+// With a split k, every chunk stores its sums and the last workgroup of the row block to arrive adds them in chunk
+// order; the others return. The sums are written and read with device-scope relaxed atomic accesses, which go to
+// memory past the per-XCD L2 caches; the stores have completed (s_waitcnt) before the workgroup's barrier and its
+// arrival, so no cache-wide fence is needed (no L2 writeback or invalidation). Then y = s_g * sum + lambda * lora
+// (SILU: SiLU(gate) * up), + residual (s_res, in output order), broadcast and rounding.
+template <int TMT, bool SILU, int KOUT, int NTHR>
+__device__ __forceinline__ void gemv_finish(const GemvArgs& g, const ProjEpi* s_pe, const uint16_t* s_res, int* s_last,
+                                            float (&vsum)[KOUT][SILU ? 2 : 1], float (&vlo)[KOUT][SILU ? 2 : 1],
+                                            int nout, int b, int c, int u0) {
+  constexpr int NR = SILU ? 2 : 1;
+  constexpr int kOut = KOUT;
+  const LinearArgs& a = g.L;
+  const int mt = g.mt;
+  if (g.nk > 1) {
+    const int64_t PB = gemv_block_floats(NR, TMT);
+    float* pb = g.pbuf + (int64_t)b * (g.nk + 1) * PB;
+#pragma unroll
+    for (int i = 0; i < kOut; ++i) {
+      const int e = threadIdx.x + i * NTHR;
+      if (e >= nout) break;
+#pragma unroll
+      for (int nr = 0; nr < NR; ++nr) {
+        __hip_atomic_store(pb + (int64_t)c * PB + (int64_t)e * NR + nr, vsum[i][nr], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        if (c == 0)
+          __hip_atomic_store(pb + (int64_t)g.nk * PB + (int64_t)e * NR + nr, vlo[i][nr], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // every store of this thread has completed
+    __syncthreads();
+    if (threadIdx.x == 0)
+      *s_last = __hip_atomic_fetch_add(g.cnt + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               (uint32_t)(g.nk - 1);
+    __syncthreads();
+    if (!*s_last) return;
+    // every output's chunk sums, kRedBatch chunks per batch of loads issued together (one memory round trip per
+    // batch, where one load after another would cost a round trip each), added in chunk order
+    constexpr int kRedBatch = 8;
+#pragma unroll
+    for (int i = 0; i < kOut; ++i)
+#pragma unroll
+      for (int nr = 0; nr < NR; ++nr) vsum[i][nr] = 0.f;
+    for (int c0 = 0; c0 < g.nk; c0 += kRedBatch) {
+      float q[kOut][NR][kRedBatch];
+#pragma unroll
+      for (int i = 0; i < kOut; ++i) {
+        const int e = threadIdx.x + i * NTHR;
+#pragma unroll
+        for (int nr = 0; nr < NR; ++nr)
+#pragma unroll
+          for (int v = 0; v < kRedBatch; ++v)
+            q[i][nr][v] = (e < nout && c0 + v < g.nk)
+                              ? __hip_atomic_load(pb + (int64_t)(c0 + v) * PB + (int64_t)e * NR + nr, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT)
+                              : 0.f;
+        if (c0 == 0) {
+#pragma unroll
+          for (int nr = 0; nr < NR; ++nr)
+            vlo[i][nr] = e < nout ? __hip_atomic_load(pb + (int64_t)g.nk * PB + (int64_t)e * NR + nr,
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                  : 0.f;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kOut; ++i)
+#pragma unroll
+        for (int nr = 0; nr < NR; ++nr)
+#pragma unroll
+          for (int v = 0; v < kRedBatch; ++v) {
+            if (c0 + v >= g.nk) break;
+            vsum[i][nr] = (c0 + v == 0) ? q[i][nr][v] : vsum[i][nr] + q[i][nr][v];
+          }
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(g.cnt + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // 6. epilogue: y = s_g * sum + lambda * lora (SILU: SiLU(gate) * up), + residual, broadcast, rounding
+#pragma unroll
+  for (int i = 0; i < kOut; ++i) {
+    const int e = threadIdx.x + i * NTHR;
+    if (e >= nout) break;
+    const int u = (int)((unsigned)e / (TMT * 256)), tok = (e >> 4) & (TMT * 16 - 1), row = e & 15;
+    if (tok >= mt) continue;
+    const int64_t gu = u0 + u;
+    const int p0 = SILU ? 0 : unit_proj(s_pe, a.nproj, gu);
+    const ProjEpi& E = s_pe[p0];
+    const int64_t n = (SILU ? gu : gu - E.rg_begin) * 16 + row;
+    if (n >= E.n) continue;
+    float val[NR];
+#pragma unroll
+    for (int nr = 0; nr < NR; ++nr) {
+      const ProjEpi& F = s_pe[SILU ? nr : p0];
+      val[nr] = F.sg * vsum[i][nr] + F.lambda * vlo[i][nr];
+    }
+    float out = val[0];
+    if (SILU) out = val[0] / (1.0f + __expf(-val[0])) * val[NR - 1];
+    if (E.res) out += bf16_to_f32(s_res[e]);
+    const int64_t gtok = a.tok0 + tok;
+    const int rep = E.y_repeat > 1 ? E.y_repeat : 1;
+    for (int gi = 0; gi < rep; ++gi) {
+      const int64_t col_out = rep > 1 ? ((n / E.head_dim) * rep + gi) * E.head_dim + n % E.head_dim : n;
+      const int64_t off = gtok * E.ldy + col_out;
+      if (E.y_dtype == QN_F32) reinterpret_cast<float*>(E.y)[off] = out;
+      else reinterpret_cast<uint16_t*>(E.y)[off] = f32_to_bf16(out);
+    }
+  }
+}
+
 template <int TMT, bool SILU, int D>
 __global__ void __launch_bounds__(kGWaves * kWave) k_gemv(GemvArgs g) {
   constexpr int NR = SILU ? 2 : 1;
@@ -1331,104 +1505,421 @@ __global__ void __launch_bounds__(kGWaves * kWave) k_gemv(GemvArgs g) {
     }
   }
 
-  // 5. split k: store this chunk's sums (and, in chunk 0, the LoRA terms); the last workgroup of the block to arrive
-  //    adds the chunks in order. The sums are written and read with device-scope relaxed atomic accesses, which go
-  //    to memory past the per-XCD L2 caches; the stores have completed (s_waitcnt) before the workgroup's barrier and
-  //    its arrival. No cache-wide fence is needed, so no L2 writeback or invalidation.
-  if (g.nk > 1) {
-    const int64_t PB = gemv_block_floats(NR, TMT);
-    float* pb = g.pbuf + (int64_t)b * (g.nk + 1) * PB;
-#pragma unroll
-    for (int i = 0; i < kOut; ++i) {
-      const int e = threadIdx.x + i * kGWaves * kWave;
-      if (e >= nout) break;
-#pragma unroll
-      for (int nr = 0; nr < NR; ++nr) {
-        __hip_atomic_store(pb + (int64_t)c * PB + (int64_t)e * NR + nr, vsum[i][nr], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-        if (c == 0)
-          __hip_atomic_store(pb + (int64_t)g.nk * PB + (int64_t)e * NR + nr, vlo[i][nr], __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // every store of this thread has completed
-    __syncthreads();
-    if (threadIdx.x == 0)
-      s_last = __hip_atomic_fetch_add(g.cnt + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-               (uint32_t)(g.nk - 1);
-    __syncthreads();
-    if (!s_last) return;
-    // every output's chunk sums, kRedBatch chunks per batch of loads issued together (one memory round trip per
-    // batch, where one load after another would cost a round trip each), added in chunk order
-    constexpr int kRedBatch = 8;
-#pragma unroll
-    for (int i = 0; i < kOut; ++i)
-#pragma unroll
-      for (int nr = 0; nr < NR; ++nr) vsum[i][nr] = 0.f;
-    for (int c0 = 0; c0 < g.nk; c0 += kRedBatch) {
-      float q[kOut][NR][kRedBatch];
-#pragma unroll
-      for (int i = 0; i < kOut; ++i) {
-        const int e = threadIdx.x + i * kGWaves * kWave;
-#pragma unroll
-        for (int nr = 0; nr < NR; ++nr)
-#pragma unroll
-          for (int v = 0; v < kRedBatch; ++v)
-            q[i][nr][v] = (e < nout && c0 + v < g.nk)
-                              ? __hip_atomic_load(pb + (int64_t)(c0 + v) * PB + (int64_t)e * NR + nr, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT)
-                              : 0.f;
-        if (c0 == 0) {
-#pragma unroll
-          for (int nr = 0; nr < NR; ++nr)
-            vlo[i][nr] = e < nout ? __hip_atomic_load(pb + (int64_t)g.nk * PB + (int64_t)e * NR + nr,
-                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                  : 0.f;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < kOut; ++i)
-#pragma unroll
-        for (int nr = 0; nr < NR; ++nr)
-#pragma unroll
-          for (int v = 0; v < kRedBatch; ++v) {
-            if (c0 + v >= g.nk) break;
-            vsum[i][nr] = (c0 + v == 0) ? q[i][nr][v] : vsum[i][nr] + q[i][nr][v];
-          }
-    }
-    if (threadIdx.x == 0) __hip_atomic_store(g.cnt + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  gemv_finish<TMT, SILU, kOut, kGWaves * kWave>(g, s_pe, s_res, &s_last, vsum, vlo, nout, b, c, u0);
+}
 
-  // 6. epilogue: y = s_g * sum + lambda * lora (SILU: SiLU(gate) * up), + residual, broadcast, rounding
+// ------------------------------------------------------------------------------------------------------------------
+// W: decode kernel for 17 to 64 tokens (TMT = 2 or 4 token tiles). At these token counts the activations of a whole
+// k-chunk no longer fit in LDS beside the rows' work, so they stream through it. A chunk's k-tiles are taken in passes
+// of kWH; a pass's activation fragments and tile scales are loaded straight into one of NB LDS buffers, LA = NB - 1
+// passes ahead, while the waves compute the current pass from another. Stream wave w serves unit slot w / kWH and
+// the k-tile w % kWH of every pass, so all stream waves move through k together and every activation tile in LDS
+// feeds all units of the workgroup: activations are read once per workgroup, weights once. Each wave keeps its own
+// weight tiles LW passes ahead in registers. One barrier per pass (after each wave's own loads into the pass's
+// buffer have landed) publishes the buffer and frees the one filled next. Every buffer is an LDS array of its own,
+// so the compiler sees that the fills in flight never overlap the buffer being read and adds no wait for them.
+// Wave 15 computes the LoRA-up of the block's units from the finished LoRA-down t (bf16 hi and lo fragments) and the
+// rows of B, one (projection, 32-rank chunk) at a time while the stream runs. Parts of a unit from its kWH waves
+// meet in LDS after the stream; split k and the epilogue are those of the decode kernel.
+constexpr int kWWaves = 16;
+constexpr int kWStream = 15;
+constexpr int kWH = 3;                   // k-tiles per pass = stream waves per unit
+constexpr int kWSlots = kWStream / kWH;  // units per workgroup (at most)
+constexpr int kWPiece = kWave * 16;      // bytes of one load into LDS (16 per lane)
+__host__ __device__ constexpr int wide_nbuf(int tmt) { return tmt <= 2 ? 4 : 2; }
+__host__ __device__ constexpr int wide_frag_pieces(int tmt) { return kWH * tmt * 4; }
+// a pass's buffer: its fragments [tt][j][s][lane], then one piece holding the tile scales [tt][j][16] (f32)
+__host__ __device__ constexpr int wide_buf_bytes(int tmt) { return (wide_frag_pieces(tmt) + 1) * kWPiece; }
+// loads into LDS per stream wave and pass (the spare ones go to a scratch piece, so every wave issues as many)
+__host__ __device__ constexpr int wide_fills(int tmt) { return (wide_frag_pieces(tmt) + 1 + kWStream - 1) / kWStream; }
+
+struct WideArgs {
+  GemvArgs G;           // rows, chunks, part sums and counters as in the decode kernel (nu counts units)
+  const u32x4* t_fin;   // LoRA-down t as bf16 hi/lo B-fragments, [p][tile][jc][hi, lo][lane] x 16 bytes
+  int64_t t_fin_bytes;
+};
+
+template <int TMT, bool SILU, int LW>
+__global__ void __launch_bounds__(kWWaves * kWave) k_wgemv(WideArgs wa) {
+  constexpr int NR = SILU ? 2 : 1;
+  constexpr int NB = wide_nbuf(TMT), LA = NB - 1;
+  constexpr int UF = NB > LW + 1 ? NB : LW + 1;  // passes per loop step: buffers and weight slots stay constant indices
+  static_assert(UF % NB == 0 && UF % (LW + 1) == 0 && LW >= LA, "pass pipeline");
+  constexpr int kBuf = wide_buf_bytes(TMT), kFrag = wide_frag_pieces(TMT), kFills = wide_fills(TMT);
+  constexpr int kTW = 2 * NR;  // weight loads per stream wave and pass
+  constexpr int kOut = (kWSlots * TMT * 256 + kWWaves * kWave - 1) / (kWWaves * kWave);
+  __shared__ __attribute__((aligned(16))) uint8_t s_b0[kBuf];
+  __shared__ __attribute__((aligned(16))) uint8_t s_b1[kBuf];
+  __shared__ __attribute__((aligned(16))) uint8_t s_b2[NB > 2 ? kBuf : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_b3[NB > 3 ? kBuf : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_spare[kWPiece];
+  __shared__ __attribute__((aligned(16))) uint8_t s_lora[kWSlots * NR * TMT * kWPiece];  // LoRA-up [u][nr][tt][lane]
+  __shared__ uint16_t s_res[kWSlots * TMT * 16 * 16];  // residual of each output (epilogue order)
+  __shared__ ProjEpi s_pe[kMaxProj];
+  __shared__ int s_last;
+  auto buf = [&](int i) __attribute__((always_inline)) -> uint8_t* {  // (i is a constant wherever this is called)
+    return i == 0 ? s_b0 : (i == 1 ? s_b1 : (i == 2 ? s_b2 : s_b3));
+  };
+  const GemvArgs& g = wa.G;
+  const LinearArgs& a = g.L;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+  const unsigned bid = blockIdx.x, nbr = (unsigned)g.nbr, nk = (unsigned)g.nk;
+  const int b = (int)(bid % nbr), c = (int)(bid / nbr);
+  const int KT = g.KT, ntiles = g.ntiles;
+  const int u0 = (int)((unsigned)b * (unsigned)g.nu / nbr);
+  const int U = (int)((unsigned)(b + 1) * (unsigned)g.nu / nbr) - u0;
+  const int t0 = (int)((unsigned)c * (unsigned)KT / nk), T = (int)((unsigned)(c + 1) * (unsigned)KT / nk) - t0;
+  const int ntl = ntiles < TMT ? ntiles : TMT;  // token tiles present (one launch covers every token)
+  const int NP = (T + kWH - 1) / kWH;          // passes
+  const bool stream_w = wave < kWStream;
+  const int su = stream_w ? wave / kWH : 0, j = stream_w ? wave % kWH : 0;
+  const bool live = stream_w && su < U;
+
+  // epilogue parameters and the residual of this thread's outputs, requested before anything else (the stream waves'
+  // wait counts below cover only the loads issued after them)
+  if (threadIdx.x < kMaxProj) {
+#pragma unroll
+    for (int q = 0; q < kMaxProj; ++q)
+      if (threadIdx.x == q && q < a.nproj) {
+        const ProjArgs& P = a.p[q];
+        s_pe[q] = ProjEpi{P.y, P.res, P.n, P.ldy, P.ld_res, gload(P.s_g), P.lambda, P.y_dtype, P.y_repeat,
+                          P.head_dim, P.rg_begin, P.r};
+      }
+  }
+  uint16_t res[kOut];
 #pragma unroll
   for (int i = 0; i < kOut; ++i) {
-    const int e = threadIdx.x + i * kGWaves * kWave;
-    if (e >= nout) break;
-    const int u = e >> (TMT == 1 ? 8 : 9), tok = (e >> 4) & (TMT * 16 - 1), row = e & 15;
-    if (tok >= mt) continue;
+    const int e = threadIdx.x + i * kWWaves * kWave;
+    const int u = (int)((unsigned)e / (TMT * 256)), tok = (e >> 4) & (TMT * 16 - 1), row = e & 15;
     const int64_t gu = u0 + u;
-    const int p0 = SILU ? 0 : unit_proj(s_pe, a.nproj, gu);
-    const ProjEpi& E = s_pe[p0];
-    const int64_t n = (SILU ? gu : gu - E.rg_begin) * 16 + row;
-    if (n >= E.n) continue;
-    float val[NR];
+    const uint16_t* rb = a.p[0].res;
+    int64_t rbeg = 0, nl = a.p[0].n, ld = a.p[0].ld_res;
+    if (!SILU) {
+#pragma unroll
+      for (int q = 1; q < kMaxProj; ++q)
+        if (q < a.nproj && gu >= a.p[q].rg_begin) {
+          rb = a.p[q].res;
+          rbeg = a.p[q].rg_begin;
+          nl = a.p[q].n;
+          ld = a.p[q].ld_res;
+        }
+    }
+    const int64_t n = (gu - rbeg) * 16 + row;
+    const bool ok = rb && u < U && tok < g.mt && n < nl;
+    res[i] = gload(ok ? rb + tok * ld + n : reinterpret_cast<const uint16_t*>(a.xsc));
+  }
+
+  // weights of this wave's unit: k-tile t0 + q*kWH + j of pass q (past the chunk: out of range, reads 0)
+  rsrc_t cd[NR], sd[NR];
+#pragma unroll
+  for (int nr = 0; nr < NR; ++nr) {
+    const int64_t gu = u0 + su;
+    int p = nr;
+    if (!SILU) {
+      p = 0;
+      for (int q = 1; q < a.nproj; ++q)
+        if (gu >= a.p[q].rg_begin) p = q;
+      p = __builtin_amdgcn_readfirstlane(p);
+    }
+    const ProjArgs& P = a.p[p];
+    const int64_t rg = SILU ? gu : gu - P.rg_begin;
+    const bool ok = live && rg * 16 < P.n;
+    cd[nr] = make_rsrc(P.codes + rg * KT * kTileCodeBytes, ok ? KT * kTileCodeBytes : 0);
+    sd[nr] = make_rsrc(P.scales + rg * KT * kTileScaleBytes, ok ? KT * kTileScaleBytes : 0);
+  }
+  const uint32_t c_off = lane * 16, s_off = ((lane % 16) * 2 + (lane / 16) / 2) * 4;
+  auto wload = [&](GTile<NR>& t, int q) __attribute__((always_inline)) {
+    const bool in = q * kWH + j < T;
+    const int kt = t0 + q * kWH + j;
+    const int kc = __builtin_amdgcn_readfirstlane(in ? kt * kTileCodeBytes : 0);
+    const int ks = __builtin_amdgcn_readfirstlane(in ? kt * kTileScaleBytes : 0);
 #pragma unroll
     for (int nr = 0; nr < NR; ++nr) {
-      const ProjEpi& F = s_pe[SILU ? nr : p0];
-      val[nr] = F.sg * vsum[i][nr] + F.lambda * vlo[i][nr];
+      t.c[nr] = __builtin_amdgcn_raw_buffer_load_b128(cd[nr], in ? c_off : kOutOfRange, kc, kNonTemporal);
+      t.sc[nr] = __builtin_amdgcn_raw_buffer_load_b32(sd[nr], in ? s_off : kOutOfRange, ks, kNonTemporal);
     }
-    float out = val[0];
-    if (SILU) out = val[0] / (1.0f + __expf(-val[0])) * val[NR - 1];
-    if (E.res) out += bf16_to_f32(s_res[e]);
-    const int64_t gtok = a.tok0 + tok;
-    const int rep = E.y_repeat > 1 ? E.y_repeat : 1;
-    for (int gi = 0; gi < rep; ++gi) {
-      const int64_t col_out = rep > 1 ? ((n / E.head_dim) * rep + gi) * E.head_dim + n % E.head_dim : n;
-      const int64_t off = gtok * E.ldy + col_out;
-      if (E.y_dtype == QN_F32) reinterpret_cast<float*>(E.y)[off] = out;
-      else reinterpret_cast<uint16_t*>(E.y)[off] = f32_to_bf16(out);
+  };
+  // activations of pass q into LDS buffer dst: load slot i*kWStream + wave is fragment piece (tt, jj, s) =
+  // (sl / (4*kWH), sl / 4 % kWH, sl % 4), then the scale piece, then spare loads (out of range, to the spare piece)
+  const rsrc_t xsrc = make_rsrc(a.xs, (int64_t)ntl * KT * 4 * kWave * 16);
+  const rsrc_t ssrc = make_rsrc(a.xsc, (int64_t)ntl * KT * 16 * 4);
+  auto fill = [&](uint8_t* dst, int q) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kFills; ++i) {
+      const int sl = i * kWStream + wave;
+      if (sl < kFrag) {
+        const int tt = sl / (4 * kWH), jj = (sl / 4) % kWH, s = sl % 4;
+        const bool ok = q * kWH + jj < T && tt < ntl;
+        const int so = __builtin_amdgcn_readfirstlane(ok ? ((tt * KT + t0 + q * kWH + jj) * 4 + s) * kWPiece : 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xsrc, (__attribute__((address_space(3))) void*)(dst + sl * kWPiece),
+                                                 16, ok ? lane * 16 : kOutOfRange, so, 0, 0);
+      } else if (sl == kFrag) {
+        const int tt = lane / (4 * kWH), jj = (lane / 4) % kWH, qd = lane % 4;
+        const bool ok = lane < TMT * kWH * 4 && q * kWH + jj < T && tt < ntl;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ssrc, (__attribute__((address_space(3))) void*)(dst + kFrag * kWPiece), 16,
+            ok ? (uint32_t)(((tt * KT + t0 + q * kWH + jj) * 16 + qd * 4) * 4) : kOutOfRange, 0, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xsrc, (__attribute__((address_space(3))) void*)s_spare, 16,
+                                                 kOutOfRange, 0, 0, 0);
+      }
+    }
+  };
+
+  f32x4 acc[NR][TMT];
+#pragma unroll
+  for (int nr = 0; nr < NR; ++nr)
+#pragma unroll
+    for (int tt = 0; tt < TMT; ++tt) acc[nr][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // pass q from buffer B with weights t. A wave whose k-tile lies past the chunk has zero weights and reads the
+  // pass's last k-tile in range (finite values), so it adds exactly zero.
+  auto compute = [&](const uint8_t* B, const GTile<NR>& t, int q) __attribute__((always_inline)) {
+    const int jl = T - q * kWH - 1;
+    const int jj = j < jl ? j : jl;
+    f32x4 part[NR][TMT];
+#pragma unroll
+    for (int nr = 0; nr < NR; ++nr)
+#pragma unroll
+      for (int tt = 0; tt < TMT; ++tt) part[nr][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 bf[TMT];
+#pragma unroll
+      for (int tt = 0; tt < TMT; ++tt)
+        bf[tt] = *reinterpret_cast<const u32x4*>(B + ((tt * kWH + jj) * 4 + s) * kWPiece + lane * 16);
+#pragma unroll
+      for (int nr = 0; nr < NR; ++nr) {
+        const uint32_t scv = ((t.sc[nr] >> (8 * s)) & 0xFFu) * 0x00800080u;  // E4M3 byte << 7 = E4M3 * 2^-8 in f16
+        const f16x2 sh = as_f16x2(scv);
+        const uint32_t cw = t.c[nr][s];
+        const f16x2 q0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 256.0f, 0) * sh;
+        const f16x2 q1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 256.0f, 1) * sh;
+        const f16x2 q2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 256.0f, 2) * sh;
+        const f16x2 q3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 256.0f, 3) * sh;
+        const f16x8 wv = {q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
+#pragma unroll
+        for (int tt = 0; tt < TMT; ++tt)
+          part[nr][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, __builtin_bit_cast(f16x8, bf[tt]), part[nr][tt],
+                                                                0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one slice's fragments live at a time
+    }
+#pragma unroll
+    for (int tt = 0; tt < TMT; ++tt) {
+      const float u = *reinterpret_cast<const float*>(B + kFrag * kWPiece + ((tt * kWH + jj) * 16 + lane % 16) * 4);
+#pragma unroll
+      for (int nr = 0; nr < NR; ++nr)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[nr][tt][e] = __builtin_fmaf(part[nr][tt][e], u, acc[nr][tt][e]);
+    }
+  };
+
+  // LoRA-up items of wave 15 (chunk 0 only): (projection p, rank chunk jc) over the block's units, in order. Item i:
+  // the B rows of the units of projection p (16 rows x ranks jc*32 + 8 (lane/16) .. + 8) and t of every token tile.
+  int pfirst = 0, nitems = 0;
+  if (SILU) {
+    nitems = a.nproj >= 2 ? (int)ceil_div(a.p[0].r, 32) + (int)ceil_div(a.p[1].r, 32) : 0;
+  } else {
+    int pl = 0;
+    for (int q = 1; q < a.nproj; ++q) {
+      if (u0 >= a.p[q].rg_begin) pfirst = q;
+      if (u0 + U - 1 >= a.p[q].rg_begin) pl = q;
+    }
+    for (int q = pfirst; q <= pl; ++q) nitems += (int)ceil_div(a.p[q].r, 32);
+  }
+  const bool lora_w = wave == kWStream && c == 0;
+  if (!lora_w) nitems = 0;
+  nitems = __builtin_amdgcn_readfirstlane(nitems);
+  auto item_of = [&](int it, int* p_out, int* jc_out) __attribute__((always_inline)) {
+    int p = SILU ? 0 : pfirst, rem = it;
+    for (int q = p; q < kMaxProj; ++q) {
+      const int n = q < a.nproj ? (int)ceil_div(a.p[q].r, 32) : 0;
+      if (rem < n) { p = q; break; }
+      rem -= n;
+    }
+    *p_out = p;
+    *jc_out = rem;
+  };
+  // (projection of unit gu from the kernel arguments: wave 15 works before any barrier has published s_pe)
+  auto unit_proj_arg = [&](int gu) __attribute__((always_inline)) {
+    int p = 0;
+    for (int q = 1; q < a.nproj; ++q)
+      if (gu >= a.p[q].rg_begin) p = q;
+    return p;
+  };
+  struct LItem {
+    u32x4 b[kWSlots], th[TMT], tl[TMT];
+  };
+  const rsrc_t tsrc = make_rsrc(wa.t_fin, wa.t_fin_bytes);
+  auto item_issue = [&](LItem& L, int it) __attribute__((always_inline)) {
+    int p, jc;
+    item_of(it, &p, &jc);
+    const ProjArgs* P = &a.p[0];
+#pragma unroll
+    for (int q = 1; q < kMaxProj; ++q)
+      if (q == p) P = &a.p[q];
+    const int r = P->r;
+    const rsrc_t bsrc = make_rsrc(P->B, P->n * r * 2);
+    const int nrows = (int)P->n;  // (n * r * 2 < 2^31: checked on the host)
+#pragma unroll
+    for (int u = 0; u < kWSlots; ++u) {
+      const int gu = u0 + u;
+      const bool mine = u < U && (SILU || unit_proj_arg(gu) == p);
+      const int n = (SILU ? gu : gu - P->rg_begin) * 16 + lane % 16;
+      const int j0 = jc * 32 + (lane / 16) * 8;
+      if (r % 8 == 0) {
+        L.b[u] = bload16(bsrc, (mine && n < nrows && j0 < r) ? (uint32_t)((n * r + j0) * 2) : kOutOfRange);
+      } else {
+        uint32_t w4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t off = (uint32_t)((n * r + j0 + 2 * e) * 2);
+          const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(
+              bsrc, (mine && n < nrows && j0 + 2 * e < r) ? off : kOutOfRange, 0, 0);
+          const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(
+              bsrc, (mine && n < nrows && j0 + 2 * e + 1 < r) ? off + 2 : kOutOfRange, 0, 0);
+          w4[e] = lo | (hi << 16);
+        }
+        L.b[u] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < TMT; ++tt) {
+      const uint32_t off = (uint32_t)(((((int64_t)p * ntiles + tt) * kRankChunks + jc) * 2 * kWave + lane) * 16);
+      L.th[tt] = bload16(tsrc, tt < ntl ? off : kOutOfRange);
+      L.tl[tt] = bload16(tsrc, tt < ntl ? off + kWave * 16 : kOutOfRange);
+    }
+  };
+  auto item_finish = [&](const LItem& L, int it) __attribute__((always_inline)) {
+    int p, jc;
+    item_of(it, &p, &jc);
+    const int nr = SILU ? p : 0;
+#pragma unroll
+    for (int u = 0; u < kWSlots; ++u) {
+      if (u >= U) break;
+      if (!SILU && unit_proj_arg(u0 + u) != p) continue;
+#pragma unroll
+      for (int tt = 0; tt < TMT; ++tt) {
+        f32x4 la = {0.f, 0.f, 0.f, 0.f};
+        la = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, L.b[u]), __builtin_bit_cast(bf16x8, L.th[tt]),
+                                                     la, 0, 0, 0);
+        la = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, L.b[u]), __builtin_bit_cast(bf16x8, L.tl[tt]),
+                                                     la, 0, 0, 0);
+        mfma_settle(la);
+        f32x4* slot = reinterpret_cast<f32x4*>(s_lora + (((u * NR + nr) * TMT + tt) * kWave + lane) * 16);
+        *slot = jc == 0 ? la : *slot + la;
+      }
+    }
+  };
+
+  // prologue: the first weight tiles and the first LA passes' activations, in the order of the pipeline: weights
+  // W(0 .. LW-LA-1), then (fill(s), W(s + LW - LA)) for s < LA; each pass q then issues (fill(q + LA), W(q + LW)).
+  // At the top of pass q the loads issued after fill(q) are W(q + LW - LA) and LA - 1 more (fill, W) pairs.
+  GTile<NR> Wt[LW + 1];
+  if (stream_w) {
+#pragma unroll
+    for (int s = 0; s < LW - LA; ++s) wload(Wt[s], s);
+#pragma unroll
+    for (int s = 0; s < LA; ++s) {
+      fill(buf(s), s);
+      wload(Wt[s + LW - LA], s + LW - LA);
     }
   }
+#pragma unroll
+  for (int i = 0; i < kOut; ++i) s_res[threadIdx.x + i * kWWaves * kWave] = res[i];
+  constexpr int kWaitFill = vmcnt_imm(kTW + (LA - 1) * (kFills + kTW));
+
+  // The stream waves and wave 15 run loops of their own with the same barriers (one per pass, UF passes per step),
+  // so that the registers of the one are not held across the other's code.
+  // (a plain barrier: a workgroup fence would also wait for the fills still in flight)
+  if (stream_w) {
+    for (int q0 = 0; q0 < NP; q0 += UF) {
+#pragma unroll
+      for (int i = 0; i < UF; ++i) {
+        const int q = q0 + i;
+        __builtin_amdgcn_s_waitcnt(kWaitFill);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        fill(buf((i + LA) % NB), q + LA);
+        wload(Wt[(i + LW) % (LW + 1)], q + LW);
+        __builtin_amdgcn_sched_barrier(0);
+        if (live && q < NP) compute(buf(i % NB), Wt[i % (LW + 1)], q);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // no load into LDS is in flight when the buffers are reused below
+  } else {
+    // wave 15: the first two items before the first barrier (their memory round trips overlap the stream waves'
+    // first loads), then one per pass
+    LItem L0;
+    if (nitems > 0) item_issue(L0, 0);
+    if (nitems > 0) item_finish(L0, 0);
+    if (nitems > 1) item_issue(L0, 1);
+    if (nitems > 1) item_finish(L0, 1);
+    int it = 2;
+    if (it < nitems) item_issue(L0, it);
+    for (int q0 = 0; q0 < NP; q0 += UF) {
+#pragma unroll
+      for (int i = 0; i < UF; ++i) {
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (it < nitems) {
+          item_finish(L0, it);
+          if (++it < nitems) item_issue(L0, it);
+        }
+      }
+    }
+    for (; it < nitems; ++it) {  // items left when the passes are few
+      item_finish(L0, it);
+      if (it + 1 < nitems) item_issue(L0, it + 1);
+    }
+  }
+  __syncthreads();
+
+  // parts of phases 1 and 2 of each unit into buffers 0 and 1; phase 0 adds them (in phase order) and leaves the sum
+  // in buffer 0
+  auto part_slot = [&](uint8_t* B, int nr, int tt) __attribute__((always_inline)) {
+    return reinterpret_cast<f32x4*>(B + ((((su * NR + nr) * TMT + tt) * kWave) + lane) * 16);
+  };
+  if (live && j > 0) {
+#pragma unroll
+    for (int nr = 0; nr < NR; ++nr)
+#pragma unroll
+      for (int tt = 0; tt < TMT; ++tt) *part_slot(j == 1 ? s_b0 : s_b1, nr, tt) = acc[nr][tt];
+  }
+  __syncthreads();
+  if (live && j == 0) {
+#pragma unroll
+    for (int nr = 0; nr < NR; ++nr)
+#pragma unroll
+      for (int tt = 0; tt < TMT; ++tt) {
+        f32x4 v = acc[nr][tt] + *part_slot(s_b0, nr, tt);
+        v += *part_slot(s_b1, nr, tt);
+        *part_slot(s_b0, nr, tt) = v;
+      }
+  }
+  __syncthreads();
+
+  const bool has_lora = c == 0;  // LoRA terms were computed in chunk 0 (read only where the projection has an adapter)
+  const int nout = U * TMT * 256;
+  float vsum[kOut][NR], vlo[kOut][NR];
+#pragma unroll
+  for (int i = 0; i < kOut; ++i) {
+    const int e = threadIdx.x + i * kWWaves * kWave;
+    const int u = (int)((unsigned)e / (TMT * 256)), tok = (e >> 4) & (TMT * 16 - 1), row = e & 15;
+    const int tt = tok / 16, col = tok % 16;
+    const int ln = (row / 4) * 16 + col, ii = row % 4;
+#pragma unroll
+    for (int nr = 0; nr < NR; ++nr) {
+      float s = 0.f, lo = 0.f;
+      if (e < nout) {
+        s = reinterpret_cast<const float*>(s_b0 + ((((u * NR + nr) * TMT + tt) * kWave) + ln) * 16)[ii];
+        if (has_lora && s_pe[SILU ? nr : unit_proj(s_pe, a.nproj, u0 + u)].r > 0)
+          lo = reinterpret_cast<const float*>(s_lora + ((((u * NR + nr) * TMT + tt) * kWave) + ln) * 16)[ii];
+      }
+      vsum[i][nr] = s;
+      vlo[i][nr] = lo;
+    }
+  }
+  gemv_finish<TMT, SILU, kOut, kWWaves * kWave>(g, s_pe, s_res, &s_last, vsum, vlo, nout, b, c, u0);
 }
 
 // ------------------------------------------------------------------------------------------------------------------
@@ -1453,7 +1944,6 @@ constexpr int kFRedBytes = kFLoraWaves * 2 * kWave * 16;      // their sums (top
 constexpr int kFMaxItems = kFusedItemsMax;
 constexpr int kFItemTiles = 4;                                // k-tiles per LoRA-down item without a split k
 constexpr uint32_t kFSpin = 1u << 24;                         // polls before a wait gives up (about a second)
-constexpr int kCoherent = 16;                                 // cache policy sc1: device-coherent, past the XCD's L2
 __host__ __device__ constexpr int fused_lds_top(int nr) {     // LDS bytes above the fragments and tile scales
   return gemv_lred_bytes(nr, 1) > kFRedBytes ? gemv_lred_bytes(nr, 1) : kFRedBytes;
 }
@@ -2198,7 +2688,7 @@ struct Opts {
 };
 
 inline bool opts_valid(const Opts& o) {
-  return o.kernel >= QN_KERNEL_AUTO && o.kernel <= QN_KERNEL_FUSED && o.nk >= 0 && o.nk <= 64 &&
+  return o.kernel >= QN_KERNEL_AUTO && o.kernel <= QN_KERNEL_WIDE && o.nk >= 0 && o.nk <= 64 &&
          (o.depth == 0 || o.depth == 2 || o.depth == 3) && o.rows >= 0 && o.waves >= 0 && (o.rows > 0) == (o.waves > 0) &&
          (o.elem == 0 || o.elem == 1);
 }
@@ -2219,13 +2709,42 @@ inline Opts opts_of(const qn_linear_opts* p) {
 // Which streaming kernel serves a call: the many-token MFMA kernel, the decode kernel (with its cut) or the general
 // kernel. Decided on the host before anything is launched; QN_ERR_UNSUPPORTED if the options name a kernel that
 // cannot serve the call.
-enum MainPath { kPathGeneral = 0, kPathDecode = 1, kPathMany = 2, kPathFused = 3 };
+enum MainPath { kPathGeneral = 0, kPathDecode = 1, kPathMany = 2, kPathFused = 3, kPathWide = 4 };
 struct Plan {
   MainPath path = kPathGeneral;
   GemvCut cut{0, 0};
   int depth = 3;
   int ctl_k = 0, nkc = 0, npairs = 0;  // fused decode kernel: LoRA-down items (see FusedArgs)
 };
+
+// Row blocks x k-chunks of the decode kernel for 17-64 tokens: at most kWSlots units per block, and with a split k
+// at most 256 blocks (one arrival counter each). Measured on the 7B shapes at 32-64 tokens, a launch is fastest in one round of workgroups
+// (a second round costs about as much as the first, more than the passes it saves) and, within one round, with the
+// fewest passes per workgroup; so the cut is the one-round cut with the fewest passes (ties: fewer k-chunks, then
+// fewer units per block), else the cut with the fewest rounds x passes. nk_only > 0: that many k-chunks, with the
+// fewest units per block that keep one round.
+constexpr double kWideMinBytes = 24e6;
+inline GemvCut wide_cut(int64_t nu, int64_t KT, int tmt, int nr, int nk_only) {
+  (void)tmt;
+  (void)nr;
+  GemvCut best{0, 0};
+  int64_t best_key = INT64_MAX;
+  for (int64_t nk = 1; nk <= KT && nk <= 64; ++nk) {
+    if (nk_only > 0 && nk != nk_only) continue;
+    for (int64_t U = 1; U <= kWSlots; ++U) {
+      const int64_t nbr = ceil_div(nu, U);
+      if (nk > 1 && nbr > 256) continue;  // (a split k has one arrival counter per block)
+      if (nbr > 16384) continue;  // (the kernel forms block * units in 32 bits)
+      const int64_t rounds = ceil_div(nbr * nk, 256), passes = ceil_div(ceil_div(KT, nk), kWH);
+      const int64_t key = (((rounds > 1 ? 1 : 0) * 4096 + rounds * passes) * 128 + nk) * 8 + U;
+      if (key < best_key) {
+        best_key = key;
+        best = GemvCut{(int)nbr, (int)nk};
+      }
+    }
+  }
+  return best;
+}
 
 // The fused decode kernel's plan, if it can serve the call: up to 16 tokens, a cut whose chunk fits in LDS beside
 // the LoRA-down reduction, with the norm no split k (the row statistics come from the chunk), and LoRA-down items
@@ -2275,6 +2794,24 @@ inline qn_status plan_main(int64_t m, int64_t KT, int64_t nu, bool silu, bool no
     *out = pl;
     return QN_OK;
   }
+  // AUTO takes the decode kernel for 17-64 tokens for calls with at least kWideMinBytes of weights (measured on the
+  // 7B/32B shapes: the wide feed-forward projections and the long-row down projection run 1.2-2.3x faster than on
+  // the general kernel; smaller projections, such as q|k|v and o, ran as fast or faster on the general kernel)
+  // and a cut that fits in one round of workgroups
+  bool wide_auto = o.kernel == QN_KERNEL_AUTO && m > 16 && m <= 64 && o.depth != 2 &&
+                   (double)nu * KT * nr * 1152.0 >= kWideMinBytes;
+  if (wide_auto) {
+    const GemvCut c = wide_cut(nu, KT, m <= 32 ? 2 : 4, nr, o.nk);
+    wide_auto = c.nbr > 0 && (int64_t)c.nbr * c.nk <= 256;
+  }
+  if (o.kernel == QN_KERNEL_WIDE || wide_auto) {
+    if (m <= 16 || m > 64 || (o.depth != 0 && o.depth != 3)) return QN_ERR_UNSUPPORTED;
+    pl.path = kPathWide;
+    pl.cut = wide_cut(nu, KT, m <= 32 ? 2 : 4, nr, o.nk);
+    if (pl.cut.nbr <= 0) return QN_ERR_UNSUPPORTED;
+    *out = pl;
+    return QN_OK;
+  }
   if (o.kernel == QN_KERNEL_MANY || (o.kernel == QN_KERNEL_AUTO && m > kMaxTokensPerLaunch)) {
     if (m <= kMaxTokensPerLaunch) return QN_ERR_UNSUPPORTED;
     pl.path = kPathMany;
@@ -2295,8 +2832,9 @@ inline qn_status plan_main(int64_t m, int64_t KT, int64_t nu, bool silu, bool no
 
 // Split-k part sums of the decode kernel (none without a split).
 size_t gemv_pbuf_bytes(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj, const Opts& o) {
-  if (!projs || nproj < 1 || m < 1 || m > 32) return 0;
-  const int tmt = (int)ceil_div(m, 16);
+  if (!projs || nproj < 1 || m < 1 || m > 64) return 0;
+  int tmt = (int)ceil_div(m, 16);
+  if (tmt == 3) tmt = 4;  // (the wide decode kernel's token tiles)
   const int64_t KT = ceil_div(k, kKTile);
   int64_t nu_flat = 0;
   for (int p = 0; p < nproj; ++p) nu_flat += ceil_div(projs[p].n, 16);
@@ -2310,7 +2848,7 @@ size_t gemv_pbuf_bytes(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj
         if (plan_main(m, KT, silu ? ceil_div(projs[0].n, 16) : nu_flat, silu, norm != 0, projs, nproj, o, fused != 0,
                       &pl) != QN_OK)
           continue;
-        if ((pl.path != kPathDecode && pl.path != kPathFused) || pl.cut.nk <= 1) continue;
+        if ((pl.path != kPathDecode && pl.path != kPathFused && pl.path != kPathWide) || pl.cut.nk <= 1) continue;
         const size_t b = (size_t)pl.cut.nbr * (pl.cut.nk + 1) * gemv_block_floats(silu ? 2 : 1, tmt) * 4;
         bytes = b > bytes ? b : bytes;
       }
@@ -3082,6 +3620,11 @@ qn_status run_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const
     pa.t_part = t_part;
     pa.cnt = reinterpret_cast<uint32_t*>(ws + wl.cnt);
     pa.ncnt = kCountWords;
+    // the decode kernel for 17-64 tokens takes t summed (its LoRA wave then needs one memory round trip per item)
+    if (plan.path == kPathWide) {
+      pa.t_fin = reinterpret_cast<u32x4*>(ws + wl.t_fin);
+      pa.t_cnt = reinterpret_cast<uint32_t*>(ws + wl.cnt) + kCountWords;
+    }
     // many tokens: row statistics in a kernel of their own (rstd with the norm, and one exponent per token)
     const bool big = m > kMaxTokensPerLaunch;
     pa.rstd_in = big && aqn ? rstd : nullptr;
@@ -3252,6 +3795,33 @@ qn_status run_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const
     QN_FGEMV(false, true, false, true) QN_FGEMV(false, true, true, true)
     QN_FGEMV(true, true, false, true) QN_FGEMV(true, true, true, true)
 #undef QN_FGEMV
+    return QN_ERR_UNSUPPORTED;  // (not reached)
+  }
+  if (plan.path == kPathWide) {
+    const int tmt = m <= 32 ? 2 : 4;
+    u32x4* t_fin = reinterpret_cast<u32x4*>(ws + wl.t_fin);  // (summed by the prologue)
+    WideArgs wa{};
+    GemvArgs& ga = wa.G;
+    ga.L = la;
+    ga.L.tok0 = 0;
+    ga.KT = (int32_t)KT;
+    ga.ntiles = (int32_t)ntiles;
+    ga.mt = (int32_t)m;
+    ga.nu = (int32_t)(silu ? ceil_div(projs[0].n, 16) : rg_total);
+    ga.nbr = plan.cut.nbr;
+    ga.nk = plan.cut.nk;
+    ga.pbuf = reinterpret_cast<float*>(ws + wl.pbuf);
+    ga.cnt = reinterpret_cast<uint32_t*>(ws + wl.cnt);
+    wa.t_fin = t_fin;
+    wa.t_fin_bytes = (int64_t)(wl.pbuf - wl.t_fin);
+    const dim3 grid((unsigned)(plan.cut.nbr * plan.cut.nk)), block(kWWaves * kWave);
+#define QN_WIDE(T_, S_, L_)                                                          \
+  if (tmt == T_ && silu == S_) {                                                    \
+    hipLaunchKernelGGL((k_wgemv<T_, S_, L_>), grid, block, 0, s, wa);              \
+    return hipGetLastError() == hipSuccess ? QN_OK : QN_ERR_HIP;                    \
+  }
+    QN_WIDE(2, false, 3) QN_WIDE(2, true, 3) QN_WIDE(4, false, 3) QN_WIDE(4, true, 1)
+#undef QN_WIDE
     return QN_ERR_UNSUPPORTED;  // (not reached)
   }
   if (plan.path == kPathDecode) {

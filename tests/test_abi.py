@@ -191,7 +191,7 @@ def test_linear_options_validation(qn):
         return L.nvfp4_lora_linear_opts(fake, m, k, k, ctypes.byref(aqn) if aqn else None, arr, 1, 0, ctypes.byref(oc),
                                         P(1 << 20), need if ws_bytes is None else ws_bytes, None)
 
-    bad = [qn.LinearOpts(kernel=5), qn.LinearOpts(kernel=-1), qn.LinearOpts(decode_kchunks=65),
+    bad = [qn.LinearOpts(kernel=6), qn.LinearOpts(kernel=-1), qn.LinearOpts(decode_kchunks=65),
            qn.LinearOpts(decode_depth=4), qn.LinearOpts(general_rows=2), qn.LinearOpts(general_waves=8),
            qn.LinearOpts(elem_store=2)]
     for o in bad:
@@ -200,6 +200,9 @@ def test_linear_options_validation(qn):
         assert L.nvfp4_lora_linear_workspace_opts(4, 128, arr, 1, ctypes.byref(oc)) == 0, o
     assert call(64, qn.LinearOpts(kernel=qn.KERNEL_DECODE)) == qn.QN_ERR_UNSUPPORTED  # decode kernel: m <= 32
     assert call(100, qn.LinearOpts(kernel=qn.KERNEL_MANY)) == qn.QN_ERR_UNSUPPORTED  # MFMA kernel: m > 128
+    assert call(16, qn.LinearOpts(kernel=qn.KERNEL_WIDE)) == qn.QN_ERR_UNSUPPORTED  # 17 <= m <= 64
+    assert call(65, qn.LinearOpts(kernel=qn.KERNEL_WIDE)) == qn.QN_ERR_UNSUPPORTED
+    assert call(40, qn.LinearOpts(kernel=qn.KERNEL_WIDE, decode_depth=2)) == qn.QN_ERR_UNSUPPORTED
     # fused decode kernel: m <= 16, depth 0 or 3, not split into phases, with the norm the whole row in one k-chunk
     norm = qn.QnAqn(gamma=256, noise=None, noise_ld=0, sigma=0.01, eps=1e-6)
     assert call(17, qn.LinearOpts(kernel=qn.KERNEL_FUSED)) == qn.QN_ERR_UNSUPPORTED

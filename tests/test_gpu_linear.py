@@ -287,6 +287,125 @@ def test_linear_kernel_paths(qn, path, m, ns, k, silu, residual, r, gqa):
         assert rel_err(ys[p].cpu().numpy(), ref) <= LINEAR_TOL, (path, p)
 
 
+def wide_fits(m, nu, k, nchunks):
+    """Whether the decode kernel for 17-64 tokens can take a call: the rule the library documents for
+    QN_KERNEL_WIDE, restated from its limits (at most 5 row units per workgroup; with a split k at most 256 row
+    blocks; a named cut of at most as many k-chunks as k-tiles)."""
+    KT = -(-k // 128)
+    if not 17 <= m <= 64 or nchunks > min(KT, 64):
+        return False
+    return -(-nu // 5) <= (256 if nchunks > 1 else 16384)
+
+
+# The decode kernel for 17 to 64 tokens, named through the options, against the oracle on every output: one and
+# several projections (with a GQA broadcast), SiLU * up, residuals, ranks none to 64 (odd ones too), ragged rows and
+# k, long rows, split-k cuts named and the library's own, token counts at and between the tile boundaries.
+@pytest.mark.parametrize("m,ns,k,silu,residual,r,gqa,nchunks", [
+    (17, [96], 3584, False, True, 12, 1, 0),
+    (24, [520, 64, 64], 1040, False, False, 64, 1, 0),
+    (32, [256], 512, False, True, 32, 1, 2),
+    (33, [384, 384], 512, True, False, 32, 1, 0),
+    (48, [1040, 1040], 384, True, False, 8, 1, 0),
+    (64, [128, 128], 1024, True, False, 0, 1, 0),
+    (64, [512, 128, 128], 640, False, False, 32, 4, 0),
+    (50, [200], 2048, False, True, 33, 1, 3),
+    (64, [2048], 4736, False, True, 32, 1, 0),
+    (64, [1024], 1040, False, False, 64, 1, 7),
+    (40, [200, 200], 2176, True, True, 12, 1, 4),
+    (20, [48], 128, False, False, 32, 1, 1),
+    (64, [6000], 256, False, False, 32, 1, 2),
+    (40, [21000], 256, False, True, 32, 1, 0),   # more than 256 row blocks: several rounds, no split
+    (20, [21000], 256, False, False, 32, 1, 2),  # refused: a split needs a counter per block
+])
+def test_linear_wide_kernel(qn, m, ns, k, silu, residual, r, gqa, nchunks):
+    opts = qn.LinearOpts(kernel=qn.KERNEL_WIDE, decode_kchunks=nchunks)
+    c = Case(m, ns, k, r=r, seed=m * 11 + k)
+    wq = [qn.quantize(dev_bf16(w), qn.LAYOUT_TILED) for w in c.w]
+    res = synth.normal_bf16(57, (m, ns[0])) if residual else None
+    ys, projs = [], []
+    for p, n in enumerate(ns):
+        rep = gqa if p == len(ns) - 1 and gqa > 1 else 1
+        y = torch.full((m, n * rep), float("nan"), dtype=torch.float32, device=DEV)
+        ys.append(y)
+        A = dev_bf16(c.A[p]) if r else None
+        B = dev_bf16(c.B[p]) if r else None
+        projs.append(qn.Projection(wq[p], None if (silu and p == 1) else y, A, B, c.lam,
+                                   residual=dev_bf16(res) if (residual and p == 0) else None,
+                                   y_repeat=rep, head_dim=64))
+    aqn = qn.make_aqn(dev_bf16(c.gamma), dev_f32(c.noise), c.sigma, 1e-6)
+    nu = -(-ns[0] // 16) if silu else sum(-(-n // 16) for n in ns)
+    if not wide_fits(m, nu, k, nchunks):
+        with pytest.raises(qn.QnError) as e:  # refused on the host, nothing launched
+            qn.lora_linear(dev_bf16(c.x), projs, aqn, qn.EPI_SILU_MUL if silu else qn.EPI_NONE, opts=opts)
+        assert e.value.status == qn.QN_ERR_UNSUPPORTED
+        return
+    qn.lora_linear(dev_bf16(c.x), projs, aqn, qn.EPI_SILU_MUL if silu else qn.EPI_NONE, opts=opts)
+    torch.cuda.synchronize()
+    if silu:
+        ref = oracle.silu_mul(c.oracle_y(0), c.oracle_y(1))
+        if residual:
+            ref = ref + bf16_bits_to_f64(res)
+        got = ys[0].cpu().numpy()
+        assert np.all(np.isfinite(got))
+        assert rel_err(got, ref) <= LINEAR_TOL
+        return
+    for p in range(len(ns)):
+        ref = c.oracle_y(p)
+        if residual and p == 0:
+            ref = ref + bf16_bits_to_f64(res)
+        rep = gqa if p == len(ns) - 1 and gqa > 1 else 1
+        if rep > 1:
+            ref = oracle.gqa_broadcast(ref, rep, 64)
+        got = ys[p].cpu().numpy()
+        assert np.all(np.isfinite(got)), p
+        assert rel_err(got, ref) <= LINEAR_TOL, p
+
+
+def test_linear_wide_kernel_refusals(qn):
+    """Calls the kernel for 17-64 tokens cannot take are refused on the host: 16 or 65 tokens, a cut of more
+    k-chunks than k-tiles, depth 2."""
+    c = Case(16, [64], 256, seed=1)
+    wq = qn.quantize(dev_bf16(c.w[0]), qn.LAYOUT_TILED)
+    for m, opts in ((16, qn.LinearOpts(kernel=qn.KERNEL_WIDE)), (65, qn.LinearOpts(kernel=qn.KERNEL_WIDE)),
+                    (32, qn.LinearOpts(kernel=qn.KERNEL_WIDE, decode_kchunks=3)),
+                    (32, qn.LinearOpts(kernel=qn.KERNEL_WIDE, decode_depth=2))):
+        x = torch.zeros(m, 256, dtype=torch.bfloat16, device=DEV)
+        y = torch.empty(m, 64, dtype=torch.float32, device=DEV)
+        with pytest.raises(qn.QnError) as e:
+            qn.lora_linear(x, [qn.Projection(wq, y)], opts=opts)
+        assert e.value.status == qn.QN_ERR_UNSUPPORTED, (m, opts)
+
+
+def test_shared_workspace_calls_of_other_shapes(qn):
+    """One workspace shared by calls of different shapes, in turn: the kernel for 17-64 tokens (SiLU pair, and long
+    rows with a split k), the fused decode kernel and the decode kernel. Each call's data regions lie at offsets of
+    their own, so the words that must stay zero between calls (arrival counters, the fused kernel's ready flags) have
+    to sit where no call writes data. Regression: with those words placed after the data, a long-row call's
+    activations landed on another call's LoRA-down arrival counters, and its next call read a t never summed (NaN)."""
+    ws = qn.Workspace(DEV)
+    cases = [(Case(40, [512, 512], 512, seed=5), qn.EPI_SILU_MUL, qn.LinearOpts(kernel=qn.KERNEL_WIDE)),
+             (Case(40, [256], 6144, seed=6), qn.EPI_NONE, qn.LinearOpts(kernel=qn.KERNEL_WIDE, decode_kchunks=4)),
+             (Case(8, [256], 512, seed=7), qn.EPI_NONE, qn.LinearOpts(kernel=qn.KERNEL_FUSED)),
+             (Case(16, [384], 3072, seed=8), qn.EPI_NONE, qn.LinearOpts(kernel=qn.KERNEL_DECODE, decode_kchunks=3))]
+    calls = []
+    for c, epi, opts in cases:
+        wq = [qn.quantize(dev_bf16(w), qn.LAYOUT_TILED) for w in c.w]
+        ys = [torch.full((c.m, n), float("nan"), dtype=torch.float32, device=DEV) for n in c.ns]
+        projs = [qn.Projection(wq[p], None if (epi == qn.EPI_SILU_MUL and p == 1) else ys[p], dev_bf16(c.A[p]),
+                               dev_bf16(c.B[p]), c.lam) for p in range(len(c.ns))]
+        aqn = qn.make_aqn(dev_bf16(c.gamma), dev_f32(c.noise), c.sigma, 1e-6)
+        ref = oracle.silu_mul(c.oracle_y(0), c.oracle_y(1)) if epi == qn.EPI_SILU_MUL else c.oracle_y(0)
+        calls.append((qn.LinearCall(dev_bf16(c.x), projs, aqn, epi, ws, opts), ys[0], ref))
+    for rep in range(3):
+        for i, (call, y, ref) in enumerate(calls):
+            y.fill_(float("nan"))
+            call()
+            torch.cuda.synchronize()
+            got = y.cpu().numpy()
+            assert np.all(np.isfinite(got)), (rep, i)
+            assert rel_err(got, ref) <= LINEAR_TOL, (rep, i)
+
+
 # The fused decode kernel without the norm (the o and down projections of a layer): its split-k form, which the calls
 # with the norm never take, on rows too long for one chunk and on cuts named through the options, with residuals,
 # several projections, mixed and odd ranks; every output checked against the oracle.
