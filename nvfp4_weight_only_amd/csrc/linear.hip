@@ -1586,27 +1586,30 @@ __global__ void __launch_bounds__(kWWaves * kWave) k_wgemv(WideArgs wa) {
                           P.head_dim, P.rg_begin, P.r};
       }
   }
+  // (32-bit indices: rows and row strides are below 2^31; kept apart from the epilogue's 64-bit ones, which the
+  // compiler would otherwise hold in registers across the stream)
   uint16_t res[kOut];
 #pragma unroll
   for (int i = 0; i < kOut; ++i) {
     const int e = threadIdx.x + i * kWWaves * kWave;
     const int u = (int)((unsigned)e / (TMT * 256)), tok = (e >> 4) & (TMT * 16 - 1), row = e & 15;
-    const int64_t gu = u0 + u;
+    const int gu = u0 + u;
     const uint16_t* rb = a.p[0].res;
-    int64_t rbeg = 0, nl = a.p[0].n, ld = a.p[0].ld_res;
+    int rbeg = 0, nl = (int)a.p[0].n;
+    uint32_t ld = (uint32_t)a.p[0].ld_res;
     if (!SILU) {
 #pragma unroll
       for (int q = 1; q < kMaxProj; ++q)
         if (q < a.nproj && gu >= a.p[q].rg_begin) {
           rb = a.p[q].res;
           rbeg = a.p[q].rg_begin;
-          nl = a.p[q].n;
-          ld = a.p[q].ld_res;
+          nl = (int)a.p[q].n;
+          ld = (uint32_t)a.p[q].ld_res;
         }
     }
-    const int64_t n = (gu - rbeg) * 16 + row;
+    const int n = (gu - rbeg) * 16 + row;
     const bool ok = rb && u < U && tok < g.mt && n < nl;
-    res[i] = gload(ok ? rb + tok * ld + n : reinterpret_cast<const uint16_t*>(a.xsc));
+    res[i] = gload(ok ? rb + ((size_t)((uint32_t)tok * ld) + (uint32_t)n) : reinterpret_cast<const uint16_t*>(a.xsc));
   }
 
   // weights of this wave's unit: k-tile t0 + q*kWH + j of pass q (past the chunk: out of range, reads 0)
