@@ -53,21 +53,49 @@ __device__ inline uint32_t e2m1_index(double a, double S) {
 
 __global__ void k_quant_init(uint32_t* amax_bits) { *amax_bits = 0u; }
 
-// Tensor amax over finite elements (as f32 bit patterns: ordered like the values for non-negative floats).
+// Tensor amax over finite elements (as f32 bit patterns: ordered like the values for non-negative floats). Workgroups
+// take whole rows; a thread takes 8 consecutive elements of a row at a time (k is a multiple of 16); VEC: the rows
+// start 16-byte aligned at every group, one 16-byte load per group. One atomic per workgroup (the waves' maxima meet
+// in LDS): atomics on one word serialize.
+template <bool VEC>
 __global__ void __launch_bounds__(kQThreads) k_quant_amax(const uint16_t* __restrict__ w, int64_t n, int64_t k,
                                                            int64_t ldw, uint32_t* amax_bits, int32_t* flags) {
+  __shared__ float s_m[kQThreads / kWave];
+  __shared__ int s_bad;
+  if (threadIdx.x == 0) s_bad = 0;
   float m = 0.0f;
   bool bad = false;
-  const int64_t total = n * k;
-  for (int64_t i = (int64_t)blockIdx.x * kQThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kQThreads) {
-    int64_t row = i / k, col = i - row * k;
-    uint16_t b = w[row * ldw + col];
-    if (!bf16_finite(b)) { bad = true; continue; }
-    m = fmaxf(m, fabsf(bf16_to_f32(b)));
+  const int64_t gpr = k / 8;
+  for (int64_t row = blockIdx.x; row < n; row += gridDim.x) {
+    for (int64_t c8 = threadIdx.x; c8 < gpr; c8 += kQThreads) {
+      const uint16_t* p = w + row * ldw + c8 * 8;
+      uint32_t q[4];
+      if (VEC) {
+        const uint4 v = *reinterpret_cast<const uint4*>(p);
+        q[0] = v.x; q[1] = v.y; q[2] = v.z; q[3] = v.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q[e] = (uint32_t)p[2 * e] | ((uint32_t)p[2 * e + 1] << 16);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint16_t b = (uint16_t)(q[e / 2] >> (16 * (e % 2)));
+        if (!bf16_finite(b)) bad = true;
+        else m = fmaxf(m, fabsf(bf16_to_f32(b)));
+      }
+    }
   }
   m = wave_max(m);
-  if ((threadIdx.x % kWave) == 0) atomicMax(amax_bits, __float_as_uint(m));
-  if (bad && flags) atomicOr(flags, 1);
+  __syncthreads();  // (s_bad initialised)
+  if ((threadIdx.x % kWave) == 0) s_m[threadIdx.x / kWave] = m;
+  if (bad) s_bad = 1;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float mm = s_m[0];
+    for (int i = 1; i < kQThreads / kWave; ++i) mm = fmaxf(mm, s_m[i]);
+    atomicMax(amax_bits, __float_as_uint(mm));
+    if (s_bad && flags) atomicOr(flags, 1);
+  }
 }
 
 // One thread per 16-element block of the padded [np x kp] grid: block scale (scale_mode 0), 16 codes, stores.
@@ -324,10 +352,13 @@ extern "C" qn_status nvfp4_quantize(const uint16_t* w, int64_t n, int64_t k, int
   const int64_t kp = layout == QN_LAYOUT_TILED ? ceil_div(k, kKTile) * kKTile : k;
   if (scale_mode == 0) {
     hipLaunchKernelGGL(k_quant_init, dim3(1), dim3(1), 0, s, reinterpret_cast<uint32_t*>(tensor_scale));
-    int64_t blocks = ceil_div(n * k, kQThreads);
-    if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL(k_quant_amax, dim3((unsigned)blocks), dim3(kQThreads), 0, s, w, n, k, ldw,
-                       reinterpret_cast<uint32_t*>(tensor_scale), d_flags);
+    const int64_t blocks = n < 1024 ? n : 1024;  // (whole rows per workgroup)
+    if (aligned(w, 16) && ldw % 8 == 0)
+      hipLaunchKernelGGL(k_quant_amax<true>, dim3((unsigned)blocks), dim3(kQThreads), 0, s, w, n, k, ldw,
+                         reinterpret_cast<uint32_t*>(tensor_scale), d_flags);
+    else
+      hipLaunchKernelGGL(k_quant_amax<false>, dim3((unsigned)blocks), dim3(kQThreads), 0, s, w, n, k, ldw,
+                         reinterpret_cast<uint32_t*>(tensor_scale), d_flags);
   }
   const int64_t nblk = np * (kp / 16);
   hipLaunchKernelGGL(k_quant_blocks, dim3((unsigned)ceil_div(nblk, kQThreads)), dim3(kQThreads), 0, s, w, n, k, ldw,

@@ -180,7 +180,8 @@ def test_qkv_ragged_boundaries_inside_workgroups(qn, m):
 # ---- the LoRA branch alone -------------------------------------------------------------------------------------------
 @pytest.mark.parametrize("m,n,k,r,kern", [(1, 4096, 4096, 32, None), (16, 18944, 3584, 32, None),
                                            (8, 3584, 18944, 32, None), (16, 520, 1040, 12, "general"),
-                                           (300, 512, 640, 64, None)])
+                                           (300, 512, 640, 64, None), (64, 18944, 3584, 32, None),
+                                           (40, 3584, 18944, 32, None), (24, 1040, 1024, 64, "wide")])
 def test_lora_term_alone(qn, m, n, k, r, kern):
     """With a zero base weight the output is lambda * B (A h) alone: checked against the oracle's LoRA term at the bar,
     relative to that term's own magnitude (the branch is about a fifth of a full output, so the bar on the full
@@ -192,7 +193,8 @@ def test_lora_term_alone(qn, m, n, k, r, kern):
     w0 = np.zeros((n, k), dtype=np.uint16)
     wq = qn.quantize(dev_bf16(w0), qn.LAYOUT_TILED)
     y = torch.full((m, n), float("nan"), dtype=torch.float32, device=DEV)
-    opts = qn.LinearOpts(kernel=qn.KERNEL_GENERAL) if kern == "general" else None
+    opts = {"general": qn.LinearOpts(kernel=qn.KERNEL_GENERAL), "wide": qn.LinearOpts(kernel=qn.KERNEL_WIDE),
+            None: None}[kern]
     qn.lora_linear(dev_bf16(h), [qn.Projection(wq, y, dev_bf16(A), dev_bf16(B), 2.0)], opts=opts)
     torch.cuda.synchronize()
     codes, sb, sg, _ = oracle.nvfp4_quantize(w0)
