@@ -64,6 +64,13 @@ def test_noalloc_two_calls_match_workspace_entry(qn):
     a, b = run_both(qn, c3, epilogue=qn.EPI_SILU_MUL)
     assert torch.equal(a[0], b[0])
     assert rel_err(b[0].cpu().numpy(), oracle.silu_mul(c3.oracle_y(0), c3.oracle_y(1))) <= LINEAR_TOL
+    # 4. the 7B gate | up at 40 tokens (the kernel for 17-64 tokens; the prologue sums t with arrival counters that
+    #    must be left zero in the array for the next call)
+    c4 = Case(40, [18944, 18944], 3584, seed=505)
+    for _ in range(2):
+        a, b = run_both(qn, c4, epilogue=qn.EPI_SILU_MUL)
+        assert torch.equal(a[0], b[0])
+    assert rel_err(b[0].cpu().numpy(), oracle.silu_mul(c4.oracle_y(0), c4.oracle_y(1))) <= LINEAR_TOL
 
 
 def test_noalloc_rejects_calls_beyond_its_array(qn):
