@@ -60,6 +60,30 @@ struct ProjArgs {
   int32_t rg_begin;  // first row group of this projection in the launch's flattened list
 };
 
+// Store one output value (f32 or bf16) at element (token row tok_off = token * ldy, column n) and, with a GQA
+// broadcast (y_repeat > 1), at the same position of each of the y_repeat copies of its head: copy g of head h sits
+// at column (h * y_repeat + g) * head_dim + n % head_dim. The head split is taken once (32-bit: n < 2^31), the
+// copies are head_dim apart.
+__device__ __forceinline__ void store_output(void* y, int32_t y_dtype, int64_t tok_off, int64_t n, int32_t y_repeat,
+                                             int32_t head_dim, float out) {
+  int64_t off = tok_off + n, step = 0;
+  int rep = 1;
+  if (y_repeat > 1) {
+    const uint32_t h = (uint32_t)n / (uint32_t)head_dim, d = (uint32_t)n - h * (uint32_t)head_dim;
+    off = tok_off + (int64_t)h * y_repeat * head_dim + d;
+    step = head_dim;
+    rep = y_repeat;
+  }
+  if (y_dtype == QN_F32) {
+    float* const p = reinterpret_cast<float*>(y) + off;
+    for (int g = 0; g < rep; ++g) p[g * step] = out;
+  } else {
+    uint16_t* const p = reinterpret_cast<uint16_t*>(y) + off;
+    const uint16_t v = f32_to_bf16(out);
+    for (int g = 0; g < rep; ++g) p[g * step] = v;
+  }
+}
+
 struct LinearArgs {
   ProjArgs p[kMaxProj];
   int32_t nproj, epilogue;
@@ -1000,13 +1024,7 @@ __global__ void __launch_bounds__(W * kWave) k_linear(LinearArgs a) {
       out = g / (1.0f + __expf(-g)) * val[kPer - 1];
     }
     if (O.res) out += bf16_to_f32(res[i]);
-    const int rep = O.y_repeat > 1 ? O.y_repeat : 1;
-    for (int g = 0; g < rep; ++g) {
-      const int64_t col_out = rep > 1 ? ((n / O.head_dim) * rep + g) * O.head_dim + n % O.head_dim : n;
-      const int64_t off = gtok * O.ldy + col_out;
-      if (O.y_dtype == QN_F32) reinterpret_cast<float*>(O.y)[off] = out;
-      else reinterpret_cast<uint16_t*>(O.y)[off] = f32_to_bf16(out);
-    }
+    store_output(O.y, O.y_dtype, gtok * O.ldy, n, O.y_repeat, O.head_dim, out);
   }
 }
 
@@ -1165,13 +1183,7 @@ __device__ __forceinline__ void gemv_finish(const GemvArgs& g, const ProjEpi* s_
     if (SILU) out = val[0] / (1.0f + __expf(-val[0])) * val[NR - 1];
     if (E.res) out += bf16_to_f32(s_res[e]);
     const int64_t gtok = a.tok0 + tok;
-    const int rep = E.y_repeat > 1 ? E.y_repeat : 1;
-    for (int gi = 0; gi < rep; ++gi) {
-      const int64_t col_out = rep > 1 ? ((n / E.head_dim) * rep + gi) * E.head_dim + n % E.head_dim : n;
-      const int64_t off = gtok * E.ldy + col_out;
-      if (E.y_dtype == QN_F32) reinterpret_cast<float*>(E.y)[off] = out;
-      else reinterpret_cast<uint16_t*>(E.y)[off] = f32_to_bf16(out);
-    }
+    store_output(E.y, E.y_dtype, gtok * E.ldy, n, E.y_repeat, E.head_dim, out);
   }
 }
 
@@ -1851,14 +1863,12 @@ __global__ void __launch_bounds__(kWWaves * kWave) k_wgemv(WideArgs wa) {
     }
     __builtin_amdgcn_s_waitcnt(0);  // no load into LDS is in flight when the buffers are reused below
   } else {
-    // wave 15: the first two items before the first barrier (their memory round trips overlap the stream waves'
-    // first loads), then one per pass
+    // wave 15: the first item before the first barrier (its memory round trip overlaps the stream waves' first
+    // loads), then one per pass
     LItem L0;
     if (nitems > 0) item_issue(L0, 0);
     if (nitems > 0) item_finish(L0, 0);
-    if (nitems > 1) item_issue(L0, 1);
-    if (nitems > 1) item_finish(L0, 1);
-    int it = 2;
+    int it = 1;
     if (it < nitems) item_issue(L0, it);
     for (int q0 = 0; q0 < NP; q0 += UF) {
 #pragma unroll
@@ -2624,13 +2634,7 @@ __global__ void __launch_bounds__(kGWaves * kWave) k_fgemv(FusedArgs f) {
       float out = val[0];
       if (SILU) out = val[0] / (1.0f + __expf(-val[0])) * val[NR - 1];
       if (E.res) out += bf16_to_f32(s_res[e]);
-      const int rep = E.y_repeat > 1 ? E.y_repeat : 1;
-      for (int gi = 0; gi < rep; ++gi) {
-        const int64_t col_out = rep > 1 ? ((n / E.head_dim) * rep + gi) * E.head_dim + n % E.head_dim : n;
-        const int64_t off = (int64_t)tok * E.ldy + col_out;
-        if (E.y_dtype == QN_F32) reinterpret_cast<float*>(E.y)[off] = out;
-        else reinterpret_cast<uint16_t*>(E.y)[off] = f32_to_bf16(out);
-      }
+      store_output(E.y, E.y_dtype, (int64_t)tok * E.ldy, n, E.y_repeat, E.head_dim, out);
     }
   }
 }
@@ -3321,13 +3325,7 @@ __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
           if (n >= E.n) continue;
           float out = o4[e];
           if (E.res) out += bf16_to_f32(E.res[tok * E.ld_res + n]);
-          const int rep = E.y_repeat > 1 ? E.y_repeat : 1;
-          for (int gi = 0; gi < rep; ++gi) {
-            const int64_t col_out = rep > 1 ? ((n / E.head_dim) * rep + gi) * E.head_dim + n % E.head_dim : n;
-            const int64_t off = tok * E.ldy + col_out;
-            if (E.y_dtype == QN_F32) reinterpret_cast<float*>(E.y)[off] = out;
-            else reinterpret_cast<uint16_t*>(E.y)[off] = f32_to_bf16(out);
-          }
+          store_output(E.y, E.y_dtype, tok * E.ldy, n, E.y_repeat, E.head_dim, out);
         }
       }
     }
