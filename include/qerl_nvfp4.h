@@ -226,7 +226,8 @@ typedef enum {
   QN_KERNEL_WIDE = 5     /* the decode streaming kernel for 17 to 64 tokens (activations streamed through LDS in
                             passes, every activation tile shared by all row groups of a workgroup, optional split
                             k); m in 17..64, else QN_ERR_UNSUPPORTED. AUTO takes it at 17 to 64 tokens for calls
-                            with at least 24 MB of packed weights (the wide feed-forward and long-row projections). */
+                            with at least 24 MB of packed weights (the wide feed-forward and long-row projections);
+                            a split k needs at most 256 row blocks of 5 row units. */
 } qn_kernel;
 
 /* Explicit options of one nvfp4_lora_linear_opts call. Zero-initialised, it asks for the library's defaults. These

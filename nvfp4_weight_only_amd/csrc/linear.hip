@@ -2802,15 +2802,12 @@ inline qn_status plan_main(int64_t m, int64_t KT, int64_t nu, bool silu, bool no
     return QN_OK;
   }
   // AUTO takes the decode kernel for 17-64 tokens for calls with at least kWideMinBytes of weights (measured on the
-  // 7B/32B shapes: the wide feed-forward projections and the long-row down projection run 1.2-2.3x faster than on
-  // the general kernel; smaller projections, such as q|k|v and o, ran as fast or faster on the general kernel)
-  // and a cut that fits in one round of workgroups
+  // 7B/32B shapes: the wide feed-forward projections and the long-row down projection run 1.2-1.9x faster than on
+  // the general kernel, the 32B gate|up also in the two rounds of workgroups its 1,728 pairs need; smaller
+  // projections, such as q|k|v and o, ran as fast or faster on the general kernel)
   bool wide_auto = o.kernel == QN_KERNEL_AUTO && m > 16 && m <= 64 && o.depth != 2 &&
                    (double)nu * KT * nr * 1152.0 >= kWideMinBytes;
-  if (wide_auto) {
-    const GemvCut c = wide_cut(nu, KT, m <= 32 ? 2 : 4, nr, o.nk);
-    wide_auto = c.nbr > 0 && (int64_t)c.nbr * c.nk <= 256;
-  }
+  if (wide_auto) wide_auto = wide_cut(nu, KT, m <= 32 ? 2 : 4, nr, o.nk).nbr > 0;
   if (o.kernel == QN_KERNEL_WIDE || wide_auto) {
     if (m <= 16 || m > 64 || (o.depth != 0 && o.depth != 3)) return QN_ERR_UNSUPPORTED;
     pl.path = kPathWide;
