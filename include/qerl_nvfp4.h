@@ -227,7 +227,9 @@ typedef enum {
                             passes, every activation tile shared by all row groups of a workgroup, optional split
                             k); m in 17..64, else QN_ERR_UNSUPPORTED. AUTO takes it at 17 to 64 tokens for calls
                             with at least 24 MB of packed weights (the wide feed-forward and long-row projections);
-                            a split k needs at most 256 row blocks of 5 row units. */
+                            a split k needs at most 256 row blocks of 5 row units. At 65 to 128 tokens AUTO runs
+                            such a call as sub-calls of at most 64 tokens on it, one after another on the stream
+                            (not a call split into its phases); the workspace size covers them. */
 } qn_kernel;
 
 /* Explicit options of one nvfp4_lora_linear_opts call. Zero-initialised, it asks for the library's defaults. These

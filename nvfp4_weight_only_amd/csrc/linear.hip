@@ -2722,7 +2722,9 @@ struct Plan {
   GemvCut cut{0, 0};
   int depth = 3;
   int ctl_k = 0, nkc = 0, npairs = 0;  // fused decode kernel: LoRA-down items (see FusedArgs)
+  bool split = false;  // run as sub-calls of at most kSplitTokens tokens, each with a plan of its own
 };
+constexpr int64_t kSplitTokens = 64;
 
 // Row blocks x k-chunks of the decode kernel for 17-64 tokens: at most kWSlots units per block, and with a split k
 // at most 256 blocks (one arrival counter each). Measured on the 7B shapes at 32-64 tokens, a launch is fastest in one round of workgroups
@@ -2801,6 +2803,20 @@ inline qn_status plan_main(int64_t m, int64_t KT, int64_t nu, bool silu, bool no
     *out = pl;
     return QN_OK;
   }
+  // AUTO at 65-128 tokens: a call whose 64-token parts would run on the decode kernel for 17-64 tokens runs as
+  // sub-calls of at most 64 tokens (rows are independent; measured per call, one call on the general kernel vs two:
+  // 7B gate|up at 128 tokens 261 vs 89 us, down 95 vs 82; 32B gate|up 456 vs 159, down 239 vs 107). Not for a call
+  // split into its phases (the sub-calls share the workspace).
+  if (o.kernel == QN_KERNEL_AUTO && allow_fused && m > kSplitTokens && m <= kMaxTokensPerLaunch) {
+    Plan sub;
+    if (plan_main(kSplitTokens, KT, nu, silu, norm, projs, nproj, o, allow_fused, &sub) == QN_OK &&
+        sub.path == kPathWide) {
+      pl.path = kPathWide;
+      pl.split = true;
+      *out = pl;
+      return QN_OK;
+    }
+  }
   // AUTO takes the decode kernel for 17-64 tokens for calls with at least kWideMinBytes of weights (measured on the
   // 7B/32B shapes: the wide feed-forward projections and the long-row down projection run 1.2-1.9x faster than on
   // the general kernel, the 32B gate|up also in the two rounds of workgroups its 1,728 pairs need; smaller
@@ -2836,7 +2852,12 @@ inline qn_status plan_main(int64_t m, int64_t KT, int64_t nu, bool silu, bool no
 
 // Split-k part sums of the decode kernel (none without a split).
 size_t gemv_pbuf_bytes(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj, const Opts& o) {
-  if (!projs || nproj < 1 || m < 1 || m > 64) return 0;
+  if (!projs || nproj < 1 || m < 1 || m > kMaxTokensPerLaunch) return 0;
+  if (m > kSplitTokens) {  // (a call run as sub-calls: the larger of theirs)
+    const size_t a = gemv_pbuf_bytes(kSplitTokens, k, projs, nproj, o);
+    const size_t b = gemv_pbuf_bytes(m - kSplitTokens, k, projs, nproj, o);
+    return a > b ? a : b;
+  }
   int tmt = (int)ceil_div(m, 16);
   if (tmt == 3) tmt = 4;  // (the wide decode kernel's token tiles)
   const int64_t KT = ceil_div(k, kKTile);
@@ -3560,9 +3581,41 @@ qn_status validate_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, 
 }
 
 // The launches of a validated call.
+// row_base: the row of the caller's call that row 0 of this one is (sub-calls of a split call; it keeps the noise
+// draws of every row those of the whole call).
 qn_status run_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const qn_aqn* aqn, const qn_proj* projs,
                      int32_t nproj, int32_t epilogue, const Opts& o, const Plan& plan, void* workspace,
-                     hipStream_t s) {
+                     hipStream_t s, int64_t row_base = 0) {
+  if (plan.split) {
+    // sub-calls of at most kSplitTokens rows, one after another on the stream (they share the workspace, whose size
+    // covers each of theirs): x, outputs, residuals and per-row noise advance by the rows before them
+    const bool silu_call = (epilogue & ~(QN_RUN_PROLOGUE_ONLY | QN_RUN_MAIN_ONLY)) == QN_EPI_SILU_MUL;
+    int64_t nu = 0;
+    for (int p = 0; p < nproj; ++p) nu += ceil_div(projs[p].n, 16);
+    if (silu_call) nu = ceil_div(projs[0].n, 16);
+    for (int64_t t0 = 0; t0 < m; t0 += kSplitTokens) {
+      const int64_t ms = m - t0 < kSplitTokens ? m - t0 : kSplitTokens;
+      qn_proj sp[kMaxProj];
+      for (int p = 0; p < nproj; ++p) {
+        sp[p] = projs[p];
+        const int64_t esz = projs[p].y_dtype == QN_F32 ? 4 : 2;
+        if (sp[p].y) sp[p].y = static_cast<char*>(sp[p].y) + t0 * sp[p].ldy * esz;
+        if (sp[p].residual) sp[p].residual += t0 * sp[p].ld_res;
+      }
+      qn_aqn sa{};
+      if (aqn) {
+        sa = *aqn;
+        if (sa.noise && sa.noise_ld) sa.noise += t0 * sa.noise_ld;
+      }
+      Plan sub;
+      const qn_status ps = plan_main(ms, ceil_div(k, kKTile), nu, silu_call, aqn != nullptr, sp, nproj, o, true, &sub);
+      if (ps != QN_OK || sub.split) return QN_ERR_UNSUPPORTED;  // (not reached: every sub-call has a plan)
+      const qn_status st = run_linear(x + t0 * ldx, ms, k, ldx, aqn ? &sa : nullptr, sp, nproj, epilogue, o, sub,
+                                      workspace, s, row_base + t0);
+      if (st != QN_OK) return st;
+    }
+    return QN_OK;
+  }
   const int32_t phases = epilogue & (QN_RUN_PROLOGUE_ONLY | QN_RUN_MAIN_ONLY);
   epilogue &= ~(QN_RUN_PROLOGUE_ONLY | QN_RUN_MAIN_ONLY);
   const bool run_prologue = phases != QN_RUN_MAIN_ONLY, run_main = phases != QN_RUN_PROLOGUE_ONLY;
@@ -3599,7 +3652,7 @@ qn_status run_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const
       pa.eps = aqn->eps;
       pa.vec_g = (uintptr_t)aqn->gamma % 16 == 0;
       pa.vec_z = aqn->noise && (uintptr_t)aqn->noise % 16 == 0 && pa.noise_ld % 4 == 0;
-      pa.draw = QnDraw{aqn->draw ? 1 : 0, aqn->seed, aqn->subseed, aqn->row_offset, aqn->draw_rows};
+      pa.draw = QnDraw{aqn->draw ? 1 : 0, aqn->seed, aqn->subseed, aqn->row_offset, aqn->draw_rows, row_base};
     }
     int npg = 0;
     for (int p = 0; p < nproj; ++p) {
@@ -3763,7 +3816,7 @@ qn_status run_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const
       fa.noise_ld = aqn->noise ? aqn->noise_ld : 0;
       fa.sigma = aqn->sigma;
       fa.eps = aqn->eps;
-      fa.draw = QnDraw{aqn->draw ? 1 : 0, aqn->seed, aqn->subseed, aqn->row_offset, aqn->draw_rows};
+      fa.draw = QnDraw{aqn->draw ? 1 : 0, aqn->seed, aqn->subseed, aqn->row_offset, aqn->draw_rows, row_base};
       vec = vec && (uintptr_t)aqn->gamma % 16 == 0 &&
             (!aqn->noise || ((uintptr_t)aqn->noise % 16 == 0 && fa.noise_ld % 4 == 0));
       // one gamma + sigma * noise for every token: noise read with a zero stride, one draw for all rows, or none

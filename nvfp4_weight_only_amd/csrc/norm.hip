@@ -42,7 +42,7 @@ void launch_norm(int64_t m, hipStream_t s, const uint16_t* x, int64_t d, int64_t
                  int64_t ldh, int vec_in, int vec_out) {
   const int vec_g = (uintptr_t)a->gamma % 16 == 0;
   const int vec_z = a->noise && (uintptr_t)a->noise % 16 == 0 && a->noise_ld % 4 == 0;
-  const QnDraw q{a->draw ? 1 : 0, a->seed, a->subseed, a->row_offset, a->draw_rows};
+  const QnDraw q{a->draw ? 1 : 0, a->seed, a->subseed, a->row_offset, a->draw_rows, 0};
   hipLaunchKernelGGL((k_aqn_rmsnorm<NT, CPT>), dim3((unsigned)m), dim3(NT), 0, s, x, d, ldx, a->gamma, a->noise,
                      a->noise_ld, q, a->sigma, a->eps, h, ldh, vec_in, vec_out, vec_g, vec_z);
 }
@@ -107,7 +107,7 @@ extern "C" qn_status aqn_noise(uint64_t seed, uint64_t subseed, uint64_t row_off
   if ((uintptr_t)eps % 4) return QN_ERR_ALIGN;
   const int64_t blocks = ceil_div(m * ceil_div(d, 8), 256);
   if (blocks > 0x7fffffff) return QN_ERR_UNSUPPORTED;
-  const QnDraw q{1, seed, subseed, row_offset, draw_rows};
+  const QnDraw q{1, seed, subseed, row_offset, draw_rows, 0};
   hipLaunchKernelGGL(k_aqn_noise, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, q, m, d, eps, ld);
   return hipGetLastError() == hipSuccess ? QN_OK : QN_ERR_HIP;
 }

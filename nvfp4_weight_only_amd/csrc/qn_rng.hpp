@@ -20,11 +20,12 @@ struct QnDraw {
   uint64_t seed, subseed;
   uint64_t row_offset;  // draw index of row 0
   int64_t draw_rows;    // rows per draw; 0: one draw for every row
+  int64_t row_base;     // row of the call that row 0 of this launch is (a call run as sub-calls of fewer rows)
 };
 
-// Draw index of row `row` of the call.
+// Draw index of row `row` of the launch (row row_base + row of the call).
 __device__ __forceinline__ uint64_t draw_index(const QnDraw& q, int64_t row) {
-  return q.row_offset + (q.draw_rows > 0 ? (uint64_t)(row / q.draw_rows) : 0ull);
+  return q.row_offset + (q.draw_rows > 0 ? (uint64_t)((q.row_base + row) / q.draw_rows) : 0ull);
 }
 
 // One Philox4x64 block at counter (c0, c1, 0, 0): per round, the two 64 x 64 -> 128-bit products of words 0 and 2

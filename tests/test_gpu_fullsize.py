@@ -8,6 +8,8 @@
   residual, gate|up with SiLU(gate)*up, down with the residual), is fed the oracle's own bf16 input of that op, and
   all of its outputs are checked on the f32 result; then the layer itself runs end to end with bf16 storage and every
   element of its bf16 tensors is checked against the oracle's chain.
+- The feed-forward calls at 80 and 128 tokens, which the library runs as sub-calls of at most 64 tokens, with the
+  norm's noise drawn in draws that straddle the sub-calls' boundary.
 - A ragged q|k|v whose projection boundaries fall inside two-row-group workgroups of the general kernel.
 - The LoRA branch alone (zero base weight), against its own scale.
 - A call on a side stream whose workspace is released while its kernels may still run.
@@ -153,6 +155,50 @@ def test_decoder_layer_7b_full(qn, layer7b, layer7b_dev, m):
     torch.cuda.synchronize()
     for name in ("q", "k", "attn", "x2", "a", "out"):
         assert bf16_chain_ok(host_bf16(getattr(bound, name)), r[name]), name
+
+
+@pytest.mark.parametrize("m,draw_rows", [(80, 0), (128, 24)])
+def test_feed_forward_split_into_sub_calls(qn, layer7b, layer7b_dev, m, draw_rows):
+    """At 65 to 128 tokens the library runs the 7B feed-forward calls as sub-calls of at most 64 tokens (80 = 64 + 16,
+    the second on the 16-token decode kernel; 128 = 64 + 64). gate|up with the norm and SiLU(gate) * up, and down with
+    the residual: every output against the oracle. The norm's noise is drawn on the device in draws of draw_rows rows
+    (24: a draw straddles the boundary at row 64), so every row must keep the draw of the whole call; the drawn call
+    also gives the bits of the same call reading the generator's buffer."""
+    shape, w, lora, g1, g2, e1, e2, sigma, qref = layer7b
+    L = layer7b_dev
+    x2 = synth.normal_bf16(synth.seed_for(2, 9, "x") + m, (m, shape.hidden))
+    a = synth.normal_bf16(synth.seed_for(2, 10, "x") + m, (m, shape.inter))
+    f32 = dict(dtype=torch.float32, device=DEV)
+
+    def proj(nm, y, **kw):
+        A, B = L.lora[nm]
+        return qn.Projection(L.w[nm], y, A, B, 2.0, **kw)
+
+    print(f"[split calls] M={m}, draws of {draw_rows} rows", flush=True)
+    draw = qn.NoiseDraw(77, 2, 5, draw_rows)
+    x2d = dev_bf16(x2)
+    ya = torch.empty(m, shape.inter, **f32)
+    qn.lora_linear(x2d, [proj("gate", ya), proj("up", None)], qn.make_aqn(L.gamma2, None, sigma, 1e-6, draw=draw),
+                   qn.EPI_SILU_MUL)
+    eps = qn.aqn_noise(draw, m, shape.hidden, DEV)
+    read = qn.make_aqn(L.gamma2, eps, sigma, 1e-6, noise_per_row=True) if draw_rows else \
+        qn.make_aqn(L.gamma2, eps[0].contiguous(), sigma, 1e-6)
+    ya2 = torch.empty(m, shape.inter, **f32)
+    qn.lora_linear(x2d, [proj("gate", ya2), proj("up", None)], read, qn.EPI_SILU_MUL)
+    yd = torch.empty(m, shape.hidden, **f32)
+    qn.lora_linear(dev_bf16(a), [proj("down", yd, residual=x2d)])
+    torch.cuda.synchronize()
+    assert torch.equal(ya, ya2)
+
+    def lin(h, nm):
+        c, sb, sg = qref[nm]
+        A, B = lora[nm]
+        return oracle.lora_linear(h, c, sb, sg, A, B, 2.0)
+
+    _, h2 = oracle.aqn_rmsnorm(x2, g2, oracle.aqn_noise(77, 2, 5, draw_rows, m, shape.hidden), sigma, 1e-6,
+                               noise_per_row=True)
+    assert rel_err(ya.cpu().numpy(), oracle.silu_mul(lin(h2, "gate"), lin(h2, "up"))) <= LINEAR_TOL
+    assert rel_err(yd.cpu().numpy(), lin(a, "down") + bf16_bits_to_f64(x2)) <= LINEAR_TOL
 
 
 @pytest.mark.parametrize("m", [1, 8, 16])
