@@ -3680,12 +3680,17 @@ qn_status run_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const
     const bool big = m > kMaxTokensPerLaunch;
     pa.rstd_in = big && aqn ? rstd : nullptr;
     pa.tok_p = big && gemm_path ? tok_p : nullptr;
-    // with the norm at decode, each token tile's statistics rows are split over four workgroups (a workgroup
-    // reads 4 rows in full instead of 16)
-    pa.tgs = aqn && !big ? 4 : 16;
     // with many tokens, two pair groups share a workgroup (h of the chunk is computed once for both)
     pa.pgm = big && norm_threads(k) == 256 ? 2 : 1;
     const int npz = npg > 0 ? (npg + pa.pgm - 1) / pa.pgm : 1;
+    // with the norm at decode, each token tile's statistics rows are split over four workgroups (a workgroup
+    // reads 4 rows in full instead of 16), or over two or one where four would take more than one round of
+    // workgroups (7B q|k|v at 64 tokens: 336 workgroups; the same bits either way)
+    pa.tgs = 16;
+    if (aqn && !big) {
+      const int64_t per_split = ntiles * ks * npz;  // workgroups per token group
+      pa.tgs = per_split * 4 <= 256 ? 4 : (per_split * 2 <= 256 ? 8 : 16);
+    }
     const dim3 grid((unsigned)(ntiles * (16 / pa.tgs)), (unsigned)ks, (unsigned)npz);
     const dim3 block(kProWaves * kWave);
     const bool vec = pa.vec_x && (!aqn || (pa.vec_g && (!aqn->noise || pa.vec_z)));

@@ -159,15 +159,17 @@ def test_linear_per_row_noise(qn):
 
 
 @pytest.mark.parametrize("m,k,per_row", [(16, 3584, False), (5, 272, True), (16, 2048, True), (1, 3968, False),
-                                         (300, 1024, False), (17, 40960, True)])
+                                         (300, 1024, False), (17, 40960, True), (128, 9216, True),
+                                         (128, 18944, False)])
 def test_fused_norm_matches_standalone_norm(qn, m, k, per_row):
     """The norm inside the linear call gives the bits of the standalone norm: y(fused) == y(norm, then plain linear),
     both calls on the same kernel and cut (without the norm the library may split k, which changes the summation
     order of the product, not h).
 
     Covers the one-wave statistics in both thread counts (k > 32768 uses 1024), the fused decode kernel's statistics
-    from registers in one and two rounds of 256 chunks, per-row noise, a ragged k and the separate statistics kernel
-    taken from 256 tokens on."""
+    from registers in one and two rounds of 256 chunks, per-row noise, a ragged k, the separate statistics kernel
+    taken from 256 tokens on, and a token tile's statistics split over four, two (128 x 9216: 72 workgroups per
+    split) and one workgroup (128 x 18944: 152)."""
     c = Case(m, [96], k, seed=m + k)
     noise = synth.normal_f32(78, (m, k) if per_row else (k,))
     wq = qn.quantize(dev_bf16(c.w[0]), qn.LAYOUT_TILED)
