@@ -223,6 +223,28 @@ def test_linear_options_validation(qn):
     assert L.nvfp4_lora_linear_workspace(4, 128, arr, 1) == L.nvfp4_lora_linear_workspace_opts(4, 128, arr, 1, None)
 
 
+def test_workspace_covers_the_sub_calls_of_a_split_call(qn):
+    """At 65 to 128 tokens a call on the big feed-forward projections runs as sub-calls of at most 64 tokens that
+    share its workspace: its size covers each sub-call's (7B gate|up with SiLU, 7B down, 32B gate|up), and grows
+    with m. Host-pure queries: nothing is launched."""
+    L = qn.lib
+
+    def ws(m, n, k, nproj):
+        p = qn.QnProj(codes=256, block_scales=256, tensor_scale=256, n=n, lora_a=256, lora_b=256, r=32, lambda_=2.0,
+                      y=256, y_dtype=0, ldy=n)
+        arr = (qn.QnProj * nproj)(*([p] * nproj))
+        return L.nvfp4_lora_linear_workspace(m, k, arr, nproj)
+
+    for n, k, nproj in [(18944, 3584, 2), (3584, 18944, 1), (27648, 5120, 2)]:
+        prev = 0
+        for m in range(1, 129):
+            w = ws(m, n, k, nproj)
+            assert w >= prev, (n, k, m)
+            prev = w
+            if m > 64:
+                assert w >= ws(64, n, k, nproj) and w >= ws(m - 64, n, k, nproj), (n, k, m)
+
+
 def test_sigma_schedule_matches_oracle(qn, orc):
     """The library's sigma_k for every stage of the ten-stage schedule (0.01 -> 5e-4) equals the oracle's; stage 3 is
     the value the 28-layer configuration uses."""
