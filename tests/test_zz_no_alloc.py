@@ -71,6 +71,14 @@ def test_noalloc_two_calls_match_workspace_entry(qn):
         a, b = run_both(qn, c4, epilogue=qn.EPI_SILU_MUL)
         assert torch.equal(a[0], b[0])
     assert rel_err(b[0].cpu().numpy(), oracle.silu_mul(c4.oracle_y(0), c4.oracle_y(1))) <= LINEAR_TOL
+    # 5. the 7B down at 80 tokens with its residual: run as two sub-calls (64 tokens on the kernel for 17-64 tokens
+    #    with a split k, then 16 on the decode kernel with its own), one after the other on the same array
+    c5 = Case(80, [3584], 18944, seed=506, aqn=False)
+    res5 = dev_bf16(np.asarray(c5.x[:, :3584]))
+    a, b = run_both(qn, c5, residual=res5, aqn=False)
+    assert torch.equal(a[0], b[0])
+    ref5 = c5.oracle_y(0) + bf16_bits_to_f64(np.asarray(c5.x[:, :3584]))
+    assert rel_err(b[0].cpu().numpy(), ref5) <= LINEAR_TOL
 
 
 def test_noalloc_rejects_calls_beyond_its_array(qn):
