@@ -19,6 +19,9 @@ cache):
                       down 5120x27648), heavy-tailed weights (Student-t nu = 4 x 0.02 x 2^e per 16-block)
   c5_prefill_m8192    8192 tokens through the 7B gate|up with LoRA and SiLU*up on the MFMA kernel, then the group
                       advantages of 8 groups of 8 Bernoulli(0.3) rewards
+  f3_mxfp4_layer7b_m16    the headline layer with MXFP4 weights (the exact tiled form through the same kernels)
+  f3_mxfp4_prefill_m8192  the prefill gate|up with MXFP4 weights on the scaled FP4 x FP8 MFMA kernel
+                      (mxfp4_lora_linear), and through the tiled form on the f16 MFMA kernel for comparison
   f2_backward_gate_m8192  backward of the 7B gate projection at 8192 tokens: dh through the frozen NVFP4 weight, dA, dB
   f4_grpo_surrogate_8192  GRPO token ratios and clipped surrogate over the same 64 responses x 128 tokens
 plus `hbm_stream_read` (a plain streaming-read kernel over 4 GiB: the achievable read rate, the second roofline
@@ -42,6 +45,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense f16 / bf16 matrix peak, published
+FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 matrix peak, published
 PROFILE = os.path.join(ROOT, "profiles", "decode_layer_7b_m16.md")
 PREFILL_PROFILE = os.path.join(ROOT, "profiles", "prefill_gateup_7b_m8192.md")
 KERNEL_SOURCE = os.path.join(ROOT, "nvfp4_weight_only_amd", "csrc", "linear.hip")
@@ -312,6 +316,43 @@ def run_c5(base, shape, dev, steps, warmup):
     if prof_us:
         r.update({"kernel_us_profile": prof_us, "frac_of_mfma_peak_profile": fl / (prof_us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS})
     del x, y
+    return r
+
+
+def run_f3_prefill(base, shape, dev, steps, warmup):
+    """MXFP4 weights at prefill: 8192 tokens through the 7B gate|up (the headline layer's seeded weights, quantized to
+    OCP MXFP4) with LoRA and SiLU*up, on the scaled FP4 x FP8 MFMA kernel (mxfp4_lora_linear, canonical weights) and,
+    for comparison, on the f16 MFMA kernel through the exact tiled form (nvfp4_lora_linear)."""
+    import torch
+    import nvfp4_weight_only_amd as qn
+    import synth
+    m, n, k = 8192, shape.inter, shape.hidden
+    s = lambda t: synth.seed_for(2, 0, t)
+    wb = {nm: bf16_dev(synth.normal_bf16(s("w_" + nm), (n, k), std=0.02), dev) for nm in ("gate", "up")}
+    canon = {nm: qn.mxfp4_quantize(w, qn.LAYOUT_ROWMAJOR) for nm, w in wb.items()}
+    tiled = {nm: qn.mxfp4_quantize(w, qn.LAYOUT_TILED) for nm, w in wb.items()}
+    del wb
+    x = bf16_dev(synth.normal_bf16(synth.seed_for(5, 0, "x"), (m, k)), dev)
+    y = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+    (Ag, Bg), (Au, Bu) = base.lora["gate"], base.lora["up"]
+    ws = qn.Workspace(dev)
+
+    def projs(w):
+        return [qn.Projection(w["gate"], y, Ag, Bg, 2.0), qn.Projection(w["up"], None, Au, Bu, 2.0)]
+
+    native_call = lambda i: qn.mxfp4_lora_linear(x, projs(canon), None, qn.EPI_SILU_MUL, ws)
+    tiled_call = qn.LinearCall(x, projs(tiled), None, qn.EPI_SILU_MUL, ws)
+    nsteps = max(5, steps // 2)
+    t_native = time_steps(native_call, nsteps, max(2, warmup // 2))
+    t_tiled = time_steps(lambda i: tiled_call(), nsteps, max(2, warmup // 2))
+    fl = prefill_flops(shape, m)
+    # the scaled instruction does the product twice (hi and lo parts of the activations) at the FP8 rate
+    mfma_work = 2 * (2 * m * n * k * 2)
+    r = {"us_per_call": t_native * 1e6, "TFLOPs": fl / t_native / 1e12, "flops_per_call": fl,
+         "frac_of_fp8_mfma_peak": mfma_work / t_native / 1e12 / FP8_PEAK_TFLOPS,
+         "kernel": "k_gemm<SILU, MX>: v_mfma_scale_f32_16x16x128_f8f6f4, E2M1 weights x E4M3 hi/lo activations",
+         "tiled_form_us_per_call": t_tiled * 1e6, "tiled_form_TFLOPs": fl / t_tiled / 1e12}
+    del x, y, canon, tiled
     return r
 
 
@@ -618,6 +659,9 @@ def main():
         if want("f3"):
             log("MXFP4 weights: 7B layer, M=16")
             cfg["f3_mxfp4_layer7b_m16"] = run_f3(base, shape, dev, args.steps, args.warmup, stream_gbs)
+        if want("f3p"):
+            log("MXFP4 weights: prefill 8192 tokens on the scaled-MFMA kernel")
+            cfg["f3_mxfp4_prefill_m8192"] = run_f3_prefill(base, shape, dev, args.steps, args.warmup)
         if want("c5"):
             log("config 5: prefill 8192 tokens")
             cfg["c5_prefill_m8192"] = run_c5(base, shape, dev, args.steps, args.warmup)

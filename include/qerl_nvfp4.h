@@ -208,6 +208,23 @@ qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx
                             const qn_proj* projs, int32_t nproj, int32_t epilogue, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/* The same call on MXFP4 weights in the canonical MX layout (mxfp4_quantize with QN_LAYOUT_ROWMAJOR: codes [n][k/2],
+ * E8M0 scales [n][k/32] in block_scales; tensor_scale unused, may be NULL), y = X q h + lambda B (A h) ["QeRL 阅读笔记"
+ * §3.1 (MXFP4) with the forward map of review §2.1], run on CDNA4's scaled FP4 x FP8 matrix instruction, which takes
+ * the E2M1 codes and their E8M0 scales as they are stored. The activations h (bf16, after the optional AQN-RMSNorm)
+ * enter it as two E4M3 parts with one E8M0 exponent per 32 values along k: hi = E4M3(h / 2^s_hi) with the block's
+ * largest |h| / 2^s_hi in [128, 256), lo = E4M3((h - hi 2^s_hi) / 2^s_lo) likewise from the remainders (round to
+ * nearest even); hi 2^s_hi + lo 2^s_lo equals h for every value within a factor 2^10 of the largest magnitude in its
+ * block, and differs from h by less than 2^-19 of that magnitude otherwise. Products and sums are f32; the LoRA branch,
+ * the norm, epilogues, residual and broadcast are those of nvfp4_lora_linear. One kernel serves every token count
+ * (tiles of 128 tokens, so it is meant for prefill; decode-sized calls are faster through the exact tiled form and
+ * nvfp4_lora_linear). Errors as nvfp4_lora_linear, and QN_ERR_SHAPE for k % 32 != 0. Workspace: zero-filled before
+ * its first use, mxfp4_lora_linear_workspace bytes, left with its control words zero (as for nvfp4_lora_linear). */
+size_t mxfp4_lora_linear_workspace(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj);
+qn_status mxfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const qn_aqn* aqn,
+                            const qn_proj* projs, int32_t nproj, int32_t epilogue, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
 /* Kernel choice for nvfp4_lora_linear_opts. A call runs one of three streaming kernels; the library picks one from
  * the token count and the shapes (QN_KERNEL_AUTO, what nvfp4_lora_linear does). Naming another one runs the same
  * computation, to the same accuracy bound, on that kernel: for checks of each kernel on the same inputs and for

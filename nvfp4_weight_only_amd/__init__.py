@@ -30,7 +30,7 @@ EXPORTS = ["nvfp4_quantize", "nvfp4_tiled_codes_bytes", "nvfp4_tiled_scales_byte
            "nvfp4_lora_linear_opts", "nvfp4_lora_linear_noalloc", "nvfp4_lora_linear_noalloc_max_bytes",
            "aqn_sigma", "grpo_group_advantage", "grpo_clipped_surrogate", "qn_stream_read", "qn_status_string",
            "nvfp4_lora_linear_backward", "nvfp4_lora_linear_backward_workspace", "mxfp4_quantize",
-           "mxfp4_dequantize", "mxfp4_scales_bytes"]
+           "mxfp4_dequantize", "mxfp4_scales_bytes", "mxfp4_lora_linear", "mxfp4_lora_linear_workspace"]
 
 
 class QnError(RuntimeError):
@@ -91,6 +91,9 @@ def _load():
         "aqn_rmsnorm": ([P, i64, i64, i64, ctypes.POINTER(QnAqn), P, i64, P], i32),
         "aqn_noise": ([ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64, i64, i64, i64, P, i64, P], i32),
         "nvfp4_lora_linear_workspace": ([i64, i64, ctypes.POINTER(QnProj), i32], sz),
+        "mxfp4_lora_linear_workspace": ([i64, i64, ctypes.POINTER(QnProj), i32], sz),
+        "mxfp4_lora_linear": ([P, i64, i64, i64, ctypes.POINTER(QnAqn), ctypes.POINTER(QnProj), i32, i32, P, sz, P],
+                              i32),
         "nvfp4_lora_linear": ([P, i64, i64, i64, ctypes.POINTER(QnAqn), ctypes.POINTER(QnProj), i32, i32, P, sz, P],
                               i32),
         "nvfp4_lora_linear_workspace_opts": ([i64, i64, ctypes.POINTER(QnProj), i32, ctypes.POINTER(QnLinearOpts)],
@@ -316,7 +319,9 @@ class Projection:
     def to_c(self) -> QnProj:
         p = QnProj()
         w = self.weight
-        p.codes, p.block_scales, p.tensor_scale = w.codes.data_ptr(), w.scales.data_ptr(), w.tensor_scale.data_ptr()
+        ts = getattr(w, "tensor_scale", None)  # (an MXFP4Weight in the canonical layout has none)
+        p.codes, p.block_scales = w.codes.data_ptr(), w.scales.data_ptr()
+        p.tensor_scale = ts.data_ptr() if ts is not None else None
         p.n = w.n
         if self.lora_a is not None:
             p.lora_a, p.lora_b, p.r = self.lora_a.data_ptr(), self.lora_b.data_ptr(), self.lora_a.shape[0]
@@ -396,6 +401,20 @@ def lora_linear(x: torch.Tensor, projs: Sequence[Projection], aqn: Optional[AqnP
     (torch's usual rule for tensors shared between streams)."""
     with _on(stream):
         LinearCall(x, projs, aqn, epilogue, workspace, opts)(stream)
+
+
+def mxfp4_lora_linear(x: torch.Tensor, projs: Sequence[Projection], aqn: Optional[AqnParams] = None,
+                      epilogue: int = EPI_NONE, workspace: Optional[Workspace] = None, stream=None):
+    """mxfp4_lora_linear: the call on MXFP4 weights in the canonical MX layout (MXFP4Weight from mxfp4_quantize with
+    LAYOUT_ROWMAJOR), on the scaled FP4 x FP8 MFMA kernel. Same arguments and workspace rules as lora_linear."""
+    m, k = x.shape
+    arr = (QnProj * len(projs))(*[p.to_c() for p in projs])
+    with _on(stream):
+        need = int(lib.mxfp4_lora_linear_workspace(m, k, arr, len(projs)))
+        ws = (workspace or Workspace(x.device)).get(need)
+    _check(lib.mxfp4_lora_linear(_ptr(x), m, k, x.stride(0), ctypes.byref(aqn.c) if aqn is not None else None, arr,
+                                 len(projs), epilogue, _ptr(ws), ws.numel(), _stream(stream)), "mxfp4_lora_linear")
+    _keep_for(ws, stream)
 
 
 def lora_linear_noalloc(x: torch.Tensor, projs: Sequence[Projection], aqn: Optional[AqnParams] = None,

@@ -98,8 +98,9 @@ struct LinearArgs {
 
 // Workspace carve-up (256-byte aligned regions).
 struct Workspace {
-  size_t xs, xsc, rstd, tok_p, t_part, t_fin, pbuf, t_fused, cnt, total;
+  size_t xs, xsc, rstd, tok_p, t_part, t_fin, pbuf, t_fused, cnt, xmx, total;
 };
+constexpr int kMxScStage = 64 * 16 * 4;  // activation E8M0 words of one (128-token block, k-tile): [lane][tile][hi, lo]
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -128,7 +129,9 @@ constexpr int kCoherent = 16;          // buffer-access cache policy sc1: device
 struct Opts;
 size_t gemv_pbuf_bytes(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj, const Opts& o);
 
-Workspace workspace_layout(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj, const Opts& o) {
+// mx: a call of mxfp4_lora_linear (the scaled-MFMA kernel at every token count: t summed for every token tile, and the
+// activations' block scales).
+Workspace workspace_layout(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj, const Opts& o, bool mx = false) {
   const int64_t KT = ceil_div(k, kKTile), kp = KT * kKTile;
   const int64_t mp = ceil_div(m, 16) * 16;
   Workspace w;
@@ -142,8 +145,9 @@ Workspace workspace_layout(int64_t m, int64_t k, const qn_proj* projs, int32_t n
   w.rstd = off;   off = align256(off + (size_t)mp * 4);
   w.tok_p = off;  off = align256(off + (size_t)mp * 4);
   w.t_part = off; off = align256(off + (size_t)nproj * (mp / 16) * kRankChunks * lora_chunks(k) * kWave * 32);
-  w.t_fin = off;  off = align256(off + (m > 16 ? (size_t)nproj * (mp / 16) * kRankChunks * 2 * kWave * 16 : 0));
-  w.pbuf = off;   off = align256(off + gemv_pbuf_bytes(m, k, projs, nproj, o));
+  w.t_fin = off;  off = align256(off + (m > 16 || mx ? (size_t)nproj * (mp / 16) * kRankChunks * 2 * kWave * 16 : 0));
+  w.pbuf = off;   off = align256(off + (mx ? 0 : gemv_pbuf_bytes(m, k, projs, nproj, o)));
+  w.xmx = off;    off = align256(off + (mx ? (size_t)ceil_div(mp, 128) * KT * kMxScStage : 0));
   w.total = off;
   return w;
 }
@@ -174,6 +178,7 @@ struct PrologueArgs {
   int32_t ncnt;
   u32x4* t_fin;       // or null: the last workgroup of each (pair group, token tile) also sums the LoRA-down chunk
   uint32_t* t_cnt;    // partials into bf16 hi/lo fragments ([p][tile][jc][hi, lo][lane]); t_cnt: their arrivals
+  uint32_t* xmx_sc;  // non-null: activations out as E4M3 hi and lo parts with E8M0 scales (the scaled-MFMA kernel)
   int32_t tgs;    // tokens per workgroup: 16 (a whole token tile) or 4 (the tile split over four workgroups)
   int32_t pgm;    // pair groups per workgroup: 1, or 2 (h computed once for both, many tokens)
   QnDraw draw;    // noise drawn on the device (draw.on) instead of read from `noise`
@@ -297,6 +302,34 @@ __device__ __forceinline__ int act_exponent(float amax) {
     pw = pw > 126 ? 126 : pw;
   }
   return pw;
+}
+
+// E8M0 exponent s of a 32-value block with largest magnitude amax for the scaled-MFMA activations: amax * 2^-s in
+// [128, 256), so every value of the block lies within the E4M3 range after the scaling; 0 for a block of zeros.
+__device__ __forceinline__ int mx_block_exp(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  const int e = (int)((__float_as_uint(amax) >> 23) & 0xffu) - 127;
+  const int s = e - 7;
+  return s < -127 ? -127 : (s > 127 ? 127 : s);
+}
+
+// x (|x| <= 256) to the nearest OCP E4M3 value, ties to even: *code = the byte (sign, 4-bit exponent with bias 7,
+// 3-bit mantissa; subnormals m * 2^-9), return = its value. The grid spacing is 2^(e - 3) in the binade [2^e, 2^(e+1))
+// for e >= -6 and 2^-9 below; x / spacing is exact (a power of two) and rintf rounds it to even.
+__device__ __forceinline__ float e4m3_round(float x, uint32_t* code) {
+  const uint32_t sgn = (__float_as_uint(x) >> 24) & 0x80u;
+  const float ax = fabsf(x);
+  int e = (int)((__float_as_uint(ax) >> 23) & 0xffu) - 127;
+  e = e < -6 ? -6 : e;
+  const float q = __uint_as_float((uint32_t)(e - 3 + 127) << 23);
+  const float r = rintf(ax / q) * q;
+  uint32_t c;
+  const int er = (int)((__float_as_uint(r) >> 23) & 0xffu) - 127;
+  if (r == 0.0f) c = 0u;
+  else if (er < -6) c = (uint32_t)(r * 512.0f);  // subnormal: m * 2^-9
+  else c = ((uint32_t)(er + 7) << 3) | ((__float_as_uint(r) >> 20) & 7u);
+  *code = sgn | c;
+  return sgn ? -r : r;
 }
 
 // Row statistics for many tokens: one wave per token. With the norm, rstd in the summation order of the standalone
@@ -521,7 +554,57 @@ __global__ void __launch_bounds__(kProWaves * kWave) k_prologue(PrologueArgs a) 
       }
     }
     *reinterpret_cast<u32x4*>(&s_h[t][kg * 8]) = u32x4{hv[0], hv[1], hv[2], hv[3]};
-    if (pz == 0) {
+    if (pz == 0 && a.xmx_sc) {
+      // scaled-MFMA activations: each 32-value block (4 consecutive lanes) as hi = E4M3(h * 2^-s_hi) and
+      // lo = E4M3((h - hi * 2^s_hi) * 2^-s_lo), both with E8M0 block exponents; in the 16x16x128 B-operand layout
+      // (lane (k / 16) % 4 * 16 + token holds k % 16 + (k / 64) * 16 of its 32 bytes), the scale of block b in lane
+      // b * 16 + token. The 8 values of this thread are one contiguous 8-byte piece of a lane.
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = lo_bf16(hv[e]);
+        v[2 * e + 1] = hi_bf16(hv[e]);
+      }
+      float am = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(v[e]));
+      am = fmaxf(am, __shfl_xor(am, 1, kWave));
+      am = fmaxf(am, __shfl_xor(am, 2, kWave));
+      const int sh = mx_block_exp(am);
+      const float dh = ldexpf(1.0f, -sh), uh = ldexpf(1.0f, sh);  // (2^-127 is subnormal: no exponent-field trick)
+      uint32_t hb[2] = {0u, 0u}, lb[2] = {0u, 0u};
+      float rr[8], ar = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint32_t c;
+        const float hval = e4m3_round(v[e] * dh, &c);
+        hb[e / 4] |= c << (8 * (e % 4));
+        rr[e] = v[e] - hval * uh;  // exact: v has 8 significant bits, hval * 2^s_hi the leading ones
+        ar = fmaxf(ar, fabsf(rr[e]));
+      }
+      ar = fmaxf(ar, __shfl_xor(ar, 1, kWave));
+      ar = fmaxf(ar, __shfl_xor(ar, 2, kWave));
+      const int sl = mx_block_exp(ar);
+      const float dl = ldexpf(1.0f, -sl);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint32_t c;
+        e4m3_round(rr[e] * dl, &c);
+        lb[e / 4] |= c << (8 * (e % 4));
+      }
+      const int64_t kt = kt0 + ktl;
+      if (mine(t)) {
+        const int L = ((jj / 2) % 4) * 16 + t, bo = (jj / 8) * 16 + (jj % 2) * 8;
+        uint8_t* const fb = reinterpret_cast<uint8_t*>(a.xs) + ((tile * a.KT + kt) * 2) * 2048 + L * 32 + bo;
+        *reinterpret_cast<u32x2*>(fb) = u32x2{hb[0], hb[1]};
+        *reinterpret_cast<u32x2*>(fb + 2048) = u32x2{lb[0], lb[1]};
+        if (jj % 4 == 0) {  // [tile block of 8][k-tile][lane][tile % 8][hi, lo] E8M0 words
+          uint32_t* const sp = a.xmx_sc + (((int64_t)(tile / 8) * a.KT + kt) * kWave + (jj / 4) * 16 + t) * 16 +
+                               (tile % 8) * 2;
+          *reinterpret_cast<u32x2*>(sp) = u32x2{(uint32_t)(sh + 127), (uint32_t)(sl + 127)};
+        }
+      }
+    } else if (pz == 0) {
       // tile amax over the 16 lanes of this (token, k-tile), then 2^p with amax * 2^p in [2^14, 2^15), read off the
       // exponent field and kept within the normal range so 2^p and 2^-p are plain f32 powers of two
       int pw;
@@ -2953,6 +3036,7 @@ constexpr int kMActLoads = 4;
 struct GemmArgs {
   LinearArgs L;
   const u32x4* t_fin;       // LoRA t fragments from k_lora_tsum
+  const uint32_t* xmx_sc;   // MX weights: the activations' E8M0 words [tile block][k-tile][lane][tile % 8][hi, lo]
   int32_t KT, ntiles, nrg;  // k-tiles; token tiles; row groups (flattened; with SILU: pairs x 2)
   int32_t nrb, ntb;         // row blocks and token blocks of the grid
   int32_t fast_store;       // outputs and residuals allow 16-byte accesses and no output is broadcast
@@ -2974,7 +3058,18 @@ __device__ __forceinline__ f16x8 dequant_frag(uint32_t cw, uint32_t scale_byte) 
   return f16x8{q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
 }
 
-template <bool SILU>
+// MX: weights in the canonical MXFP4 layout (codes [n][k/2], E8M0 scales [n][k/32]) on the scaled FP4 x FP8 MFMA
+// (v_mfma_scale_f32_16x16x128_f8f6f4: one k-tile per instruction), against activations given as E4M3 hi and lo parts
+// with E8M0 block scales (two MFMAs per product, no unpack); no tensor scale and no per-token exponent.
+constexpr int kMSc = kWave * 16 * 4;  // activation scale words of a stage: [lane][token tile][hi, lo]
+static_assert(kMSc == kMxScStage, "activation scale stage");
+struct MWX {
+  u32x4 c[4];       // the lane's 32 codes (row lane % 16, 32-block lane / 16) of each slot
+  uint32_t sc[4];   // their E8M0 scale
+};
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+template <bool SILU, bool MX>
 __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
   // Four stages. Stages 2 and 3 are arrays of their own: the compiler then knows that a stage being read and one
   // being filled by a load into LDS never overlap, and issues no wait for the in-flight fills before each stage's
@@ -2987,11 +3082,16 @@ __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
   uint8_t* const s_st1 = s_st + kMAct;
   uint8_t* const s_st2 = s_st2a;
   uint8_t* const s_st3 = s_st3a;
+  __shared__ __attribute__((aligned(16))) uint8_t s_sc0[MX ? kMSc : 16];  // MX: the stages' activation scales
+  __shared__ __attribute__((aligned(16))) uint8_t s_sc1[MX ? kMSc : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_sc2[MX ? kMSc : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_sc3[MX ? kMSc : 16];
   __shared__ ProjEpi s_pe[kMaxProj];
   __shared__ float s_tsc[kMTT * 16];  // the tokens' 2^-p
   const LinearArgs& a = g.L;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
   const int KT = g.KT;
+  const int kh = (int)(a.k / 2), ks32 = (int)(a.k / 32);  // MX: bytes of codes and of scales per row
 
   // workgroup -> (row block, token block). Workgroup ids go round-robin over the 8 XCDs; each XCD's ids are given a
   // contiguous range of tiles, walked kMTBGroup token blocks at a time, row blocks outer.
@@ -3036,8 +3136,14 @@ __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
     pj[jj] = p;
     rgl[jj] = rl;
     const ProjArgs& P = a.p[p];
-    cd[jj] = make_rsrc(P.codes + rl * KT * kTileCodeBytes, live ? (int64_t)KT * kTileCodeBytes : 0);
-    sd[jj] = make_rsrc(P.scales + rl * KT * kTileScaleBytes, live ? (int64_t)KT * kTileScaleBytes : 0);
+    if (MX) {  // the row group's rows that exist (the canonical layout has no padding rows)
+      const int64_t rows = live ? (P.n - rl * 16 < 16 ? P.n - rl * 16 : 16) : 0;
+      cd[jj] = make_rsrc(P.codes + rl * 16 * kh, rows * kh);
+      sd[jj] = make_rsrc(P.scales + rl * 16 * ks32, rows * ks32);
+    } else {
+      cd[jj] = make_rsrc(P.codes + rl * KT * kTileCodeBytes, live ? (int64_t)KT * kTileCodeBytes : 0);
+      sd[jj] = make_rsrc(P.scales + rl * KT * kTileScaleBytes, live ? (int64_t)KT * kTileScaleBytes : 0);
+    }
   }
   const uint32_t c_off = lane * 16, s_off = ((lane % 16) * 2 + (lane / 16) / 2) * 4;
   const rsrc_t xsrc = make_rsrc(a.xs + (int64_t)tile0 * KT * 4 * kWave, (int64_t)ntl * KT * 4 * kWave * 16);
@@ -3086,6 +3192,30 @@ __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) w.sc[jj] = __builtin_amdgcn_raw_buffer_load_b32(sd[jj], in ? s_off : kOutOfRange, ks, 0);
   };
+  // MX: the lane's codes and scale of k-tile kt for every slot (a 32-block past k, or a tile past KT, reads 0), and
+  // the activation scale words of the stage (1 KB per wave pair: every wave issues two 4-byte loads per lane, so the
+  // wait counts are the same in every wave)
+  auto w_load_mx = [&](MWX& w, int kt) __attribute__((always_inline)) {
+    const bool in = kt < KT && kt * kKTile + (lane / 16) * 32 < (int)a.k;
+    const uint32_t co = (uint32_t)((lane % 16) * kh + (lane / 16) * 16), so = (uint32_t)((lane % 16) * ks32 + lane / 16);
+    const int kc = __builtin_amdgcn_readfirstlane(kt < KT ? kt * 64 : 0), kb = __builtin_amdgcn_readfirstlane(kt < KT ? kt * 4 : 0);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      w.c[jj] = __builtin_amdgcn_raw_buffer_load_b128(cd[jj], in ? co : kOutOfRange, kc, 0);
+      w.sc[jj] = __builtin_amdgcn_raw_buffer_load_b8(sd[jj], in ? so : kOutOfRange, kb, 0);
+    }
+  };
+  const rsrc_t scsrc = make_rsrc(g.xmx_sc + (int64_t)(tile0 / kMTT) * KT * (kMSc / 4), MX ? (int64_t)KT * kMSc : 0);
+  auto sc_load = [&](uint8_t* scst, int kt) __attribute__((always_inline)) {
+    const bool in = kt < KT;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q0 = (2 * (wave & (kMWaves - 1)) + i) * kWave * 4;  // this load's first byte in the stage (256 each)
+      const int so = __builtin_amdgcn_readfirstlane(in ? kt * kMSc + q0 : 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(scsrc, (__attribute__((address_space(3))) void*)(scst + q0), 4,
+                                               in ? lane * 4 : kOutOfRange, so, 0, 0);
+    }
+  };
 
   f32x4 acc[4][kMTT];
 #pragma unroll
@@ -3131,13 +3261,51 @@ __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
   // compute kt (which requests the weights of kt + 1). Loads in order: act 0, act 1, act 2, W 0, then per step
   // act kt+3, W kt+1 (12 loads). Before step kt the loads issued after act kt that may be outstanding are at most
   // act kt+1, W kt-1 (landed: used in step kt-1), act kt+2, W kt, i.e. 32.
+  // MX: one k-tile: the next k-tile's weights requested first (into the other register set), the lane's 16 scale
+  // words from the stage, then per token tile its hi and lo fragments (32 bytes each) and two scaled MFMAs per slot
+  auto compute_mx = [&](const uint8_t* st, const uint8_t* scst, const MWX& w, MWX& wn, int kt_next)
+      __attribute__((always_inline)) {
+    w_load_mx(wn, kt_next);
+    u32x4 s4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s4[q] = *reinterpret_cast<const u32x4*>(scst + lane * 64 + q * 16);
+    const uint8_t* const stl = st + lane * 32;
+#pragma unroll
+    for (int i = 0; i < kMTT; ++i) {
+      const i32x8 hb = *reinterpret_cast<const i32x8*>(stl + (i * 2) * 2048);
+      const i32x8 lb = *reinterpret_cast<const i32x8*>(stl + (i * 2 + 1) * 2048);
+      const int shi = (int)s4[i / 2][(i % 2) * 2], slo = (int)s4[i / 2][(i % 2) * 2 + 1];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const i32x8 aw = {(int)w.c[jj][0], (int)w.c[jj][1], (int)w.c[jj][2], (int)w.c[jj][3], 0, 0, 0, 0};
+        acc[jj][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw, hb, acc[jj][i], 4, 0, 0, (int)w.sc[jj], 0, shi);
+        acc[jj][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw, lb, acc[jj][i], 4, 0, 0, (int)w.sc[jj], 0, slo);
+      }
+      // one token tile's fragments live at a time: the MFMAs have no memory effects, so without this statement the
+      // compiler sinks them past later steps' barriers and holds (spills) every tile's fragments until then; the
+      // statement takes this tile's results, which pins the MFMAs above it and the next tile's LDS reads below it
+      asm volatile("" : "+v"(acc[0][i]), "+v"(acc[1][i]), "+v"(acc[2][i]), "+v"(acc[3][i])::"memory");
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   MW W;
-  act_load(s_st0, 0);
-  act_load(s_st1, 1);
-  act_load(s_st2, 2);
-  w_load_half(W, 0, 0);
-  w_load_half(W, 0, 1);
-  w_load_sc(W, 0);
+  MWX WX[2];
+  if constexpr (MX) {
+    act_load(s_st0, 0);
+    sc_load(s_sc0, 0);
+    act_load(s_st1, 1);
+    sc_load(s_sc1, 1);
+    act_load(s_st2, 2);
+    sc_load(s_sc2, 2);
+    w_load_mx(WX[0], 0);
+  } else {
+    act_load(s_st0, 0);
+    act_load(s_st1, 1);
+    act_load(s_st2, 2);
+    w_load_half(W, 0, 0);
+    w_load_half(W, 0, 1);
+    w_load_sc(W, 0);
+  }
   // the epilogue's per-projection parameters and the tokens' 2^-p, fetched now (their latency overlaps that of the
   // first loads) and kept in LDS
   if (threadIdx.x < kMaxProj) {
@@ -3145,17 +3313,21 @@ __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
     for (int q = 0; q < kMaxProj; ++q)
       if (threadIdx.x == q && q < a.nproj) {
         const ProjArgs& P = a.p[q];
-        s_pe[q] = ProjEpi{P.y, P.res, P.n, P.ldy, P.ld_res, gload(P.s_g), P.lambda, P.y_dtype, P.y_repeat,
-                          P.head_dim, P.rg_begin, P.r};
+        s_pe[q] = ProjEpi{P.y, P.res, P.n, P.ldy, P.ld_res, MX ? 1.0f : gload(P.s_g), P.lambda, P.y_dtype,
+                          P.y_repeat, P.head_dim, P.rg_begin, P.r};  // (MX weights carry no tensor scale)
       }
   }
   if (threadIdx.x < kMTT * 16) {
     const int i = threadIdx.x / 16;
-    s_tsc[threadIdx.x] = i < ntl ? gload(a.xsc + (int64_t)(tile0 + i) * KT * 16 + threadIdx.x % 16) : 0.f;
+    if (MX) s_tsc[threadIdx.x] = 1.0f;  // (the block scales carry the activations' range)
+    else s_tsc[threadIdx.x] = i < ntl ? gload(a.xsc + (int64_t)(tile0 + i) * KT * 16 + threadIdx.x % 16) : 0.f;
   }
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
   constexpr int kWaitAct = vmcnt_imm(2 * (kMActLoads + 12));
+  // MX, step kt: loads in order act+scales kt (6), W kt-2 (8), act+scales kt+1, W kt-1, act+scales kt+2, W kt; the
+  // ones after act+scales kt may be outstanding: 3 * 8 + 2 * 6
+  constexpr int kWaitMX = vmcnt_imm(3 * 8 + 2 * (kMActLoads + 2));
   // A plain s_barrier (a compiler barrier for memory, no fence): a workgroup fence would also wait for the next
   // stages' loads into LDS, which are meant to stay in flight.
   auto step = [&](const uint8_t* st_use, uint8_t* st_next, int kt) __attribute__((always_inline)) {
@@ -3166,11 +3338,34 @@ __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
     compute(st_use, W, kt + 1);  // (a k-tile past KT has zero weights and zero activations: adds exactly zero)
     __builtin_amdgcn_sched_barrier(0);
   };
-  for (int kt = 0; kt < KT; kt += 4) {
-    step(s_st0, s_st3, kt);
-    step(s_st1, s_st0, kt + 1);
-    step(s_st2, s_st1, kt + 2);
-    step(s_st3, s_st2, kt + 3);
+  auto step_mx = [&](const uint8_t* st_use, const uint8_t* sc_use, uint8_t* st_next, uint8_t* sc_next, int kt,
+                     const MWX& wc, MWX& wn) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(kWaitMX);
+    asm volatile("s_barrier" ::: "memory");
+    act_load(st_next, kt + 3);
+    sc_load(sc_next, kt + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_mx(st_use, sc_use, wc, wn, kt + 1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  if constexpr (MX) {
+    for (int kt = 0; kt < KT; kt += 4) {
+      step_mx(s_st0, s_sc0, s_st3, s_sc3, kt, WX[0], WX[1]);
+      step_mx(s_st1, s_sc1, s_st0, s_sc0, kt + 1, WX[1], WX[0]);
+      step_mx(s_st2, s_sc2, s_st1, s_sc1, kt + 2, WX[0], WX[1]);
+      step_mx(s_st3, s_sc3, s_st2, s_sc2, kt + 3, WX[1], WX[0]);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int i = 0; i < kMTT; ++i) mfma_settle(acc[jj][i]);  // (read by the epilogue past the loop's exit)
+  } else {
+    for (int kt = 0; kt < KT; kt += 4) {
+      step(s_st0, s_st3, kt);
+      step(s_st1, s_st0, kt + 1);
+      step(s_st2, s_st1, kt + 2);
+      step(s_st3, s_st2, kt + 3);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();  // every wave is done with the stages
@@ -3496,11 +3691,12 @@ bool general_shape(int64_t mt, bool silu, int64_t nrg, int64_t KT, const Opts& o
 }
 
 // All host-side validation of a call (nothing is launched on failure); on success the plan of its main kernel.
+// mx: weights in the canonical MXFP4 layout for the scaled-MFMA kernel (k % 32 == 0; no tensor scale; byte scales).
 qn_status validate_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const qn_aqn* aqn,
                           const qn_proj* projs, int32_t nproj, int32_t epilogue, const Opts& o, void* workspace,
-                          size_t workspace_bytes, Plan* plan, bool check_workspace) {
+                          size_t workspace_bytes, Plan* plan, bool check_workspace, bool mx = false) {
   if (!opts_valid(o)) return QN_ERR_VALUE;
-  if (m < 0 || k < 0 || k % 16 != 0) return QN_ERR_SHAPE;
+  if (m < 0 || k < 0 || k % (mx ? 32 : 16) != 0) return QN_ERR_SHAPE;
   if (!projs) return QN_ERR_NULL;
   if (nproj < 1) return QN_ERR_SHAPE;
   if (nproj > kMaxProj) return QN_ERR_UNSUPPORTED;
@@ -3526,12 +3722,13 @@ qn_status validate_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, 
     const qn_proj& P = projs[p];
     if (P.n == 0) continue;
     const bool needs_y = !(epilogue == QN_EPI_SILU_MUL && p == 1);
-    if (!P.codes || !P.block_scales || !P.tensor_scale || (needs_y && !P.y)) return QN_ERR_NULL;
+    if (!P.codes || !P.block_scales || (!mx && !P.tensor_scale) || (needs_y && !P.y)) return QN_ERR_NULL;
     if (P.r > 0 && (!P.lora_a || !P.lora_b)) return QN_ERR_NULL;
     const int64_t width = P.y_repeat > 1 ? P.n * P.y_repeat : P.n;
     if (needs_y && P.ldy < width) return QN_ERR_SHAPE;
     if (P.residual && P.ld_res < P.n) return QN_ERR_SHAPE;
-    if (!aligned(P.codes, 16) || !aligned(P.block_scales, 4) || !aligned(P.tensor_scale, 4)) return QN_ERR_ALIGN;
+    if (!aligned(P.codes, 16) || (!mx && (!aligned(P.block_scales, 4) || !aligned(P.tensor_scale, 4))))
+      return QN_ERR_ALIGN;
     if (P.r > 0 && (!aligned(P.lora_a, 16) || !aligned(P.lora_b, 2))) return QN_ERR_ALIGN;
     if (P.r > 0 && P.r % 8 == 0 && !aligned(P.lora_b, 16)) return QN_ERR_ALIGN;
   }
@@ -3556,10 +3753,15 @@ qn_status validate_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, 
   int64_t rg_total = 0;
   for (int p = 0; p < nproj; ++p) rg_total += ceil_div(projs[p].n, 16);
   const int64_t nrg = silu ? 2 * ceil_div(projs[0].n, 16) : rg_total;
-  const qn_status ps =
-      plan_main(m, KT, silu ? ceil_div(projs[0].n, 16) : rg_total, silu, aqn != nullptr, projs, nproj, o, phases == 0,
-                plan);
-  if (ps != QN_OK) return ps;
+  if (mx) {
+    if (o.kernel != QN_KERNEL_AUTO) return QN_ERR_UNSUPPORTED;
+    *plan = Plan{};
+    plan->path = kPathMany;
+  } else {
+    const qn_status ps = plan_main(m, KT, silu ? ceil_div(projs[0].n, 16) : rg_total, silu, aqn != nullptr, projs,
+                                   nproj, o, phases == 0, plan);
+    if (ps != QN_OK) return ps;
+  }
   if (plan->path == kPathGeneral && nrg > 0) {
     for (int64_t t0 = 0; t0 < m; t0 += kMaxTokensPerLaunch) {
       const int64_t mt = (m - t0) < kMaxTokensPerLaunch ? (m - t0) : kMaxTokensPerLaunch;
@@ -3572,7 +3774,7 @@ qn_status validate_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, 
     if (nrb * ceil_div(ceil_div(m, 16), kMTT) >= ((int64_t)1 << 31)) return QN_ERR_UNSUPPORTED;
   }
   if (check_workspace) {
-    const Workspace wl = workspace_layout(m, k, projs, nproj, o);
+    const Workspace wl = workspace_layout(m, k, projs, nproj, o, mx);
     if (!workspace || workspace_bytes < wl.total) return QN_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return QN_ERR_ALIGN;
     if (wl.total - wl.t_part >= ((size_t)1 << 31)) return QN_ERR_UNSUPPORTED;
@@ -3585,7 +3787,7 @@ qn_status validate_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, 
 // draws of every row those of the whole call).
 qn_status run_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const qn_aqn* aqn, const qn_proj* projs,
                      int32_t nproj, int32_t epilogue, const Opts& o, const Plan& plan, void* workspace,
-                     hipStream_t s, int64_t row_base = 0) {
+                     hipStream_t s, int64_t row_base = 0, bool mx = false) {
   if (plan.split) {
     // sub-calls of at most kSplitTokens rows, one after another on the stream (they share the workspace, whose size
     // covers each of theirs): x, outputs, residuals and per-row noise advance by the rows before them
@@ -3619,7 +3821,7 @@ qn_status run_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const
   const int32_t phases = epilogue & (QN_RUN_PROLOGUE_ONLY | QN_RUN_MAIN_ONLY);
   epilogue &= ~(QN_RUN_PROLOGUE_ONLY | QN_RUN_MAIN_ONLY);
   const bool run_prologue = phases != QN_RUN_MAIN_ONLY, run_main = phases != QN_RUN_PROLOGUE_ONLY;
-  const Workspace wl = workspace_layout(m, k, projs, nproj, o);
+  const Workspace wl = workspace_layout(m, k, projs, nproj, o, mx);
   char* ws = static_cast<char*>(workspace);
   const int64_t KT = ceil_div(k, kKTile), kp = KT * kKTile;
   const int64_t ntiles = ceil_div(m, 16);
@@ -3676,10 +3878,12 @@ qn_status run_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const
       pa.t_fin = reinterpret_cast<u32x4*>(ws + wl.t_fin);
       pa.t_cnt = reinterpret_cast<uint32_t*>(ws + wl.cnt) + kCountWords;
     }
-    // many tokens: row statistics in a kernel of their own (rstd with the norm, and one exponent per token)
-    const bool big = m > kMaxTokensPerLaunch;
+    // many tokens (and every call of the scaled-MFMA kernel): row statistics in a kernel of their own (rstd with the
+    // norm, and one exponent per token, which the scaled-MFMA activations do not use: they carry block scales)
+    const bool big = m > kMaxTokensPerLaunch || mx;
     pa.rstd_in = big && aqn ? rstd : nullptr;
-    pa.tok_p = big && gemm_path ? tok_p : nullptr;
+    pa.tok_p = big && gemm_path && !mx ? tok_p : nullptr;
+    pa.xmx_sc = mx ? reinterpret_cast<uint32_t*>(ws + wl.xmx) : nullptr;
     // with many tokens, two pair groups share a workgroup (h of the chunk is computed once for both)
     pa.pgm = big && norm_threads(k) == 256 ? 2 : 1;
     const int npz = npg > 0 ? (npg + pa.pgm - 1) / pa.pgm : 1;
@@ -3707,7 +3911,7 @@ qn_status run_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const
                             rstd, tok_p);                                                                     \
   } while (0)
     if (!aqn) {
-      if (big) QN_STATS(256, false);
+      if (big && !mx) QN_STATS(256, false);  // (without the norm the scaled-MFMA path needs no statistics)
       if (pa.pgm == 2) QN_PRO(256, false, 2);
       else QN_PRO(256, false, 1);
     } else if (norm_threads(k) == 256) {
@@ -3778,6 +3982,7 @@ qn_status run_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const
     ga.L = la;
     ga.L.tok0 = 0;
     ga.t_fin = t_fin;
+    ga.xmx_sc = mx ? reinterpret_cast<const uint32_t*>(ws + wl.xmx) : nullptr;
     ga.KT = (int32_t)KT;
     ga.ntiles = (int32_t)ntiles;
     ga.nrg = (int32_t)nrg;
@@ -3795,8 +4000,13 @@ qn_status run_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const
     ga.fast_store = fast ? 1 : 0;
     ga.t_lds = silu && projs[0].r <= 32 && projs[1].r <= 32 ? 1 : 0;
     const dim3 grid((unsigned)(ga.nrb * ga.ntb)), block(kMWaves * kWave);
-    if (silu) hipLaunchKernelGGL((k_gemm<true>), grid, block, 0, s, ga);
-    else hipLaunchKernelGGL((k_gemm<false>), grid, block, 0, s, ga);
+    if (mx) {
+      if (silu) hipLaunchKernelGGL((k_gemm<true, true>), grid, block, 0, s, ga);
+      else hipLaunchKernelGGL((k_gemm<false, true>), grid, block, 0, s, ga);
+    } else {
+      if (silu) hipLaunchKernelGGL((k_gemm<true, false>), grid, block, 0, s, ga);
+      else hipLaunchKernelGGL((k_gemm<false, false>), grid, block, 0, s, ga);
+    }
     return hipGetLastError() == hipSuccess ? QN_OK : QN_ERR_HIP;
   }
   if (plan.path == kPathFused) {
@@ -3983,6 +4193,22 @@ extern "C" qn_status nvfp4_lora_linear_noalloc(const uint16_t* x, int64_t m, int
   st = scratch_of_current_device(&ws);
   if (st != QN_OK) return st;
   return run_linear(x, m, k, ldx, aqn, projs, nproj, epilogue, o, plan, ws, (hipStream_t)stream);
+}
+
+extern "C" size_t mxfp4_lora_linear_workspace(int64_t m, int64_t k, const qn_proj* projs, int32_t nproj) {
+  if (m <= 0 || k <= 0 || nproj <= 0 || !projs) return 0;
+  return workspace_layout(m, k, projs, nproj, Opts{}, true).total;
+}
+
+extern "C" qn_status mxfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const qn_aqn* aqn,
+                                       const qn_proj* projs, int32_t nproj, int32_t epilogue, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  const Opts o;
+  Plan plan;
+  const qn_status st =
+      validate_linear(x, m, k, ldx, aqn, projs, nproj, epilogue, o, workspace, workspace_bytes, &plan, true, true);
+  if (st != QN_OK || m == 0 || k == 0) return st;
+  return run_linear(x, m, k, ldx, aqn, projs, nproj, epilogue, o, plan, workspace, (hipStream_t)stream, 0, true);
 }
 
 extern "C" qn_status nvfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const qn_aqn* aqn,

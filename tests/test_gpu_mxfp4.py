@@ -8,7 +8,10 @@
   through nvfp4_dequantize equals the MXFP4 reconstruction bit for bit, and a block too far below the tensor's largest
   is reported;
 - the linear through every kernel (decode, general, many-token) and the backward with MXFP4 weights, against the
-  oracle's MXFP4 linear at the linear bar (max |y - r| / max |r| <= 2e-3).
+  oracle's MXFP4 linear at the linear bar (max |y - r| / max |r| <= 2e-3);
+- mxfp4_lora_linear on the scaled FP4 x FP8 MFMA kernel (canonical weights, activations as E4M3 hi and lo parts with
+  block scales) against the same oracle: ragged shapes and token counts, wide-range activations, the SiLU epilogue,
+  a residual, and the 7B gate|up weights at 512 tokens on sampled rows.
 """
 import numpy as np
 import pytest
@@ -16,7 +19,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import DEV, LINEAR_TOL, dev_bf16, dev_f32, host_u8, rel_err
+from gpu_util import DEV, LINEAR_TOL, bf16_bits_to_f64, dev_bf16, dev_f32, host_u8, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -161,6 +164,74 @@ def test_linear_with_mxfp4_weights(qn, m, ns, k, path):
     ys = c.gpu(qn, opts=opts)
     for p in range(len(ns)):
         assert rel_err(ys[p].cpu().numpy(), c.ref(p)) <= LINEAR_TOL, (path, p)
+
+
+def native(qn, c, epilogue=0, residual=None):
+    """The case through mxfp4_lora_linear: canonical MX weights on the scaled FP4 x FP8 MFMA kernel."""
+    ys, projs = [], []
+    for p, n in enumerate(c.ns):
+        wq = qn.mxfp4_quantize(dev_bf16(c.w[p]), qn.LAYOUT_ROWMAJOR)
+        y = torch.full((c.m, n), float("nan"), dtype=torch.float32, device=DEV)
+        ys.append(y)
+        A = dev_bf16(c.A[p]) if c.r else None
+        B = dev_bf16(c.B[p]) if c.r else None
+        projs.append(qn.Projection(wq, None if (epilogue and p == 1) else y, A, B, c.lam, residual=residual))
+    aqn = qn.make_aqn(dev_bf16(c.gamma), dev_f32(c.noise), c.sigma, 1e-6) if c.aqn else None
+    qn.mxfp4_lora_linear(dev_bf16(c.x), projs, aqn, epilogue)
+    torch.cuda.synchronize()
+    return ys
+
+
+@pytest.mark.parametrize("m,ns,k,r,aqn", [(5, [96], 256, 32, True), (130, [200, 72], 1056, 16, True),
+                                          (300, [1000], 512, 0, False), (256, [512], 4096, 64, True),
+                                          (1, [48], 32, 32, False), (129, [16, 40, 24], 384, 32, True)])
+def test_native_mxfp4_linear(qn, m, ns, k, r, aqn):
+    """mxfp4_lora_linear on the scaled-MFMA kernel against the oracle's MXFP4 linear: one to three projections,
+    ragged n (1000, 40) and token counts (1, 5, 129, 130, 300), a k whose last 128-wide k-tile is a single 32-block
+    (1056) and k = 32, ranks 0 to 64, with and without the norm."""
+    c = MxCase(m, ns, k, r=r, seed=7 * m + k, aqn=aqn)
+    ys = native(qn, c)
+    for p in range(len(ns)):
+        assert rel_err(ys[p].cpu().numpy(), c.ref(p)) <= LINEAR_TOL, p
+
+
+def test_native_mxfp4_wide_range_activations(qn):
+    """Activations spanning 2^-20..2^0 within every 32-block (normal values times 2^e, e uniform on -20..0), so many
+    values lie below the hi part's range and live in the lo part, or below both."""
+    c = MxCase(140, [256], 1024, seed=11, aqn=False)
+    rng = np.random.default_rng(11)
+    x = rng.normal(0.0, 1.0, c.x.shape) * 2.0 ** rng.integers(-20, 1, c.x.shape)
+    c.x = (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    y = native(qn, c)[0]
+    assert rel_err(y.cpu().numpy(), c.ref(0)) <= LINEAR_TOL
+
+
+def test_native_mxfp4_silu_epilogue_and_residual(qn):
+    """SiLU(gate) * up from a gate|up pair, and a single projection with a residual added, on the scaled-MFMA
+    kernel."""
+    c = MxCase(200, [384, 384], 640, seed=12)
+    y = native(qn, c, epilogue=qn.EPI_SILU_MUL)[0]
+    assert rel_err(y.cpu().numpy(), oracle.silu_mul(c.ref(0), c.ref(1))) <= LINEAR_TOL
+    c2 = MxCase(150, [256], 512, seed=13)
+    res = synth.normal_bf16(synth.seed_for(153, 0, "x"), (150, 256))
+    y2 = native(qn, c2, residual=dev_bf16(res))[0]
+    assert rel_err(y2.cpu().numpy(), c2.ref(0) + bf16_bits_to_f64(res)) <= LINEAR_TOL
+
+
+def test_native_mxfp4_7b_gate_up_sampled(qn):
+    """The 7B gate|up weights (18,944 x 3,584 each, canonical MXFP4) at 512 tokens with the norm and SiLU(gate) * up,
+    every output of 48 sampled rows against the oracle on those rows."""
+    m, n, k = 512, 18944, 3584
+    s = lambda t: synth.seed_for(154, 0, t)
+    c = MxCase(m, [n, n], k, seed=14)
+    y = native(qn, c, epilogue=qn.EPI_SILU_MUL)[0].cpu().numpy()
+    rows = np.random.default_rng(14).choice(n, 48, replace=False)
+    h = c.h()
+    outs = []
+    for p in range(2):
+        cc, sc, _ = oracle.mxfp4_quantize(c.w[p][rows])
+        outs.append(oracle.mxfp4_lora_linear(h, cc, sc, c.A[p], c.B[p][rows], c.lam))
+    assert rel_err(y[:, rows], oracle.silu_mul(outs[0], outs[1])) <= LINEAR_TOL
 
 
 def test_linear_silu_epilogue_with_mxfp4_weights(qn):
