@@ -313,24 +313,6 @@ __device__ __forceinline__ int mx_block_exp(float amax) {
   return s < -127 ? -127 : (s > 127 ? 127 : s);
 }
 
-// x (|x| <= 256) to the nearest OCP E4M3 value, ties to even: *code = the byte (sign, 4-bit exponent with bias 7,
-// 3-bit mantissa; subnormals m * 2^-9), return = its value. The grid spacing is 2^(e - 3) in the binade [2^e, 2^(e+1))
-// for e >= -6 and 2^-9 below; x / spacing is exact (a power of two) and rintf rounds it to even.
-__device__ __forceinline__ float e4m3_round(float x, uint32_t* code) {
-  const uint32_t sgn = (__float_as_uint(x) >> 24) & 0x80u;
-  const float ax = fabsf(x);
-  int e = (int)((__float_as_uint(ax) >> 23) & 0xffu) - 127;
-  e = e < -6 ? -6 : e;
-  const float q = __uint_as_float((uint32_t)(e - 3 + 127) << 23);
-  const float r = rintf(ax / q) * q;
-  uint32_t c;
-  const int er = (int)((__float_as_uint(r) >> 23) & 0xffu) - 127;
-  if (r == 0.0f) c = 0u;
-  else if (er < -6) c = (uint32_t)(r * 512.0f);  // subnormal: m * 2^-9
-  else c = ((uint32_t)(er + 7) << 3) | ((__float_as_uint(r) >> 20) & 7u);
-  *code = sgn | c;
-  return sgn ? -r : r;
-}
 
 // Row statistics for many tokens: one wave per token. With the norm, rstd in the summation order of the standalone
 // norm; then the token's largest |h| over its whole row (h exactly as the prologue computes it), giving one exponent
@@ -571,26 +553,28 @@ __global__ void __launch_bounds__(kProWaves * kWave) k_prologue(PrologueArgs a) 
       am = fmaxf(am, __shfl_xor(am, 1, kWave));
       am = fmaxf(am, __shfl_xor(am, 2, kWave));
       const int sh = mx_block_exp(am);
+      // (v_cvt_pk_fp8_f32: two f32 to OCP E4M3, round to nearest even; every scaled value lies within 256, so
+      // nothing saturates)
       const float dh = ldexpf(1.0f, -sh), uh = ldexpf(1.0f, sh);  // (2^-127 is subnormal: no exponent-field trick)
       uint32_t hb[2] = {0u, 0u}, lb[2] = {0u, 0u};
       float rr[8], ar = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint32_t c;
-        const float hval = e4m3_round(v[e] * dh, &c);
-        hb[e / 4] |= c << (8 * (e % 4));
-        rr[e] = v[e] - hval * uh;  // exact: v has 8 significant bits, hval * 2^s_hi the leading ones
-        ar = fmaxf(ar, fabsf(rr[e]));
+      for (int e = 0; e < 4; ++e) {
+        const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[2 * e] * dh, v[2 * e + 1] * dh, 0, false);
+        hb[e / 2] |= ((uint32_t)pk & 0xFFFFu) << (16 * (e % 2));
+        // the remainders, exact: v has 8 significant bits and hi * 2^s_hi its leading ones
+        rr[2 * e] = v[2 * e] - __builtin_amdgcn_cvt_f32_fp8(pk, 0) * uh;
+        rr[2 * e + 1] = v[2 * e + 1] - __builtin_amdgcn_cvt_f32_fp8(pk, 1) * uh;
+        ar = fmaxf(ar, fmaxf(fabsf(rr[2 * e]), fabsf(rr[2 * e + 1])));
       }
       ar = fmaxf(ar, __shfl_xor(ar, 1, kWave));
       ar = fmaxf(ar, __shfl_xor(ar, 2, kWave));
       const int sl = mx_block_exp(ar);
       const float dl = ldexpf(1.0f, -sl);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint32_t c;
-        e4m3_round(rr[e] * dl, &c);
-        lb[e / 4] |= c << (8 * (e % 4));
+      for (int e = 0; e < 4; ++e) {
+        const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(rr[2 * e] * dl, rr[2 * e + 1] * dl, 0, false);
+        lb[e / 2] |= ((uint32_t)pk & 0xFFFFu) << (16 * (e % 2));
       }
       const int64_t kt = kt0 + ktl;
       if (mine(t)) {
@@ -3275,10 +3259,16 @@ __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
       const i32x8 hb = *reinterpret_cast<const i32x8*>(stl + (i * 2) * 2048);
       const i32x8 lb = *reinterpret_cast<const i32x8*>(stl + (i * 2 + 1) * 2048);
       const int shi = (int)s4[i / 2][(i % 2) * 2], slo = (int)s4[i / 2][(i % 2) * 2 + 1];
+      // the four slots' hi products, then their lo products: each lo MFMA accumulates onto its slot's hi result,
+      // issued four instructions earlier (back to back, every second MFMA would wait for the one before it)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const i32x8 aw = {(int)w.c[jj][0], (int)w.c[jj][1], (int)w.c[jj][2], (int)w.c[jj][3], 0, 0, 0, 0};
         acc[jj][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw, hb, acc[jj][i], 4, 0, 0, (int)w.sc[jj], 0, shi);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const i32x8 aw = {(int)w.c[jj][0], (int)w.c[jj][1], (int)w.c[jj][2], (int)w.c[jj][3], 0, 0, 0, 0};
         acc[jj][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw, lb, acc[jj][i], 4, 0, 0, (int)w.sc[jj], 0, slo);
       }
       // one token tile's fragments live at a time: the MFMAs have no memory effects, so without this statement the
