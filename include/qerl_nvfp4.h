@@ -262,6 +262,13 @@ typedef struct {
   int32_t general_waves;  /* library's shape) or both > 0 naming a built pair (else QN_ERR_UNSUPPORTED) */
   int32_t elem_store;     /* 0 or 1; many-token kernel: 1 stores outputs element by element instead of in 16-byte
                              pieces through LDS (same values) */
+  void* main_begin;       /* both NULL, or two hipEvent_t created with timing (the caller's, not retained): the main */
+  void* main_end;         /* streaming kernel is launched by hipExtLaunchKernel, which records them at that launch's
+                             own begin and end (a kernel trace's interval; events recorded on the stream around the
+                             call would also take in the dispatch). Events created with hipEventDisableSystemFence
+                             leave out the system-scope release the end event otherwise adds to the kernel.
+                             Measurement only: the results are the same. A call with several main launches (token
+                             blocks, sub-calls) leaves the last one's. One NULL and one not: QN_ERR_VALUE */
 } qn_linear_opts;
 
 /* Workspace bytes of nvfp4_lora_linear_opts with these options (host, pure); 0 if the options are invalid or name

@@ -56,7 +56,8 @@ class QnProj(ctypes.Structure):
 
 class QnLinearOpts(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("decode_kchunks", ctypes.c_int32), ("decode_depth", ctypes.c_int32),
-                ("general_rows", ctypes.c_int32), ("general_waves", ctypes.c_int32), ("elem_store", ctypes.c_int32)]
+                ("general_rows", ctypes.c_int32), ("general_waves", ctypes.c_int32), ("elem_store", ctypes.c_int32),
+                ("main_begin", ctypes.c_void_p), ("main_end", ctypes.c_void_p)]
 
 
 @dataclass
@@ -68,10 +69,12 @@ class LinearOpts:
     general_rows: int = 0
     general_waves: int = 0
     elem_store: int = 0
+    main_events: tuple = None  # (begin, end): timing events as objects with a `cuda_event` handle, each recorded once
 
     def to_c(self) -> QnLinearOpts:
+        ev = (None, None) if self.main_events is None else tuple(e.cuda_event for e in self.main_events)
         return QnLinearOpts(self.kernel, self.decode_kchunks, self.decode_depth, self.general_rows,
-                            self.general_waves, self.elem_store)
+                            self.general_waves, self.elem_store, ev[0], ev[1])
 
 
 def _load():
@@ -385,10 +388,18 @@ class LinearCall:
         self.ws = (workspace or Workspace(x.device)).get(need)
         self.ws_bytes = self.ws.numel()
 
-    def __call__(self, stream=None, phases: int = 0):
+    def __call__(self, stream=None, phases: int = 0, main_events=None):
+        """main_events: a (begin, end) pair of timing events (objects with a `cuda_event` handle, such as
+        torch.cuda.Event), each recorded once before so it exists, that this launch's main kernel records at its own
+        begin and end (qn_linear_opts main_begin / main_end)."""
+        ref = self.opts_ref
+        if main_events is not None:
+            oc = QnLinearOpts.from_buffer_copy(self.opts) if self.opts is not None else QnLinearOpts()
+            oc.main_begin, oc.main_end = main_events[0].cuda_event, main_events[1].cuda_event
+            ref = ctypes.byref(oc)
         _check(lib.nvfp4_lora_linear_opts(_ptr(self.x), self.m, self.k, self.x.stride(0),
                                           ctypes.byref(self.aqn.c) if self.aqn is not None else None, self.arr,
-                                          len(self.projs), self.epilogue | phases, self.opts_ref, _ptr(self.ws),
+                                          len(self.projs), self.epilogue | phases, ref, _ptr(self.ws),
                                           self.ws_bytes, _stream(stream)),
                "nvfp4_lora_linear")
         _keep_for(self.ws, stream)

@@ -28,6 +28,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <hip/hip_ext.h>
 #include <mutex>
 #include <type_traits>
 
@@ -2757,14 +2758,22 @@ inline bool gemv_default(const GemvCut& cut, int64_t nu, int64_t KT, int tmt, in
 }
 
 // Options of one call (qn_linear_opts, zero = defaults).
+// The caller's event pair of a call's main kernel (both null: none). With a pair the launch goes through
+// hipExtLaunchKernel, which records the two events at the launch's own begin and end, the interval a kernel trace
+// reports (an event recorded on the stream before and after a launch also takes in its dispatch).
+struct MainEvents {
+  hipEvent_t begin = nullptr, end = nullptr;
+};
+
 struct Opts {
   int kernel = QN_KERNEL_AUTO, nk = 0, depth = 0, rows = 0, waves = 0, elem = 0;
+  MainEvents ev;
 };
 
 inline bool opts_valid(const Opts& o) {
   return o.kernel >= QN_KERNEL_AUTO && o.kernel <= QN_KERNEL_WIDE && o.nk >= 0 && o.nk <= 64 &&
          (o.depth == 0 || o.depth == 2 || o.depth == 3) && o.rows >= 0 && o.waves >= 0 && (o.rows > 0) == (o.waves > 0) &&
-         (o.elem == 0 || o.elem == 1);
+         (o.elem == 0 || o.elem == 1) && (o.ev.begin == nullptr) == (o.ev.end == nullptr);
 }
 
 inline Opts opts_of(const qn_linear_opts* p) {
@@ -2776,6 +2785,8 @@ inline Opts opts_of(const qn_linear_opts* p) {
     o.rows = p->general_rows;
     o.waves = p->general_waves;
     o.elem = p->elem_store;
+    o.ev.begin = static_cast<hipEvent_t>(p->main_begin);
+    o.ev.end = static_cast<hipEvent_t>(p->main_end);
   }
   return o;
 }
@@ -3603,17 +3614,25 @@ __global__ void __launch_bounds__(kMWaves * kWave) k_gemm(GemmArgs g) {
   epilogue_pair(2);
 }
 
+// A call's main-kernel launch, with the caller's event pair (MainEvents) when there is one.
+template <typename K, typename A>
+inline void launch_main(K kernel, dim3 grid, dim3 block, hipStream_t s, const MainEvents& ev, const A& args) {
+  if (ev.begin) hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.begin, ev.end, 0, args);
+  else hipLaunchKernelGGL(kernel, grid, block, 0, s, args);
+}
+
 template <int TMT, int R, int W, bool SILU>
-void launch_linear(const LinearArgs& a, int64_t nwg, hipStream_t s) {
-  hipLaunchKernelGGL((k_linear<TMT, R, W, SILU>), dim3((unsigned)nwg), dim3(W * kWave), 0, s, a);
+void launch_linear(const LinearArgs& a, int64_t nwg, hipStream_t s, const MainEvents& ev) {
+  launch_main(k_linear<TMT, R, W, SILU>, dim3((unsigned)nwg), dim3(W * kWave), s, ev, a);
 }
 
 // The instantiated (TMT, R, W, SILU) combinations; returns false if the combination is not built. With a null
 // `a` it only answers whether the combination is built.
-bool dispatch_linear(int tmt, int R, int W, bool silu, const LinearArgs* a, int64_t nwg, hipStream_t s) {
+bool dispatch_linear(int tmt, int R, int W, bool silu, const LinearArgs* a, int64_t nwg, hipStream_t s,
+                     const MainEvents& ev = MainEvents{}) {
 #define QN_CASE(T_, R_, W_, S_)                         \
   if (tmt == T_ && R == R_ && W == W_ && silu == S_) { \
-    if (a) launch_linear<T_, R_, W_, S_>(*a, nwg, s);  \
+    if (a) launch_linear<T_, R_, W_, S_>(*a, nwg, s, ev); \
     return true;                                       \
   }
   QN_CASE(1, 1, 4, false) QN_CASE(1, 1, 8, false) QN_CASE(1, 1, 16, false)
@@ -3991,11 +4010,11 @@ qn_status run_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const
     ga.t_lds = silu && projs[0].r <= 32 && projs[1].r <= 32 ? 1 : 0;
     const dim3 grid((unsigned)(ga.nrb * ga.ntb)), block(kMWaves * kWave);
     if (mx) {
-      if (silu) hipLaunchKernelGGL((k_gemm<true, true>), grid, block, 0, s, ga);
-      else hipLaunchKernelGGL((k_gemm<false, true>), grid, block, 0, s, ga);
+      if (silu) launch_main(k_gemm<true, true>, grid, block, s, o.ev, ga);
+      else launch_main(k_gemm<false, true>, grid, block, s, o.ev, ga);
     } else {
-      if (silu) hipLaunchKernelGGL((k_gemm<true, false>), grid, block, 0, s, ga);
-      else hipLaunchKernelGGL((k_gemm<false, false>), grid, block, 0, s, ga);
+      if (silu) launch_main(k_gemm<true, false>, grid, block, s, o.ev, ga);
+      else launch_main(k_gemm<false, false>, grid, block, s, o.ev, ga);
     }
     return hipGetLastError() == hipSuccess ? QN_OK : QN_ERR_HIP;
   }
@@ -4041,7 +4060,7 @@ qn_status run_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const
     const bool gsh = aqn && fa.g_shared;
 #define QN_FGEMV(S_, A_, V_, G_)                                                                     \
   if (silu == S_ && (aqn != nullptr) == A_ && vec == V_ && gsh == G_) {                             \
-    hipLaunchKernelGGL((k_fgemv<S_, A_, V_, G_>), grid, block, 0, s, fa);                           \
+    launch_main(k_fgemv<S_, A_, V_, G_>, grid, block, s, o.ev, fa);                                 \
     return hipGetLastError() == hipSuccess ? QN_OK : QN_ERR_HIP;                                    \
   }
     QN_FGEMV(false, false, false, false) QN_FGEMV(false, false, true, false)
@@ -4073,7 +4092,7 @@ qn_status run_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const
     const dim3 grid((unsigned)(plan.cut.nbr * plan.cut.nk)), block(kWWaves * kWave);
 #define QN_WIDE(T_, S_, L_)                                                          \
   if (tmt == T_ && silu == S_) {                                                    \
-    hipLaunchKernelGGL((k_wgemv<T_, S_, L_>), grid, block, 0, s, wa);              \
+    launch_main(k_wgemv<T_, S_, L_>, grid, block, s, o.ev, wa);                    \
     return hipGetLastError() == hipSuccess ? QN_OK : QN_ERR_HIP;                    \
   }
     QN_WIDE(2, false, 3) QN_WIDE(2, true, 3) QN_WIDE(4, false, 3) QN_WIDE(4, true, 1)
@@ -4098,7 +4117,7 @@ qn_status run_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const
     const int depth = plan.depth;  // weight tiles in flight per wave
 #define QN_GEMV(T_, S_, D_)                                                            \
   if (tmt == T_ && silu == S_ && depth == D_) {                                       \
-    hipLaunchKernelGGL((k_gemv<T_, S_, D_>), grid, block, 0, s, ga);                  \
+    launch_main(k_gemv<T_, S_, D_>, grid, block, s, o.ev, ga);                        \
     return hipGetLastError() == hipSuccess ? QN_OK : QN_ERR_HIP;                       \
   }
     QN_GEMV(1, false, 2) QN_GEMV(1, false, 3) QN_GEMV(1, true, 2) QN_GEMV(1, true, 3)
@@ -4111,7 +4130,7 @@ qn_status run_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, const
     const int64_t mt = (m - t0) < kMaxTokensPerLaunch ? (m - t0) : kMaxTokensPerLaunch;
     int tmt, R, W;
     general_shape(mt, silu, nrg, KT, o, &tmt, &R, &W);  // (built: checked in validation)
-    dispatch_linear(tmt, R, W, silu, &la, ceil_div(nrg, R), s);
+    dispatch_linear(tmt, R, W, silu, &la, ceil_div(nrg, R), s, o.ev);
   }
   return hipGetLastError() == hipSuccess ? QN_OK : QN_ERR_HIP;
 }

@@ -198,6 +198,18 @@ def test_linear_options_validation(qn):
         assert call(4, o) == qn.QN_ERR_VALUE, o
         oc = o.to_c()
         assert L.nvfp4_lora_linear_workspace_opts(4, 128, arr, 1, ctypes.byref(oc)) == 0, o
+    # the main kernel's event pair: both or neither (nothing is recorded before the options are checked), and it
+    # does not change the workspace
+    for begin, end in ((256, None), (None, 256)):
+        oc = qn.LinearOpts().to_c()
+        oc.main_begin, oc.main_end = begin, end
+        assert L.nvfp4_lora_linear_workspace_opts(4, 128, arr, 1, ctypes.byref(oc)) == 0
+        assert L.nvfp4_lora_linear_opts(fake, 4, 128, 128, None, arr, 1, 0, ctypes.byref(oc), P(1 << 20), 1 << 20,
+                                        None) == qn.QN_ERR_VALUE
+    oc = qn.LinearOpts().to_c()
+    oc.main_begin, oc.main_end = 256, 512
+    assert L.nvfp4_lora_linear_workspace_opts(4, 128, arr, 1, ctypes.byref(oc)) == L.nvfp4_lora_linear_workspace(
+        4, 128, arr, 1)
     assert call(64, qn.LinearOpts(kernel=qn.KERNEL_DECODE)) == qn.QN_ERR_UNSUPPORTED  # decode kernel: m <= 32
     assert call(100, qn.LinearOpts(kernel=qn.KERNEL_MANY)) == qn.QN_ERR_UNSUPPORTED  # MFMA kernel: m > 128
     assert call(16, qn.LinearOpts(kernel=qn.KERNEL_WIDE)) == qn.QN_ERR_UNSUPPORTED  # 17 <= m <= 64

@@ -559,6 +559,23 @@ def test_linear_many_tokens_row_scales(qn):
         assert np.abs(y[t] - ref[t]).max() <= LINEAR_TOL * np.abs(ref[t]).max(), t
 
 
+@pytest.mark.parametrize("m,n,k,kernel", [(16, 512, 2048, "AUTO"), (8, 128, 256, "FUSED"), (16, 96, 256, "GENERAL"),
+                                          (40, 256, 1024, "WIDE"), (300, 256, 512, "AUTO")])
+def test_linear_main_kernel_events(qn, m, n, k, kernel):
+    """A call whose main kernel records the caller's event pair (qn_linear_opts main_begin / main_end, a launch
+    through hipExtLaunchKernel, for timing) gives the same bits as the same call without it, on the decode, fused,
+    general, 17-64-token and many-token kernels, and the pair spans a positive time."""
+    c = Case(m, [n], k, seed=13)
+    kid = getattr(qn, "KERNEL_" + kernel)
+    ref = c.gpu(qn, opts=qn.LinearOpts(kernel=kid))[0].clone()
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    for e in ev:
+        e.record()  # each event exists before the launch records it
+    got = c.gpu(qn, opts=qn.LinearOpts(kernel=kid, main_events=ev))[0]
+    assert torch.equal(ref, got)
+    assert ev[0].elapsed_time(ev[1]) > 0.0
+
+
 def test_linear_deterministic(qn):
     c = Case(16, [512], 2048, seed=11)
     a = c.gpu(qn)[0].clone()
