@@ -14,7 +14,8 @@ from typing import Optional, Sequence
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libqerl_nvfp4.so")
+# QERL_NVFP4_LIB: another build of this library to load instead (the sanitizer test's host-only build)
+LIB_PATH = os.environ.get("QERL_NVFP4_LIB") or os.path.join(_HERE, "libqerl_nvfp4.so")
 
 QN_OK, QN_ERR_NULL, QN_ERR_SHAPE, QN_ERR_ALIGN, QN_ERR_VALUE, QN_ERR_WORKSPACE, QN_ERR_UNSUPPORTED, QN_ERR_HIP = range(8)
 LAYOUT_ROWMAJOR, LAYOUT_TILED = 0, 1

@@ -27,15 +27,27 @@ def build(force: bool = False) -> str:
     return _LIB
 
 
+# the same source built with AddressSanitizer and UndefinedBehaviorSanitizer (the sanitizer test loads it in a
+# process started with the ASan runtime preloaded, through QERL_ORACLE_LIB)
+SANITIZE_FLAGS = ["-std=c++17", "-O1", "-g", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+                  "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
+
+
+def build_sanitized(out: str) -> str:
+    subprocess.check_call(["g++", *SANITIZE_FLAGS, _SRC, "-o", out])
+    return out
+
+
 _lib = None
 
 
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        path = os.environ.get("QERL_ORACLE_LIB") or _LIB
+        if path == _LIB and not os.path.exists(_LIB):
             build()
-        L = ctypes.CDLL(_LIB)
+        L = ctypes.CDLL(path)
         P, i64, i32, dbl, f32, u16, u64 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double,
                                            ctypes.c_float, ctypes.c_uint16, ctypes.c_uint64)
         sig = {
