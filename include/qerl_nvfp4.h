@@ -225,8 +225,8 @@ qn_status mxfp4_lora_linear(const uint16_t* x, int64_t m, int64_t k, int64_t ldx
                             const qn_proj* projs, int32_t nproj, int32_t epilogue, void* workspace,
                             size_t workspace_bytes, void* stream);
 
-/* Kernel choice for nvfp4_lora_linear_opts. A call runs one of three streaming kernels; the library picks one from
- * the token count and the shapes (QN_KERNEL_AUTO, what nvfp4_lora_linear does). Naming another one runs the same
+/* Kernel choice for nvfp4_lora_linear_opts. A call runs one of the streaming kernels below; the library picks one
+ * from the token count and the shapes (QN_KERNEL_AUTO, what nvfp4_lora_linear does). Naming another one runs the same
  * computation, to the same accuracy bound, on that kernel: for checks of each kernel on the same inputs and for
  * timing them side by side. */
 typedef enum {
