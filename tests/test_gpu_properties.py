@@ -8,6 +8,7 @@
 - split-k invariance: the decode kernels' k-chunk counts change only the order of the f32 partial sums.
 - row independence: each row of a batch equals the call on that row alone, up to f32 summation order (different
   batch sizes may take different kernels and cuts; on the cases here the rows came out bit-identical).
+- special cases, bit for bit: sigma = 0 is the plain RMSNorm whatever the noise; B = 0 is lambda = 0.
 """
 import numpy as np
 import pytest
@@ -89,3 +90,25 @@ def test_rows_match_single_token_calls(qn, m, n, k):
         torch.cuda.synchronize()
         err = float((y1[0] - ys[r]).abs().max() / ys[r].abs().max())
         assert err <= SUM_ORDER_TOL, (r, err)
+
+
+def test_zero_sigma_ignores_the_noise(qn):
+    """sigma = 0 is the plain RMSNorm whatever noise is given: the standalone norm and the fused prologue give the
+    bits they give without noise."""
+    c = Case(16, [256], 1024, seed=25, aqn=True, sigma=0.0)
+    x, g, z = dev_bf16(c.x), dev_bf16(c.gamma), dev_f32(c.noise)
+    assert torch.equal(qn.aqn_rmsnorm(x, g, z, 0.0, 1e-6).view(torch.int16),
+                       qn.aqn_rmsnorm(x, g, None, 0.0, 1e-6).view(torch.int16))
+    y = c.gpu(qn)[0].clone()
+    c.noise = np.zeros_like(c.noise)
+    assert torch.equal(c.gpu(qn)[0], y)
+
+
+@pytest.mark.parametrize("m", [16, 300])
+def test_zero_adapter_is_the_base(qn, m):
+    """B = 0 gives the bits of lambda = 0: the LoRA term adds exactly zero."""
+    c = Case(m, [256], 512, seed=26, aqn=True)
+    c.B = [np.zeros_like(b) for b in c.B]
+    y = c.gpu(qn)[0].clone()
+    c.lam = 0.0
+    assert torch.equal(c.gpu(qn)[0], y)
