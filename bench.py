@@ -617,7 +617,8 @@ def main():
     x = bf16_dev(synth.normal_bf16(synth.seed_for(2, 0, "x"), (m, shape.hidden)), dev)
     bound = [L.bind(x, ws) for L in layers]
     stream = torch.cuda.current_stream()
-    sampled = [i for i in range(args.steps) if i % args.event_every == 0]
+    # every n-th timed step, the first n - 1 skipped (step 0 follows the synchronisation that opens the timed region)
+    sampled = [i for i in range(args.steps) if i % args.event_every == args.event_every - 1]
     ev = launch_event_pairs(sampled, stream)
     timed = {"on": False}
 

@@ -32,7 +32,7 @@ def test_decode_line():
     assert d["config"]["workload"] and d["config"]["global_batch"] == 16
     rf = d["roofline"]
     assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
-    assert rf["event_samples"] == 4
+    assert rf["event_samples"] == 4  # steps 1, 3, 5, 7
     # the kernel's own interval: shorter than the step, and the achieved rate below the peak
     assert 0 < rf["launch_us_events"] < d["ms_per_step"] * 1e3
     assert rf["achieved"] == pytest.approx(rf["bytes_per_launch"] / (rf["launch_us_events"] * 1e-6) / 1e9)
